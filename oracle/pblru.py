@@ -1,0 +1,280 @@
+"""PB-LRU replacement state of one layer group (oracle; test infrastructure only).
+
+Source: UlaCache summary (paper-daily.com, "UlaCache: Unified Logical
+Addressing for Sparse LLM Serving").
+
+* Section 2 (unified logical addresses): every KV entry has a fixed logical
+  address; a mapping table records the GPU slot or CPU slot holding it; a move
+  changes only the mapping. In DP mode a GPU has one GPU pool and one CPU pool,
+  and an entry lives in exactly one of them, never both. Layers that share a
+  selection do the lookup and de-duplication once per group.
+* Section 3 (PB-LRU): every slot accessed in the same scheduling round goes
+  into the same bucket; each layer group keeps a ring of recent buckets and a
+  cold bucket; each round the current bucket advances by one and whatever is
+  left in the bucket about to be reused moves to cold (labels only, no data
+  moves); victims are free slots first, then the cold bucket, then the ring
+  buckets from oldest to newest, never the current bucket. Data moves first,
+  then the mapping is updated and completion is signalled.
+
+Readings where the pages are silent (each restated where it is used):
+
+* a scheduling round is one ``step`` call of one group; the ring advances at
+  the start of the step, before hits are marked; ``cur`` starts at 0;
+* de-duplication keeps the first occurrence in row-major (set, index) order;
+  ``-1`` entries are padding; hits and misses are counted per unique entry;
+* inside a bucket victims are taken in ascending slot order; ring buckets are
+  visited from ``cur+1`` (oldest) to ``cur-1`` (newest), modulo the ring;
+* the i-th miss (in unique order) takes the i-th victim; the victim's rows go
+  to the host slot that the miss vacated (a swap), or that host slot becomes
+  free when the victim slot was free;
+* slots loaded by the step, like hits, join the current bucket;
+* an append takes the lowest free GPU slot (joining the cold bucket), else the
+  lowest free host slot; appends never evict;
+* more unique entries than GPU slots is a capacity error and changes nothing;
+* the completion signal is a per-group step counter ``flag``.
+
+The canonical state compared with the engine after every step: ``map``
+(``s`` = GPU slot s, ``0x80000000 | h`` = host slot h, ``0xFFFFFFFF`` = never
+appended), the owners ``gown``/``hown`` (-1 = empty), the bucket bitsets
+(free, cold, ring[0..B-1]; slot s is bit ``s & 31`` of word ``s >> 5``),
+``cur``, ``flag`` and the step statistics.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+ABSENT = np.uint32(0xFFFFFFFF)
+HOST_BIT = np.uint32(0x80000000)
+
+
+class OracleError(Exception):
+    """An error the engine must report with the same name; state is unchanged."""
+
+    def __init__(self, name: str, msg: str = ""):
+        super().__init__(f"{name}: {msg}" if msg else name)
+        self.name = name
+
+
+@dataclass
+class StepStats:
+    unique: int = 0
+    hits: int = 0
+    misses: int = 0
+    evictions: int = 0
+    from_free: int = 0
+    invalid: int = 0
+
+    def as_tuple(self):
+        return (self.unique, self.hits, self.misses, self.evictions, self.from_free, self.invalid)
+
+
+def pack_bits(mask: np.ndarray) -> np.ndarray:
+    """Bool [P] -> uint32 [ceil(P/32)], slot s = bit (s & 31) of word (s >> 5)."""
+    P = mask.size
+    W = (P + 31) // 32
+    b = np.packbits(np.asarray(mask, dtype=bool), bitorder="little")
+    b = np.concatenate([b, np.zeros(W * 4 - b.size, dtype=np.uint8)])
+    return b.view("<u4").astype(np.uint32)
+
+
+class PBLRUGroup:
+    """The state of one layer group: map, owners, buckets and (optionally) pools."""
+
+    def __init__(self, N: int, P: int, H: int, B: int, layers: int, row_bytes: int,
+                 full_data: bool = True):
+        if B < 1 or P < 1 or H < 0 or N < 1 or layers < 1:
+            raise OracleError("EINVAL", "bad sizes")
+        self.N, self.P, self.H, self.B = N, P, H, B
+        self.layers, self.row_bytes = layers, row_bytes
+        self.full_data = full_data
+        # init: nothing appended, every GPU slot free, no bucket populated
+        self.map = np.full(N, ABSENT, dtype=np.uint32)
+        self.gown = np.full(P, -1, dtype=np.int32)
+        self.hown = np.full(H, -1, dtype=np.int32)
+        self.free = np.ones(P, dtype=bool)
+        self.cold = np.zeros(P, dtype=bool)
+        self.ring = np.zeros((B, P), dtype=bool)
+        self.cur = 0
+        self.flag = 0
+        self.last = StepStats()
+        self.last_lists = None     # (U, hit slots, misses, miss host slots, victims) of the last step
+        if full_data:
+            self.gpu = np.zeros((P, layers, row_bytes), dtype=np.uint8)
+            self.host = np.zeros((H, layers, row_bytes), dtype=np.uint8)
+
+    # ------------------------------------------------------------------
+    def append(self, las: np.ndarray, rows: Optional[np.ndarray]) -> None:
+        """Make new logical entries resident (placement is the library's choice, section 2).
+
+        Reading: in list order, each entry takes the lowest free GPU slot (and
+        joins the cold bucket) if one exists, otherwise the lowest free host
+        slot; appends never evict. Taking the lowest remaining free slot one
+        entry at a time hands out the free slots in ascending order, so the
+        first min(n, #free) entries get the free GPU slots in ascending order
+        and the rest get the free host slots in ascending order.
+        """
+        las = np.asarray(las, dtype=np.int64).reshape(-1)
+        n = las.size
+        if n == 0:
+            return
+        if las.min() < 0 or las.max() >= self.N:
+            raise OracleError("ERANGE", "address out of range")
+        if np.unique(las).size != n:
+            raise OracleError("EDUP", "address repeated in one append")
+        if (self.map[las] != ABSENT).any():
+            raise OracleError("EDUP", "address already appended")
+        free_gpu = np.flatnonzero(self.free)
+        free_host = np.flatnonzero(self.hown == -1)
+        if n > free_gpu.size + free_host.size:
+            raise OracleError("EHOSTFULL", "no room for the append")
+        if self.full_data:
+            rows = np.asarray(rows, dtype=np.uint8).reshape(n, self.layers, self.row_bytes)
+        n_gpu = min(n, free_gpu.size)
+        s = free_gpu[:n_gpu]
+        la_g = las[:n_gpu]
+        self.map[la_g] = s.astype(np.uint32)
+        self.gown[s] = la_g
+        self.free[s] = False
+        self.cold[s] = True
+        h = free_host[: n - n_gpu]
+        la_h = las[n_gpu:]
+        self.map[la_h] = HOST_BIT | h.astype(np.uint32)
+        self.hown[h] = la_h
+        if self.full_data:
+            self.gpu[s] = rows[:n_gpu]
+            self.host[h] = rows[n_gpu:]
+
+    # ------------------------------------------------------------------
+    def step(self, sel: np.ndarray) -> StepStats:
+        """One scheduling round of this group over its selection sets."""
+        sel = np.asarray(sel, dtype=np.int64)
+        flat = sel.reshape(-1)
+        t = self.flag + 1
+
+        # S1 validate: -1 padding, else an appended address in [0, N)
+        valid = flat != -1
+        v = flat[valid]
+        if v.size and (v.min() < 0 or v.max() >= self.N):
+            raise OracleError("ERANGE", "selected address out of range")
+        if v.size and (self.map[v] == ABSENT).any():
+            raise OracleError("ERANGE", "selected address never appended")
+
+        # S2 de-duplicate once for the whole group (section 2): first occurrence
+        # in row-major order
+        _, first = np.unique(v, return_index=True)
+        U = v[np.sort(first)]
+        invalid = int(flat.size - v.size)
+
+        # S3 lookup through the mapping table (section 2)
+        loc = self.map[U]
+        on_host = (loc & HOST_BIT) != 0
+        hit_slots = loc[~on_host].astype(np.int64)
+        miss_la = U[on_host]
+        miss_h = (loc[on_host] & ~HOST_BIT).astype(np.int64)
+
+        # S4 capacity: the current bucket is never evicted, so every unique entry
+        # needs its own GPU slot (reading: an error that changes nothing)
+        if U.size > self.P:
+            raise OracleError("ECAPACITY", "more unique entries than GPU slots")
+
+        # S5 the current bucket advances one position; the survivors of the
+        # bucket about to be reused move to cold (labels only) (section 3)
+        self.cur = (self.cur + 1) % self.B
+        self.cold |= self.ring[self.cur]
+        self.ring[self.cur] = False
+
+        # S6 hit marking: a hit slot leaves its bucket and joins the current one
+        # (hit slots are distinct, so the order of these updates is immaterial)
+        self.cold[hit_slots] = False
+        self.ring[:, hit_slots] = False
+        self.ring[self.cur, hit_slots] = True
+
+        # S7 victims: free, then cold, then ring oldest -> newest, never current,
+        # ascending slot order inside each bucket (section 3)
+        order = [self.free, self.cold]
+        order += [self.ring[(self.cur + j) % self.B] for j in range(1, self.B)]
+        candidates = np.concatenate([np.flatnonzero(b) for b in order])
+        m = miss_la.size
+        victims = candidates[:m]
+        assert victims.size == m   # guaranteed by S4: |free|+|cold|+|other rings| >= P - |hits| >= m
+
+        # S8 move the data first (section 3): the missed rows come from the host,
+        # the victims' rows go to the host slot the miss vacated. Pairs are
+        # disjoint (distinct victims, distinct host slots), so the moves commute.
+        owners = self.gown[victims].astype(np.int64)
+        evict = owners != -1
+        if self.full_data:
+            tmp = self.gpu[victims].copy()
+            self.gpu[victims] = self.host[miss_h]
+            self.host[miss_h[evict]] = tmp[evict]
+
+        # S9 then update the mapping table and owners (section 3)
+        self.map[miss_la] = victims.astype(np.uint32)
+        self.gown[victims] = miss_la
+        self.map[owners[evict]] = HOST_BIT | miss_h[evict].astype(np.uint32)
+        self.hown[miss_h[evict]] = owners[evict]
+        self.hown[miss_h[~evict]] = -1
+        # the loaded slots join the current bucket
+        self.free[victims] = False
+        self.cold[victims] = False
+        self.ring[:, victims] = False
+        self.ring[self.cur, victims] = True
+
+        # S10 signal completion
+        self.flag = t
+        n_free = int((~evict).sum())
+        self.last = StepStats(unique=int(U.size), hits=int(hit_slots.size), misses=int(m),
+                              evictions=int(m - n_free), from_free=n_free, invalid=invalid)
+        self.last_lists = (U, hit_slots, miss_la, miss_h, victims)
+        return self.last
+
+    # ------------------------------------------------------------------
+    def gather(self, sel: np.ndarray, layer: int, step: Optional[int] = None) -> np.ndarray:
+        """Rows of one layer for every selected entry, uint8 [n_sets][k][row_bytes].
+
+        Attention reads the selected entries at their (new) GPU locations only
+        after the completion signal (section 3). Reading: ``-1`` gives a zero
+        row; an entry not GPU-resident, or a gather of a step that has not
+        completed, is an error.
+        """
+        if not self.full_data:
+            raise OracleError("EINVAL", "gather needs full-data mode")
+        if step is not None and step != self.flag:
+            raise OracleError("ENOTRESIDENT", "gather of a step that has not completed")
+        if not (0 <= layer < self.layers):
+            raise OracleError("EINVAL", "layer out of range")
+        sel = np.asarray(sel, dtype=np.int64)
+        out = np.zeros(sel.shape + (self.row_bytes,), dtype=np.uint8)
+        valid = sel != -1
+        la = sel[valid]
+        if la.size and (la.min() < 0 or la.max() >= self.N):
+            raise OracleError("ERANGE", "gathered address out of range")
+        loc = self.map[la]
+        if (loc & HOST_BIT).any():    # also catches ABSENT
+            raise OracleError("ENOTRESIDENT", "gathered entry is not on the GPU")
+        out[valid] = self.gpu[loc.astype(np.int64), layer]
+        return out
+
+    # ------------------------------------------------------------------
+    def bitsets(self) -> np.ndarray:
+        """uint32 [B+2][ceil(P/32)]: free, cold, ring[0], ..., ring[B-1]."""
+        return np.stack([pack_bits(self.free), pack_bits(self.cold)]
+                        + [pack_bits(self.ring[b]) for b in range(self.B)])
+
+    def export_state(self) -> dict:
+        return dict(map=self.map.copy(), gown=self.gown.copy(), hown=self.hown.copy(),
+                    bitsets=self.bitsets(), cur=int(self.cur), flag=int(self.flag),
+                    stats=self.last.as_tuple())
+
+    def read_row(self, la: int) -> np.ndarray:
+        """The stored rows [layers][row_bytes] of one entry, wherever it lives."""
+        loc = self.map[la]
+        if loc == ABSENT:
+            raise OracleError("ERANGE", "never appended")
+        if loc & HOST_BIT:
+            return self.host[int(loc & ~HOST_BIT)].copy()
+        return self.gpu[int(loc)].copy()

@@ -1,0 +1,85 @@
+"""PB-LRU oracle against the brute-force exact LRU (UlaCache summary, sections 3-4).
+
+* With a ring at least as long as the trace no bucket is ever folded, the
+  cold bucket holds only appended slots (stamp ``s - P``) and ring buckets
+  are visited oldest to newest with ascending slots inside: that is exactly
+  LRU with step-granular stamps and ascending-slot ties. The two must agree
+  bit for bit: mapping table, owners, victims and statistics after every step.
+* With a short ring the pages report a GPU hit rate within 0.1 percentage
+  point of exact LRU on replayed serving traces; the tiny 4 x 4096 workload
+  (ring of 4, seed 0) is checked against that bound.
+"""
+
+import numpy as np
+import pytest
+
+from oracle.exact_lru import ExactLRUGroup
+from oracle.pblru import PBLRUGroup
+from synth import Trace, preset
+import dataclasses
+
+from tracegen import padded_selections, tiny_workload
+
+
+def _run_both(trace, sels):
+    wl = trace.wl
+    pb = PBLRUGroup(trace.N, trace.P, trace.H, wl.ring, wl.layers, wl.row_bytes, full_data=False)
+    lru = ExactLRUGroup(trace.N, trace.P, trace.H)
+    load = trace.initial_load_order()
+    pb.append(load, None)
+    lru.append(load)
+    for t, sel in enumerate(sels, 1):
+        app = trace.appends(t)
+        pb.append(app, None)
+        lru.append(app)
+        pb.step(sel)
+        lru.step(sel)
+        yield t, pb, lru
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_long_ring_equals_exact_lru(seed):
+    wl = tiny_workload(seed)
+    wl = dataclasses.replace(wl, ring=wl.steps + 1)
+    tr = Trace(wl)
+    for t, pb, lru in _run_both(tr, padded_selections(tr, 0, seed)):
+        assert list(pb.last_lists[4]) == lru.last_victims, f"step {t}"
+        assert pb.last.as_tuple() == lru.last
+        assert [int(x) for x in pb.map] == lru.map_array()
+        assert list(pb.gown) == lru.gown and list(pb.hown) == lru.hown
+
+
+def test_tiny_long_ring_equals_exact_lru():
+    wl = dataclasses.replace(preset("tiny_4x4k"), ring=9)
+    tr = Trace(wl)
+    for t, pb, lru in _run_both(tr, tr.selections(0)):
+        assert list(pb.last_lists[4]) == lru.last_victims
+        assert pb.last.as_tuple() == lru.last
+        assert [int(x) for x in pb.map] == lru.map_array()
+
+
+def _hit_rates(wl):
+    tr = Trace(wl)
+    hp = up = hl = ul = 0
+    for t, pb, lru in _run_both(tr, tr.selections(0)):
+        hp += pb.last.hits
+        up += pb.last.unique
+        hl += lru.last[1]
+        ul += lru.last[0]
+    return hp / up, hl / ul
+
+
+def test_tiny_hit_rate_within_a_tenth_of_a_point():
+    pb, lru = _hit_rates(preset("tiny_4x4k"))
+    assert abs(pb - lru) * 100 <= 0.1, (pb, lru)
+
+
+@pytest.mark.slow
+def test_tiny_hit_rate_spread_over_seeds():
+    """The PB-LRU - LRU hit-rate gap stays within the pages' 0.1 point on 20 seeds."""
+    gaps = []
+    for seed in range(20):
+        pb, lru = _hit_rates(dataclasses.replace(preset("tiny_4x4k"), seed=seed))
+        gaps.append((pb - lru) * 100)
+    print("PB-LRU minus exact-LRU hit rate (pp) over seeds 0-19:", np.round(gaps, 3))
+    assert max(abs(g) for g in gaps) <= 0.1

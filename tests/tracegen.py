@@ -1,0 +1,37 @@
+"""Small random workloads for the property and parity tests (inputs only)."""
+
+import numpy as np
+
+from synth import Trace, Workload
+
+
+def tiny_workload(seed: int, ring: int = None, steps: int = None, sets: int = None,
+                  layers: int = None, pool: int = None) -> Workload:
+    rng = np.random.default_rng([seed, 77])
+    R = int(rng.integers(1, 5))
+    ctx = int(rng.integers(40, 120))
+    k = int(rng.integers(4, ctx // 4))
+    steps = int(rng.integers(3, 10)) if steps is None else steps
+    appends = int(rng.integers(0, 3))
+    S = (1 if rng.random() < 0.6 else 3) if sets is None else sets
+    hist = R * ctx
+    if pool is None:   # at least one slot per unique entry a step can select
+        pool = int(rng.integers(R * S * k, hist + 1))
+    return Workload(
+        name=f"rand{seed}", requests=R, ctx_fixed=ctx, ctx_range=None, sets_per_request=S,
+        draft_keep=0.5, groups=1, layers=int(rng.integers(1, 4)) if layers is None else layers,
+        k=k, pool_frac=0.0, pool_slots=pool, ring=int(rng.integers(1, 6)) if ring is None else ring,
+        steps=steps, appends=appends, overlap=float(rng.choice([0.0, 0.5, 0.8])),
+        p_recent=0.5, window=16, row_bytes=64, seed=seed % 256)
+
+
+def with_padding(sel: np.ndarray, rng, frac: float = 0.1) -> np.ndarray:
+    """Replace a random share of entries by -1 padding."""
+    out = sel.copy()
+    out[rng.random(out.shape) < frac] = -1
+    return out
+
+
+def padded_selections(trace: Trace, g: int, seed: int, frac: float = 0.1):
+    rng = np.random.default_rng([seed, 99])
+    return [with_padding(s, rng, frac) for s in trace.selections(g)]
