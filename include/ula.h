@@ -1,0 +1,208 @@
+/*
+ * ula.h -- C ABI of the PB-LRU KV residency engine for MI355X (gfx950).
+ *
+ * The engine implements, for one GPU in data-parallel form, the residency
+ * layer described in "UlaCache: Unified Logical Addressing for Sparse LLM
+ * Serving" (paper-daily.com summary):
+ *
+ *  - Section 2: the serving engine allocates and selects KV entries by fixed
+ *    logical address only; the library decides whether the GPU pool or the
+ *    host pool holds each entry, moves it, and keeps a logical->physical
+ *    mapping table. In DP mode an entry lives in exactly one of the two
+ *    pools. Layers that share one sparse selection look up and de-duplicate
+ *    it once per layer group.
+ *  - Section 3: the shared GPU pool is managed by PB-LRU: a bucket per
+ *    scheduling round, a ring of recent buckets plus a cold bucket per layer
+ *    group, bucket bitmaps with summaries, victims taken from free slots, then
+ *    cold, then ring buckets oldest to newest, never the current bucket. Data
+ *    moves first, then the mapping is updated and completion is signalled;
+ *    readers wait for the signal.
+ *
+ * Conventions
+ *  - Every layer group g in [0, num_groups) has its own GPU pool of
+ *    gpu_slots slots, host pool of host_slots slots, mapping table over
+ *    logical addresses [0, logical_capacity), and replacement state.
+ *  - A slot holds the rows of all layers_per_group layers of one logical
+ *    entry; a row is row_bytes opaque bytes (FP8 latent, rope and scales in
+ *    the pages' model; never interpreted here).
+ *  - Mapping table encoding (uint32): s < 2^31 = GPU slot s; 0x80000000|h =
+ *    host slot h; 0xFFFFFFFF = never appended.
+ *  - Bucket bitsets: words of 32 bits, slot s is bit (s & 31) of word
+ *    (s >> 5); order free, cold, ring[0] .. ring[B-1].
+ *  - All calls that take a stream enqueue work on that HIP stream
+ *    (hipStream_t passed as uint64_t; 0 = null stream) and return without
+ *    waiting, unless stated otherwise. Device-side errors of an enqueued call
+ *    are reported by the next ula_sync.
+ *
+ * Ownership
+ *  - The caller allocates and owns the device workspace (ula_device_bytes
+ *    bytes, 256-byte aligned, device memory) and the pinned host pool
+ *    (ula_host_bytes bytes, page-locked and device-mapped, e.g. from
+ *    ula_host_alloc), the selection and output buffers and the streams. They
+ *    must outlive all work enqueued on them. The library owns only the
+ *    opaque context and the layout inside the two buffers.
+ *
+ * Errors
+ *  - Every call returns ULA_OK (0) or a negative code. Errors detected on the
+ *    host are returned at once and change nothing. Errors detected on the
+ *    device during an enqueued step or gather are latched per group; the
+ *    remaining kernels of that call exit before changing any state, the next
+ *    ula_sync returns the code and the context becomes unusable (ULA_ESTATE)
+ *    for every call but ula_export_state, ula_sync and ula_destroy.
+ *  - ULA_ECAPACITY is detected before any state changes, so an exported state
+ *    after it is the state before the failed step.
+ *
+ * Threading: a context belongs to one host thread. Groups are independent and
+ * may be driven on different streams; calls on one group must be ordered.
+ */
+#ifndef ULA_H
+#define ULA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ULA_OK = 0,
+  ULA_EINVAL = -1,       /* bad argument or configuration */
+  ULA_ERANGE = -2,       /* logical address outside [0, N) or never appended */
+  ULA_EDUP = -3,         /* append of an address already appended, or twice in one call */
+  ULA_EHOSTFULL = -4,    /* no free GPU or host slot left for an append */
+  ULA_ECAPACITY = -5,    /* a step selects more distinct entries than the GPU pool holds */
+  ULA_ENOTRESIDENT = -6, /* gather before its step completed, or of an entry not on the GPU */
+  ULA_ESTATE = -7,       /* the context was poisoned by an earlier device error */
+  ULA_EHIP = -8          /* a HIP runtime call failed; ula_strerror gives its text */
+};
+
+typedef struct ula_ctx ula_ctx;
+
+typedef struct {
+  int32_t num_groups;        /* layer groups, each with its own pools and state, >= 1 */
+  int32_t layers_per_group;  /* layers sharing one selection, >= 1 */
+  int32_t row_bytes;         /* bytes per row, multiple of 16, <= 4096 */
+  int32_t ring_buckets;      /* B >= 1 ring buckets (plus one cold and one free bucket) */
+  int32_t logical_capacity;  /* N: logical addresses [0, N), 1 <= N < 2^31 */
+  int32_t gpu_slots;         /* P >= 1 GPU slots per group */
+  int32_t host_slots;        /* H >= 0 host slots per group, P + H < 2^31 */
+  int32_t max_sets;          /* most selection sets per step */
+  int32_t max_k;             /* most entries per selection set; max_sets * max_k < 2^31 */
+  int32_t max_append;        /* most addresses staged per append chunk, >= 1 */
+} ula_config;
+
+typedef struct {
+  int64_t unique;     /* distinct valid addresses selected by the step */
+  int64_t hits;       /* of those, already on the GPU */
+  int64_t misses;     /* of those, brought in from the host pool */
+  int64_t evictions;  /* misses whose victim slot held an entry (sent to the host) */
+  int64_t from_free;  /* misses that took a free GPU slot */
+  int64_t invalid;    /* -1 padding entries in the selection */
+} ula_step_stats;
+
+typedef struct {             /* caller-allocated host buffers filled by ula_export_state */
+  uint32_t* map;             /* [N] mapping table */
+  int32_t* gown;             /* [P] owner logical address of each GPU slot, -1 = empty */
+  int32_t* hown;             /* [H] owner logical address of each host slot, -1 = empty */
+  uint32_t* bitsets;         /* [(B + 2)][ceil(P / 32)]: free, cold, ring[0..B-1] */
+  int32_t cur;               /* current ring bucket */
+  int64_t flag;              /* last completed step (completion counter) */
+  ula_step_stats last;       /* statistics of that step */
+} ula_state_host;
+
+/* Bytes of device workspace / pinned host pool a configuration needs; 0 for an
+ * invalid configuration. Pure host functions (no device is touched). */
+size_t ula_device_bytes(const ula_config* cfg);
+size_t ula_host_bytes(const ula_config* cfg);
+
+/* Lay out the workspace, initialise every group (nothing appended, all GPU slots
+ * free, all host slots free, cur = 0, flag = 0) on `stream`, and return a context.
+ * dev_ws: device memory of ula_device_bytes(cfg) bytes, 256-byte aligned.
+ * host_pinned: pinned, device-mapped host memory of ula_host_bytes(cfg) bytes
+ * (may be NULL when host_slots == 0). Errors: ULA_EINVAL, ULA_EHIP. */
+int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t stream,
+             ula_ctx** out);
+
+/* Append n new logical entries to group g (section 2: the library decides the
+ * pool). In list order each entry takes the lowest free GPU slot (joining the
+ * cold bucket) or, when none is free, the lowest free host slot; appends never
+ * evict. la_host: n addresses in host memory. rows: n x layers_per_group x
+ * row_bytes bytes, packed, in device memory (rows_on_device = 1) or host memory
+ * (rows_on_device = 0); rows must stay valid until the stream reaches the call.
+ * Validated on the host first: ULA_EINVAL (bad g or n < 0), ULA_ERANGE (address
+ * outside [0, N)), ULA_EDUP (already appended or repeated), ULA_EHOSTFULL (not
+ * enough free slots in total); nothing changes on error. */
+int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host,
+               const void* rows, int32_t rows_on_device, uint64_t stream);
+
+/* One decode step (one scheduling round) of group g over n_sets x k selected
+ * addresses (device memory, row-major, -1 = padding), section 3: de-duplicate
+ * (first occurrence in row-major order) and look up once for the group; advance
+ * the ring and fold the reused bucket into cold; move hits into the current
+ * bucket; pick one victim per miss (free, cold, ring oldest -> newest, ascending
+ * slot inside a bucket, never the current bucket); swap the missed rows in from
+ * the host pool and the victims' rows out to the host slots they vacate; then
+ * update the mapping table and owners and raise the completion counter to the
+ * step number. Enqueued on `stream` with no host synchronisation.
+ * Host errors: ULA_EINVAL (bad g, n_sets > max_sets, k > max_k, negative sizes),
+ * ULA_ESTATE. Device errors (reported by ula_sync): ULA_ERANGE, ULA_ECAPACITY. */
+int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
+             uint64_t stream);
+
+/* Gather layer `layer` of every selected entry of group g into out_dev
+ * (device memory, n_sets x k x row_bytes bytes, packed; a -1 entry gives a zero
+ * row). Reads the GPU pool through the mapping table after checking that the
+ * group's completion counter equals the group's last step (section 3: readers
+ * wait for the signal); call it once per layer of the group. On a stream other
+ * than the step's, order it after the step first (event, or a stream wait on
+ * ula_flag_address reaching the step number).
+ * Host errors: ULA_EINVAL, ULA_ESTATE, ULA_ENOTRESIDENT (no step yet).
+ * Device errors (reported by ula_sync): ULA_ENOTRESIDENT (counter not reached,
+ * or an entry not on the GPU), ULA_ERANGE. */
+int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32_t k,
+               const int32_t* sel_dev, void* out_dev, uint64_t stream);
+
+/* Wait for `stream`, then report the first latched device error of any group
+ * (poisoning the context) or ULA_OK. per_group_out (nullable, num_groups
+ * entries) receives each group's last step statistics. */
+int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out);
+
+/* Copy group g's canonical state into caller host buffers (synchronises the
+ * device first). Works on a poisoned context. */
+int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out);
+
+/* Read back the stored rows (all layers, layers_per_group x row_bytes bytes
+ * each) of n appended entries of group g into host memory, from whichever pool
+ * holds them (synchronises the device). ULA_ERANGE if an address was never
+ * appended. */
+int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host,
+                  void* out_host);
+
+/* Device address of group g's completion counter (int64, equals the last
+ * completed step), for hipStreamWaitValue64 on another stream. */
+int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr);
+
+/* Per-phase timing of the last step of group g, in milliseconds, when enabled
+ * with ula_set_timing: [0] lookup + de-duplication, [1] fold + hit marking,
+ * [2] victim selection, [3] row swap over the host link, [4] commit + signal.
+ * ula_read_timing synchronises on the step's last event. */
+int ula_set_timing(ula_ctx* ctx, int32_t enable);
+int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out5);
+
+/* Release the context (not the caller's buffers). Waits for no stream. */
+int ula_destroy(ula_ctx* ctx);
+
+/* Text of an error code (also the last HIP error text for ULA_EHIP). */
+const char* ula_strerror(int code);
+
+/* Pinned, device-mapped host memory for the host pool (hipHostMalloc);
+ * NULL on failure. ula_host_free returns ULA_OK or ULA_EHIP. */
+void* ula_host_alloc(size_t bytes);
+int ula_host_free(void* p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULA_H */

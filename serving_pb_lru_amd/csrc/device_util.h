@@ -1,0 +1,91 @@
+// Wavefront and workgroup primitives for gfx950 (64-lane wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ula_internal.h"
+
+namespace ula {
+
+// 16 bytes moved as one vector access (global_load/store_dwordx4)
+typedef uint32_t vec4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Number of set bits of `mask` below this lane (the lane's rank among the
+// lanes whose ballot bit is set).
+__device__ __forceinline__ int rank_below(unsigned long long mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    int u = __shfl_up(v, d, kWave);
+    if (lane_id() >= d) v += u;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a whole workgroup of NT threads; `total` receives
+// the sum over the workgroup. `scratch` holds NT / 64 + 1 ints of LDS. Every thread
+// of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_sum(int v, int* scratch, int& total) {
+  constexpr int NW = NT / kWave;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  int inc = wave_inclusive_sum(v);
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < NW ? scratch[lane] : 0;
+    int wi = wave_inclusive_sum(w);
+    if (lane < NW) scratch[lane] = wi - w;   // exclusive wave offsets
+    if (lane == NW - 1) scratch[NW] = wi;    // total
+  }
+  __syncthreads();
+  int res = scratch[wave] + inc - v;
+  total = scratch[NW];
+  __syncthreads();
+  return res;
+}
+
+// Latch the first device error of a group; later kernels read it and exit.
+__device__ __forceinline__ void latch(Counters* c, int code) {
+  atomicCAS(&c->status, 0, code);
+}
+
+__device__ __forceinline__ int status_of(const Counters* c) {
+  return __hip_atomic_load(&c->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block-uniform error check for kernels that use workgroup barriers: every
+// thread of the workgroup sees the same answer.
+__device__ __forceinline__ bool block_failed(const Counters* c) {
+  __shared__ int s_status;
+  if (threadIdx.x == 0) s_status = status_of(c);
+  __syncthreads();
+  return s_status != 0;
+}
+
+__device__ __forceinline__ uint32_t* bucket_words(const GroupDev& g, int id) {
+  return id == kHostFreeId ? g.hbm : g.bm + (size_t)id * g.W;
+}
+__device__ __forceinline__ uint32_t* bucket_tcnt(const GroupDev& g, int id) {
+  return id == kHostFreeId ? g.htcnt : g.tcnt + (size_t)id * g.T;
+}
+__device__ __forceinline__ int bucket_nwords(const GroupDev& g, int id) {
+  return id == kHostFreeId ? g.WH : g.W;
+}
+__device__ __forceinline__ int bucket_ntiles(const GroupDev& g, int id) {
+  return id == kHostFreeId ? g.TH : g.T;
+}
+__device__ __forceinline__ int32_t* bucket_count(const GroupDev& g, int id) {
+  return id == kHostFreeId ? &g.ctr->hfree : &g.ctr->bcnt[id];
+}
+
+}  // namespace ula

@@ -1,0 +1,523 @@
+// Host runtime of the residency engine: configuration checks, workspace
+// layout, launch sequencing on the caller's stream, error latching and state
+// export. Implements the C ABI declared in include/ula.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "ula_internal.h"
+
+using namespace ula;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kStageSlots = 4;   // pinned staging buffers per group for appended addresses
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+thread_local std::string g_hip_error;
+
+int hip_fail(hipError_t e, const char* what) {
+  g_hip_error = std::string(what) + ": " + hipGetErrorString(e);
+  return ULA_EHIP;
+}
+
+#define HIP_TRY(expr)                                 \
+  do {                                                \
+    hipError_t e_ = (expr);                           \
+    if (e_ != hipSuccess) return hip_fail(e_, #expr); \
+  } while (0)
+
+struct Dims {
+  int64_t N, P, H, B, NB, W, T, WH, TH, Lg, row_bytes, slot_bytes;
+  int64_t maxU, maxBlk, maxItems, maxApp;
+};
+
+bool check_config(const ula_config* c, Dims* d) {
+  if (!c) return false;
+  if (c->num_groups < 1 || c->num_groups > 4096) return false;
+  if (c->layers_per_group < 1 || c->layers_per_group > 256) return false;
+  if (c->row_bytes < 16 || c->row_bytes > 4096 || c->row_bytes % 16) return false;
+  if (c->ring_buckets < 1 || c->ring_buckets > kMaxRing) return false;
+  if (c->logical_capacity < 1) return false;
+  if (c->gpu_slots < 1 || c->host_slots < 0) return false;
+  if ((int64_t)c->gpu_slots + c->host_slots >= (1ll << 31)) return false;
+  if (c->max_sets < 1 || c->max_k < 1 || c->max_append < 1) return false;
+  const int64_t nsel = (int64_t)c->max_sets * c->max_k;
+  if (nsel >= (1ll << 31)) return false;
+  d->N = c->logical_capacity;
+  d->P = c->gpu_slots;
+  d->H = c->host_slots;
+  d->B = c->ring_buckets;
+  d->NB = d->B + 2;
+  d->W = (d->P + 31) / 32;
+  d->T = (d->W + kTileWords - 1) / kTileWords;
+  d->WH = (d->H + 31) / 32;
+  d->TH = (d->WH + kTileWords - 1) / kTileWords;
+  d->Lg = c->layers_per_group;
+  d->row_bytes = c->row_bytes;
+  d->slot_bytes = d->Lg * d->row_bytes;
+  d->maxU = std::min<int64_t>(nsel, d->P);
+  d->maxBlk = (nsel + kScanBlock - 1) / kScanBlock;
+  d->maxApp = c->max_append;
+  d->maxItems = std::max<int64_t>(d->maxU, d->maxApp) + 2;
+  // 16-byte piece counts handled with 32-bit indices and FastDiv (< 2^31)
+  if (nsel * (d->row_bytes / 16) >= (1ll << 31)) return false;
+  if (d->maxU * (d->slot_bytes / 16) >= (1ll << 31)) return false;
+  if (d->maxApp * (d->slot_bytes / 16) >= (1ll << 31)) return false;
+  return true;
+}
+
+struct Layout {
+  size_t map, tag, gown, stamp, hown, bm, tcnt, hbm, htcnt, hits, mla, mh, vict, blk, items,
+      app_la, app_dst, app_rows, pool, group_bytes;
+  size_t counters_bytes, total;
+};
+
+Layout layout_of(const ula_config* c, const Dims& d) {
+  Layout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.map = take(4 * d.N);
+  L.tag = take(8 * d.N);
+  L.gown = take(4 * d.P);
+  L.stamp = take(4 * d.P);
+  L.hown = take(4 * d.H);
+  L.bm = take(4 * d.NB * d.W);
+  L.tcnt = take(4 * d.NB * d.T);
+  L.hbm = take(4 * d.WH);
+  L.htcnt = take(4 * d.TH);
+  L.hits = take(4 * d.maxU);
+  L.mla = take(4 * d.maxU);
+  L.mh = take(4 * d.maxU);
+  L.vict = take(4 * d.maxU);
+  L.blk = take(4 * 3 * d.maxBlk);
+  L.items = take(sizeof(SelItem) * d.maxItems);
+  L.app_la = take(4 * d.maxApp);
+  L.app_dst = take(4 * d.maxApp);
+  L.app_rows = take((size_t)d.maxApp * d.slot_bytes);
+  L.pool = take((size_t)d.P * d.slot_bytes);
+  L.group_bytes = o;
+  L.counters_bytes = align_up(sizeof(Counters) * c->num_groups);
+  L.total = L.counters_bytes + L.group_bytes * c->num_groups;
+  return L;
+}
+
+const char* kMessages[] = {
+    "ok",
+    "invalid argument or configuration",
+    "logical address out of range or never appended",
+    "logical address already appended or repeated in one append",
+    "no free GPU or host slot left for the append",
+    "a step selects more distinct entries than the GPU pool holds",
+    "gathered entry not resident on the GPU, or its step has not completed",
+    "context poisoned by an earlier device error",
+    "HIP runtime error",
+};
+
+}  // namespace
+
+struct GroupHost {
+  GroupDev d;
+  std::vector<uint64_t> appended;   // host mirror: which addresses were appended
+  int64_t n_appended = 0;
+  int64_t steps = 0;                // steps enqueued
+  int32_t* stage[kStageSlots] = {};
+  hipEvent_t stage_ev[kStageSlots] = {};
+  bool stage_used[kStageSlots] = {};
+  int stage_next = 0;
+  hipEvent_t ev[6] = {};
+};
+
+struct ula_ctx {
+  ula_config cfg;
+  Dims dims;
+  Layout lay;
+  uint8_t* dev = nullptr;
+  uint8_t* host = nullptr;
+  Counters* ctrs = nullptr;
+  std::vector<GroupHost> groups;
+  int poisoned = 0;
+  int timing = 0;
+};
+
+extern "C" {
+
+size_t ula_device_bytes(const ula_config* cfg) {
+  Dims d;
+  if (!check_config(cfg, &d)) return 0;
+  return layout_of(cfg, d).total;
+}
+
+size_t ula_host_bytes(const ula_config* cfg) {
+  Dims d;
+  if (!check_config(cfg, &d)) return 0;
+  return (size_t)cfg->num_groups * d.H * d.slot_bytes;
+}
+
+const char* ula_strerror(int code) {
+  if (code == ULA_EHIP && !g_hip_error.empty()) return g_hip_error.c_str();
+  if (code > 0 || code < ULA_EHIP) return "unknown error code";
+  return kMessages[-code];
+}
+
+void* ula_host_alloc(size_t bytes) {
+  void* p = nullptr;
+  if (hipHostMalloc(&p, bytes ? bytes : 1, hipHostMallocMapped) != hipSuccess) return nullptr;
+  return p;
+}
+
+int ula_host_free(void* p) {
+  if (!p) return ULA_OK;
+  HIP_TRY(hipHostFree(p));
+  return ULA_OK;
+}
+
+static void destroy_ctx(ula_ctx* ctx) {
+  for (auto& g : ctx->groups) {
+    for (int i = 0; i < kStageSlots; ++i) {
+      if (g.stage_ev[i]) (void)hipEventDestroy(g.stage_ev[i]);
+      if (g.stage[i]) (void)hipHostFree(g.stage[i]);
+    }
+    for (auto& e : g.ev)
+      if (e) (void)hipEventDestroy(e);
+  }
+  delete ctx;
+}
+
+int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t stream,
+             ula_ctx** out) {
+  if (!out) return ULA_EINVAL;
+  *out = nullptr;
+  Dims d;
+  if (!check_config(cfg, &d)) return ULA_EINVAL;
+  if (!dev_ws || ((uintptr_t)dev_ws % kAlign)) return ULA_EINVAL;
+  if (d.H > 0 && !host_pinned) return ULA_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  ula_ctx* ctx = new (std::nothrow) ula_ctx();
+  if (!ctx) return ULA_EINVAL;
+  ctx->cfg = *cfg;
+  ctx->dims = d;
+  ctx->lay = layout_of(cfg, d);
+  ctx->dev = static_cast<uint8_t*>(dev_ws);
+  ctx->ctrs = reinterpret_cast<Counters*>(ctx->dev);
+  uint8_t* hdev = nullptr;
+  if (host_pinned) {
+    void* p = nullptr;
+    hipError_t e = hipHostGetDevicePointer(&p, host_pinned, 0);
+    if (e != hipSuccess) {
+      delete ctx;
+      return hip_fail(e, "hipHostGetDevicePointer(host pool)");
+    }
+    hdev = static_cast<uint8_t*>(p);
+  }
+  ctx->host = hdev;
+  ctx->groups.resize(cfg->num_groups);
+  const Layout& L = ctx->lay;
+  int rc = ULA_OK;
+  for (int gi = 0; gi < cfg->num_groups && rc == ULA_OK; ++gi) {
+    GroupHost& gh = ctx->groups[gi];
+    uint8_t* b = ctx->dev + L.counters_bytes + (size_t)gi * L.group_bytes;
+    GroupDev& g = gh.d;
+    g.ctr = ctx->ctrs + gi;
+    g.map = reinterpret_cast<uint32_t*>(b + L.map);
+    g.tag = reinterpret_cast<unsigned long long*>(b + L.tag);
+    g.gown = reinterpret_cast<int32_t*>(b + L.gown);
+    g.stamp = reinterpret_cast<int32_t*>(b + L.stamp);
+    g.hown = reinterpret_cast<int32_t*>(b + L.hown);
+    g.bm = reinterpret_cast<uint32_t*>(b + L.bm);
+    g.tcnt = reinterpret_cast<uint32_t*>(b + L.tcnt);
+    g.hbm = reinterpret_cast<uint32_t*>(b + L.hbm);
+    g.htcnt = reinterpret_cast<uint32_t*>(b + L.htcnt);
+    g.hit_slots = reinterpret_cast<uint32_t*>(b + L.hits);
+    g.miss_la = reinterpret_cast<int32_t*>(b + L.mla);
+    g.miss_h = reinterpret_cast<uint32_t*>(b + L.mh);
+    g.victims = reinterpret_cast<uint32_t*>(b + L.vict);
+    g.blk = reinterpret_cast<uint32_t*>(b + L.blk);
+    g.items = reinterpret_cast<SelItem*>(b + L.items);
+    g.app_la = reinterpret_cast<int32_t*>(b + L.app_la);
+    g.app_dst = reinterpret_cast<uint32_t*>(b + L.app_dst);
+    g.app_rows = b + L.app_rows;
+    g.pool = b + L.pool;
+    g.host = hdev ? hdev + (size_t)gi * d.H * d.slot_bytes : nullptr;
+    g.N = (int32_t)d.N;
+    g.P = (int32_t)d.P;
+    g.H = (int32_t)d.H;
+    g.B = (int32_t)d.B;
+    g.NB = (int32_t)d.NB;
+    g.W = (int32_t)d.W;
+    g.T = (int32_t)d.T;
+    g.WH = (int32_t)d.WH;
+    g.TH = (int32_t)d.TH;
+    g.Lg = (int32_t)d.Lg;
+    g.row_bytes = (int32_t)d.row_bytes;
+    g.slot_bytes = (int32_t)d.slot_bytes;
+    gh.appended.assign((d.N + 63) / 64, 0);
+
+    hipError_t e = hipSuccess;
+    if (e == hipSuccess) e = launch_init_counters(g.ctr, g.P, g.H, s);
+    if (e == hipSuccess) e = launch_fill_u32(g.map, d.N, kAbsent, s);
+    if (e == hipSuccess) e = launch_fill_u64(g.tag, d.N, 0ull, s);
+    if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.gown), d.P, 0xFFFFFFFFu, s);
+    if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.stamp), d.P, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.hown), d.H, 0xFFFFFFFFu, s);
+    if (e == hipSuccess) e = launch_fill_u32(g.bm, d.NB * d.W, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32(g.tcnt, d.NB * d.T, 0u, s);
+    if (e == hipSuccess) e = launch_init_bitmap(g.bm + kFree * d.W, g.W, d.P, g.tcnt + kFree * d.T, g.T, s);
+    if (e == hipSuccess) e = launch_init_bitmap(g.hbm, g.WH, d.H, g.htcnt, g.TH, s);
+    for (int i = 0; i < kStageSlots && e == hipSuccess; ++i) {
+      e = hipHostMalloc(reinterpret_cast<void**>(&gh.stage[i]), sizeof(int32_t) * d.maxApp,
+                        hipHostMallocDefault);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.stage_ev[i], hipEventDisableTiming);
+    }
+    for (int i = 0; i < 6 && e == hipSuccess; ++i) e = hipEventCreate(&gh.ev[i]);
+    if (e != hipSuccess) rc = hip_fail(e, "ula_init");
+  }
+  if (rc == ULA_OK) {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) rc = hip_fail(e, "hipStreamSynchronize(init)");
+  }
+  if (rc != ULA_OK) {
+    destroy_ctx(ctx);
+    return rc;
+  }
+  *out = ctx;
+  return ULA_OK;
+}
+
+int ula_destroy(ula_ctx* ctx) {
+  if (!ctx) return ULA_EINVAL;
+  destroy_ctx(ctx);
+  return ULA_OK;
+}
+
+int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, const void* rows,
+               int32_t rows_on_device, uint64_t stream) {
+  if (!ctx) return ULA_EINVAL;
+  if (ctx->poisoned) return ULA_ESTATE;
+  if (group < 0 || group >= ctx->cfg.num_groups || n < 0) return ULA_EINVAL;
+  if (n == 0) return ULA_OK;
+  if (!la_host || !rows) return ULA_EINVAL;
+  GroupHost& gh = ctx->groups[group];
+  const Dims& d = ctx->dims;
+  // validate the whole batch first; nothing changes on error
+  for (int32_t i = 0; i < n; ++i)
+    if (la_host[i] < 0 || la_host[i] >= d.N) return ULA_ERANGE;
+  {
+    std::vector<int32_t> sorted(la_host, la_host + n);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return ULA_EDUP;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t la = (uint32_t)la_host[i];
+    if (gh.appended[la >> 6] >> (la & 63) & 1ull) return ULA_EDUP;
+  }
+  if (gh.n_appended + n > d.P + d.H) return ULA_EHOSTFULL;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const GroupDev& g = gh.d;
+  for (int32_t off = 0; off < n; off += (int32_t)d.maxApp) {
+    const int32_t cnt = (int32_t)std::min<int64_t>(n - off, d.maxApp);
+    // addresses go through a pinned staging slot so the copy is truly asynchronous
+    const int k = gh.stage_next;
+    gh.stage_next = (k + 1) % kStageSlots;
+    if (gh.stage_used[k]) HIP_TRY(hipEventSynchronize(gh.stage_ev[k]));
+    gh.stage_used[k] = true;
+    std::memcpy(gh.stage[k], la_host + off, sizeof(int32_t) * cnt);
+    HIP_TRY(hipMemcpyAsync(g.app_la, gh.stage[k], sizeof(int32_t) * cnt, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipEventRecord(gh.stage_ev[k], s));
+    const uint8_t* src = static_cast<const uint8_t*>(rows) + (size_t)off * d.slot_bytes;
+    if (!rows_on_device) {
+      HIP_TRY(hipMemcpyAsync(g.app_rows, src, (size_t)cnt * d.slot_bytes, hipMemcpyHostToDevice, s));
+      src = g.app_rows;
+    }
+    PlanArgs a{};
+    a.mode = kPlanAppend;
+    a.n = cnt;
+    a.norder = 2;
+    a.dest = kCold;
+    a.order[0] = kFree;
+    a.order[1] = kHostFreeId;
+    HIP_TRY(launch_plan(g, a, s));
+    HIP_TRY(launch_extract(g, kPlanAppend, kCold, 0u, cnt, s));
+    HIP_TRY(launch_place(g, cnt, src, s));
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t la = (uint32_t)la_host[i];
+    gh.appended[la >> 6] |= 1ull << (la & 63);
+  }
+  gh.n_appended += n;
+  return ULA_OK;
+}
+
+int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
+             uint64_t stream) {
+  if (!ctx) return ULA_EINVAL;
+  if (ctx->poisoned) return ULA_ESTATE;
+  if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
+  if (n_sets < 0 || k < 0 || n_sets > ctx->cfg.max_sets || k > ctx->cfg.max_k) return ULA_EINVAL;
+  const int32_t n = n_sets * k;
+  if (n > 0 && !sel_dev) return ULA_EINVAL;
+  GroupHost& gh = ctx->groups[group];
+  const GroupDev& g = gh.d;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t t = gh.steps + 1;
+  const int32_t cur = (int32_t)(t % ctx->dims.B);
+  const int32_t nblk = (n + kScanBlock - 1) / kScanBlock;
+  const bool tm = ctx->timing != 0;
+
+  if (tm) HIP_TRY(hipEventRecord(gh.ev[0], s));
+  HIP_TRY(launch_tag(g, sel_dev, n, (uint32_t)t, s));
+  HIP_TRY(launch_count(g, sel_dev, n, (uint32_t)t, s));
+  HIP_TRY(launch_scan(g, nblk, s));
+  if (tm) HIP_TRY(hipEventRecord(gh.ev[1], s));
+  HIP_TRY(launch_fold(g, cur, s));
+  HIP_TRY(launch_compact(g, sel_dev, n, (uint32_t)t, cur, s));
+  if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
+  PlanArgs a{};
+  a.mode = kPlanStep;
+  a.dest = ring_id(cur);
+  a.order[0] = kFree;
+  a.order[1] = kCold;
+  a.norder = 2;
+  for (int j = 1; j < ctx->dims.B; ++j) a.order[a.norder++] = (int8_t)ring_id((cur + j) % ctx->dims.B);
+  HIP_TRY(launch_plan(g, a, s));
+  const int32_t max_pairs = (int32_t)std::min<int64_t>(n, ctx->dims.maxU);
+  HIP_TRY(launch_extract(g, kPlanStep, a.dest, (uint32_t)t, max_pairs, s));
+  if (tm) HIP_TRY(hipEventRecord(gh.ev[3], s));
+  HIP_TRY(launch_swap(g, max_pairs, s));
+  if (tm) HIP_TRY(hipEventRecord(gh.ev[4], s));
+  HIP_TRY(launch_commit(g, (long long)t, s));
+  if (tm) HIP_TRY(hipEventRecord(gh.ev[5], s));
+  gh.steps = t;
+  return ULA_OK;
+}
+
+int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32_t k,
+               const int32_t* sel_dev, void* out_dev, uint64_t stream) {
+  if (!ctx) return ULA_EINVAL;
+  if (ctx->poisoned) return ULA_ESTATE;
+  if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
+  if (layer < 0 || layer >= ctx->cfg.layers_per_group) return ULA_EINVAL;
+  if (n_sets < 0 || k < 0 || n_sets > ctx->cfg.max_sets || k > ctx->cfg.max_k) return ULA_EINVAL;
+  const int32_t n = n_sets * k;
+  if (n > 0 && (!sel_dev || !out_dev)) return ULA_EINVAL;
+  GroupHost& gh = ctx->groups[group];
+  if (gh.steps == 0) return ULA_ENOTRESIDENT;
+  HIP_TRY(launch_gather(gh.d, sel_dev, n, layer, static_cast<uint8_t*>(out_dev), (long long)gh.steps,
+                        reinterpret_cast<hipStream_t>(stream)));
+  return ULA_OK;
+}
+
+static int read_counters(ula_ctx* ctx, std::vector<Counters>& out) {
+  out.resize(ctx->cfg.num_groups);
+  HIP_TRY(hipMemcpy(out.data(), ctx->ctrs, sizeof(Counters) * out.size(), hipMemcpyDeviceToHost));
+  return ULA_OK;
+}
+
+static void fill_stats(const Counters& c, ula_step_stats* s) {
+  s->unique = c.stats[0];
+  s->hits = c.stats[1];
+  s->misses = c.stats[2];
+  s->evictions = c.stats[3];
+  s->from_free = c.stats[4];
+  s->invalid = c.stats[5];
+}
+
+int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out) {
+  if (!ctx) return ULA_EINVAL;
+  HIP_TRY(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
+  std::vector<Counters> c;
+  int rc = read_counters(ctx, c);
+  if (rc) return rc;
+  int first = ULA_OK;
+  for (size_t i = 0; i < c.size(); ++i) {
+    if (per_group_out) fill_stats(c[i], &per_group_out[i]);
+    if (c[i].status && first == ULA_OK) first = c[i].status;
+  }
+  if (first != ULA_OK) ctx->poisoned = first;
+  return first;
+}
+
+int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out) {
+  if (!ctx || !out) return ULA_EINVAL;
+  if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
+  if (!out->map || !out->gown || !out->bitsets || (ctx->dims.H > 0 && !out->hown)) return ULA_EINVAL;
+  HIP_TRY(hipDeviceSynchronize());
+  const GroupDev& g = ctx->groups[group].d;
+  const Dims& d = ctx->dims;
+  HIP_TRY(hipMemcpy(out->map, g.map, 4 * d.N, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(out->gown, g.gown, 4 * d.P, hipMemcpyDeviceToHost));
+  if (d.H > 0) HIP_TRY(hipMemcpy(out->hown, g.hown, 4 * d.H, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(out->bitsets, g.bm, 4 * d.NB * d.W, hipMemcpyDeviceToHost));
+  Counters c;
+  HIP_TRY(hipMemcpy(&c, g.ctr, sizeof(Counters), hipMemcpyDeviceToHost));
+  out->flag = c.flag;
+  out->cur = (int32_t)(c.flag % d.B);   // the ring advances exactly once per completed step
+  fill_stats(c, &out->last);
+  return ULA_OK;
+}
+
+int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, void* out_host) {
+  if (!ctx || n < 0) return ULA_EINVAL;
+  if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
+  if (n == 0) return ULA_OK;
+  if (!la_host || !out_host) return ULA_EINVAL;
+  const Dims& d = ctx->dims;
+  for (int32_t i = 0; i < n; ++i)
+    if (la_host[i] < 0 || la_host[i] >= d.N) return ULA_ERANGE;
+  HIP_TRY(hipDeviceSynchronize());
+  const GroupDev& g = ctx->groups[group].d;
+  std::vector<uint32_t> map(d.N);
+  HIP_TRY(hipMemcpy(map.data(), g.map, 4 * d.N, hipMemcpyDeviceToHost));
+  for (int32_t i = 0; i < n; ++i)
+    if (map[la_host[i]] == kAbsent) return ULA_ERANGE;
+  uint8_t* o = static_cast<uint8_t*>(out_host);
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t loc = map[la_host[i]];
+    if (loc & kHostBit) {
+      HIP_TRY(hipMemcpy(o + (size_t)i * d.slot_bytes,
+                        g.host + (size_t)(loc & ~kHostBit) * d.slot_bytes, d.slot_bytes,
+                        hipMemcpyDefault));
+    } else {
+      HIP_TRY(hipMemcpy(o + (size_t)i * d.slot_bytes, g.pool + (size_t)loc * d.slot_bytes,
+                        d.slot_bytes, hipMemcpyDeviceToHost));
+    }
+  }
+  return ULA_OK;
+}
+
+int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr) {
+  if (!ctx || !dev_ptr) return ULA_EINVAL;
+  if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
+  *dev_ptr = &ctx->groups[group].d.ctr->flag;
+  return ULA_OK;
+}
+
+int ula_set_timing(ula_ctx* ctx, int32_t enable) {
+  if (!ctx) return ULA_EINVAL;
+  ctx->timing = enable ? 1 : 0;
+  return ULA_OK;
+}
+
+int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out5) {
+  if (!ctx || !ms_out5) return ULA_EINVAL;
+  if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
+  GroupHost& gh = ctx->groups[group];
+  HIP_TRY(hipEventSynchronize(gh.ev[5]));
+  for (int i = 0; i < 5; ++i) HIP_TRY(hipEventElapsedTime(&ms_out5[i], gh.ev[i], gh.ev[i + 1]));
+  return ULA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+// Internal layout and kernel interfaces of the PB-LRU residency engine (gfx950).
+//
+// One layer group owns, inside the caller's device workspace:
+//   map    u32[N]        logical -> physical (GPU slot, 0x80000000|host slot, or absent)
+//   tag    u64[N]        de-duplication scratch: (step << 32) | ~position, max wins
+//   gown   i32[P]        owner address of each GPU slot, -1 = empty
+//   stamp  i32[P]        step that last put the slot in a ring bucket (0 = never);
+//                        lets hit marking find a slot's bucket in O(1): the slot
+//                        is in ring[stamp % B] if step - stamp < B, else in cold
+//   hown   i32[H]        owner address of each host slot, -1 = empty
+//   bm     u32[NB][W]    bucket bitmaps, NB = B + 2: free, cold, ring[0..B-1]
+//   tcnt   u32[NB][T]    summary level 1: set bits per 2048-slot span (64 words,
+//                        one wavefront load) of each bucket, kept exact
+//   hbm    u32[WH]       free host slots bitmap, htcnt u32[TH] its span counts
+//   lists  hit slots, misses (address, host slot), victims, block sums, work items
+//   stage  append addresses, destinations and (host-sourced) rows
+//   pool   u8[P][Lg][row_bytes]   the GPU pool, slot-major: one slot holds all
+//                        layers of its group contiguously
+// The host pool is u8[H][Lg][row_bytes] per group in pinned, device-mapped memory.
+// All groups' counters sit in one array at the front of the workspace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ula.h"
+
+namespace ula {
+
+constexpr uint32_t kAbsent = 0xFFFFFFFFu;
+constexpr uint32_t kHostBit = 0x80000000u;
+constexpr int kWave = 64;
+constexpr int kTileWords = 64;                  // bitmap words per summary span
+constexpr int kTileShift = 11;                  // 2048 slots per span
+constexpr int kScanBlock = 1024;                // selection entries per de-dup block
+constexpr int kMaxRing = 64;                    // B <= 64
+constexpr int kMaxBuckets = kMaxRing + 2;
+
+// bucket ids
+constexpr int kFree = 0;
+constexpr int kCold = 1;
+__host__ __device__ constexpr int ring_id(int b) { return 2 + b; }
+
+struct alignas(64) Counters {
+  int32_t status;        // first latched device error of the group, 0 = none
+  int32_t done;          // ticket of the commit kernel's last-block signal
+  long long flag;        // completion counter: last completed step
+  long long stats[6];    // unique, hits, misses, evictions, from_free, invalid
+  int32_t n_unique, n_hits, n_miss, n_invalid;
+  int32_t n_items;       // work items written by the last selection plan
+  int32_t hfree;         // free host slots
+  int32_t bcnt[kMaxBuckets];  // slots per bucket
+  int32_t pad[2];
+};
+static_assert(sizeof(Counters) % 64 == 0, "counter block alignment");
+
+struct SelItem {         // one summary span of one bitmap to extract set bits from
+  int32_t src;           // bucket id, or kHostFreeId for the free-host bitmap
+  int32_t tile;          // span index
+  int32_t out_off;       // rank of the span's first taken bit in the output list
+  int32_t take;          // how many of its lowest set bits to take
+};
+constexpr int kHostFreeId = kMaxBuckets;
+
+struct GroupDev {        // device view of one group, passed by value to kernels
+  Counters* ctr;
+  uint32_t* map;
+  unsigned long long* tag;
+  int32_t* gown;
+  int32_t* stamp;
+  int32_t* hown;
+  uint32_t* bm;
+  uint32_t* tcnt;
+  uint32_t* hbm;
+  uint32_t* htcnt;
+  uint32_t* hit_slots;
+  int32_t* miss_la;
+  uint32_t* miss_h;
+  uint32_t* victims;
+  uint32_t* blk;         // 3 words per de-dup block: hits, misses, invalid (then offsets)
+  SelItem* items;
+  int32_t* app_la;
+  uint32_t* app_dst;
+  uint8_t* app_rows;
+  uint8_t* pool;
+  uint8_t* host;
+  int32_t N, P, H, B, NB, W, T, WH, TH, Lg, row_bytes, slot_bytes;
+};
+
+// unsigned division by a run-time constant d (1 <= d < 2^31) for n < 2^31:
+// q = (umulhi(m, n) + n) >> l with l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1
+// (Granlund and Montgomery, "Division by invariant integers using multiplication", 1994)
+struct FastDiv {
+  uint32_t d, m, l;
+  __host__ FastDiv() : d(1), m(1), l(0) {}
+  __host__ explicit FastDiv(uint32_t div) : d(div) {
+    l = 0;
+    while ((1ull << l) < div) ++l;
+    m = (uint32_t)(((1ull << 32) * ((1ull << l) - div)) / div + 1);
+  }
+  __host__ __device__ inline uint32_t div(uint32_t n) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    uint32_t t = __umulhi(m, n);
+#else
+    uint32_t t = (uint32_t)(((uint64_t)m * n) >> 32);
+#endif
+    return (t + n) >> l;
+  }
+};
+
+enum PlanMode : int32_t { kPlanStep = 0, kPlanAppend = 1 };
+
+struct PlanArgs {
+  int32_t mode;
+  int32_t n;             // append: entries to place
+  int32_t norder;
+  int32_t dest;          // bucket the taken GPU slots join
+  int8_t order[kMaxBuckets + 1];
+};
+
+// ---- launchers (one translation unit per kernel family) ----------------
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+hipError_t launch_fill_u64(unsigned long long* p, size_t n, unsigned long long v, hipStream_t s);
+hipError_t launch_init_bitmap(uint32_t* words, int32_t nwords, int64_t nbits, uint32_t* tcnt,
+                              int32_t ntiles, hipStream_t s);
+hipError_t launch_init_counters(Counters* c, int32_t P, int32_t H, hipStream_t s);
+
+hipError_t launch_tag(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
+hipError_t launch_count(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
+hipError_t launch_scan(const GroupDev& g, int32_t nblk, hipStream_t s);
+hipError_t launch_fold(const GroupDev& g, int32_t cur, hipStream_t s);
+hipError_t launch_compact(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t,
+                          int32_t cur, hipStream_t s);
+hipError_t launch_plan(const GroupDev& g, const PlanArgs& a, hipStream_t s);
+hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, uint32_t t,
+                          int32_t max_items, hipStream_t s);
+hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s);
+hipError_t launch_swap(const GroupDev& g, int32_t max_pairs, hipStream_t s);
+hipError_t launch_commit(const GroupDev& g, long long t, hipStream_t s);
+hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
+                         uint8_t* out, long long want_flag, hipStream_t s);
+
+}  // namespace ula

@@ -1,0 +1,226 @@
+"""Python binding of libula.so: argument marshalling only.
+
+Every step of the residency path runs in the HIP kernels behind the C ABI in
+include/ula.h; this module turns torch tensors and numpy arrays into pointers
+and sizes, and error codes into exceptions. PyTorch supplies the device
+workspace and the streams. There is no fallback: without the built library
+every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libula.so")
+
+ERROR_NAMES = {0: "OK", -1: "EINVAL", -2: "ERANGE", -3: "EDUP", -4: "EHOSTFULL",
+               -5: "ECAPACITY", -6: "ENOTRESIDENT", -7: "ESTATE", -8: "EHIP"}
+
+
+class UlaConfig(ctypes.Structure):
+    _fields_ = [("num_groups", ctypes.c_int32), ("layers_per_group", ctypes.c_int32),
+                ("row_bytes", ctypes.c_int32), ("ring_buckets", ctypes.c_int32),
+                ("logical_capacity", ctypes.c_int32), ("gpu_slots", ctypes.c_int32),
+                ("host_slots", ctypes.c_int32), ("max_sets", ctypes.c_int32),
+                ("max_k", ctypes.c_int32), ("max_append", ctypes.c_int32)]
+
+
+class UlaStepStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("unique", "hits", "misses", "evictions", "from_free", "invalid")]
+
+    def as_tuple(self):
+        return (self.unique, self.hits, self.misses, self.evictions, self.from_free, self.invalid)
+
+
+class UlaStateHost(ctypes.Structure):
+    _fields_ = [("map", ctypes.c_void_p), ("gown", ctypes.c_void_p), ("hown", ctypes.c_void_p),
+                ("bitsets", ctypes.c_void_p), ("cur", ctypes.c_int32), ("flag", ctypes.c_int64),
+                ("last", UlaStepStats)]
+
+
+class UlaError(RuntimeError):
+    def __init__(self, code: int, where: str, text: str):
+        self.code = code
+        self.name = ERROR_NAMES.get(code, str(code))
+        super().__init__(f"{where}: {self.name} ({text})")
+
+
+_lib = None
+
+# (name, restype, argtypes) of every symbol include/ula.h declares
+SIGNATURES = [
+    ("ula_device_bytes", ctypes.c_size_t, [ctypes.POINTER(UlaConfig)]),
+    ("ula_host_bytes", ctypes.c_size_t, [ctypes.POINTER(UlaConfig)]),
+    ("ula_init", ctypes.c_int, [ctypes.POINTER(UlaConfig), ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_uint64, ctypes.POINTER(ctypes.c_void_p)]),
+    ("ula_append", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64]),
+    ("ula_step", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                ctypes.c_void_p, ctypes.c_uint64]),
+    ("ula_gather", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64]),
+    ("ula_sync", ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
+    ("ula_export_state", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(UlaStateHost)]),
+    ("ula_read_rows", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                     ctypes.c_void_p]),
+    ("ula_flag_address", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_void_p)]),
+    ("ula_set_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
+    ("ula_read_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    ("ula_destroy", ctypes.c_int, [ctypes.c_void_p]),
+    ("ula_strerror", ctypes.c_char_p, [ctypes.c_int]),
+    ("ula_host_alloc", ctypes.c_void_p, [ctypes.c_size_t]),
+    ("ula_host_free", ctypes.c_int, [ctypes.c_void_p]),
+]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libula.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with serving_pb_lru_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise UlaError(rc, where, lib().ula_strerror(rc).decode())
+
+
+def _ptr(x) -> int:
+    """Device pointer of a torch tensor, or address of a numpy array."""
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return x.ctypes.data
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Engine:
+    """One engine context: per group a GPU pool, a pinned host pool and PB-LRU state."""
+
+    def __init__(self, num_groups: int, layers: int, row_bytes: int, ring: int, logical_capacity: int,
+                 gpu_slots: int, host_slots: int, max_sets: int, max_k: int, max_append: int = 4096,
+                 device: str = "cuda", stream=None):
+        import torch
+        self.cfg = UlaConfig(num_groups, layers, row_bytes, ring, logical_capacity, gpu_slots,
+                             host_slots, max_sets, max_k, max_append)
+        L = lib()
+        nbytes = L.ula_device_bytes(ctypes.byref(self.cfg))
+        if nbytes == 0:
+            raise UlaError(-1, "ula_device_bytes", "invalid configuration")
+        self.device_bytes = nbytes
+        self.host_bytes = L.ula_host_bytes(ctypes.byref(self.cfg))
+        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.host = None
+        if self.host_bytes:
+            self.host = L.ula_host_alloc(self.host_bytes)
+            if not self.host:
+                raise UlaError(-8, "ula_host_alloc", f"could not pin {self.host_bytes} bytes")
+        self.ctx = ctypes.c_void_p()
+        _check(L.ula_init(ctypes.byref(self.cfg), self.ws.data_ptr(), self.host, _stream(stream),
+                          ctypes.byref(self.ctx)), "ula_init")
+        self.num_groups, self.layers, self.row_bytes, self.ring = num_groups, layers, row_bytes, ring
+        self.N, self.P, self.H = logical_capacity, gpu_slots, host_slots
+
+    # -- calls ---------------------------------------------------------------
+    def append(self, group: int, las: np.ndarray, rows, stream=None) -> None:
+        """rows: torch CUDA uint8 tensor or numpy uint8 array [n][layers][row_bytes]."""
+        las = np.ascontiguousarray(las, dtype=np.int32)
+        on_dev = 1 if hasattr(rows, "is_cuda") and rows.is_cuda else 0
+        if not on_dev:
+            rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        _check(lib().ula_append(self.ctx, group, las.size, las.ctypes.data, _ptr(rows), on_dev,
+                                _stream(stream)), "ula_append")
+
+    def step(self, group: int, sel, stream=None) -> None:
+        """sel: torch CUDA int32 tensor [n_sets][k] (or [k] for one set)."""
+        n_sets, k = (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
+        _check(lib().ula_step(self.ctx, group, n_sets, k, sel.data_ptr(), _stream(stream)), "ula_step")
+
+    def gather(self, group: int, layer: int, sel, out=None, stream=None):
+        import torch
+        n_sets, k = (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
+        if out is None:
+            out = torch.empty((n_sets, k, self.row_bytes), dtype=torch.uint8, device=sel.device)
+        _check(lib().ula_gather(self.ctx, group, layer, n_sets, k, sel.data_ptr(), out.data_ptr(),
+                                _stream(stream)), "ula_gather")
+        return out
+
+    def sync(self, stream=None) -> List[tuple]:
+        st = (UlaStepStats * self.num_groups)()
+        _check(lib().ula_sync(self.ctx, _stream(stream), st), "ula_sync")
+        return [s.as_tuple() for s in st]
+
+    def sync_code(self, stream=None) -> int:
+        """ula_sync's return code without raising (for error-path tests)."""
+        return lib().ula_sync(self.ctx, _stream(stream), None)
+
+    def export_state(self, group: int) -> dict:
+        W = (self.P + 31) // 32
+        out = dict(map=np.empty(self.N, np.uint32), gown=np.empty(self.P, np.int32),
+                   hown=np.empty(max(self.H, 1), np.int32),
+                   bitsets=np.empty((self.ring + 2, W), np.uint32))
+        sh = UlaStateHost(out["map"].ctypes.data, out["gown"].ctypes.data, out["hown"].ctypes.data,
+                          out["bitsets"].ctypes.data, 0, 0, UlaStepStats())
+        _check(lib().ula_export_state(self.ctx, group, ctypes.byref(sh)), "ula_export_state")
+        out["hown"] = out["hown"][: self.H]
+        out["cur"] = int(sh.cur)
+        out["flag"] = int(sh.flag)
+        out["stats"] = sh.last.as_tuple()
+        return out
+
+    def read_rows(self, group: int, las: np.ndarray) -> np.ndarray:
+        las = np.ascontiguousarray(las, dtype=np.int32)
+        out = np.empty((las.size, self.layers, self.row_bytes), dtype=np.uint8)
+        _check(lib().ula_read_rows(self.ctx, group, las.size, las.ctypes.data, out.ctypes.data),
+               "ula_read_rows")
+        return out
+
+    def flag_address(self, group: int) -> int:
+        p = ctypes.c_void_p()
+        _check(lib().ula_flag_address(self.ctx, group, ctypes.byref(p)), "ula_flag_address")
+        return p.value
+
+    def set_timing(self, enable: bool) -> None:
+        _check(lib().ula_set_timing(self.ctx, 1 if enable else 0), "ula_set_timing")
+
+    def read_timing(self, group: int) -> List[float]:
+        ms = (ctypes.c_float * 5)()
+        _check(lib().ula_read_timing(self.ctx, group, ms), "ula_read_timing")
+        return list(ms)
+
+    def close(self) -> None:
+        if getattr(self, "ctx", None) is not None and self.ctx.value:
+            import torch
+            torch.cuda.synchronize()
+            lib().ula_destroy(self.ctx)
+            self.ctx = None
+        if getattr(self, "host", None):
+            lib().ula_host_free(self.host)
+            self.host = None
+        self.ws = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,79 @@
+"""Run one trace through the HIP engine and the oracle side by side (GPU tests).
+
+After the initial load and after every step the exported engine state (mapping
+table, owners, bucket bitsets, current bucket, completion counter, step
+statistics) must equal the oracle's bit for bit, and so must every gathered
+byte.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+from oracle.replay import initial_load as oracle_load, new_group
+from serving_pb_lru_amd.replay import engine_for, initial_load
+from synth import Trace, rows_for
+from synth.device import rows_device
+
+FIELDS = ("map", "gown", "hown", "bitsets")
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def assert_same_state(st: dict, ref: dict, where: str) -> None:
+    for key in FIELDS:
+        a, b = np.asarray(st[key]), np.asarray(ref[key])
+        if not np.array_equal(a, b):
+            bad = np.flatnonzero(a.reshape(-1) != b.reshape(-1))
+            raise AssertionError(f"{where}: {key} differs at {bad.size} places, first {bad[:5]}: "
+                                 f"engine {a.reshape(-1)[bad[:5]]} oracle {b.reshape(-1)[bad[:5]]}")
+    assert st["cur"] == ref["cur"], f"{where}: cur {st['cur']} vs {ref['cur']}"
+    assert st["flag"] == ref["flag"], f"{where}: flag {st['flag']} vs {ref['flag']}"
+    assert tuple(st["stats"]) == tuple(ref["stats"]), f"{where}: stats {st['stats']} vs {ref['stats']}"
+
+
+def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, check_every=1):
+    """selections: optional {g: list of int32 [n_sets][k]} overriding the trace's."""
+    import torch
+    tr = Trace(wl, steps)
+    groups = list(range(wl.groups)) if groups is None else groups
+    say(f"parity {wl.name}: N={tr.N} P={tr.P} H={tr.H} groups={groups} steps={tr.steps}")
+    eng = engine_for(tr, max_append=max_append)
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    try:
+        initial_load(eng, tr, groups, rows)
+        ora = {}
+        for g in groups:
+            ora[g] = new_group(tr, full_data=True)
+            oracle_load(ora[g], tr, g)
+            assert_same_state(eng.export_state(g), ora[g].export_state(), f"group {g} after load")
+        sels = {g: (iter(selections[g]) if selections else tr.selections(g)) for g in groups}
+        for t in range(1, tr.steps + 1):
+            app = tr.appends(t)
+            for g in groups:
+                sel = next(sels[g])
+                dsel = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
+                if app.size:
+                    eng.append(g, app, rows(app, g))
+                eng.step(g, dsel)
+                outs = [eng.gather(g, l, dsel) for l in range(wl.layers)]
+                ora[g].append(app, rows_for(wl.seed, g, app, wl.layers, wl.row_bytes))
+                ora[g].step(sel)
+                eng.sync()
+                if t % check_every == 0 or t == tr.steps:
+                    assert_same_state(eng.export_state(g), ora[g].export_state(), f"group {g} step {t}")
+                for l in range(wl.layers):
+                    ref = ora[g].gather(sel, l, step=t)
+                    got = outs[l].cpu().numpy()
+                    if not np.array_equal(got, ref):
+                        bad = np.argwhere((got != ref).any(axis=-1))
+                        raise AssertionError(f"group {g} step {t} layer {l}: gathered rows differ at "
+                                             f"{len(bad)} rows, first {bad[:5].tolist()}")
+        return ora
+    finally:
+        eng.close()
