@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of the PB-LRU KV residency engine on one MI355X.
+
+One step = the whole per-decode-step path for every layer group of the
+workload: the step's appends, ula_step (de-duplication and lookup, fold and hit
+marking, victim selection, host-link swap, commit and completion signal) and
+one ula_gather per layer of the group. Inputs (selection sets for every step
+and the appended rows) are resident in HBM before the timed region; the GPU
+pool starts full (initial load untimed). W warm-up steps run first (they carry
+the cold-start misses), then exactly K steps are timed between two device
+synchronisations.
+
+value = selected row-layers resolved and gathered per second
+      = K * sum over groups of (n_sets * k * layers) / timed wall seconds.
+
+Printed as one JSON line, with:
+  roofline      the gather kernel against HBM peak (1312 algorithmic bytes per
+                gathered row-layer: 656 read + 656 written), its launch duration
+                measured with HIP events on the engine's stream;
+  miss_path     the miss path against the host link, per direction: missed rows
+                in (k_swap_in, 656 * layers bytes per miss) and evicted rows out
+                (k_writeback on the side stream, 656 * layers bytes per
+                eviction), from a second replay with per-phase events;
+  cpu_baseline  the CPU oracle timed on this host's cores over the same steps
+                (a bounded sample; a baseline, not the target).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+for _v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_v, "1")
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from synth import Trace, preset  # noqa: E402
+
+METRIC = "selected KV rows resolved+gathered/s; gather GB/s and miss GB/s vs peak"
+HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E
+LINK_PEAK_GBS = 32 * 16 * 128 / 130 / 8  # PCIe 5.0 x16 per direction = 63.0 GB/s
+DEFAULT_WORKLOAD = "r16_64k_g1x3"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=56)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-phases", action="store_true", help="skip the per-phase replay")
+    return p.parse_args()
+
+
+def rows_per_step(tr) -> int:
+    wl = tr.wl
+    return wl.groups * tr.n_sets * tr.k * wl.layers
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(tr, W: int, K: int, budget: float) -> dict:
+    """Replay the trace through the oracle on one core; time steps W+1 .. W+K."""
+    from oracle.pblru import PBLRUGroup
+    from oracle.replay import initial_load as oracle_load, new_group
+    from synth import rows_for
+
+    wl = tr.wl
+    old_aff = os.sched_getaffinity(0)
+    core = min(old_aff)
+    os.sched_setaffinity(0, {core})
+    try:
+        groups = list(range(wl.groups))
+        ora = {}
+        for g in groups[:1]:
+            ora[g] = new_group(tr, full_data=True)
+            oracle_load(ora[g], tr, g)
+        sels = {g: tr.selections(g) for g in groups[:1]}
+        spent, timed, rows = 0.0, 0, 0
+        for t in range(1, W + K + 1):
+            app = tr.appends(t)
+            for g in groups[:1]:
+                sel = next(sels[g])
+                app_rows = rows_for(wl.seed, g, app, wl.layers, wl.row_bytes)
+                t0 = time.perf_counter()
+                ora[g].append(app, app_rows)
+                ora[g].step(sel)
+                for l in range(wl.layers):
+                    ora[g].gather(sel, l, step=t)
+                dt = time.perf_counter() - t0
+                if t > W:
+                    spent += dt
+                    rows += tr.n_sets * tr.k * wl.layers
+            if t > W:
+                timed += 1
+                if spent > budget:
+                    break
+        return {"value": rows / spent if spent else None, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": (f"{wl.name}: group 0 of {wl.groups}, steps {W + 1}..{W + timed} after an "
+                           f"untimed load and {W} untimed steps, full-data mode (rows moved), "
+                           f"one core; {spent:.1f} s of CPU work")}
+    finally:
+        os.sched_setaffinity(0, old_aff)
+
+
+# ---------------------------------------------------------------------------
+def gpu_run(tr, W: int, K: int, phases: bool) -> dict:
+    import torch
+
+    from serving_pb_lru_amd.replay import engine_for, initial_load
+    from synth.device import rows_device
+
+    wl = tr.wl
+    groups = list(range(wl.groups))
+    torch.cuda.set_device(0)
+    stream = torch.cuda.Stream()   # a created stream: launches on the legacy null stream cost more
+    torch.cuda.set_stream(stream)
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+
+    # inputs for every step, resident in HBM before timing
+    sels = {g: [torch.from_numpy(s).cuda() for s in tr.selections(g)] for g in groups}
+    apps = [tr.appends(t) for t in range(1, tr.steps + 1)]
+    app_rows = {g: [rows(a, g) for a in apps] for g in groups}
+    outs = {g: [torch.empty((tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
+                for _ in range(wl.layers)] for g in groups}
+
+    def run_step(eng, t, gather_events=None):
+        for g in groups:
+            if apps[t - 1].size:
+                eng.append(g, apps[t - 1], app_rows[g][t - 1])
+            sel = sels[g][t - 1]
+            eng.step(g, sel)
+            for l in range(wl.layers):
+                if gather_events is not None:
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    eng.gather(g, l, sel, out=outs[g][l])
+                    b.record()
+                    gather_events.append((a, b))
+                else:
+                    eng.gather(g, l, sel, out=outs[g][l])
+
+    # ---- timed replay ----------------------------------------------------
+    eng = engine_for(tr, max_append=1 << 16)
+    initial_load(eng, tr, groups, rows)
+    torch.cuda.synchronize()
+    for t in range(1, W + 1):
+        run_step(eng, t)
+    torch.cuda.synchronize()
+    gev = []
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    t0 = time.perf_counter()
+    for t in range(W + 1, W + K + 1):
+        run_step(eng, t, gev)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    eng.sync()   # raises if the device latched an error
+    ev_ms = start.elapsed_time(end)
+    gather_ms = [a.elapsed_time(b) for a, b in gev]
+    eng.close()
+    del eng
+    res = dict(wall_s=wall, event_ms=ev_ms, gather_ms=gather_ms)
+
+    # ---- per-phase replay (diagnostic, synchronises every step) --------------
+    if phases:
+        eng = engine_for(tr, max_append=1 << 16)
+        initial_load(eng, tr, groups, rows)
+        eng.set_timing(True)
+        torch.cuda.synchronize()
+        ph = np.zeros(6)
+        h2d = d2h = 0
+        n = 0
+        for t in range(1, W + K + 1):
+            for g in groups:
+                if apps[t - 1].size:
+                    eng.append(g, apps[t - 1], app_rows[g][t - 1])
+                eng.step(g, sels[g][t - 1])
+                ms = eng.read_timing(g)
+                st = eng.sync()[g]
+                if t > W:
+                    ph += ms
+                    h2d += st[2]
+                    d2h += st[3]
+                    n += 1
+        eng.close()
+        res.update(phase_ms=(ph / max(n, 1)).tolist(), swap_in_ms_total=float(ph[3]),
+                   writeback_ms_total=float(ph[5]), h2d_rows=int(h2d), d2h_rows=int(d2h), group_steps=n)
+    return res
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the engine is the single-GPU DP form; each GPU of a node would run its own "
+              "independent engine over its own requests.", file=sys.stderr)
+        sys.exit(2)
+    W, K = args.warmup, args.steps
+    wl = preset(args.workload)
+    tr = Trace(wl, steps=max(W + K, 1))
+    per_step = rows_per_step(tr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(tr, W, K, args.cpu_seconds)
+
+    r = gpu_run(tr, W, K, not args.no_phases)
+    value = per_step * K / r["wall_s"]
+    ms_per_step = r["event_ms"] / K
+
+    g_ms = float(np.mean(r["gather_ms"]))
+    rows_per_gather = tr.n_sets * tr.k
+    g_bytes = 1312 * rows_per_gather
+    g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": "k_gather", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": g_bytes, "launch_ms": round(g_ms, 5)}
+    miss = None
+    if "phase_ms" in r:
+        slot = wl.layers * wl.row_bytes
+        up = r["h2d_rows"] * slot
+        down = r["d2h_rows"] * slot
+        t_in = r["swap_in_ms_total"] * 1e-3
+        t_out = r["writeback_ms_total"] * 1e-3
+        gin = up / t_in / 1e9 if t_in > 0 else None
+        gout = down / t_out / 1e9 if t_out > 0 else None
+        rnd = lambda x, d: None if x is None else round(x, d)
+        miss = {"bound": "host-link", "peak": round(LINK_PEAK_GBS, 1), "unit": "GB/s per direction",
+                "h2d": {"kernel": "k_swap_in", "achieved": rnd(gin, 2),
+                        "frac": rnd(None if gin is None else gin / LINK_PEAK_GBS, 4),
+                        "bytes_per_step": up / r["group_steps"]},
+                "d2h": {"kernel": "k_writeback (side stream)", "achieved": rnd(gout, 2),
+                        "frac": rnd(None if gout is None else gout / LINK_PEAK_GBS, 4),
+                        "bytes_per_step": down / r["group_steps"]},
+                "phase_ms_per_group_step": {k: round(v, 5) for k, v in zip(
+                    ["lookup_dedup", "mark_fold", "victims", "swap_in", "commit", "writeback"],
+                    r["phase_ms"])}}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K,
+        "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": wl.name, "requests": wl.requests,
+                   "context": wl.ctx_fixed if wl.ctx_fixed else list(wl.ctx_range),
+                   "sets_per_request": wl.sets_per_request, "groups": wl.groups,
+                   "layers_per_group": wl.layers, "k": wl.k, "gpu_slots": tr.P, "host_slots": tr.H,
+                   "ring": wl.ring, "row_bytes": wl.row_bytes, "overlap": wl.overlap,
+                   "row_layers_per_step": per_step},
+        "roofline": roofline,
+        "miss_path": miss,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -141,10 +141,14 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host,
  * (first occurrence in row-major order) and look up once for the group; advance
  * the ring and fold the reused bucket into cold; move hits into the current
  * bucket; pick one victim per miss (free, cold, ring oldest -> newest, ascending
- * slot inside a bucket, never the current bucket); swap the missed rows in from
- * the host pool and the victims' rows out to the host slots they vacate; then
+ * slot inside a bucket, never the current bucket); bring the missed rows in from
+ * the host pool (the victims' rows are staged in device memory first); then
  * update the mapping table and owners and raise the completion counter to the
- * step number. Enqueued on `stream` with no host synchronisation.
+ * step number. The staged victim rows are written to the host slots their
+ * misses vacated on a library-owned side stream, overlapping the work that
+ * follows; the group's next step waits for that write-back before it reads the
+ * host pool, and ula_sync waits for it too. Enqueued on `stream` with no host
+ * synchronisation.
  * Host errors: ULA_EINVAL (bad g, n_sets > max_sets, k > max_k, negative sizes),
  * ULA_ESTATE. Device errors (reported by ula_sync): ULA_ERANGE, ULA_ECAPACITY. */
 int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
@@ -184,11 +188,13 @@ int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host
 int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr);
 
 /* Per-phase timing of the last step of group g, in milliseconds, when enabled
- * with ula_set_timing: [0] lookup + de-duplication, [1] fold + hit marking,
- * [2] victim selection, [3] row swap over the host link, [4] commit + signal.
- * ula_read_timing synchronises on the step's last event. */
+ * with ula_set_timing: [0] lookup + de-duplication, [1] hit marking + fold,
+ * [2] victim selection, [3] missed rows in over the host link, [4] commit +
+ * signal, [5] evicted rows out over the host link (on the group's side stream,
+ * overlapping what follows the step). ula_read_timing synchronises on the
+ * step's last events. */
 int ula_set_timing(ula_ctx* ctx, int32_t enable);
-int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out5);
+int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out6);
 
 /* Release the context (not the caller's buffers). Waits for no stream. */
 int ula_destroy(ula_ctx* ctx);

@@ -30,6 +30,13 @@ __device__ __forceinline__ int wave_inclusive_sum(int v) {
   return v;
 }
 
+// Sum over the 64 lanes of a wavefront, returned to every lane.
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;
+}
+
 // Exclusive prefix sum over a whole workgroup of NT threads; `total` receives
 // the sum over the workgroup. `scratch` holds NT / 64 + 1 ints of LDS. Every thread
 // of the workgroup must call it.
@@ -86,6 +93,23 @@ __device__ __forceinline__ int bucket_ntiles(const GroupDev& g, int id) {
 }
 __device__ __forceinline__ int32_t* bucket_count(const GroupDev& g, int id) {
   return id == kHostFreeId ? &g.ctr->hfree : &g.ctr->bcnt[id];
+}
+
+// Piece c of appended entry i: copy 16 bytes of its rows to the destination
+// chosen for it (app_dst: a GPU slot, or a host slot with the host bit); the
+// lane of piece 0 also publishes the mapping and owner entries of `la`.
+__device__ __forceinline__ void place_piece(const GroupDev& g, uint32_t i, uint32_t c, int32_t la,
+                                            const uint8_t* __restrict__ rows) {
+  const uint32_t d = g.app_dst[i];
+  const vec4u v = reinterpret_cast<const vec4u*>(rows + (size_t)i * g.slot_bytes)[c];
+  uint8_t* dst = (d & kHostBit) ? g.host + (size_t)(d & ~kHostBit) * g.slot_bytes
+                                : g.pool + (size_t)d * g.slot_bytes;
+  reinterpret_cast<vec4u*>(dst)[c] = v;
+  if (c == 0) {
+    g.map[la] = d;
+    if (d & kHostBit) g.hown[d & ~kHostBit] = la;
+    else g.gown[d] = la;
+  }
 }
 
 }  // namespace ula

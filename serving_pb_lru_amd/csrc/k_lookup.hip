@@ -12,13 +12,13 @@
 //            tags of earlier steps have a smaller t and never match).
 //   count    per block of 1024 entries: how many first occurrences are hits
 //            (GPU-resident) and misses (host-resident), and how many are padding.
-//   scan     one workgroup: exclusive offsets of the block counts; totals;
-//            the capacity check (more distinct entries than GPU slots is an
-//            error raised before any state changes).
-//   compact  per block: wavefront ballot + mbcnt ranks the first occurrences
-//            inside each wavefront, LDS adds the wavefront offsets, the block
-//            offset comes from the scan: hits and misses land in first-occurrence
-//            order. Each hit then leaves its bucket for the current ring bucket.
+//   compact  per block: the block's output offsets are the sums of the earlier
+//            blocks' counts, the totals give the capacity check (more distinct
+//            entries than GPU slots is an error raised before any state
+//            changes); wavefront ballot + mbcnt ranks the first occurrences
+//            inside each wavefront and LDS adds the wavefront offsets, so hits
+//            and misses land in first-occurrence order. Each hit is stamped
+//            with the step and its span marked dirty.
 #include "device_util.h"
 
 namespace ula {
@@ -81,98 +81,101 @@ __global__ __launch_bounds__(kScanBlock) void k_count(GroupDev g, const int32_t*
   }
 }
 
-// One workgroup turns the per-block counts into exclusive offsets (in place)
-// and publishes the step's totals.
-__global__ __launch_bounds__(1024) void k_scan(GroupDev g, int32_t nblk) {
-  __shared__ int scratch[1024 / kWave + 1];
-  if (block_failed(g.ctr)) return;
-  int base_h = 0, base_m = 0, base_p = 0;
-  for (int b0 = 0; b0 < nblk; b0 += 1024) {
-    int b = b0 + threadIdx.x;
-    int h = b < nblk ? (int)g.blk[3 * b] : 0;
-    int m = b < nblk ? (int)g.blk[3 * b + 1] : 0;
-    int p = b < nblk ? (int)g.blk[3 * b + 2] : 0;
-    int th, tm, tp;
-    int eh = block_exclusive_sum<1024>(h, scratch, th);
-    int em = block_exclusive_sum<1024>(m, scratch, tm);
-    block_exclusive_sum<1024>(p, scratch, tp);
-    if (b < nblk) {
-      g.blk[3 * b] = (uint32_t)(base_h + eh);
-      g.blk[3 * b + 1] = (uint32_t)(base_m + em);
-    }
-    base_h += th;
-    base_m += tm;
-    base_p += tp;
-  }
-  if (threadIdx.x == 0) {
-    Counters* c = g.ctr;
-    int u = base_h + base_m;
-    c->n_hits = base_h;
-    c->n_miss = base_m;
-    c->n_unique = u;
-    c->n_invalid = base_p;
-    c->stats[0] = u;
-    c->stats[1] = base_h;
-    c->stats[2] = base_m;
-    c->stats[3] = 0;
-    c->stats[4] = 0;
-    c->stats[5] = base_p;
-    if (u > g.P) latch(c, ULA_ECAPACITY);
-  }
-}
-
+// Every workgroup adds up the counts of the workgroups before it (a few KB read
+// from cache) to find its output offsets, and all of them add up the totals:
+// they reach the same capacity verdict, so either every workgroup writes or
+// none does. Workgroup 0 publishes the totals.
 __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_t* __restrict__ sel,
-                                                        int32_t n, uint32_t t, int32_t cur) {
+                                                        int32_t n, uint32_t t, int32_t nblk) {
   __shared__ int s_h[kScanBlock / kWave], s_m[kScanBlock / kWave];
-  __shared__ int s_delta[kMaxBuckets];
+  __shared__ int s_tot[3][kScanBlock / kWave];
+  __shared__ int s_base[3];
   if (block_failed(g.ctr)) return;
-  for (int i = threadIdx.x; i < g.NB; i += blockDim.x) s_delta[i] = 0;
+  const int wave = threadIdx.x / kWave;
+  const int lane = lane_id();
+  {
+    // counts of earlier workgroups (offsets) and of all workgroups (totals)
+    int bh = 0, bmi = 0, ah = 0, am = 0, ap = 0;
+    for (int b = threadIdx.x; b < nblk; b += kScanBlock) {
+      const int h = (int)g.blk[3 * b], m = (int)g.blk[3 * b + 1], p = (int)g.blk[3 * b + 2];
+      ah += h;
+      am += m;
+      ap += p;
+      if (b < (int)blockIdx.x) {
+        bh += h;
+        bmi += m;
+      }
+    }
+    bh = wave_sum(bh);
+    bmi = wave_sum(bmi);
+    ah = wave_sum(ah);
+    am = wave_sum(am);
+    ap = wave_sum(ap);
+    if (lane == 0) {
+      s_h[wave] = bh;
+      s_m[wave] = bmi;
+      s_tot[0][wave] = ah;
+      s_tot[1][wave] = am;
+      s_tot[2][wave] = ap;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int x[5] = {0, 0, 0, 0, 0};
+      for (int w = 0; w < kScanBlock / kWave; ++w) {
+        x[0] += s_h[w];
+        x[1] += s_m[w];
+        x[2] += s_tot[0][w];
+        x[3] += s_tot[1][w];
+        x[4] += s_tot[2][w];
+      }
+      s_base[0] = x[0];
+      s_base[1] = x[1];
+      const int u = x[2] + x[3];
+      s_base[2] = u > g.P;
+      if (blockIdx.x == 0) {
+        Counters* c = g.ctr;
+        c->n_hits = x[2];
+        c->n_miss = x[3];
+        c->n_unique = u;
+        c->n_invalid = x[4];
+        c->stats[0] = u;
+        c->stats[1] = x[2];
+        c->stats[2] = x[3];
+        c->stats[3] = 0;
+        c->stats[4] = 0;
+        c->stats[5] = x[4];
+        if (u > g.P) latch(c, ULA_ECAPACITY);
+      }
+    }
+    __syncthreads();
+    if (s_base[2]) return;   // capacity error: nothing is written (uniform)
+  }
   const int e = blockIdx.x * kScanBlock + threadIdx.x;
   int32_t la;
   uint32_t loc;
   int c = classify(g, sel, n, e, t, la, loc);
-  const int wave = threadIdx.x / kWave;
-  const int lane = lane_id();
   unsigned long long bh = __ballot(c == 1), bm = __ballot(c == 2);
   if (lane == 0) {
     s_h[wave] = __popcll(bh);
     s_m[wave] = __popcll(bm);
   }
   __syncthreads();
-  if (c == 1 || c == 2) {
-    int off = 0;
-    if (c == 1) {
-      for (int w = 0; w < wave; ++w) off += s_h[w];
-      int pos = (int)g.blk[3 * blockIdx.x] + off + rank_below(bh);
-      g.hit_slots[pos] = loc;
-      // hit marking: the slot leaves its bucket and joins ring[cur]
-      const uint32_t s = loc;
-      const int32_t st = g.stamp[s];
-      const int ob = (st > 0 && (int64_t)t - st < g.B) ? ring_id(st % g.B) : kCold;
-      const int nb = ring_id(cur);
-      const uint32_t bit = 1u << (s & 31);
-      atomicAnd(&g.bm[(size_t)ob * g.W + (s >> 5)], ~bit);
-      atomicOr(&g.bm[(size_t)nb * g.W + (s >> 5)], bit);
-      atomicSub(&g.tcnt[(size_t)ob * g.T + (s >> kTileShift)], 1u);
-      atomicAdd(&g.tcnt[(size_t)nb * g.T + (s >> kTileShift)], 1u);
-      g.stamp[s] = (int32_t)t;
-      atomicSub(&s_delta[ob], 1);
-    } else {
-      for (int w = 0; w < wave; ++w) off += s_m[w];
-      int pos = (int)g.blk[3 * blockIdx.x + 1] + off + rank_below(bm);
-      g.miss_la[pos] = la;
-      g.miss_h[pos] = loc & ~kHostBit;
-    }
+  if (c == 1) {
+    int off = s_base[0];
+    for (int w = 0; w < wave; ++w) off += s_h[w];
+    g.hit_slots[off + rank_below(bh)] = loc;
+    // the bucket move itself is done word-parallel by the mark kernel, which
+    // finds this step's hits by their stamp; every writer of a span's dirty
+    // word writes the same value
+    g.stamp[loc] = (int32_t)t;
+    g.dirty[loc >> kTileShift] = (int32_t)t;
+  } else if (c == 2) {
+    int off = s_base[1];
+    for (int w = 0; w < wave; ++w) off += s_m[w];
+    const int pos = off + rank_below(bm);
+    g.miss_la[pos] = la;
+    g.miss_h[pos] = loc & ~kHostBit;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int nh = 0;
-    for (int w = 0; w < kScanBlock / kWave; ++w) nh += s_h[w];
-    s_delta[ring_id(cur)] += nh;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < g.NB; i += blockDim.x)
-    if (s_delta[i]) atomicAdd(&g.ctr->bcnt[i], s_delta[i]);
 }
 
 hipError_t launch_tag(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s) {
@@ -189,15 +192,10 @@ hipError_t launch_count(const GroupDev& g, const int32_t* sel, int32_t n, uint32
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const GroupDev& g, int32_t nblk, hipStream_t s) {
-  k_scan<<<1, 1024, 0, s>>>(g, nblk);
-  return hipGetLastError();
-}
-
-hipError_t launch_compact(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t,
-                          int32_t cur, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  k_compact<<<(n + kScanBlock - 1) / kScanBlock, kScanBlock, 0, s>>>(g, sel, n, t, cur);
+hipError_t launch_compact(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s) {
+  const int nblk = (n + kScanBlock - 1) / kScanBlock;
+  // one workgroup even for an empty selection: it publishes the (zero) totals
+  k_compact<<<nblk > 0 ? nblk : 1, kScanBlock, 0, s>>>(g, sel, n, t, nblk);
   return hipGetLastError();
 }
 

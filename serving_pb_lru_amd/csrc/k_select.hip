@@ -17,8 +17,8 @@
 //            it give each contributing span its work-item index, so empty spans
 //            never produce work.
 //
-//   fold     one wavefront per span of ring[cur] with a non-zero count: cold |=
-//            ring[cur]; ring[cur] = 0; the span counts move along.
+//   mark     fold and hit marking in one word-parallel pass over the spans that
+//            have hits or survivors to fold (see the kernel).
 //   plan     one workgroup: the quota of each bucket in eviction order (from
 //            the exact bucket counts), then, per bucket with a quota, its
 //            level-1 counts 1024 spans at a time, scanned across the workgroup to
@@ -33,50 +33,114 @@
 
 namespace ula {
 
-__global__ __launch_bounds__(256) void k_fold(GroupDev g, int32_t cur) {
-  if (status_of(g.ctr)) return;
-  const int rb = ring_id(cur);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    g.ctr->bcnt[kCold] += g.ctr->bcnt[rb];
-    g.ctr->bcnt[rb] = 0;
-  }
+// Fold and hit marking, word-parallel and free of global atomics. One
+// wavefront per 2048-slot span, lane = bitmap word. A span is visited only if
+// it holds hits of this step (dirty == t) or survivors in ring[cur] to fold;
+// the others are skipped from the summaries alone. For word w with hit mask
+// hm (slots stamped t):
+//   cold     <- (cold | ring[cur]) & ~hm      fold, then hits leave cold
+//   ring[cur] <- hm                           hits join the new current bucket
+//   ring[b]  <- ring[b] & ~hm  (b != cur)     hits leave older ring buckets
+// Hits are never free slots. Span counts are recomputed by wavefront popcount
+// sums; bucket-count changes go to per-workgroup partials that the plan kernel
+// adds up.
+__global__ __launch_bounds__(256) void k_mark(GroupDev g, uint32_t t, int32_t cur) {
+  __shared__ int s_delta[kMaxBuckets];
+  if (block_failed(g.ctr)) return;
+  for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x) s_delta[i] = 0;
+  __syncthreads();
   const int lane = lane_id();
   const int nwaves = gridDim.x * (blockDim.x / kWave);
-  uint32_t* ring = g.bm + (size_t)rb * g.W;
+  const int rc = ring_id(cur);
   uint32_t* cold = g.bm + (size_t)kCold * g.W;
-  uint32_t* rt = g.tcnt + (size_t)rb * g.T;
+  uint32_t* ring = g.bm + (size_t)rc * g.W;
   uint32_t* ct = g.tcnt + (size_t)kCold * g.T;
+  uint32_t* rt = g.tcnt + (size_t)rc * g.T;
   for (int tile = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; tile < g.T;
        tile += nwaves) {
-    const uint32_t cnt = rt[tile];
-    if (cnt == 0) continue;                 // empty span: skipped via the summary
+    const bool hits = g.dirty[tile] == (int32_t)t;
+    const int fold_cnt = (int)rt[tile];
+    if (!hits && fold_cnt == 0) continue;     // nothing to fold, no hit: skip the span
     const int w = tile * kTileWords + lane;
-    if (w < g.W) {
-      const uint32_t r = ring[w];
-      if (r) {
-        cold[w] |= r;
-        ring[w] = 0;
+    const bool valid = w < g.W;
+    uint32_t hm = 0;
+    if (hits && valid) {
+      const vec4u* sp = reinterpret_cast<const vec4u*>(g.stamp + (size_t)w * 32);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const vec4u s4 = sp[q];
+        hm |= (uint32_t)(s4.x == t) << (4 * q) | (uint32_t)(s4.y == t) << (4 * q + 1) |
+              (uint32_t)(s4.z == t) << (4 * q + 2) | (uint32_t)(s4.w == t) << (4 * q + 3);
       }
     }
+    const uint32_t oc = valid ? cold[w] : 0u;
+    const uint32_t orr = (valid && fold_cnt) ? ring[w] : 0u;
+    const uint32_t nc = (oc | orr) & ~hm;
+    if (valid) {
+      if (nc != oc) cold[w] = nc;
+      if (hm != orr) ring[w] = hm;
+    }
+    const int c_cold = wave_sum(__popc(nc));
+    const int c_ring = wave_sum(__popc(hm));
     if (lane == 0) {
-      ct[tile] += cnt;
-      rt[tile] = 0;
+      const int old_cold = (int)ct[tile];
+      ct[tile] = (uint32_t)c_cold;
+      rt[tile] = (uint32_t)c_ring;
+      atomicAdd(&s_delta[kCold], c_cold - old_cold);
+      atomicAdd(&s_delta[rc], c_ring - fold_cnt);
+    }
+    if (hits) {
+      // hits leave the other ring buckets; eight buckets' words in flight at once
+      for (int b0 = 0; b0 < g.B; b0 += 8) {
+        int ob[8];
+        uint32_t x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int b = b0 + j;
+          ob[j] = (b < g.B && b != cur) ? (int)g.tcnt[(size_t)ring_id(b) * g.T + tile] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          x[j] = (ob[j] && valid) ? g.bm[(size_t)ring_id(b0 + j) * g.W + w] : 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (!ob[j]) continue;               // empty span of this bucket (wave-uniform)
+          const int id = ring_id(b0 + j);
+          const uint32_t nx = x[j] & ~hm;
+          if (valid && nx != x[j]) g.bm[(size_t)id * g.W + w] = nx;
+          const int cb = wave_sum(__popc(nx));
+          if (lane == 0 && cb != ob[j]) {
+            g.tcnt[(size_t)id * g.T + tile] = (uint32_t)cb;
+            atomicAdd(&s_delta[id], cb - ob[j]);
+          }
+        }
+      }
     }
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x)
+    g.partial[blockIdx.x * kMaxBuckets + i] = s_delta[i];
 }
 
-// Selection plan. STEP mode: m = misses of the step, sources in eviction order,
-// destination ring[cur]. APPEND mode: m = n, sources [free, free host slots]:
-// the first min(n, free GPU slots) entries take free GPU slots (joining cold),
-// the rest free host slots.
-__global__ __launch_bounds__(1024) void k_plan(GroupDev g, PlanArgs a) {
-  __shared__ int scratch[1024 / kWave + 1];
-  __shared__ unsigned long long s_nonempty[1024 / kWave];  // level-2 summary of a 1024-span chunk
-  if (block_failed(g.ctr)) return;
+// Selection plan (one 1024-thread workgroup). STEP mode: m = misses of the
+// step, sources in eviction order, destination ring[cur]. APPEND mode: m = n,
+// sources [free, free host slots]: the first min(n, free GPU slots) entries take
+// free GPU slots (joining cold), the rest free host slots.
+__device__ void plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
+                          unsigned long long* s_nonempty) {
   Counters* c = g.ctr;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
+  if (a.mode == kPlanStep) {
+    // bucket counts: add the mark kernel's per-workgroup deltas
+    for (int i = tid; i < g.NB; i += blockDim.x) {
+      int s = 0;
+      for (int b = 0; b < kMarkBlocks; ++b) s += g.partial[b * kMaxBuckets + i];
+      c->bcnt[i] += s;
+    }
+    __syncthreads();
+  }
   const int m = (a.mode == kPlanStep) ? c->n_miss : a.n;
   int off = 0;       // output entries planned so far
   int nitems = 0;    // work items written so far
@@ -130,52 +194,90 @@ __global__ __launch_bounds__(1024) void k_plan(GroupDev g, PlanArgs a) {
   }
 }
 
-// STEP: taken GPU slots join ring[cur] (dest) with stamp t; the output list is
-// the victims. APPEND: taken GPU slots join cold (dest) with stamp 0, taken
-// host slots leave the free-host bitmap; the output list is the destinations
-// (host slots carry the host bit).
-__global__ __launch_bounds__(256) void k_extract(GroupDev g, int32_t mode, int32_t dest, uint32_t t) {
-  if (status_of(g.ctr)) return;
-  const int nitems = g.ctr->n_items;
+__global__ __launch_bounds__(1024) void k_plan(GroupDev g, PlanArgs a) {
+  __shared__ int scratch[1024 / kWave + 1];
+  __shared__ unsigned long long s_nonempty[1024 / kWave];  // level-2 summary of a 1024-span chunk
+  if (block_failed(g.ctr)) return;
+  plan_body(g, a, scratch, s_nonempty);
+}
+
+// One wavefront takes the lowest `take` set bits of one span of one bitmap.
+// STEP: taken GPU slots join ring[cur] (dest); the output list is the victims,
+// and victims taken from the free bucket carry the top bit (their slot holds no
+// row to evict). APPEND: taken GPU slots join cold (dest), taken host slots
+// leave the free-host bitmap; the output list is the destinations (host slots
+// carry the host bit).
+__device__ __forceinline__ void extract_item(const GroupDev& g, const SelItem it, int32_t mode,
+                                             int32_t dest, uint32_t* out) {
   const int lane = lane_id();
-  const int nwaves = gridDim.x * (blockDim.x / kWave);
-  uint32_t* out = (mode == kPlanStep) ? g.victims : g.app_dst;
-  const int32_t new_stamp = (mode == kPlanStep) ? (int32_t)t : 0;
-  for (int i = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; i < nitems; i += nwaves) {
-    const SelItem it = g.items[i];
-    const bool host = it.src == kHostFreeId;
-    uint32_t* words = bucket_words(g, it.src);
-    const int w = it.tile * kTileWords + lane;
-    const uint32_t x = w < bucket_nwords(g, it.src) ? words[w] : 0u;
-    const int cnt = __popc(x);
-    const int ex = wave_inclusive_sum(cnt) - cnt;
-    int mine = it.take - ex;                    // lowest set bits this lane gives
-    mine = mine < 0 ? 0 : (mine > cnt ? cnt : mine);
-    uint32_t y = x, taken = 0;
-    for (int r = 0; r < mine; ++r) {
-      const uint32_t low = y & (0u - y);
-      const uint32_t slot = (uint32_t)w * 32u + (uint32_t)(__ffs(y) - 1);
-      y ^= low;
-      taken |= low;
-      out[it.out_off + ex + r] = host ? (kHostBit | slot) : slot;
-      if (!host) g.stamp[slot] = new_stamp;
-    }
-    if (taken) {
-      words[w] = x & ~taken;
-      if (!host) atomicOr(&g.bm[(size_t)dest * g.W + w], taken);
-    }
-    if (lane == 0) {
-      bucket_tcnt(g, it.src)[it.tile] -= (uint32_t)it.take;
-      if (!host) atomicAdd(&g.tcnt[(size_t)dest * g.T + it.tile], (uint32_t)it.take);
-    }
+  const bool host = it.src == kHostFreeId;
+  const uint32_t flag = (host || (mode == kPlanStep && it.src == kFree)) ? kHostBit : 0u;
+  uint32_t* words = bucket_words(g, it.src);
+  const int w = it.tile * kTileWords + lane;
+  const uint32_t x = w < bucket_nwords(g, it.src) ? words[w] : 0u;
+  const int cnt = __popc(x);
+  const int ex = wave_inclusive_sum(cnt) - cnt;
+  int mine = it.take - ex;                    // lowest set bits this lane gives
+  mine = mine < 0 ? 0 : (mine > cnt ? cnt : mine);
+  uint32_t y = x, taken = 0;
+  for (int r = 0; r < mine; ++r) {
+    const uint32_t low = y & (0u - y);
+    const uint32_t slot = (uint32_t)w * 32u + (uint32_t)(__ffs(y) - 1);
+    y ^= low;
+    taken |= low;
+    out[it.out_off + ex + r] = flag | slot;
+  }
+  if (taken) {
+    words[w] = x & ~taken;
+    if (!host) atomicOr(&g.bm[(size_t)dest * g.W + w], taken);
+  }
+  if (lane == 0) {
+    bucket_tcnt(g, it.src)[it.tile] -= (uint32_t)it.take;
+    if (!host) atomicAdd(&g.tcnt[(size_t)dest * g.T + it.tile], (uint32_t)it.take);
   }
 }
 
-hipError_t launch_fold(const GroupDev& g, int32_t cur, hipStream_t s) {
-  int blocks = (g.T + 3) / 4;
-  if (blocks > 2048) blocks = 2048;
-  if (blocks < 1) blocks = 1;
-  k_fold<<<blocks, 256, 0, s>>>(g, cur);
+__global__ __launch_bounds__(256) void k_extract(GroupDev g, int32_t mode, int32_t dest) {
+  if (status_of(g.ctr)) return;
+  const int nitems = g.ctr->n_items;
+  const int nwaves = gridDim.x * (blockDim.x / kWave);
+  uint32_t* out = (mode == kPlanStep) ? g.victims : g.app_dst;
+  for (int i = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; i < nitems; i += nwaves)
+    extract_item(g, g.items[i], mode, dest, out);
+}
+
+// A small append in one workgroup: plan, extraction and placement back to back
+// (the same steps as the plan / extract / place kernels), with the addresses
+// passed by value so that no copy precedes the launch.
+__global__ __launch_bounds__(1024) void k_append_small(GroupDev g, SmallAppend a,
+                                                       const uint8_t* __restrict__ rows,
+                                                       FastDiv per_slot) {
+  __shared__ int scratch[1024 / kWave + 1];
+  __shared__ unsigned long long s_nonempty[1024 / kWave];
+  if (block_failed(g.ctr)) return;
+  PlanArgs p{};
+  p.mode = kPlanAppend;
+  p.n = a.n;
+  p.norder = 2;
+  p.dest = kCold;
+  p.order[0] = kFree;
+  p.order[1] = kHostFreeId;
+  plan_body(g, p, scratch, s_nonempty);
+  __syncthreads();
+  const int nitems = g.ctr->n_items;
+  for (int i = threadIdx.x / kWave; i < nitems; i += blockDim.x / kWave)
+    extract_item(g, g.items[i], kPlanAppend, kCold, g.app_dst);
+  __syncthreads();
+  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
+  const uint32_t total = (uint32_t)a.n * chunks;
+  for (uint32_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
+    const uint32_t i = per_slot.div(idx);
+    place_piece(g, i, idx - i * chunks, a.las[i], rows);
+  }
+}
+
+hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, hipStream_t s) {
+  k_mark<<<kMarkBlocks, 256, 0, s>>>(g, t, cur);
   return hipGetLastError();
 }
 
@@ -184,12 +286,18 @@ hipError_t launch_plan(const GroupDev& g, const PlanArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, uint32_t t,
-                          int32_t max_items, hipStream_t s) {
+hipError_t launch_append_small(const GroupDev& g, const SmallAppend& a, const uint8_t* rows,
+                              hipStream_t s) {
+  k_append_small<<<1, 1024, 0, s>>>(g, a, rows, FastDiv((uint32_t)g.slot_bytes / 16u));
+  return hipGetLastError();
+}
+
+hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, int32_t max_items,
+                          hipStream_t s) {
   int blocks = (max_items + 3) / 4;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
-  k_extract<<<blocks, 256, 0, s>>>(g, mode, dest, t);
+  k_extract<<<blocks, 256, 0, s>>>(g, mode, dest);
   return hipGetLastError();
 }
 

@@ -75,8 +75,8 @@ bool check_config(const ula_config* c, Dims* d) {
 }
 
 struct Layout {
-  size_t map, tag, gown, stamp, hown, bm, tcnt, hbm, htcnt, hits, mla, mh, vict, blk, items,
-      app_la, app_dst, app_rows, pool, group_bytes;
+  size_t map, tag, gown, stamp, dirty, hown, bm, tcnt, hbm, htcnt, hits, mla, mh, vict, blk,
+      partial, items, app_la, app_dst, app_rows, evict_rows, wb_h, pool, group_bytes;
   size_t counters_bytes, total;
 };
 
@@ -91,7 +91,8 @@ Layout layout_of(const ula_config* c, const Dims& d) {
   L.map = take(4 * d.N);
   L.tag = take(8 * d.N);
   L.gown = take(4 * d.P);
-  L.stamp = take(4 * d.P);
+  L.stamp = take(4 * 32 * d.W);
+  L.dirty = take(4 * d.T);
   L.hown = take(4 * d.H);
   L.bm = take(4 * d.NB * d.W);
   L.tcnt = take(4 * d.NB * d.T);
@@ -102,10 +103,13 @@ Layout layout_of(const ula_config* c, const Dims& d) {
   L.mh = take(4 * d.maxU);
   L.vict = take(4 * d.maxU);
   L.blk = take(4 * 3 * d.maxBlk);
+  L.partial = take(4 * kMarkBlocks * kMaxBuckets);
   L.items = take(sizeof(SelItem) * d.maxItems);
   L.app_la = take(4 * d.maxApp);
   L.app_dst = take(4 * d.maxApp);
   L.app_rows = take((size_t)d.maxApp * d.slot_bytes);
+  L.evict_rows = take((size_t)d.maxU * d.slot_bytes);
+  L.wb_h = take(4 * d.maxU);
   L.pool = take((size_t)d.P * d.slot_bytes);
   L.group_bytes = o;
   L.counters_bytes = align_up(sizeof(Counters) * c->num_groups);
@@ -137,6 +141,9 @@ struct GroupHost {
   bool stage_used[kStageSlots] = {};
   int stage_next = 0;
   hipEvent_t ev[6] = {};
+  hipStream_t wb_stream = nullptr;   // side stream of the deferred eviction write-back
+  hipEvent_t ev_swapped = nullptr, ev_wb = nullptr, ev_wb0 = nullptr, ev_wb1 = nullptr;
+  bool wb_pending = false;
 };
 
 struct ula_ctx {
@@ -189,8 +196,12 @@ static void destroy_ctx(ula_ctx* ctx) {
       if (g.stage_ev[i]) (void)hipEventDestroy(g.stage_ev[i]);
       if (g.stage[i]) (void)hipHostFree(g.stage[i]);
     }
+    if (g.wb_stream) (void)hipStreamSynchronize(g.wb_stream);
     for (auto& e : g.ev)
       if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : {g.ev_swapped, g.ev_wb, g.ev_wb0, g.ev_wb1})
+      if (e) (void)hipEventDestroy(e);
+    if (g.wb_stream) (void)hipStreamDestroy(g.wb_stream);
   }
   delete ctx;
 }
@@ -235,6 +246,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     g.tag = reinterpret_cast<unsigned long long*>(b + L.tag);
     g.gown = reinterpret_cast<int32_t*>(b + L.gown);
     g.stamp = reinterpret_cast<int32_t*>(b + L.stamp);
+    g.dirty = reinterpret_cast<int32_t*>(b + L.dirty);
     g.hown = reinterpret_cast<int32_t*>(b + L.hown);
     g.bm = reinterpret_cast<uint32_t*>(b + L.bm);
     g.tcnt = reinterpret_cast<uint32_t*>(b + L.tcnt);
@@ -245,10 +257,13 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     g.miss_h = reinterpret_cast<uint32_t*>(b + L.mh);
     g.victims = reinterpret_cast<uint32_t*>(b + L.vict);
     g.blk = reinterpret_cast<uint32_t*>(b + L.blk);
+    g.partial = reinterpret_cast<int32_t*>(b + L.partial);
     g.items = reinterpret_cast<SelItem*>(b + L.items);
     g.app_la = reinterpret_cast<int32_t*>(b + L.app_la);
     g.app_dst = reinterpret_cast<uint32_t*>(b + L.app_dst);
     g.app_rows = b + L.app_rows;
+    g.evict_rows = b + L.evict_rows;
+    g.wb_h = reinterpret_cast<uint32_t*>(b + L.wb_h);
     g.pool = b + L.pool;
     g.host = hdev ? hdev + (size_t)gi * d.H * d.slot_bytes : nullptr;
     g.N = (int32_t)d.N;
@@ -270,7 +285,8 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     if (e == hipSuccess) e = launch_fill_u32(g.map, d.N, kAbsent, s);
     if (e == hipSuccess) e = launch_fill_u64(g.tag, d.N, 0ull, s);
     if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.gown), d.P, 0xFFFFFFFFu, s);
-    if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.stamp), d.P, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.stamp), 32 * d.W, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.dirty), d.T, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.hown), d.H, 0xFFFFFFFFu, s);
     if (e == hipSuccess) e = launch_fill_u32(g.bm, d.NB * d.W, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(g.tcnt, d.NB * d.T, 0u, s);
@@ -282,6 +298,11 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
       if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.stage_ev[i], hipEventDisableTiming);
     }
     for (int i = 0; i < 6 && e == hipSuccess; ++i) e = hipEventCreate(&gh.ev[i]);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&gh.wb_stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.ev_swapped, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.ev_wb, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreate(&gh.ev_wb0);
+    if (e == hipSuccess) e = hipEventCreate(&gh.ev_wb1);
     if (e != hipSuccess) rc = hip_fail(e, "ula_init");
   }
   if (rc == ULA_OK) {
@@ -327,31 +348,39 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const GroupDev& g = gh.d;
-  for (int32_t off = 0; off < n; off += (int32_t)d.maxApp) {
-    const int32_t cnt = (int32_t)std::min<int64_t>(n - off, d.maxApp);
-    // addresses go through a pinned staging slot so the copy is truly asynchronous
-    const int k = gh.stage_next;
-    gh.stage_next = (k + 1) % kStageSlots;
-    if (gh.stage_used[k]) HIP_TRY(hipEventSynchronize(gh.stage_ev[k]));
-    gh.stage_used[k] = true;
-    std::memcpy(gh.stage[k], la_host + off, sizeof(int32_t) * cnt);
-    HIP_TRY(hipMemcpyAsync(g.app_la, gh.stage[k], sizeof(int32_t) * cnt, hipMemcpyHostToDevice, s));
-    HIP_TRY(hipEventRecord(gh.stage_ev[k], s));
-    const uint8_t* src = static_cast<const uint8_t*>(rows) + (size_t)off * d.slot_bytes;
-    if (!rows_on_device) {
-      HIP_TRY(hipMemcpyAsync(g.app_rows, src, (size_t)cnt * d.slot_bytes, hipMemcpyHostToDevice, s));
-      src = g.app_rows;
+  if (n <= kSmallAppend && n <= d.maxApp && rows_on_device) {
+    // decode-time appends: one workgroup, addresses passed by value
+    SmallAppend a{};
+    a.n = n;
+    std::memcpy(a.las, la_host, sizeof(int32_t) * n);
+    HIP_TRY(launch_append_small(g, a, static_cast<const uint8_t*>(rows), s));
+  } else {
+    for (int32_t off = 0; off < n; off += (int32_t)d.maxApp) {
+      const int32_t cnt = (int32_t)std::min<int64_t>(n - off, d.maxApp);
+      // addresses go through a pinned staging slot so the copy is truly asynchronous
+      const int k = gh.stage_next;
+      gh.stage_next = (k + 1) % kStageSlots;
+      if (gh.stage_used[k]) HIP_TRY(hipEventSynchronize(gh.stage_ev[k]));
+      gh.stage_used[k] = true;
+      std::memcpy(gh.stage[k], la_host + off, sizeof(int32_t) * cnt);
+      HIP_TRY(hipMemcpyAsync(g.app_la, gh.stage[k], sizeof(int32_t) * cnt, hipMemcpyHostToDevice, s));
+      HIP_TRY(hipEventRecord(gh.stage_ev[k], s));
+      const uint8_t* src = static_cast<const uint8_t*>(rows) + (size_t)off * d.slot_bytes;
+      if (!rows_on_device) {
+        HIP_TRY(hipMemcpyAsync(g.app_rows, src, (size_t)cnt * d.slot_bytes, hipMemcpyHostToDevice, s));
+        src = g.app_rows;
+      }
+      PlanArgs a{};
+      a.mode = kPlanAppend;
+      a.n = cnt;
+      a.norder = 2;
+      a.dest = kCold;
+      a.order[0] = kFree;
+      a.order[1] = kHostFreeId;
+      HIP_TRY(launch_plan(g, a, s));
+      HIP_TRY(launch_extract(g, kPlanAppend, kCold, cnt, s));
+      HIP_TRY(launch_place(g, cnt, src, s));
     }
-    PlanArgs a{};
-    a.mode = kPlanAppend;
-    a.n = cnt;
-    a.norder = 2;
-    a.dest = kCold;
-    a.order[0] = kFree;
-    a.order[1] = kHostFreeId;
-    HIP_TRY(launch_plan(g, a, s));
-    HIP_TRY(launch_extract(g, kPlanAppend, kCold, 0u, cnt, s));
-    HIP_TRY(launch_place(g, cnt, src, s));
   }
   for (int32_t i = 0; i < n; ++i) {
     const uint32_t la = (uint32_t)la_host[i];
@@ -374,16 +403,14 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t t = gh.steps + 1;
   const int32_t cur = (int32_t)(t % ctx->dims.B);
-  const int32_t nblk = (n + kScanBlock - 1) / kScanBlock;
   const bool tm = ctx->timing != 0;
 
   if (tm) HIP_TRY(hipEventRecord(gh.ev[0], s));
   HIP_TRY(launch_tag(g, sel_dev, n, (uint32_t)t, s));
   HIP_TRY(launch_count(g, sel_dev, n, (uint32_t)t, s));
-  HIP_TRY(launch_scan(g, nblk, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[1], s));
-  HIP_TRY(launch_fold(g, cur, s));
-  HIP_TRY(launch_compact(g, sel_dev, n, (uint32_t)t, cur, s));
+  HIP_TRY(launch_compact(g, sel_dev, n, (uint32_t)t, s));
+  HIP_TRY(launch_mark(g, (uint32_t)t, cur, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
   PlanArgs a{};
   a.mode = kPlanStep;
@@ -394,11 +421,20 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   for (int j = 1; j < ctx->dims.B; ++j) a.order[a.norder++] = (int8_t)ring_id((cur + j) % ctx->dims.B);
   HIP_TRY(launch_plan(g, a, s));
   const int32_t max_pairs = (int32_t)std::min<int64_t>(n, ctx->dims.maxU);
-  HIP_TRY(launch_extract(g, kPlanStep, a.dest, (uint32_t)t, max_pairs, s));
+  HIP_TRY(launch_extract(g, kPlanStep, a.dest, max_pairs, s));
+  // the previous step's write-back must land before host slots are read again
+  if (gh.wb_pending) HIP_TRY(hipStreamWaitEvent(s, gh.ev_wb, 0));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[3], s));
-  HIP_TRY(launch_swap(g, max_pairs, s));
+  HIP_TRY(launch_swap_in(g, max_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[4], s));
-  HIP_TRY(launch_commit(g, (long long)t, s));
+  HIP_TRY(hipEventRecord(gh.ev_swapped, s));
+  HIP_TRY(hipStreamWaitEvent(gh.wb_stream, gh.ev_swapped, 0));
+  if (tm) HIP_TRY(hipEventRecord(gh.ev_wb0, gh.wb_stream));
+  HIP_TRY(launch_writeback(g, max_pairs, gh.wb_stream));
+  if (tm) HIP_TRY(hipEventRecord(gh.ev_wb1, gh.wb_stream));
+  HIP_TRY(hipEventRecord(gh.ev_wb, gh.wb_stream));
+  gh.wb_pending = true;
+  HIP_TRY(launch_commit(g, (long long)t, max_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[5], s));
   gh.steps = t;
   return ULA_OK;
@@ -438,6 +474,7 @@ static void fill_stats(const Counters& c, ula_step_stats* s) {
 int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out) {
   if (!ctx) return ULA_EINVAL;
   HIP_TRY(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
+  for (auto& gh : ctx->groups) HIP_TRY(hipStreamSynchronize(gh.wb_stream));
   std::vector<Counters> c;
   int rc = read_counters(ctx, c);
   if (rc) return rc;
@@ -511,12 +548,14 @@ int ula_set_timing(ula_ctx* ctx, int32_t enable) {
   return ULA_OK;
 }
 
-int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out5) {
-  if (!ctx || !ms_out5) return ULA_EINVAL;
+int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out6) {
+  if (!ctx || !ms_out6) return ULA_EINVAL;
   if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
   GroupHost& gh = ctx->groups[group];
   HIP_TRY(hipEventSynchronize(gh.ev[5]));
-  for (int i = 0; i < 5; ++i) HIP_TRY(hipEventElapsedTime(&ms_out5[i], gh.ev[i], gh.ev[i + 1]));
+  HIP_TRY(hipEventSynchronize(gh.ev_wb1));
+  for (int i = 0; i < 5; ++i) HIP_TRY(hipEventElapsedTime(&ms_out6[i], gh.ev[i], gh.ev[i + 1]));
+  HIP_TRY(hipEventElapsedTime(&ms_out6[5], gh.ev_wb0, gh.ev_wb1));
   return ULA_OK;
 }
 

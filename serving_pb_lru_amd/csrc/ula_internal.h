@@ -4,16 +4,20 @@
 //   map    u32[N]        logical -> physical (GPU slot, 0x80000000|host slot, or absent)
 //   tag    u64[N]        de-duplication scratch: (step << 32) | ~position, max wins
 //   gown   i32[P]        owner address of each GPU slot, -1 = empty
-//   stamp  i32[P]        step that last put the slot in a ring bucket (0 = never);
-//                        lets hit marking find a slot's bucket in O(1): the slot
-//                        is in ring[stamp % B] if step - stamp < B, else in cold
+//   stamp  i32[32 W]     step that last hit the slot (0 = never); the slots with
+//                        stamp == t are the hits of step t. Padded to whole
+//                        32-slot words (padding stays 0) so a lane reads one
+//                        word's 32 stamps as eight 16-byte loads
+//   dirty  i32[T]        step that last had a hit in each 2048-slot span
 //   hown   i32[H]        owner address of each host slot, -1 = empty
 //   bm     u32[NB][W]    bucket bitmaps, NB = B + 2: free, cold, ring[0..B-1]
 //   tcnt   u32[NB][T]    summary level 1: set bits per 2048-slot span (64 words,
 //                        one wavefront load) of each bucket, kept exact
 //   hbm    u32[WH]       free host slots bitmap, htcnt u32[TH] its span counts
-//   lists  hit slots, misses (address, host slot), victims, block sums, work items
-//   stage  append addresses, destinations and (host-sourced) rows
+//   lists  hit slots, misses (address, host slot), victims, block sums, work items,
+//          per-block bucket-count deltas of the mark kernel
+//   stage  append addresses, destinations and (host-sourced) rows; evicted rows
+//          awaiting their write-back to the host, with their host slots
 //   pool   u8[P][Lg][row_bytes]   the GPU pool, slot-major: one slot holds all
 //                        layers of its group contiguously
 // The host pool is u8[H][Lg][row_bytes] per group in pinned, device-mapped memory.
@@ -36,6 +40,7 @@ constexpr int kTileShift = 11;                  // 2048 slots per span
 constexpr int kScanBlock = 1024;                // selection entries per de-dup block
 constexpr int kMaxRing = 64;                    // B <= 64
 constexpr int kMaxBuckets = kMaxRing + 2;
+constexpr int kMarkBlocks = 128;                // fixed grid of the fold + hit-marking kernel
 
 // bucket ids
 constexpr int kFree = 0;
@@ -51,7 +56,8 @@ struct alignas(64) Counters {
   int32_t n_items;       // work items written by the last selection plan
   int32_t hfree;         // free host slots
   int32_t bcnt[kMaxBuckets];  // slots per bucket
-  int32_t pad[2];
+  int32_t wb_n;          // pairs of the last swap, for its deferred write-back
+  int32_t pad[1];
 };
 static_assert(sizeof(Counters) % 64 == 0, "counter block alignment");
 
@@ -69,6 +75,7 @@ struct GroupDev {        // device view of one group, passed by value to kernels
   unsigned long long* tag;
   int32_t* gown;
   int32_t* stamp;
+  int32_t* dirty;
   int32_t* hown;
   uint32_t* bm;
   uint32_t* tcnt;
@@ -79,10 +86,13 @@ struct GroupDev {        // device view of one group, passed by value to kernels
   uint32_t* miss_h;
   uint32_t* victims;
   uint32_t* blk;         // 3 words per de-dup block: hits, misses, invalid (then offsets)
+  int32_t* partial;      // [kMarkBlocks][kMaxBuckets] bucket-count deltas of the mark kernel
   SelItem* items;
   int32_t* app_la;
   uint32_t* app_dst;
   uint8_t* app_rows;
+  uint8_t* evict_rows;   // [maxU][slot_bytes] evicted rows staged for the write-back
+  uint32_t* wb_h;        // [maxU] host slot each staged row goes to, or absent
   uint8_t* pool;
   uint8_t* host;
   int32_t N, P, H, B, NB, W, T, WH, TH, Lg, row_bytes, slot_bytes;
@@ -119,6 +129,13 @@ struct PlanArgs {
   int8_t order[kMaxBuckets + 1];
 };
 
+constexpr int kSmallAppend = 256;   // appends up to this size run as one workgroup
+
+struct SmallAppend {
+  int32_t n;
+  int32_t las[kSmallAppend];
+};
+
 // ---- launchers (one translation unit per kernel family) ----------------
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_fill_u64(unsigned long long* p, size_t n, unsigned long long v, hipStream_t s);
@@ -128,16 +145,17 @@ hipError_t launch_init_counters(Counters* c, int32_t P, int32_t H, hipStream_t s
 
 hipError_t launch_tag(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
 hipError_t launch_count(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
-hipError_t launch_scan(const GroupDev& g, int32_t nblk, hipStream_t s);
-hipError_t launch_fold(const GroupDev& g, int32_t cur, hipStream_t s);
-hipError_t launch_compact(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t,
-                          int32_t cur, hipStream_t s);
+hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, hipStream_t s);
+hipError_t launch_compact(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
 hipError_t launch_plan(const GroupDev& g, const PlanArgs& a, hipStream_t s);
-hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, uint32_t t,
-                          int32_t max_items, hipStream_t s);
+hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, int32_t max_items,
+                          hipStream_t s);
+hipError_t launch_append_small(const GroupDev& g, const SmallAppend& a, const uint8_t* rows,
+                              hipStream_t s);
 hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s);
-hipError_t launch_swap(const GroupDev& g, int32_t max_pairs, hipStream_t s);
-hipError_t launch_commit(const GroupDev& g, long long t, hipStream_t s);
+hipError_t launch_swap_in(const GroupDev& g, int32_t max_pairs, hipStream_t s);
+hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s);
+hipError_t launch_commit(const GroupDev& g, long long t, int32_t max_pairs, hipStream_t s);
 hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
                          uint8_t* out, long long want_flag, hipStream_t s);
 
