@@ -182,18 +182,20 @@ def gpu_run(tr, W: int, K: int, phases: bool) -> dict:
         ph = np.zeros(6)
         h2d = d2h = 0
         n = 0
+        prev_evict = {g: 0 for g in groups}
         for t in range(1, W + K + 1):
             for g in groups:
                 if apps[t - 1].size:
                     eng.append(g, apps[t - 1], app_rows[g][t - 1])
                 eng.step(g, sels[g][t - 1])
-                ms = eng.read_timing(g)
+                ms = eng.read_timing(g)   # [5] is the write-back of the previous step's evictions
                 st = eng.sync()[g]
                 if t > W:
                     ph += ms
                     h2d += st[2]
-                    d2h += st[3]
+                    d2h += prev_evict[g]
                     n += 1
+                prev_evict[g] = st[3]
         eng.close()
         res.update(phase_ms=(ph / max(n, 1)).tolist(), swap_in_ms_total=float(ph[3]),
                    writeback_ms_total=float(ph[5]), h2d_rows=int(h2d), d2h_rows=int(d2h), group_steps=n)

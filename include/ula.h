@@ -145,10 +145,11 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host,
  * the host pool (the victims' rows are staged in device memory first); then
  * update the mapping table and owners and raise the completion counter to the
  * step number. The staged victim rows are written to the host slots their
- * misses vacated on a library-owned side stream, overlapping the work that
- * follows; the group's next step waits for that write-back before it reads the
- * host pool, and ula_sync waits for it too. Enqueued on `stream` with no host
- * synchronisation.
+ * misses vacated on a library-owned side stream, launched at the start of the
+ * group's next step so that it overlaps that step's lookup and selection; the
+ * next step's swap waits for it before it reads the host pool, and ula_sync,
+ * ula_export_state and ula_read_rows complete it. Enqueued on `stream` with no
+ * host synchronisation.
  * Host errors: ULA_EINVAL (bad g, n_sets > max_sets, k > max_k, negative sizes),
  * ULA_ESTATE. Device errors (reported by ula_sync): ULA_ERANGE, ULA_ECAPACITY. */
 int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
@@ -167,9 +168,10 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
 int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32_t k,
                const int32_t* sel_dev, void* out_dev, uint64_t stream);
 
-/* Wait for `stream`, then report the first latched device error of any group
- * (poisoning the context) or ULA_OK. per_group_out (nullable, num_groups
- * entries) receives each group's last step statistics. */
+/* Wait for `stream`, complete every group's outstanding eviction write-back,
+ * then report the first latched device error of any group (poisoning the
+ * context) or ULA_OK. per_group_out (nullable, num_groups entries) receives
+ * each group's last step statistics. */
 int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out);
 
 /* Copy group g's canonical state into caller host buffers (synchronises the
@@ -190,9 +192,9 @@ int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr);
 /* Per-phase timing of the last step of group g, in milliseconds, when enabled
  * with ula_set_timing: [0] lookup + de-duplication, [1] hit marking + fold,
  * [2] victim selection, [3] missed rows in over the host link, [4] commit +
- * signal, [5] evicted rows out over the host link (on the group's side stream,
- * overlapping what follows the step). ula_read_timing synchronises on the
- * step's last events. */
+ * signal, [5] the previous step's evicted rows out over the host link (on the
+ * group's side stream, launched at the start of this step; 0 if none was
+ * timed). ula_read_timing synchronises on the step's last events. */
 int ula_set_timing(ula_ctx* ctx, int32_t enable);
 int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out6);
 

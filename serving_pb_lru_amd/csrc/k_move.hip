@@ -84,10 +84,11 @@ __global__ __launch_bounds__(256) void k_swap_in(GroupDev g, FastDiv per_slot) {
 }
 
 // Miss path, deferred part (side stream): the staged victim rows go to the host
-// slots their misses vacated. It overlaps the gathers; the next step's
-// k_swap_in waits for it, so a later read of one of these host slots always
-// sees the written row. It depends only on wb_n / wb_h / evict_rows, which no
-// kernel rewrites before that wait.
+// slots their misses vacated. It is launched when the group's next step starts
+// and overlaps that step's lookup and selection; the next k_swap_in waits for
+// it, so a later read of one of these host slots always sees the written row.
+// It depends only on wb_n / wb_h / evict_rows, which no kernel rewrites before
+// that wait.
 __global__ __launch_bounds__(256) void k_writeback(GroupDev g, FastDiv per_slot) {
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
   const uint32_t total = (uint32_t)g.ctr->wb_n * chunks;
@@ -184,9 +185,8 @@ hipError_t launch_swap_in(const GroupDev& g, int32_t max_pairs, hipStream_t s) {
 }
 
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s) {
-  // A few workgroups are enough to keep the link busy (1 MB of stores in
-  // flight); a full-chip grid would hold the compute units that the gathers
-  // running at the same time need.
+  // 64 workgroups keep about 1 MB of stores in flight, enough to saturate the
+  // link; more would only hold compute units the concurrent kernels need.
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
   int blocks = grid_for_pairs(max_pairs, chunks);
   if (blocks > 64) blocks = 64;

@@ -142,8 +142,11 @@ struct GroupHost {
   int stage_next = 0;
   hipEvent_t ev[6] = {};
   hipStream_t wb_stream = nullptr;   // side stream of the deferred eviction write-back
-  hipEvent_t ev_swapped = nullptr, ev_wb = nullptr, ev_wb0 = nullptr, ev_wb1 = nullptr;
-  bool wb_pending = false;
+  hipEvent_t ev_fork = nullptr, ev_wb = nullptr, ev_wb0 = nullptr, ev_wb1 = nullptr;
+  bool wb_staged = false;    // evicted rows staged by the last swap, write-back not launched yet
+  bool wb_pending = false;   // write-back launched on the side stream, not yet waited for
+  bool wb_timed = false;     // ev_wb0 / ev_wb1 hold a measured write-back
+  hipStream_t last_stream = nullptr;   // stream of the group's last step
 };
 
 struct ula_ctx {
@@ -199,7 +202,7 @@ static void destroy_ctx(ula_ctx* ctx) {
     if (g.wb_stream) (void)hipStreamSynchronize(g.wb_stream);
     for (auto& e : g.ev)
       if (e) (void)hipEventDestroy(e);
-    for (hipEvent_t e : {g.ev_swapped, g.ev_wb, g.ev_wb0, g.ev_wb1})
+    for (hipEvent_t e : {g.ev_fork, g.ev_wb, g.ev_wb0, g.ev_wb1})
       if (e) (void)hipEventDestroy(e);
     if (g.wb_stream) (void)hipStreamDestroy(g.wb_stream);
   }
@@ -299,7 +302,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     }
     for (int i = 0; i < 6 && e == hipSuccess; ++i) e = hipEventCreate(&gh.ev[i]);
     if (e == hipSuccess) e = hipStreamCreateWithFlags(&gh.wb_stream, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.ev_swapped, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.ev_fork, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.ev_wb, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreate(&gh.ev_wb0);
     if (e == hipSuccess) e = hipEventCreate(&gh.ev_wb1);
@@ -390,6 +393,38 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
   return ULA_OK;
 }
 
+// The write-back of a step's evicted rows is launched at the start of the
+// group's next step, on the side stream, so that it overlaps that step's
+// latency-bound lookup and selection kernels and not the HBM-bound gathers
+// (host-link writes slow concurrent HBM traffic). The next swap waits for it.
+static int fork_writeback(ula_ctx* ctx, GroupHost& gh, hipStream_t s) {
+  if (!gh.wb_staged) return ULA_OK;
+  const int32_t max_pairs = (int32_t)ctx->dims.maxU;
+  HIP_TRY(hipEventRecord(gh.ev_fork, s));
+  HIP_TRY(hipStreamWaitEvent(gh.wb_stream, gh.ev_fork, 0));
+  if (ctx->timing) HIP_TRY(hipEventRecord(gh.ev_wb0, gh.wb_stream));
+  HIP_TRY(launch_writeback(gh.d, max_pairs, gh.wb_stream));
+  if (ctx->timing) {
+    HIP_TRY(hipEventRecord(gh.ev_wb1, gh.wb_stream));
+    gh.wb_timed = true;
+  }
+  HIP_TRY(hipEventRecord(gh.ev_wb, gh.wb_stream));
+  gh.wb_staged = false;
+  gh.wb_pending = true;
+  return ULA_OK;
+}
+
+// Finish every group's outstanding write-back (before the host looks at state).
+static int flush_writebacks(ula_ctx* ctx) {
+  for (auto& gh : ctx->groups) {
+    int rc = fork_writeback(ctx, gh, gh.last_stream);
+    if (rc) return rc;
+  }
+  HIP_TRY(hipDeviceSynchronize());
+  for (auto& gh : ctx->groups) gh.wb_pending = false;
+  return ULA_OK;
+}
+
 int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
              uint64_t stream) {
   if (!ctx) return ULA_EINVAL;
@@ -405,6 +440,11 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   const int32_t cur = (int32_t)(t % ctx->dims.B);
   const bool tm = ctx->timing != 0;
 
+  {
+    int rc = fork_writeback(ctx, gh, s);
+    if (rc) return rc;
+  }
+  gh.last_stream = s;
   if (tm) HIP_TRY(hipEventRecord(gh.ev[0], s));
   HIP_TRY(launch_tag(g, sel_dev, n, (uint32_t)t, s));
   HIP_TRY(launch_count(g, sel_dev, n, (uint32_t)t, s));
@@ -423,17 +463,14 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   const int32_t max_pairs = (int32_t)std::min<int64_t>(n, ctx->dims.maxU);
   HIP_TRY(launch_extract(g, kPlanStep, a.dest, max_pairs, s));
   // the previous step's write-back must land before host slots are read again
-  if (gh.wb_pending) HIP_TRY(hipStreamWaitEvent(s, gh.ev_wb, 0));
+  if (gh.wb_pending) {
+    HIP_TRY(hipStreamWaitEvent(s, gh.ev_wb, 0));
+    gh.wb_pending = false;
+  }
   if (tm) HIP_TRY(hipEventRecord(gh.ev[3], s));
   HIP_TRY(launch_swap_in(g, max_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[4], s));
-  HIP_TRY(hipEventRecord(gh.ev_swapped, s));
-  HIP_TRY(hipStreamWaitEvent(gh.wb_stream, gh.ev_swapped, 0));
-  if (tm) HIP_TRY(hipEventRecord(gh.ev_wb0, gh.wb_stream));
-  HIP_TRY(launch_writeback(g, max_pairs, gh.wb_stream));
-  if (tm) HIP_TRY(hipEventRecord(gh.ev_wb1, gh.wb_stream));
-  HIP_TRY(hipEventRecord(gh.ev_wb, gh.wb_stream));
-  gh.wb_pending = true;
+  gh.wb_staged = true;
   HIP_TRY(launch_commit(g, (long long)t, max_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[5], s));
   gh.steps = t;
@@ -474,7 +511,10 @@ static void fill_stats(const Counters& c, ula_step_stats* s) {
 int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out) {
   if (!ctx) return ULA_EINVAL;
   HIP_TRY(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
-  for (auto& gh : ctx->groups) HIP_TRY(hipStreamSynchronize(gh.wb_stream));
+  {
+    int rc = flush_writebacks(ctx);
+    if (rc) return rc;
+  }
   std::vector<Counters> c;
   int rc = read_counters(ctx, c);
   if (rc) return rc;
@@ -491,7 +531,10 @@ int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out) {
   if (!ctx || !out) return ULA_EINVAL;
   if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
   if (!out->map || !out->gown || !out->bitsets || (ctx->dims.H > 0 && !out->hown)) return ULA_EINVAL;
-  HIP_TRY(hipDeviceSynchronize());
+  {
+    int rc = flush_writebacks(ctx);
+    if (rc) return rc;
+  }
   const GroupDev& g = ctx->groups[group].d;
   const Dims& d = ctx->dims;
   HIP_TRY(hipMemcpy(out->map, g.map, 4 * d.N, hipMemcpyDeviceToHost));
@@ -514,7 +557,10 @@ int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host
   const Dims& d = ctx->dims;
   for (int32_t i = 0; i < n; ++i)
     if (la_host[i] < 0 || la_host[i] >= d.N) return ULA_ERANGE;
-  HIP_TRY(hipDeviceSynchronize());
+  {
+    int rc = flush_writebacks(ctx);
+    if (rc) return rc;
+  }
   const GroupDev& g = ctx->groups[group].d;
   std::vector<uint32_t> map(d.N);
   HIP_TRY(hipMemcpy(map.data(), g.map, 4 * d.N, hipMemcpyDeviceToHost));
@@ -553,9 +599,12 @@ int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out6) {
   if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
   GroupHost& gh = ctx->groups[group];
   HIP_TRY(hipEventSynchronize(gh.ev[5]));
-  HIP_TRY(hipEventSynchronize(gh.ev_wb1));
   for (int i = 0; i < 5; ++i) HIP_TRY(hipEventElapsedTime(&ms_out6[i], gh.ev[i], gh.ev[i + 1]));
-  HIP_TRY(hipEventElapsedTime(&ms_out6[5], gh.ev_wb0, gh.ev_wb1));
+  ms_out6[5] = 0.f;
+  if (gh.wb_timed) {
+    HIP_TRY(hipEventSynchronize(gh.ev_wb1));
+    HIP_TRY(hipEventElapsedTime(&ms_out6[5], gh.ev_wb0, gh.ev_wb1));
+  }
   return ULA_OK;
 }
 

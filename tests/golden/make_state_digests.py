@@ -1,0 +1,58 @@
+"""Write tests/golden/digests_<workload>.json from the CPU oracle only.
+
+For every workload preset, every layer group and every step, the oracle (in
+metadata mode: mapping table, owners, buckets, no row bytes) replays the seeded
+synthetic trace and the digest of its exported state is stored: after the
+initial load (step 0) and after each step. The GPU parity tests replay the same
+inputs through the engine and compare digests. Usage:
+
+    python tests/golden/make_state_digests.py [workload ...]
+"""
+
+import json
+import os
+import sys
+from concurrent.futures import ProcessPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.dirname(HERE))
+
+from digests import digest  # noqa: E402
+from oracle.replay import initial_load, new_group  # noqa: E402
+from synth import PRESETS, Trace, preset  # noqa: E402
+
+
+def group_digests(name: str, g: int) -> list:
+    tr = Trace(preset(name))
+    grp = new_group(tr, full_data=False)
+    initial_load(grp, tr, g)
+    out = [digest(grp.export_state())]
+    sels = tr.selections(g)
+    for t in range(1, tr.steps + 1):
+        grp.append(tr.appends(t), None)
+        grp.step(next(sels))
+        out.append(digest(grp.export_state()))
+    return out
+
+
+def main(names):
+    jobs = [(n, g) for n in names for g in range(preset(n).groups)]
+    with ProcessPoolExecutor(max_workers=min(6, len(jobs))) as ex:
+        res = list(ex.map(group_digests, [j[0] for j in jobs], [j[1] for j in jobs]))
+    by = {}
+    for (n, g), d in zip(jobs, res):
+        by.setdefault(n, {})[g] = d
+    for n in names:
+        wl = preset(n)
+        doc = {"workload": n, "source": "oracle/ (metadata mode) via tests/golden/make_state_digests.py",
+               "digest": "xxh3_64 of the little-endian bytes of map, gown, hown, bitsets",
+               "steps": wl.steps, "groups": [by[n][g] for g in range(wl.groups)]}
+        with open(os.path.join(HERE, f"digests_{n}.json"), "w") as f:
+            json.dump(doc, f, separators=(",", ":"))
+        print("wrote", n, flush=True)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:] or list(PRESETS))

@@ -1,0 +1,98 @@
+"""Full-size parity on the GPU: every workload preset at its real sizes.
+
+After the initial load and after every step the digest of the engine's
+exported state (mapping table, owners, bucket bitsets, current bucket,
+completion counter, step statistics) must equal the digest the CPU oracle
+produced for the same seeded inputs (tests/golden/digests_<workload>.json,
+written by tests/golden/make_state_digests.py from oracle/ alone). Gathered
+bytes are checked on sampled rows against their closed form (row contents are
+a function of group, address and layer), and stored rows on sampled addresses
+(wherever they live, GPU or host pool) likewise.
+
+Layer groups are independent (their own pools, maps and buckets), so each
+group runs in an engine of its own; that keeps the pinned host pool of the
+24-group workload within one group's share at a time.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+from digests import digest
+from gpu_harness import say
+from synth import Trace, preset, rows_for
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _golden(name):
+    with open(os.path.join(HERE, "golden", f"digests_{name}.json")) as f:
+        return json.load(f)
+
+
+def _cmp(got, want, where):
+    for k in ("map", "gown", "hown", "bitsets", "cur", "flag", "stats"):
+        assert got[k] == want[k], f"{where}: {k} differs (engine {got[k]}, oracle {want[k]})"
+
+
+def run_group(name: str, g: int, samples: int = 1024):
+    import torch
+    from serving_pb_lru_amd import Engine
+    from synth.device import rows_device
+
+    wl = preset(name)
+    tr = Trace(wl)
+    gold = _golden(name)["groups"][g]
+    say(f"full parity {name} group {g}: N={tr.N} P={tr.P} H={tr.H} steps={tr.steps}")
+    eng = Engine(1, wl.layers, wl.row_bytes, wl.ring, tr.N, tr.P, tr.H, tr.n_sets, tr.k,
+                 max_append=1 << 16)
+    rows = lambda las: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    rng = np.random.default_rng([g, 2024])
+    try:
+        order = tr.initial_load_order()
+        for s in range(0, order.size, 1 << 18):
+            las = order[s:s + (1 << 18)]
+            eng.append(0, las, rows(las))
+        _cmp(digest(eng.export_state(0)), gold[0], f"{name} g{g} after load")
+        known = [order]
+        sels = tr.selections(g)
+        for t in range(1, tr.steps + 1):
+            sel = next(sels)
+            dsel = torch.from_numpy(sel).cuda()
+            app = tr.appends(t)
+            known.append(app)
+            if app.size:
+                eng.append(0, app, rows(app))
+            eng.step(0, dsel)
+            outs = [eng.gather(0, l, dsel) for l in range(wl.layers)]
+            eng.sync()
+            _cmp(digest(eng.export_state(0)), gold[t], f"{name} g{g} step {t}")
+            flat = sel.reshape(-1)
+            idx = rng.choice(flat.size, size=min(samples, flat.size), replace=False)
+            want = rows_for(wl.seed, g, flat[idx], wl.layers, wl.row_bytes)
+            tidx = torch.from_numpy(idx).cuda()
+            for l in range(wl.layers):
+                got = outs[l].view(-1, wl.row_bytes).index_select(0, tidx).cpu().numpy()
+                assert np.array_equal(got, want[:, l]), f"{name} g{g} step {t} layer {l}: gathered rows differ"
+            pool = np.concatenate(known)
+            probe = pool[rng.choice(pool.size, size=128, replace=False)]
+            assert np.array_equal(eng.read_rows(0, probe),
+                                  rows_for(wl.seed, g, probe, wl.layers, wl.row_bytes)), \
+                f"{name} g{g} step {t}: stored rows differ"
+    finally:
+        eng.close()
+
+
+CASES = ([("tiny_4x4k", 0), ("r16_64k_g1x3", 0)]
+         + [("r64_64k128k_g24x3", g) for g in range(24)]
+         + [("spec3_r128_64k128k_g4", g) for g in range(4)]
+         + [("evict_r256_128k_g2", g) for g in range(2)]
+         + [("evict_r256_128k_g2_ctl98", g) for g in range(2)])
+
+
+@pytest.mark.parametrize("name,g", CASES, ids=[f"{n}-g{g}" for n, g in CASES])
+def test_full_size_parity(name, g):
+    run_group(name, g)
