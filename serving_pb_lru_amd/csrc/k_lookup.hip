@@ -132,7 +132,9 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
       s_base[1] = x[1];
       const int u = x[2] + x[3];
       s_base[2] = u > g.P;
-      if (blockIdx.x == 0) {
+      if (blockIdx.x == 0 && u > g.P) {
+        latch(g.ctr, ULA_ECAPACITY);   // before anything changes, statistics included
+      } else if (blockIdx.x == 0) {
         Counters* c = g.ctr;
         c->n_hits = x[2];
         c->n_miss = x[3];
@@ -144,7 +146,6 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
         c->stats[3] = 0;
         c->stats[4] = 0;
         c->stats[5] = x[4];
-        if (u > g.P) latch(c, ULA_ECAPACITY);
       }
     }
     __syncthreads();

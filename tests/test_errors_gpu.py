@@ -1,0 +1,247 @@
+"""Error paths, empty steps, ordering and determinism of the engine (GPU).
+
+Errors found on the host return at once and change nothing; errors found on
+the device are latched, the rest of the step changes nothing, ula_sync
+reports them and the context refuses further work (ULA_ESTATE) while its
+state stays exportable. Every error is provoked by host-chosen arguments that
+the kernels check: no kernel faults or waits on purpose.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+from digests import digest
+from gpu_harness import run_parity
+from oracle.replay import initial_load as oracle_load, new_group
+from synth import Trace, preset, rows_for, scaled
+from tracegen import tiny_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _engine(wl=None, steps=None):
+    """An engine over the tiny workload with its initial history loaded."""
+    from serving_pb_lru_amd.replay import engine_for, initial_load
+    from synth.device import rows_device
+    wl = wl or preset("tiny_4x4k")
+    tr = Trace(wl, steps)
+    eng = engine_for(tr, max_append=4096)
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    initial_load(eng, tr, [0], rows)
+    return tr, eng, rows
+
+
+def _cuda(a):
+    import torch
+    return torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def _state(eng):
+    return digest(eng.export_state(0))
+
+
+@pytest.mark.parametrize("bad", ["range", "never_appended", "negative", "capacity"])
+def test_device_errors_latch_and_change_nothing(bad):
+    from serving_pb_lru_amd import Engine, UlaError
+    from synth.device import rows_device
+    tr = Trace(preset("tiny_4x4k"))
+    wl = tr.wl
+    # max_k wide enough for a step with more distinct entries than GPU slots
+    eng = Engine(1, wl.layers, wl.row_bytes, wl.ring, tr.N, tr.P, tr.H, max_sets=tr.n_sets,
+                 max_k=tr.P + 1, max_append=4096)
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    try:
+        order = tr.initial_load_order()
+        eng.append(0, order, rows(order, 0))
+        sel = next(tr.selections(0)).copy()
+        if bad == "range":
+            sel[0, 5] = tr.N
+        elif bad == "never_appended":
+            sel[0, 5] = tr.appends(3)[0]          # reserved address, appended later
+        elif bad == "negative":
+            sel[0, 5] = -7
+        else:
+            sel = order[: tr.P + 1][None, :]       # all appended, all distinct
+        want = "ECAPACITY" if bad == "capacity" else "ERANGE"
+        before = _state(eng)
+        d = _cuda(sel)
+        eng.step(0, d)
+        with pytest.raises(UlaError) as e:
+            eng.sync()
+        assert e.value.name == want
+        assert _state(eng) == before
+        for call in (lambda: eng.step(0, d), lambda: eng.gather(0, 0, d),
+                     lambda: eng.append(0, tr.appends(1), rows(tr.appends(1), 0))):
+            with pytest.raises(UlaError) as e:
+                call()
+            assert e.value.name == "ESTATE"
+    finally:
+        eng.close()
+
+
+def test_host_errors_change_nothing():
+    from serving_pb_lru_amd import UlaError
+    tr, eng, rows = _engine()
+    try:
+        sel = _cuda(next(tr.selections(0)))
+        with pytest.raises(UlaError) as e:
+            eng.gather(0, 0, sel)                 # no step yet
+        assert e.value.name == "ENOTRESIDENT"
+        before = _state(eng)
+        app = tr.appends(1)
+        cases = [
+            ("ERANGE", lambda: eng.append(0, np.array([tr.N]), rows(np.array([0]), 0))),
+            ("EDUP", lambda: eng.append(0, np.array([0]), rows(np.array([0]), 0))),
+            ("EDUP", lambda: eng.append(0, np.array([app[0], app[0]]), rows(np.array([0, 0]), 0))),
+            ("EINVAL", lambda: eng.step(1, sel)),
+            ("EINVAL", lambda: eng.step(0, _cuda(np.zeros((tr.n_sets + 1, tr.k))))),
+            ("EINVAL", lambda: eng.gather(0, 1, sel)),
+        ]
+        for name, fn in cases:
+            with pytest.raises(UlaError) as e:
+                fn()
+            assert e.value.name == name
+        eng.sync()
+        assert _state(eng) == before
+    finally:
+        eng.close()
+
+
+def test_host_pool_full_rejected():
+    from serving_pb_lru_amd import Engine, UlaError
+    eng = Engine(1, 1, 64, 2, logical_capacity=16, gpu_slots=4, host_slots=4, max_sets=1, max_k=4)
+    try:
+        eng.append(0, np.arange(8), rows_for(0, 0, np.arange(8), 1, 64))
+        before = _state(eng)
+        with pytest.raises(UlaError) as e:
+            eng.append(0, np.array([9]), rows_for(0, 0, [9], 1, 64))
+        assert e.value.name == "EHOSTFULL"
+        assert _state(eng) == before
+    finally:
+        eng.close()
+
+
+def test_gather_of_host_resident_entry_latches():
+    from serving_pb_lru_amd import UlaError
+    tr, eng, rows = _engine()
+    try:
+        sel = next(tr.selections(0))
+        app = tr.appends(1)
+        eng.append(0, app, rows(app, 0))
+        eng.step(0, _cuda(sel))
+        eng.sync()
+        st = eng.export_state(0)
+        on_host = int(np.flatnonzero(st["map"] & 0x80000000 != 0)[0])
+        before = digest(st)
+        eng.gather(0, 0, _cuda([[on_host]]))
+        with pytest.raises(UlaError) as e:
+            eng.sync()
+        assert e.value.name == "ENOTRESIDENT"
+        assert _state(eng) == before
+    finally:
+        eng.close()
+
+
+def test_empty_and_all_padding_steps_match_oracle():
+    import torch
+    tr, eng, rows = _engine()
+    wl = tr.wl
+    ora = new_group(tr, full_data=True)
+    oracle_load(ora, tr, 0)
+    try:
+        for i, sel in enumerate([np.zeros((0, tr.k), np.int32), np.full((tr.n_sets, 7), -1, np.int32),
+                                 next(tr.selections(0))]):
+            if i == 2:   # the trace's first selection may pick the positions appended with it
+                app = tr.appends(1)
+                eng.append(0, app, rows(app, 0))
+                ora.append(app, rows_for(wl.seed, 0, app, wl.layers, wl.row_bytes))
+            d = _cuda(sel)
+            eng.step(0, d)
+            outs = [eng.gather(0, l, d) for l in range(wl.layers)]
+            eng.sync()
+            ora.step(sel)
+            st = eng.export_state(0)
+            ref = ora.export_state()
+            assert digest(st) == digest(ref)
+            for l in range(wl.layers):
+                assert np.array_equal(outs[l].cpu().numpy(), ora.gather(sel, l, step=ora.flag))
+    finally:
+        eng.close()
+
+
+def test_gather_on_second_stream_ordered_by_event():
+    import torch
+    tr, eng, rows = _engine()
+    wl = tr.wl
+    try:
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        busy = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        sel = next(tr.selections(0))
+        d = _cuda(sel)
+        app = tr.appends(1)
+        app_rows = rows(app, 0)
+        torch.cuda.synchronize()
+        busy.fill_(3)                              # keeps the main stream busy for a while
+        eng.append(0, app, app_rows)
+        eng.step(0, d)
+        done = torch.cuda.Event()
+        done.record(main)
+        side.wait_event(done)
+        out = eng.gather(0, 0, d, stream=side)
+        torch.cuda.synchronize()
+        eng.sync()
+        want = rows_for(wl.seed, 0, sel.reshape(-1), wl.layers, wl.row_bytes)[:, 0]
+        assert np.array_equal(out.cpu().numpy().reshape(-1, wl.row_bytes), want)
+    finally:
+        eng.close()
+
+
+def test_unordered_gather_is_correct_or_refused():
+    """A gather issued on another stream without ordering either runs after
+    the step completed (correct rows) or sees the completion counter behind and
+    reports ENOTRESIDENT; it never returns rows of a half-finished step."""
+    import torch
+    from serving_pb_lru_amd import UlaError
+    tr, eng, rows = _engine()
+    wl = tr.wl
+    try:
+        side = torch.cuda.Stream()
+        busy = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        sels = tr.selections(0)
+        for t in (1, 2):
+            sel = next(sels)
+            d = _cuda(sel)
+            app = tr.appends(t)
+            eng.append(0, app, rows(app, 0))
+            eng.step(0, d)
+            eng.sync()
+        sel = next(sels)
+        d = _cuda(sel)
+        app = tr.appends(3)
+        app_rows = rows(app, 0)
+        torch.cuda.synchronize()
+        busy.fill_(1)
+        eng.append(0, app, app_rows)
+        eng.step(0, d)
+        out = eng.gather(0, 0, d, stream=side)
+        torch.cuda.synchronize()
+        try:
+            eng.sync()
+        except UlaError as e:
+            assert e.name == "ENOTRESIDENT"
+            return
+        want = rows_for(wl.seed, 0, sel.reshape(-1), wl.layers, wl.row_bytes)[:, 0]
+        assert np.array_equal(out.cpu().numpy().reshape(-1, wl.row_bytes), want)
+    finally:
+        eng.close()
+
+
+def test_runs_are_deterministic():
+    """Two runs from a fresh start must both match the oracle at every step
+    (atomics may complete in any order; the state must not depend on it)."""
+    wl = scaled(preset("spec3_r128_64k128k_g4"), 32)
+    run_parity(wl, steps=4, groups=[0])
+    run_parity(wl, steps=4, groups=[0])
