@@ -55,10 +55,43 @@ def parse():
     p.add_argument("--steps", type=int, default=56)
     p.add_argument("--warmup", type=int, default=8)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--cpu-seconds", type=float, default=20.0, help="budget of the CPU oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="timed CPU work of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-phases", action="store_true", help="skip the per-phase replay")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run 5 plain device-to-device copies of MIB MiB (counter calibration) and exit")
     return p.parse_args()
+
+
+def calibrate_copy(mib: int) -> None:
+    """A plain copy of known size, so that HBM byte counters can be scaled."""
+    import torch
+    torch.cuda.set_device(0)
+    a = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": mib << 20, "copies": 5}), flush=True)
+
+
+def gather_traffic(workload: str):
+    """HBM bytes per gather launch from the committed rocprofv3 counter record
+    (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or
+    None when there is no record for this workload or the kernel source changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_k_gather_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "serving_pb_lru_amd", "csrc", "k_gather.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["k_gather_hip_sha256"]:
+            return None
+    return rec["traffic_bytes_per_launch"]
 
 
 def rows_per_step(tr) -> int:
@@ -67,46 +100,48 @@ def rows_per_step(tr) -> int:
 
 
 # ---------------------------------------------------------------------------
-def cpu_baseline(tr, W: int, K: int, budget: float) -> dict:
-    """Replay the trace through the oracle on one core; time steps W+1 .. W+K."""
-    from oracle.pblru import PBLRUGroup
+def cpu_baseline(tr, W: int, K: int, seconds: float) -> dict:
+    """Replay the trace through the oracle on one core and time steps W+1 .. W+K.
+
+    The replay (untimed load and warm-up, timed steps) is repeated from a fresh
+    start until about `seconds` of timed CPU work have accumulated.
+    """
     from oracle.replay import initial_load as oracle_load, new_group
     from synth import rows_for
 
     wl = tr.wl
     old_aff = os.sched_getaffinity(0)
-    core = min(old_aff)
-    os.sched_setaffinity(0, {core})
+    os.sched_setaffinity(0, {min(old_aff)})
     try:
-        groups = list(range(wl.groups))
-        ora = {}
-        for g in groups[:1]:
-            ora[g] = new_group(tr, full_data=True)
-            oracle_load(ora[g], tr, g)
-        sels = {g: tr.selections(g) for g in groups[:1]}
-        spent, timed, rows = 0.0, 0, 0
-        for t in range(1, W + K + 1):
-            app = tr.appends(t)
-            for g in groups[:1]:
-                sel = next(sels[g])
-                app_rows = rows_for(wl.seed, g, app, wl.layers, wl.row_bytes)
+        import copy
+        loaded = new_group(tr, full_data=True)
+        oracle_load(loaded, tr, 0)
+        spent, timed, rows, replays = 0.0, 0, 0, 0
+        while spent < seconds and replays < 20:
+            replays += 1
+            grp = copy.deepcopy(loaded)     # a fresh replay from the loaded state
+            sels = tr.selections(0)
+            for t in range(1, W + K + 1):
+                sel = next(sels)
+                app = tr.appends(t)
+                app_rows = rows_for(wl.seed, 0, app, wl.layers, wl.row_bytes)
                 t0 = time.perf_counter()
-                ora[g].append(app, app_rows)
-                ora[g].step(sel)
+                grp.append(app, app_rows)
+                grp.step(sel)
                 for l in range(wl.layers):
-                    ora[g].gather(sel, l, step=t)
+                    grp.gather(sel, l, step=t)
                 dt = time.perf_counter() - t0
                 if t > W:
                     spent += dt
                     rows += tr.n_sets * tr.k * wl.layers
-            if t > W:
-                timed += 1
-                if spent > budget:
-                    break
-        return {"value": rows / spent if spent else None, "unit": "rows/s", "cores": 1, "kind": "oracle",
-                "sample": (f"{wl.name}: group 0 of {wl.groups}, steps {W + 1}..{W + timed} after an "
-                           f"untimed load and {W} untimed steps, full-data mode (rows moved), "
-                           f"one core; {spent:.1f} s of CPU work")}
+                    timed += 1
+            del grp
+        return {"value": round(rows / spent, 1) if spent else None, "unit": "rows/s", "cores": 1,
+                "kind": "oracle",
+                "sample": (f"{wl.name} group 0 of {wl.groups}: steps {W + 1}..{W + K} of the trace, "
+                           f"replayed {replays}x from the untimed loaded state and {W} untimed steps "
+                           f"({timed} timed steps, {spent:.1f} s of CPU work); full-data mode "
+                           f"(rows moved and gathered); one core")}
     finally:
         os.sched_setaffinity(0, old_aff)
 
@@ -204,6 +239,9 @@ def gpu_run(tr, W: int, K: int, phases: bool) -> dict:
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
@@ -228,7 +266,7 @@ def main():
     g_bytes = 1312 * rows_per_gather
     g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": "k_gather", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": gather_traffic(wl.name),
                 "bytes_per_launch": g_bytes, "launch_ms": round(g_ms, 5)}
     miss = None
     if "phase_ms" in r:
