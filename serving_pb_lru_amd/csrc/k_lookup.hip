@@ -152,9 +152,28 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
     if (s_base[2]) return;   // capacity error: nothing is written (uniform)
   }
   const int e = blockIdx.x * kScanBlock + threadIdx.x;
-  int32_t la;
-  uint32_t loc;
-  int c = classify(g, sel, n, e, t, la, loc);
+  // classify and resolve every entry (repeats included) for the gathers
+  int c = 0;
+  int32_t la = -1;
+  uint32_t loc = 0;
+  if (e < n) {
+    la = sel[e];
+    if (la == -1) {
+      c = 3;
+      g.res[e] = make_uint2(0xFFFFFFFFu, kAbsent);
+    } else {
+      const unsigned long long key = g.tag[la];
+      loc = g.map[la];
+      if (key == dedup_key(t, (uint32_t)e)) {
+        c = (loc & kHostBit) ? 2 : 1;
+        g.res[e] = make_uint2((uint32_t)la, c == 1 ? loc : kAbsent);   // a miss's slot comes at commit
+      } else {
+        // a repeat: a hit resolves to its slot, a missed entry to its first occurrence
+        const uint32_t first = ~(uint32_t)key;
+        g.res[e] = make_uint2((uint32_t)la, (loc & kHostBit) ? (kHostBit | first) : loc);
+      }
+    }
+  }
   unsigned long long bh = __ballot(c == 1), bm = __ballot(c == 2);
   if (lane == 0) {
     s_h[wave] = __popcll(bh);
@@ -176,6 +195,7 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
     const int pos = off + rank_below(bm);
     g.miss_la[pos] = la;
     g.miss_h[pos] = loc & ~kHostBit;
+    g.miss_e[pos] = e;
   }
 }
 

@@ -134,6 +134,7 @@ __global__ __launch_bounds__(256) void k_commit(GroupDev g, long long t) {
     const int32_t old = g.gown[v];
     g.map[la] = v;
     g.gown[v] = la;
+    g.res[g.miss_e[i]].y = v;      // the step's selection now resolves to the loaded slot
     if (old != -1) {
       g.map[old] = kHostBit | h;
       g.hown[h] = old;

@@ -36,7 +36,7 @@ int hip_fail(hipError_t e, const char* what) {
 
 struct Dims {
   int64_t N, P, H, B, NB, W, T, WH, TH, Lg, row_bytes, slot_bytes;
-  int64_t maxU, maxBlk, maxItems, maxApp;
+  int64_t maxU, maxBlk, maxItems, maxApp, nsel;
 };
 
 bool check_config(const ula_config* c, Dims* d) {
@@ -64,6 +64,7 @@ bool check_config(const ula_config* c, Dims* d) {
   d->row_bytes = c->row_bytes;
   d->slot_bytes = d->Lg * d->row_bytes;
   d->maxU = std::min<int64_t>(nsel, d->P);
+  d->nsel = nsel;
   d->maxBlk = (nsel + kScanBlock - 1) / kScanBlock;
   d->maxApp = c->max_append;
   d->maxItems = std::max<int64_t>(d->maxU, d->maxApp) + 2;
@@ -76,7 +77,7 @@ bool check_config(const ula_config* c, Dims* d) {
 
 struct Layout {
   size_t map, tag, gown, stamp, dirty, hown, bm, tcnt, hbm, htcnt, hits, mla, mh, vict, blk,
-      partial, items, app_la, app_dst, app_rows, evict_rows, wb_h, pool, group_bytes;
+      partial, items, app_la, app_dst, app_rows, evict_rows, wb_h, miss_e, res, pool, group_bytes;
   size_t counters_bytes, total;
 };
 
@@ -110,6 +111,8 @@ Layout layout_of(const ula_config* c, const Dims& d) {
   L.app_rows = take((size_t)d.maxApp * d.slot_bytes);
   L.evict_rows = take((size_t)d.maxU * d.slot_bytes);
   L.wb_h = take(4 * d.maxU);
+  L.miss_e = take(4 * d.maxU);
+  L.res = take(8 * d.nsel);
   L.pool = take((size_t)d.P * d.slot_bytes);
   L.group_bytes = o;
   L.counters_bytes = align_up(sizeof(Counters) * c->num_groups);
@@ -136,6 +139,7 @@ struct GroupHost {
   std::vector<uint64_t> appended;   // host mirror: which addresses were appended
   int64_t n_appended = 0;
   int64_t steps = 0;                // steps enqueued
+  int32_t last_n = 0;               // selection entries of the last step (resolved in res)
   int32_t* stage[kStageSlots] = {};
   hipEvent_t stage_ev[kStageSlots] = {};
   bool stage_used[kStageSlots] = {};
@@ -267,6 +271,8 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     g.app_rows = b + L.app_rows;
     g.evict_rows = b + L.evict_rows;
     g.wb_h = reinterpret_cast<uint32_t*>(b + L.wb_h);
+    g.miss_e = reinterpret_cast<int32_t*>(b + L.miss_e);
+    g.res = reinterpret_cast<uint2*>(b + L.res);
     g.pool = b + L.pool;
     g.host = hdev ? hdev + (size_t)gi * d.H * d.slot_bytes : nullptr;
     g.N = (int32_t)d.N;
@@ -474,6 +480,7 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   HIP_TRY(launch_commit(g, (long long)t, max_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[5], s));
   gh.steps = t;
+  gh.last_n = n;
   return ULA_OK;
 }
 
@@ -489,7 +496,7 @@ int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32
   GroupHost& gh = ctx->groups[group];
   if (gh.steps == 0) return ULA_ENOTRESIDENT;
   HIP_TRY(launch_gather(gh.d, sel_dev, n, layer, static_cast<uint8_t*>(out_dev), (long long)gh.steps,
-                        reinterpret_cast<hipStream_t>(stream)));
+                        gh.last_n, reinterpret_cast<hipStream_t>(stream)));
   return ULA_OK;
 }
 

@@ -14,8 +14,11 @@
 //   tcnt   u32[NB][T]    summary level 1: set bits per 2048-slot span (64 words,
 //                        one wavefront load) of each bucket, kept exact
 //   hbm    u32[WH]       free host slots bitmap, htcnt u32[TH] its span counts
-//   lists  hit slots, misses (address, host slot), victims, block sums, work items,
-//          per-block bucket-count deltas of the mark kernel
+//   lists  hit slots, misses (address, host slot, first entry), victims, block
+//          sums, work items, per-block bucket-count deltas of the mark kernel
+//   res    the step's selection resolved to GPU slots, entry by entry, so that
+//          every per-layer gather reads slots sequentially instead of looking
+//          each address up in the mapping table again
 //   stage  append addresses, destinations and (host-sourced) rows; evicted rows
 //          awaiting their write-back to the host, with their host slots
 //   pool   u8[P][Lg][row_bytes]   the GPU pool, slot-major: one slot holds all
@@ -84,6 +87,10 @@ struct GroupDev {        // device view of one group, passed by value to kernels
   uint32_t* hit_slots;
   int32_t* miss_la;
   uint32_t* miss_h;
+  int32_t* miss_e;       // [maxU] selection entry of each miss's first occurrence
+  uint2* res;            // [max_sets * max_k] per selection entry of the last step:
+                         //   (address, GPU slot), or (address, 0x80000000 | entry of the
+                         //   first occurrence) for a repeated miss; (-1, absent) for padding
   uint32_t* victims;
   uint32_t* blk;         // 3 words per de-dup block: hits, misses, invalid (then offsets)
   int32_t* partial;      // [kMarkBlocks][kMaxBuckets] bucket-count deltas of the mark kernel
@@ -157,6 +164,6 @@ hipError_t launch_swap_in(const GroupDev& g, int32_t max_pairs, hipStream_t s);
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s);
 hipError_t launch_commit(const GroupDev& g, long long t, int32_t max_pairs, hipStream_t s);
 hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
-                         uint8_t* out, long long want_flag, hipStream_t s);
+                         uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s);
 
 }  // namespace ula
