@@ -190,8 +190,8 @@ int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host
 int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr);
 
 /* Per-phase timing of the last step of group g, in milliseconds, when enabled
- * with ula_set_timing: [0] lookup + de-duplication, [1] hit marking + fold,
- * [2] victim selection, [3] missed rows in over the host link, [4] commit +
+ * with ula_set_timing: [0] lookup + de-duplication, [1] hit marking + fold +
+ * victim planning, [2] victim extraction, [3] missed rows in over the host link, [4] commit +
  * signal, [5] the previous step's evicted rows out over the host link (on the
  * group's side stream, launched at the start of this step; 0 if none was
  * timed). ula_read_timing synchronises on the step's last events. */

@@ -38,16 +38,14 @@ __global__ void k_init_bitmap(uint32_t* words, int32_t nwords, int64_t nbits, ui
   }
 }
 
+// Every field starts at zero (one lane per 32-bit word of the block, so that
+// no field can be left uninitialised), then the non-zero ones are set.
 __global__ void k_init_counters(Counters* c, int32_t P, int32_t H) {
+  uint32_t* words = reinterpret_cast<uint32_t*>(c);
+  for (int i = threadIdx.x; i < (int)(sizeof(Counters) / 4); i += blockDim.x) words[i] = 0u;
+  __syncthreads();
   if (threadIdx.x != 0) return;
-  c->status = 0;
-  c->done = 0;
-  c->flag = 0;
-  for (int i = 0; i < 6; ++i) c->stats[i] = 0;
-  c->n_unique = c->n_hits = c->n_miss = c->n_invalid = 0;
-  c->n_items = 0;
   c->hfree = H;
-  for (int i = 0; i < kMaxBuckets; ++i) c->bcnt[i] = 0;
   c->bcnt[kFree] = P;
 }
 

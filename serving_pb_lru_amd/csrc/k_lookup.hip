@@ -10,15 +10,19 @@
 //            with a 64-bit atomic max, so after the kernel tag[la] holds the key
 //            of la's first occurrence in step t (a smaller e gives a larger ~e;
 //            tags of earlier steps have a smaller t and never match).
-//   count    per block of 1024 entries: how many first occurrences are hits
-//            (GPU-resident) and misses (host-resident), and how many are padding.
-//   compact  per block: the block's output offsets are the sums of the earlier
-//            blocks' counts, the totals give the capacity check (more distinct
-//            entries than GPU slots is an error raised before any state
-//            changes); wavefront ballot + mbcnt ranks the first occurrences
-//            inside each wavefront and LDS adds the wavefront offsets, so hits
-//            and misses land in first-occurrence order. Each hit is stamped
-//            with the step and its span marked dirty.
+//   compact  single pass with a decoupled look-back: workgroups take tickets in
+//            start order; each classifies its 1024 entries (first occurrence on
+//            the GPU = hit, on the host = miss, padding) with wavefront ballots,
+//            publishes its counts, and adds up its predecessors' published
+//            counts (or a predecessor's inclusive prefix) to get its output
+//            offsets, so hits and misses land in first-occurrence order. A
+//            predecessor always started earlier and publishes before it waits,
+//            so every wait ends; waits are bounded all the same. Padding entries
+//            are counted by the tag kernel. The last
+//            workgroup knows the totals: more distinct entries than GPU slots is
+//            a capacity error raised before any state changes. Each hit is
+//            stamped with the step and its span marked dirty; every entry is
+//            resolved for the gathers.
 #include "device_util.h"
 
 namespace ula {
@@ -30,10 +34,19 @@ __device__ __forceinline__ unsigned long long dedup_key(uint32_t t, uint32_t e) 
 __global__ __launch_bounds__(256) void k_tag(GroupDev g, const int32_t* __restrict__ sel,
                                              int32_t n, uint32_t t) {
   if (status_of(g.ctr)) return;
+  // the compaction of this step uses the descriptors of parity t & 1, last used
+  // two steps ago
+  unsigned long long* desc = g.desc + (size_t)(t & 1u) * g.maxBlk;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < g.maxBlk; i += gridDim.x * blockDim.x)
+    desc[i] = 0ull;
   bool bad = false;
+  int pad = 0;
   for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x) {
     int32_t la = sel[e];
-    if (la == -1) continue;
+    if (la == -1) {
+      ++pad;
+      continue;
+    }
     if (la < 0 || la >= g.N || g.map[la] == kAbsent) {
       bad = true;
       continue;
@@ -41,118 +54,46 @@ __global__ __launch_bounds__(256) void k_tag(GroupDev g, const int32_t* __restri
     atomicMax(&g.tag[la], dedup_key(t, (uint32_t)e));
   }
   if (bad) latch(g.ctr, ULA_ERANGE);
+  // padding entries of the step (statistics); one atomic per wavefront that saw any
+  pad = wave_sum(pad);
+  if (pad && lane_id() == 0) atomicAdd(&g.ctr->pad_acc, pad);
 }
 
-// Classify entry e: 1 = first occurrence on the GPU, 2 = first occurrence on
-// the host, 3 = padding, 0 = repeated. `loc` receives the mapping entry.
-__device__ __forceinline__ int classify(const GroupDev& g, const int32_t* __restrict__ sel,
-                                        int32_t n, int e, uint32_t t, int32_t& la,
-                                        uint32_t& loc) {
-  la = -1;
-  loc = 0;
-  if (e >= n) return 0;
-  la = sel[e];
-  if (la == -1) return 3;
-  if (g.tag[la] != dedup_key(t, (uint32_t)e)) return 0;
-  loc = g.map[la];
-  return (loc & kHostBit) ? 2 : 1;
+// Look-back descriptor of a workgroup: status in bits 62-63 (0 = not yet, 1 =
+// its own counts, 2 = inclusive prefix), misses in bits 31-61, hits in bits 0-30.
+// The counts travel inside the descriptor, so relaxed atomics suffice.
+constexpr unsigned long long kDescAgg = 1ull << 62;
+constexpr unsigned long long kDescPre = 2ull << 62;
+constexpr uint32_t kCount31 = 0x7FFFFFFFu;
+constexpr int kSpinLimit = 1 << 16;
+
+__device__ __forceinline__ unsigned long long desc_pack(unsigned long long status, uint32_t h, uint32_t m) {
+  return status | ((unsigned long long)m << 31) | (unsigned long long)h;
 }
 
-__global__ __launch_bounds__(kScanBlock) void k_count(GroupDev g, const int32_t* __restrict__ sel,
-                                                      int32_t n, uint32_t t) {
-  __shared__ int s[3][kScanBlock / kWave];
-  if (block_failed(g.ctr)) return;
-  const int e = blockIdx.x * kScanBlock + threadIdx.x;
-  int32_t la;
-  uint32_t loc;
-  int c = classify(g, sel, n, e, t, la, loc);
-  const int wave = threadIdx.x / kWave;
-  unsigned long long bh = __ballot(c == 1), bm = __ballot(c == 2), bp = __ballot(c == 3);
-  if (lane_id() == 0) {
-    s[0][wave] = __popcll(bh);
-    s[1][wave] = __popcll(bm);
-    s[2][wave] = __popcll(bp);
-  }
-  __syncthreads();
-  if (threadIdx.x < 3) {
-    int sum = 0;
-    for (int w = 0; w < kScanBlock / kWave; ++w) sum += s[threadIdx.x][w];
-    g.blk[3 * blockIdx.x + threadIdx.x] = (uint32_t)sum;
-  }
-}
-
-// Every workgroup adds up the counts of the workgroups before it (a few KB read
-// from cache) to find its output offsets, and all of them add up the totals:
-// they reach the same capacity verdict, so either every workgroup writes or
-// none does. Workgroup 0 publishes the totals.
 __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_t* __restrict__ sel,
                                                         int32_t n, uint32_t t, int32_t nblk) {
-  __shared__ int s_h[kScanBlock / kWave], s_m[kScanBlock / kWave];
-  __shared__ int s_tot[3][kScanBlock / kWave];
-  __shared__ int s_base[3];
+  constexpr int NW = kScanBlock / kWave;
+  __shared__ int s_h[NW], s_m[NW];
+  __shared__ int s_vid, s_fail;
+  __shared__ uint32_t s_eh, s_em;
   if (block_failed(g.ctr)) return;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
-  {
-    // counts of earlier workgroups (offsets) and of all workgroups (totals)
-    int bh = 0, bmi = 0, ah = 0, am = 0, ap = 0;
-    for (int b = threadIdx.x; b < nblk; b += kScanBlock) {
-      const int h = (int)g.blk[3 * b], m = (int)g.blk[3 * b + 1], p = (int)g.blk[3 * b + 2];
-      ah += h;
-      am += m;
-      ap += p;
-      if (b < (int)blockIdx.x) {
-        bh += h;
-        bmi += m;
-      }
-    }
-    bh = wave_sum(bh);
-    bmi = wave_sum(bmi);
-    ah = wave_sum(ah);
-    am = wave_sum(am);
-    ap = wave_sum(ap);
-    if (lane == 0) {
-      s_h[wave] = bh;
-      s_m[wave] = bmi;
-      s_tot[0][wave] = ah;
-      s_tot[1][wave] = am;
-      s_tot[2][wave] = ap;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int x[5] = {0, 0, 0, 0, 0};
-      for (int w = 0; w < kScanBlock / kWave; ++w) {
-        x[0] += s_h[w];
-        x[1] += s_m[w];
-        x[2] += s_tot[0][w];
-        x[3] += s_tot[1][w];
-        x[4] += s_tot[2][w];
-      }
-      s_base[0] = x[0];
-      s_base[1] = x[1];
-      const int u = x[2] + x[3];
-      s_base[2] = u > g.P;
-      if (blockIdx.x == 0 && u > g.P) {
-        latch(g.ctr, ULA_ECAPACITY);   // before anything changes, statistics included
-      } else if (blockIdx.x == 0) {
-        Counters* c = g.ctr;
-        c->n_hits = x[2];
-        c->n_miss = x[3];
-        c->n_unique = u;
-        c->n_invalid = x[4];
-        c->stats[0] = u;
-        c->stats[1] = x[2];
-        c->stats[2] = x[3];
-        c->stats[3] = 0;
-        c->stats[4] = 0;
-        c->stats[5] = x[4];
-      }
-    }
-    __syncthreads();
-    if (s_base[2]) return;   // capacity error: nothing is written (uniform)
+  if (threadIdx.x == 0) {
+    s_vid = atomicAdd(&g.ctr->lb_ticket, 1);
+    s_fail = 0;
   }
-  const int e = blockIdx.x * kScanBlock + threadIdx.x;
+  __syncthreads();
+  const int vid = s_vid;
+  if (vid < 0 || vid >= nblk) {            // a corrupt ticket: never index with it
+    if (threadIdx.x == 0) latch(g.ctr, ULA_ESTATE);
+    return;
+  }
+  unsigned long long* desc = g.desc + (size_t)(t & 1u) * g.maxBlk;
+
   // classify and resolve every entry (repeats included) for the gathers
+  const int e = vid * kScanBlock + threadIdx.x;
   int c = 0;
   int32_t la = -1;
   uint32_t loc = 0;
@@ -174,49 +115,119 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
       }
     }
   }
-  unsigned long long bh = __ballot(c == 1), bm = __ballot(c == 2);
+  const unsigned long long bh = __ballot(c == 1), bm = __ballot(c == 2);
   if (lane == 0) {
     s_h[wave] = __popcll(bh);
     s_m[wave] = __popcll(bm);
   }
   __syncthreads();
+
+  // publish this workgroup's counts, then look back for its offsets (wave 0)
+  if (wave == 0) {
+    uint32_t ah = 0, am = 0;
+    for (int w = 0; w < NW; ++w) {
+      ah += s_h[w];
+      am += s_m[w];
+    }
+    if (lane == 0)
+      __hip_atomic_store(&desc[vid], desc_pack(vid == 0 ? kDescPre : kDescAgg, ah, am), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t eh = 0, em = 0;
+    int j = vid - 1;     // predecessor examined by lane 0
+    int spins = 0;
+    while (j >= 0) {
+      const int k = j - lane;
+      const unsigned long long d =
+          k >= 0 ? __hip_atomic_load(&desc[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kDescPre;
+      const unsigned long long st = d & (3ull << 62);
+      const unsigned long long pre = __ballot(st == kDescPre);
+      const unsigned long long zero = __ballot(st == 0ull);
+      // lanes up to the nearest inclusive prefix must all have published
+      const unsigned long long upto = pre ? ((pre & (0ull - pre)) << 1) - 1 : ~0ull;
+      if (zero & upto) {
+        if (++spins > kSpinLimit || status_of(g.ctr)) {
+          if (lane == 0) s_fail = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        continue;
+      }
+      const bool take = (upto >> lane) & 1ull;
+      int vh = take ? (int)(d & kCount31) : 0;
+      int vm = take ? (int)((d >> 31) & kCount31) : 0;
+      eh += (uint32_t)wave_sum(vh);
+      em += (uint32_t)wave_sum(vm);
+      if (pre) break;
+      j -= kWave;
+    }
+    if (lane == 0) {
+      if (vid > 0 && !s_fail)
+        __hip_atomic_store(&desc[vid], desc_pack(kDescPre, eh + ah, em + am), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      s_eh = eh;
+      s_em = em;
+      if (vid == nblk - 1 && !s_fail) {
+        // the last workgroup: every other one has published, so the totals are known
+        Counters* cs = g.ctr;
+        const int th = (int)(eh + ah), tm = (int)(em + am);
+        const int tp = cs->pad_acc;   // counted by the tag kernel, which has completed
+        const int u = th + tm;
+        cs->lb_ticket = 0;
+        cs->pad_acc = 0;
+        if (u > g.P) {
+          latch(cs, ULA_ECAPACITY);   // before anything changes, statistics included
+        } else {
+          cs->n_hits = th;
+          cs->n_miss = tm;
+          cs->n_unique = u;
+          cs->n_invalid = tp;
+          cs->stats[0] = u;
+          cs->stats[1] = th;
+          cs->stats[2] = tm;
+          cs->stats[3] = 0;
+          cs->stats[4] = 0;
+          cs->stats[5] = tp;
+        }
+      }
+      if (s_fail && !status_of(g.ctr)) latch(g.ctr, ULA_ESTATE);   // a wait that never ended: give up cleanly
+    }
+  }
+  __syncthreads();
+  if (s_fail) return;
   if (c == 1) {
-    int off = s_base[0];
+    int off = (int)s_eh;
     for (int w = 0; w < wave; ++w) off += s_h[w];
-    g.hit_slots[off + rank_below(bh)] = loc;
+    const int pos = off + rank_below(bh);
+    if (pos < g.maxU) g.hit_slots[pos] = loc;   // beyond the lists only on a capacity error
     // the bucket move itself is done word-parallel by the mark kernel, which
     // finds this step's hits by their stamp; every writer of a span's dirty
     // word writes the same value
     g.stamp[loc] = (int32_t)t;
     g.dirty[loc >> kTileShift] = (int32_t)t;
   } else if (c == 2) {
-    int off = s_base[1];
+    int off = (int)s_em;
     for (int w = 0; w < wave; ++w) off += s_m[w];
     const int pos = off + rank_below(bm);
-    g.miss_la[pos] = la;
-    g.miss_h[pos] = loc & ~kHostBit;
-    g.miss_e[pos] = e;
+    if (pos < g.maxU) {
+      g.miss_la[pos] = la;
+      g.miss_h[pos] = loc & ~kHostBit;
+      g.miss_e[pos] = e;
+    }
   }
 }
 
 hipError_t launch_tag(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
   int blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;   // also clears the look-back descriptors
   k_tag<<<blocks, 256, 0, s>>>(g, sel, n, t);
   return hipGetLastError();
 }
 
-hipError_t launch_count(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  k_count<<<(n + kScanBlock - 1) / kScanBlock, kScanBlock, 0, s>>>(g, sel, n, t);
-  return hipGetLastError();
-}
-
 hipError_t launch_compact(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s) {
-  const int nblk = (n + kScanBlock - 1) / kScanBlock;
-  // one workgroup even for an empty selection: it publishes the (zero) totals
-  k_compact<<<nblk > 0 ? nblk : 1, kScanBlock, 0, s>>>(g, sel, n, t, nblk);
+  int nblk = (n + kScanBlock - 1) / kScanBlock;
+  if (nblk < 1) nblk = 1;   // one workgroup even for an empty selection: it publishes the (zero) totals
+  k_compact<<<nblk, kScanBlock, 0, s>>>(g, sel, n, t, nblk);
   return hipGetLastError();
 }
 

@@ -18,8 +18,10 @@
 //            never produce work.
 //
 //   mark     fold and hit marking in one word-parallel pass over the spans that
-//            have hits or survivors to fold (see the kernel).
-//   plan     one workgroup: the quota of each bucket in eviction order (from
+//            have hits or survivors to fold (see the kernel); its last
+//            workgroup then runs the plan.
+//   plan     one workgroup (the last one of the mark kernel for a step, a
+//            kernel of its own for an append): the quota of each bucket in eviction order (from
 //            the exact bucket counts), then, per bucket with a quota, its
 //            level-1 counts 1024 spans at a time, scanned across the workgroup to
 //            give each contributing span its output offset and how many bits it
@@ -32,95 +34,6 @@
 #include "device_util.h"
 
 namespace ula {
-
-// Fold and hit marking, word-parallel and free of global atomics. One
-// wavefront per 2048-slot span, lane = bitmap word. A span is visited only if
-// it holds hits of this step (dirty == t) or survivors in ring[cur] to fold;
-// the others are skipped from the summaries alone. For word w with hit mask
-// hm (slots stamped t):
-//   cold     <- (cold | ring[cur]) & ~hm      fold, then hits leave cold
-//   ring[cur] <- hm                           hits join the new current bucket
-//   ring[b]  <- ring[b] & ~hm  (b != cur)     hits leave older ring buckets
-// Hits are never free slots. Span counts are recomputed by wavefront popcount
-// sums; bucket-count changes go to per-workgroup partials that the plan kernel
-// adds up.
-__global__ __launch_bounds__(256) void k_mark(GroupDev g, uint32_t t, int32_t cur) {
-  __shared__ int s_delta[kMaxBuckets];
-  if (block_failed(g.ctr)) return;
-  for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x) s_delta[i] = 0;
-  __syncthreads();
-  const int lane = lane_id();
-  const int nwaves = gridDim.x * (blockDim.x / kWave);
-  const int rc = ring_id(cur);
-  uint32_t* cold = g.bm + (size_t)kCold * g.W;
-  uint32_t* ring = g.bm + (size_t)rc * g.W;
-  uint32_t* ct = g.tcnt + (size_t)kCold * g.T;
-  uint32_t* rt = g.tcnt + (size_t)rc * g.T;
-  for (int tile = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; tile < g.T;
-       tile += nwaves) {
-    const bool hits = g.dirty[tile] == (int32_t)t;
-    const int fold_cnt = (int)rt[tile];
-    if (!hits && fold_cnt == 0) continue;     // nothing to fold, no hit: skip the span
-    const int w = tile * kTileWords + lane;
-    const bool valid = w < g.W;
-    uint32_t hm = 0;
-    if (hits && valid) {
-      const vec4u* sp = reinterpret_cast<const vec4u*>(g.stamp + (size_t)w * 32);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const vec4u s4 = sp[q];
-        hm |= (uint32_t)(s4.x == t) << (4 * q) | (uint32_t)(s4.y == t) << (4 * q + 1) |
-              (uint32_t)(s4.z == t) << (4 * q + 2) | (uint32_t)(s4.w == t) << (4 * q + 3);
-      }
-    }
-    const uint32_t oc = valid ? cold[w] : 0u;
-    const uint32_t orr = (valid && fold_cnt) ? ring[w] : 0u;
-    const uint32_t nc = (oc | orr) & ~hm;
-    if (valid) {
-      if (nc != oc) cold[w] = nc;
-      if (hm != orr) ring[w] = hm;
-    }
-    const int c_cold = wave_sum(__popc(nc));
-    const int c_ring = wave_sum(__popc(hm));
-    if (lane == 0) {
-      const int old_cold = (int)ct[tile];
-      ct[tile] = (uint32_t)c_cold;
-      rt[tile] = (uint32_t)c_ring;
-      atomicAdd(&s_delta[kCold], c_cold - old_cold);
-      atomicAdd(&s_delta[rc], c_ring - fold_cnt);
-    }
-    if (hits) {
-      // hits leave the other ring buckets; eight buckets' words in flight at once
-      for (int b0 = 0; b0 < g.B; b0 += 8) {
-        int ob[8];
-        uint32_t x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int b = b0 + j;
-          ob[j] = (b < g.B && b != cur) ? (int)g.tcnt[(size_t)ring_id(b) * g.T + tile] : 0;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          x[j] = (ob[j] && valid) ? g.bm[(size_t)ring_id(b0 + j) * g.W + w] : 0u;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (!ob[j]) continue;               // empty span of this bucket (wave-uniform)
-          const int id = ring_id(b0 + j);
-          const uint32_t nx = x[j] & ~hm;
-          if (valid && nx != x[j]) g.bm[(size_t)id * g.W + w] = nx;
-          const int cb = wave_sum(__popc(nx));
-          if (lane == 0 && cb != ob[j]) {
-            g.tcnt[(size_t)id * g.T + tile] = (uint32_t)cb;
-            atomicAdd(&s_delta[id], cb - ob[j]);
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x)
-    g.partial[blockIdx.x * kMaxBuckets + i] = s_delta[i];
-}
 
 // Selection plan (one 1024-thread workgroup). STEP mode: m = misses of the
 // step, sources in eviction order, destination ring[cur]. APPEND mode: m = n,
@@ -201,6 +114,117 @@ __global__ __launch_bounds__(1024) void k_plan(GroupDev g, PlanArgs a) {
   plan_body(g, a, scratch, s_nonempty);
 }
 
+// Fold and hit marking, word-parallel and free of global atomics. One
+// wavefront per 2048-slot span, lane = bitmap word. A span is visited only if
+// it holds hits of this step (dirty == t) or survivors in ring[cur] to fold;
+// the others are skipped from the summaries alone. For word w with hit mask
+// hm (slots stamped t):
+//   cold     <- (cold | ring[cur]) & ~hm      fold, then hits leave cold
+//   ring[cur] <- hm                           hits join the new current bucket
+//   ring[b]  <- ring[b] & ~hm  (b != cur)     hits leave older ring buckets
+// Hits are never free slots. Span counts are recomputed by wavefront popcount
+// sums; bucket-count changes go to per-workgroup partials, which the last
+// workgroup adds up when it plans the step's victims.
+__global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t cur, PlanArgs a) {
+  __shared__ int s_delta[kMaxBuckets];
+  __shared__ int s_last;
+  __shared__ int scratch[1024 / kWave + 1];
+  __shared__ unsigned long long s_nonempty[1024 / kWave];
+  if (block_failed(g.ctr)) return;
+  for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x) s_delta[i] = 0;
+  __syncthreads();
+  const int lane = lane_id();
+  const int nwaves = gridDim.x * (blockDim.x / kWave);
+  const int rc = ring_id(cur);
+  uint32_t* cold = g.bm + (size_t)kCold * g.W;
+  uint32_t* ring = g.bm + (size_t)rc * g.W;
+  uint32_t* ct = g.tcnt + (size_t)kCold * g.T;
+  uint32_t* rt = g.tcnt + (size_t)rc * g.T;
+  for (int tile = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; tile < g.T;
+       tile += nwaves) {
+    const bool hits = g.dirty[tile] == (int32_t)t;
+    const int fold_cnt = (int)rt[tile];
+    if (!hits && fold_cnt == 0) continue;     // nothing to fold, no hit: skip the span
+    const int w = tile * kTileWords + lane;
+    const bool valid = w < g.W;
+    uint32_t hm = 0;
+    if (hits && valid) {
+      const vec4u* sp = reinterpret_cast<const vec4u*>(g.stamp + (size_t)w * 32);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const vec4u s4 = sp[q];
+        hm |= (uint32_t)(s4.x == t) << (4 * q) | (uint32_t)(s4.y == t) << (4 * q + 1) |
+              (uint32_t)(s4.z == t) << (4 * q + 2) | (uint32_t)(s4.w == t) << (4 * q + 3);
+      }
+    }
+    const uint32_t oc = valid ? cold[w] : 0u;
+    const uint32_t orr = (valid && fold_cnt) ? ring[w] : 0u;
+    const uint32_t nc = (oc | orr) & ~hm;
+    if (valid) {
+      if (nc != oc) cold[w] = nc;
+      if (hm != orr) ring[w] = hm;
+    }
+    const int c_cold = wave_sum(__popc(nc));
+    const int c_ring = wave_sum(__popc(hm));
+    if (lane == 0) {
+      const int old_cold = (int)ct[tile];
+      ct[tile] = (uint32_t)c_cold;
+      rt[tile] = (uint32_t)c_ring;
+      atomicAdd(&s_delta[kCold], c_cold - old_cold);
+      atomicAdd(&s_delta[rc], c_ring - fold_cnt);
+    }
+    if (hits) {
+      // hits leave the other ring buckets; eight buckets' words in flight at once
+      for (int b0 = 0; b0 < g.B; b0 += 8) {
+        int ob[8];
+        uint32_t x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int b = b0 + j;
+          ob[j] = (b < g.B && b != cur) ? (int)g.tcnt[(size_t)ring_id(b) * g.T + tile] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          x[j] = (ob[j] && valid) ? g.bm[(size_t)ring_id(b0 + j) * g.W + w] : 0u;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          if (!ob[j]) continue;               // empty span of this bucket (wave-uniform)
+          const int id = ring_id(b0 + j);
+          const uint32_t nx = x[j] & ~hm;
+          if (valid && nx != x[j]) g.bm[(size_t)id * g.W + w] = nx;
+          const int cb = wave_sum(__popc(nx));
+          if (lane == 0 && cb != ob[j]) {
+            g.tcnt[(size_t)id * g.T + tile] = (uint32_t)cb;
+            atomicAdd(&s_delta[id], cb - ob[j]);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x)
+    g.partial[blockIdx.x * kMaxBuckets + i] = s_delta[i];
+  // The last workgroup to finish plans the victims: one release per workgroup
+  // before its ticket, the acquire-release ticket, and an acquire in the last
+  // workgroup make every workgroup's bitmaps, span counts and partials visible.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    const int ticket = __hip_atomic_fetch_add(&g.ctr->done_mark, 1, __ATOMIC_ACQ_REL,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    s_last = ticket == (int)gridDim.x - 1;
+    if (ticket < 0 || ticket >= (int)gridDim.x) latch(g.ctr, ULA_ESTATE);   // corrupt ticket: no plan
+    if (s_last) {
+      g.ctr->done_mark = 0;
+      __threadfence();
+    }
+  }
+  __syncthreads();
+  if (!s_last) return;
+  plan_body(g, a, scratch, s_nonempty);
+}
+
+
 // One wavefront takes the lowest `take` set bits of one span of one bitmap.
 // STEP: taken GPU slots join ring[cur] (dest); the output list is the victims,
 // and victims taken from the free bucket carry the top bit (their slot holds no
@@ -276,8 +300,8 @@ __global__ __launch_bounds__(1024) void k_append_small(GroupDev g, SmallAppend a
   }
 }
 
-hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, hipStream_t s) {
-  k_mark<<<kMarkBlocks, 256, 0, s>>>(g, t, cur);
+hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArgs& a, hipStream_t s) {
+  k_mark<<<kMarkBlocks, 1024, 0, s>>>(g, t, cur, a);
   return hipGetLastError();
 }
 

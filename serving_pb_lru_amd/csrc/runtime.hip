@@ -103,7 +103,7 @@ Layout layout_of(const ula_config* c, const Dims& d) {
   L.mla = take(4 * d.maxU);
   L.mh = take(4 * d.maxU);
   L.vict = take(4 * d.maxU);
-  L.blk = take(4 * 3 * d.maxBlk);
+  L.blk = take(8 * 2 * d.maxBlk);
   L.partial = take(4 * kMarkBlocks * kMaxBuckets);
   L.items = take(sizeof(SelItem) * d.maxItems);
   L.app_la = take(4 * d.maxApp);
@@ -263,7 +263,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     g.miss_la = reinterpret_cast<int32_t*>(b + L.mla);
     g.miss_h = reinterpret_cast<uint32_t*>(b + L.mh);
     g.victims = reinterpret_cast<uint32_t*>(b + L.vict);
-    g.blk = reinterpret_cast<uint32_t*>(b + L.blk);
+    g.desc = reinterpret_cast<unsigned long long*>(b + L.blk);
     g.partial = reinterpret_cast<int32_t*>(b + L.partial);
     g.items = reinterpret_cast<SelItem*>(b + L.items);
     g.app_la = reinterpret_cast<int32_t*>(b + L.app_la);
@@ -287,6 +287,8 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     g.Lg = (int32_t)d.Lg;
     g.row_bytes = (int32_t)d.row_bytes;
     g.slot_bytes = (int32_t)d.slot_bytes;
+    g.maxU = (int32_t)d.maxU;
+    g.maxBlk = (int32_t)std::max<int64_t>(d.maxBlk, 1);
     gh.appended.assign((d.N + 63) / 64, 0);
 
     hipError_t e = hipSuccess;
@@ -296,6 +298,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.gown), d.P, 0xFFFFFFFFu, s);
     if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.stamp), 32 * d.W, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.dirty), d.T, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u64(g.desc, 2 * g.maxBlk, 0ull, s);
     if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.hown), d.H, 0xFFFFFFFFu, s);
     if (e == hipSuccess) e = launch_fill_u32(g.bm, d.NB * d.W, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(g.tcnt, d.NB * d.T, 0u, s);
@@ -453,11 +456,8 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   gh.last_stream = s;
   if (tm) HIP_TRY(hipEventRecord(gh.ev[0], s));
   HIP_TRY(launch_tag(g, sel_dev, n, (uint32_t)t, s));
-  HIP_TRY(launch_count(g, sel_dev, n, (uint32_t)t, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[1], s));
   HIP_TRY(launch_compact(g, sel_dev, n, (uint32_t)t, s));
-  HIP_TRY(launch_mark(g, (uint32_t)t, cur, s));
-  if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
   PlanArgs a{};
   a.mode = kPlanStep;
   a.dest = ring_id(cur);
@@ -465,7 +465,8 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   a.order[1] = kCold;
   a.norder = 2;
   for (int j = 1; j < ctx->dims.B; ++j) a.order[a.norder++] = (int8_t)ring_id((cur + j) % ctx->dims.B);
-  HIP_TRY(launch_plan(g, a, s));
+  HIP_TRY(launch_mark(g, (uint32_t)t, cur, a, s));   // ends with the victim plan
+  if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
   const int32_t max_pairs = (int32_t)std::min<int64_t>(n, ctx->dims.maxU);
   HIP_TRY(launch_extract(g, kPlanStep, a.dest, max_pairs, s));
   // the previous step's write-back must land before host slots are read again

@@ -43,7 +43,7 @@ constexpr int kTileShift = 11;                  // 2048 slots per span
 constexpr int kScanBlock = 1024;                // selection entries per de-dup block
 constexpr int kMaxRing = 64;                    // B <= 64
 constexpr int kMaxBuckets = kMaxRing + 2;
-constexpr int kMarkBlocks = 128;                // fixed grid of the fold + hit-marking kernel
+constexpr int kMarkBlocks = 32;                 // fixed grid (1024 threads each) of the mark kernel
 
 // bucket ids
 constexpr int kFree = 0;
@@ -60,7 +60,10 @@ struct alignas(64) Counters {
   int32_t hfree;         // free host slots
   int32_t bcnt[kMaxBuckets];  // slots per bucket
   int32_t wb_n;          // pairs of the last swap, for its deferred write-back
-  int32_t pad[1];
+  int32_t done_mark;     // ticket of the mark kernel's last-workgroup plan
+  int32_t lb_ticket;     // order in which compaction workgroups start (look-back scan)
+  int32_t pad_acc;       // padding entries counted by the compaction workgroups
+  int32_t pad[2];
 };
 static_assert(sizeof(Counters) % 64 == 0, "counter block alignment");
 
@@ -92,7 +95,7 @@ struct GroupDev {        // device view of one group, passed by value to kernels
                          //   (address, GPU slot), or (address, 0x80000000 | entry of the
                          //   first occurrence) for a repeated miss; (-1, absent) for padding
   uint32_t* victims;
-  uint32_t* blk;         // 3 words per de-dup block: hits, misses, invalid (then offsets)
+  unsigned long long* desc;  // [2][maxBlk] look-back descriptors of the compaction, by step parity
   int32_t* partial;      // [kMarkBlocks][kMaxBuckets] bucket-count deltas of the mark kernel
   SelItem* items;
   int32_t* app_la;
@@ -103,6 +106,7 @@ struct GroupDev {        // device view of one group, passed by value to kernels
   uint8_t* pool;
   uint8_t* host;
   int32_t N, P, H, B, NB, W, T, WH, TH, Lg, row_bytes, slot_bytes;
+  int32_t maxU, maxBlk;  // capacity of the hit / miss / victim lists; compaction workgroups
 };
 
 // unsigned division by a run-time constant d (1 <= d < 2^31) for n < 2^31:
@@ -151,8 +155,7 @@ hipError_t launch_init_bitmap(uint32_t* words, int32_t nwords, int64_t nbits, ui
 hipError_t launch_init_counters(Counters* c, int32_t P, int32_t H, hipStream_t s);
 
 hipError_t launch_tag(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
-hipError_t launch_count(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
-hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, hipStream_t s);
+hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArgs& a, hipStream_t s);
 hipError_t launch_compact(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
 hipError_t launch_plan(const GroupDev& g, const PlanArgs& a, hipStream_t s);
 hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, int32_t max_items,

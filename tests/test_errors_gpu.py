@@ -245,3 +245,20 @@ def test_runs_are_deterministic():
     wl = scaled(preset("spec3_r128_64k128k_g4"), 32)
     run_parity(wl, steps=4, groups=[0])
     run_parity(wl, steps=4, groups=[0])
+
+
+def test_engine_on_dirty_workspace_matches_oracle():
+    """Regression: every counter the kernels rely on is initialised by ula_init,
+    whatever the workspace memory held before (here: all bits set)."""
+    import torch
+    from serving_pb_lru_amd import lib
+    from serving_pb_lru_amd.ula import UlaConfig
+    import ctypes
+    wl = tiny_workload(5)
+    tr = Trace(wl)
+    cfg = UlaConfig(1, wl.layers, wl.row_bytes, wl.ring, tr.N, tr.P, tr.H, tr.n_sets, tr.k, 4096)
+    nbytes = lib().ula_device_bytes(ctypes.byref(cfg))
+    junk = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    del junk                      # the caching allocator hands this block to the engine
+    run_parity(wl, max_append=4096)
