@@ -142,14 +142,15 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host,
  * the ring and fold the reused bucket into cold; move hits into the current
  * bucket; pick one victim per miss (free, cold, ring oldest -> newest, ascending
  * slot inside a bucket, never the current bucket); bring the missed rows in from
- * the host pool (the victims' rows are staged in device memory first); then
- * update the mapping table and owners and raise the completion counter to the
- * step number. The staged victim rows are written to the host slots their
- * misses vacated on a library-owned side stream, launched at the start of the
- * group's next step so that it overlaps that step's lookup and selection; the
- * next step's swap waits for it before it reads the host pool, and ula_sync,
- * ula_export_state and ula_read_rows complete it. Enqueued on `stream` with no
- * host synchronisation.
+ * the host pool; then update the mapping table and owners and raise the
+ * completion counter to the step number. Data path: the missed rows are read
+ * into device memory in the same launch that marks the hits and plans the
+ * victims; the victims' rows are staged in device memory as the missed rows
+ * replace them; the staged rows reach the host slots their misses vacated
+ * during the group's next step, beside that step's reads from the host (a miss
+ * of a row evicted by the previous step reads its staged copy), or when
+ * ula_export_state or ula_read_rows needs the host pool current. Enqueued on
+ * `stream` with no host synchronisation.
  * Host errors: ULA_EINVAL (bad g, n_sets > max_sets, k > max_k, negative sizes),
  * ULA_ESTATE. Device errors (reported by ula_sync): ULA_ERANGE, ULA_ECAPACITY. */
 int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
@@ -168,19 +169,20 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
 int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32_t k,
                const int32_t* sel_dev, void* out_dev, uint64_t stream);
 
-/* Wait for `stream`, complete every group's outstanding eviction write-back,
- * then report the first latched device error of any group (poisoning the
- * context) or ULA_OK. per_group_out (nullable, num_groups entries) receives
- * each group's last step statistics. */
+/* Wait for `stream`, then report the first latched device error of any group
+ * (poisoning the context) or ULA_OK. per_group_out (nullable, num_groups
+ * entries) receives each group's last step statistics. */
 int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out);
 
-/* Copy group g's canonical state into caller host buffers (synchronises the
- * device first). Works on a poisoned context. */
+/* Copy group g's canonical state into caller host buffers (writes any staged
+ * evicted rows to the host pool and synchronises the device first). Works on a
+ * poisoned context. */
 int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out);
 
 /* Read back the stored rows (all layers, layers_per_group x row_bytes bytes
  * each) of n appended entries of group g into host memory, from whichever pool
- * holds them (synchronises the device). ULA_ERANGE if an address was never
+ * holds them (writes any staged evicted rows to the host pool and synchronises
+ * the device first). ULA_ERANGE if an address was never
  * appended. */
 int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host,
                   void* out_host);
@@ -191,12 +193,12 @@ int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr);
 
 /* Per-phase timing of the last step of group g, in milliseconds, when enabled
  * with ula_set_timing: [0] lookup + de-duplication, [1] hit marking + fold +
- * victim planning, [2] victim extraction, [3] missed rows in over the host link, [4] commit +
- * signal, [5] the previous step's evicted rows out over the host link (on the
- * group's side stream, launched at the start of this step; 0 if none was
- * timed). ula_read_timing synchronises on the step's last events. */
+ * victim planning, with the missed rows read in and the previous step's
+ * evicted rows written out over the host link in the same launch, [2] victim
+ * extraction, [3] rows into the victim slots + commit + signal.
+ * ula_read_timing synchronises on the step's last event. */
 int ula_set_timing(ula_ctx* ctx, int32_t enable);
-int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out6);
+int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out4);
 
 /* Release the context (not the caller's buffers). Waits for no stream. */
 int ula_destroy(ula_ctx* ctx);

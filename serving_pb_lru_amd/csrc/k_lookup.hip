@@ -209,9 +209,22 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
     for (int w = 0; w < wave; ++w) off += s_m[w];
     const int pos = off + rank_below(bm);
     if (pos < g.maxU) {
+      const uint32_t h = loc & ~kHostBit;
       g.miss_la[pos] = la;
-      g.miss_h[pos] = loc & ~kHostBit;
+      g.miss_h[pos] = h;
       g.miss_e[pos] = e;
+      // a row evicted by the previous step may still be on its way to the host:
+      // read it from its staging copy instead
+      const unsigned long long st = g.hs_stage[h];
+      uint32_t from = kAbsent;
+      if ((uint32_t)(st >> 32) == t - 1u) {
+        from = (uint32_t)st;
+        if (from >= (uint32_t)g.maxU) {   // corrupt staging record: no row to read
+          latch(g.ctr, ULA_ESTATE);
+          from = kAbsent;
+        }
+      }
+      g.miss_stage[pos] = from;
     }
   }
 }

@@ -1,5 +1,5 @@
-// Data movement and commit: append placement, the miss-path swap over the host
-// link, and the commit that updates the mapping table and signals completion.
+// Data movement and commit: append placement, the HBM part of the miss-path
+// swap, and the commit that updates the mapping table and signals completion.
 //
 // UlaCache summary (paper-daily.com), section 3: move the data first, then
 // update the mapping and signal completion; readers wait for the signal, so
@@ -9,13 +9,13 @@
 // to that same host slot (a swap), so host occupancy is unchanged and no entry
 // is ever held twice; a victim taken from the free bucket frees the host slot.
 //
-// The host pool is pinned, device-mapped memory that the kernels read and
-// write directly over PCIe with 16-byte vector accesses. PCIe keeps read
-// requests behind earlier posted writes in the same direction, so a swap that
-// mixes both stalls its reads on its own write-back; the miss path therefore
-// splits: reads into the pool first (critical path), then the write-back of
-// the evicted rows from an HBM staging copy on a side stream.
-#include "device_util.h"
+// The miss path runs in three parts: the missed rows are read into HBM early
+// (prefetch workgroups of the mark launch), the swap into the victim slots is
+// HBM to HBM (here), and the evicted rows, staged in HBM by the swap, go to the
+// host in the next step's mark launch, beside that step's reads.
+#include <algorithm>
+
+#include "miss_path.h"
 
 namespace ula {
 
@@ -34,115 +34,81 @@ __global__ __launch_bounds__(256) void k_place(GroupDev g, int32_t n, const uint
   }
 }
 
-// Miss path, critical part: pair i brings the missed rows of host slot
-// miss_h[i] into GPU slot victims[i] (all layers: one contiguous slot_bytes run
-// on each side). The victim's own rows are first copied to an HBM staging row
-// so that the slot can be overwritten at once; only reads cross the host link
-// here, so no read request queues behind write traffic.
-__global__ __launch_bounds__(256) void k_swap_in(GroupDev g, FastDiv per_slot) {
-  if (status_of(g.ctr)) return;
+// Miss path, HBM part, fused with the commit. Pair i moves the missed rows,
+// already prefetched into miss_rows[i], into victim slot victims[i]; a victim
+// that holds an entry first copies its rows to the staging buffer, from which
+// the next step's mark launch (or a stand-alone write-back before the host
+// reads state) writes them to the host slot the miss vacated. The thread of piece 0 of a pair also commits it: mapping table,
+// owners, the step's resolved selection, and the staging record of its host
+// slot (so that a miss of the evicted entry in the next step reads the staged
+// copy instead of a host slot whose write may still be in flight). A victim
+// that was free releases its host slot instead. Every workgroup then releases
+// its writes and takes a ticket; the last one raises the completion counter.
+__global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, FastDiv per_slot) {
+  __shared__ int s_freed;
+  if (block_failed(g.ctr)) return;
+  if (threadIdx.x == 0) s_freed = 0;
+  __syncthreads();
   const int m = g.ctr->n_miss;
+  uint8_t* stage = g.evict_rows;
+  uint32_t* wbh = g.wb_h;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    g.ctr->wb_n = m;
+    g.ctr->wb_step = t;
+  }
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
   const uint32_t total = (uint32_t)m * chunks;
   const uint32_t stride = gridDim.x * blockDim.x;
-  if (blockIdx.x == 0 && threadIdx.x == 0) g.ctr->wb_n = m;
+  int freed = 0;
   constexpr int U = 4;
   for (uint32_t base = blockIdx.x * blockDim.x + threadIdx.x; base < total; base += U * stride) {
-    vec4u hv[U], gv[U];
+    vec4u mv[U], gv[U];
     vec4u* gp[U];
-    const vec4u* hp[U];
     vec4u* sp[U];
     bool ev[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t idx = base + u * stride;
-      ev[u] = false;
       gp[u] = nullptr;
+      ev[u] = false;
       if (idx < total) {
         const uint32_t i = per_slot.div(idx);
         const uint32_t c = idx - i * chunks;
         const uint32_t vv = g.victims[i];
-        const uint32_t h = g.miss_h[i];
         const uint32_t v = vv & ~kHostBit;
-        ev[u] = (vv & kHostBit) == 0;          // the victim slot holds a row to evict
+        ev[u] = (vv & kHostBit) == 0;          // the victim slot holds an entry to evict
         gp[u] = reinterpret_cast<vec4u*>(g.pool + (size_t)v * g.slot_bytes) + c;
-        hp[u] = reinterpret_cast<const vec4u*>(g.host + (size_t)h * g.slot_bytes) + c;
-        sp[u] = reinterpret_cast<vec4u*>(g.evict_rows + (size_t)i * g.slot_bytes) + c;
+        sp[u] = reinterpret_cast<vec4u*>(stage + (size_t)i * g.slot_bytes) + c;
         if (ev[u]) gv[u] = *gp[u];
-        hv[u] = *hp[u];
-        if (c == 0) g.wb_h[i] = ev[u] ? h : kAbsent;
+        mv[u] = reinterpret_cast<const vec4u*>(g.miss_rows + (size_t)i * g.slot_bytes)[c];
+        if (c == 0) {
+          const int32_t la = g.miss_la[i];
+          const uint32_t h = g.miss_h[i];
+          const int32_t old = g.gown[v];
+          g.map[la] = v;
+          g.gown[v] = la;
+          g.res[g.miss_e[i]].y = v;      // the step's selection now resolves to the loaded slot
+          if (old != -1) {
+            g.map[old] = kHostBit | h;
+            g.hown[h] = old;
+            wbh[i] = h;
+            g.hs_stage[h] = ((unsigned long long)t << 32) | i;
+          } else {
+            g.hown[h] = -1;
+            wbh[i] = kAbsent;
+            atomicOr(&g.hbm[h >> 5], 1u << (h & 31));
+            atomicAdd(&g.htcnt[h >> kTileShift], 1u);
+            ++freed;
+          }
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (gp[u]) {
         if (ev[u]) *sp[u] = gv[u];
-        *gp[u] = hv[u];
+        *gp[u] = mv[u];
       }
-    }
-  }
-}
-
-// Miss path, deferred part (side stream): the staged victim rows go to the host
-// slots their misses vacated. It is launched when the group's next step starts
-// and overlaps that step's lookup and selection; the next k_swap_in waits for
-// it, so a later read of one of these host slots always sees the written row.
-// It depends only on wb_n / wb_h / evict_rows, which no kernel rewrites before
-// that wait.
-__global__ __launch_bounds__(256) void k_writeback(GroupDev g, FastDiv per_slot) {
-  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
-  const uint32_t total = (uint32_t)g.ctr->wb_n * chunks;
-  const uint32_t stride = gridDim.x * blockDim.x;
-  constexpr int U = 4;
-  for (uint32_t base = blockIdx.x * blockDim.x + threadIdx.x; base < total; base += U * stride) {
-    vec4u v[U];
-    vec4u* hp[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t idx = base + u * stride;
-      hp[u] = nullptr;
-      if (idx < total) {
-        const uint32_t i = per_slot.div(idx);
-        const uint32_t c = idx - i * chunks;
-        const uint32_t h = g.wb_h[i];
-        if (h != kAbsent) {
-          hp[u] = reinterpret_cast<vec4u*>(g.host + (size_t)h * g.slot_bytes) + c;
-          v[u] = reinterpret_cast<const vec4u*>(g.evict_rows + (size_t)i * g.slot_bytes)[c];
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (hp[u]) *hp[u] = v[u];
-  }
-}
-
-// Commit after the data has moved: mapping table and owners; a victim that was
-// free releases its host slot. Then the last workgroup to finish raises the
-// completion counter to t with a system-scope release.
-__global__ __launch_bounds__(256) void k_commit(GroupDev g, long long t) {
-  __shared__ int s_freed;
-  if (block_failed(g.ctr)) return;
-  if (threadIdx.x == 0) s_freed = 0;
-  __syncthreads();
-  const int m = g.ctr->n_miss;
-  int freed = 0;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < m; i += gridDim.x * blockDim.x) {
-    const uint32_t v = g.victims[i] & ~kHostBit;
-    const int32_t la = g.miss_la[i];
-    const uint32_t h = g.miss_h[i];
-    const int32_t old = g.gown[v];
-    g.map[la] = v;
-    g.gown[v] = la;
-    g.res[g.miss_e[i]].y = v;      // the step's selection now resolves to the loaded slot
-    if (old != -1) {
-      g.map[old] = kHostBit | h;
-      g.hown[h] = old;
-    } else {
-      g.hown[h] = -1;
-      atomicOr(&g.hbm[h >> 5], 1u << (h & 31));
-      atomicAdd(&g.htcnt[h >> kTileShift], 1u);
-      ++freed;
     }
   }
   if (freed) atomicAdd(&s_freed, freed);
@@ -157,9 +123,20 @@ __global__ __launch_bounds__(256) void k_commit(GroupDev g, long long t) {
     const int ticket = __hip_atomic_fetch_add(&g.ctr->done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (ticket == (int)gridDim.x - 1) {
       g.ctr->done = 0;
-      __hip_atomic_store(&g.ctr->flag, t, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&g.ctr->flag, (long long)t, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+}
+
+// Stand-alone write-back of whatever rows the last swap staged, for when the
+// host is about to read state. It does not test the error status: an error
+// latched by a later step (whose mark launch then never wrote these rows out)
+// must not stop the write-back of an earlier completed one. Rewriting rows a
+// mark launch already wrote out is harmless: nothing else writes those host
+// slots meanwhile.
+__global__ __launch_bounds__(256) void k_writeback(GroupDev g, FastDiv per_slot) {
+  const uint32_t t = g.ctr->wb_step;
+  if (t != 0) writeback_rows(g, t, per_slot, blockIdx.x, gridDim.x);
 }
 
 hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s) {
@@ -172,35 +149,25 @@ hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipSt
   return hipGetLastError();
 }
 
-static int grid_for_pairs(int32_t max_pairs, uint32_t chunks) {
+static int grid_for_pairs(int32_t max_pairs, uint32_t chunks, int threads, int cap) {
   size_t total = (size_t)max_pairs * chunks;
-  int blocks = (int)((total + 1023) / 1024);
-  if (blocks > 2048) blocks = 2048;
+  size_t per_block = (size_t)threads * 4;
+  int blocks = (int)std::min<size_t>((total + per_block - 1) / per_block, (size_t)cap);
   return blocks < 1 ? 1 : blocks;
 }
 
-hipError_t launch_swap_in(const GroupDev& g, int32_t max_pairs, hipStream_t s) {
+hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s) {
+  // At most 128 workgroups: HBM-to-HBM copies need no more to reach full
+  // bandwidth, and each workgroup costs one ticket on the completion counter.
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
-  k_swap_in<<<grid_for_pairs(max_pairs, chunks), 256, 0, s>>>(g, FastDiv(chunks));
+  k_swap_commit<<<grid_for_pairs(max_pairs, chunks, 512, 128), 512, 0, s>>>(g, t, FastDiv(chunks));
   return hipGetLastError();
 }
 
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s) {
-  // 64 workgroups keep about 1 MB of stores in flight, enough to saturate the
-  // link; more would only hold compute units the concurrent kernels need.
+  // 64 workgroups keep about 1 MB of stores in flight, enough to saturate the link
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
-  int blocks = grid_for_pairs(max_pairs, chunks);
-  if (blocks > 64) blocks = 64;
-  k_writeback<<<blocks, 256, 0, s>>>(g, FastDiv(chunks));
-  return hipGetLastError();
-}
-
-hipError_t launch_commit(const GroupDev& g, long long t, int32_t max_pairs, hipStream_t s) {
-  // few workgroups: each one takes a ticket on one counter to find the last
-  int blocks = (max_pairs + 4095) / 4096;
-  if (blocks > 32) blocks = 32;
-  if (blocks < 1) blocks = 1;
-  k_commit<<<blocks, 256, 0, s>>>(g, t);
+  k_writeback<<<grid_for_pairs(max_pairs, chunks, 256, 64), 256, 0, s>>>(g, FastDiv(chunks));
   return hipGetLastError();
 }
 

@@ -19,7 +19,10 @@
 //
 //   mark     fold and hit marking in one word-parallel pass over the spans that
 //            have hits or survivors to fold (see the kernel); its last
-//            workgroup then runs the plan.
+//            workgroup then runs the plan. The same launch carries the
+//            host-link work of the miss path (missed rows in, the previous
+//            step's evicted rows out), so the transfers overlap the marking and
+//            the planning.
 //   plan     one workgroup (the last one of the mark kernel for a step, a
 //            kernel of its own for an append): the quota of each bucket in eviction order (from
 //            the exact bucket counts), then, per bucket with a quota, its
@@ -31,7 +34,9 @@
 //            each lane writes the slots of its lowest set bits that fall below
 //            the span's quota, in ascending slot order. The taken bits leave
 //            their bucket and join the destination bucket.
-#include "device_util.h"
+#include <algorithm>
+
+#include "miss_path.h"
 
 namespace ula {
 
@@ -125,16 +130,32 @@ __global__ __launch_bounds__(1024) void k_plan(GroupDev g, PlanArgs a) {
 // Hits are never free slots. Span counts are recomputed by wavefront popcount
 // sums; bucket-count changes go to per-workgroup partials, which the last
 // workgroup adds up when it plans the step's victims.
-__global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t cur, PlanArgs a) {
+//
+// The same launch carries the host-link work of the miss path in extra
+// workgroups: `pf` prefetch workgroups read the step's missed rows into HBM
+// (victims are not known yet; the swap kernel moves them into the victim slots
+// over HBM), and the rest write the previous step's evicted rows out, when
+// wb_step names that step. Both link directions then run concurrently, and only
+// beside this kernel's own marking and planning.
+__global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t cur, PlanArgs a,
+                                               FastDiv per_slot, int32_t pf, uint32_t wb_step) {
   __shared__ int s_delta[kMaxBuckets];
   __shared__ int s_last;
   __shared__ int scratch[1024 / kWave + 1];
   __shared__ unsigned long long s_nonempty[1024 / kWave];
   if (block_failed(g.ctr)) return;
+  if (blockIdx.x >= kMarkBlocks + pf) {
+    writeback_rows(g, wb_step, per_slot, blockIdx.x - kMarkBlocks - pf, gridDim.x - kMarkBlocks - pf);
+    return;
+  }
+  if (blockIdx.x >= kMarkBlocks) {
+    prefetch_misses(g, per_slot, blockIdx.x - kMarkBlocks, pf);
+    return;
+  }
   for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x) s_delta[i] = 0;
   __syncthreads();
   const int lane = lane_id();
-  const int nwaves = gridDim.x * (blockDim.x / kWave);
+  const int nwaves = kMarkBlocks * (blockDim.x / kWave);
   const int rc = ring_id(cur);
   uint32_t* cold = g.bm + (size_t)kCold * g.W;
   uint32_t* ring = g.bm + (size_t)rc * g.W;
@@ -212,8 +233,8 @@ __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t c
     __threadfence();
     const int ticket = __hip_atomic_fetch_add(&g.ctr->done_mark, 1, __ATOMIC_ACQ_REL,
                                               __HIP_MEMORY_SCOPE_AGENT);
-    s_last = ticket == (int)gridDim.x - 1;
-    if (ticket < 0 || ticket >= (int)gridDim.x) latch(g.ctr, ULA_ESTATE);   // corrupt ticket: no plan
+    s_last = ticket == kMarkBlocks - 1;
+    if (ticket < 0 || ticket >= kMarkBlocks) latch(g.ctr, ULA_ESTATE);   // corrupt ticket: no plan
     if (s_last) {
       g.ctr->done_mark = 0;
       __threadfence();
@@ -300,8 +321,22 @@ __global__ __launch_bounds__(1024) void k_append_small(GroupDev g, SmallAppend a
   }
 }
 
-hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArgs& a, hipStream_t s) {
-  k_mark<<<kMarkBlocks, 1024, 0, s>>>(g, t, cur, a);
+hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArgs& a,
+                       int32_t max_pairs, int32_t wb_pairs, hipStream_t s) {
+  // Prefetch workgroups: enough for the largest possible miss list, at most
+  // kPrefetchBlocks (about 2 MB of host reads in flight). Write-back
+  // workgroups: enough for the previous step's pairs, at most kWritebackBlocks
+  // (about 1 MB of host writes in flight, which saturates the link). None of
+  // either without a host pool, since a step then never misses.
+  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
+  auto blocks_for = [&](int32_t pairs, int cap) {
+    const int64_t n = ((int64_t)pairs * chunks + 4 * 1024 - 1) / (4 * 1024);
+    return (int)std::min<int64_t>(n, cap);
+  };
+  const int pf = g.H > 0 ? blocks_for(max_pairs, kPrefetchBlocks) : 0;
+  const int wb = g.H > 0 ? blocks_for(wb_pairs, kWritebackBlocks) : 0;
+  k_mark<<<kMarkBlocks + pf + wb, 1024, 0, s>>>(g, t, cur, a, FastDiv(chunks), pf,
+                                                wb > 0 ? t - 1u : 0u);
   return hipGetLastError();
 }
 

@@ -1,0 +1,87 @@
+// Host-link parts of the miss path, shared by the mark kernel (which runs them
+// in extra workgroups beside the hit marking) and the stand-alone write-back.
+//
+// UlaCache summary (paper-daily.com), section 3: data moves before the
+// mapping changes; section 2: an entry lives in exactly one pool. Pair i of a
+// step brings the missed entry miss_la[i] in from host slot miss_h[i] and sends
+// the entry of its victim slot out to that same host slot.
+//
+// The host pool is pinned, device-mapped memory read and written directly with
+// 16-byte vector accesses. Both directions of the link run at once: a step's
+// prefetch reads its missed rows while the previous step's evicted rows are
+// written out. The two never touch the same host slot: a slot written by the
+// write-back of step t - 1 holds an entry evicted by step t - 1, and a miss of
+// that entry in step t reads the staged copy instead (miss_stage).
+#pragma once
+
+#include "device_util.h"
+
+namespace ula {
+
+// Missed rows of step t (all layers, one contiguous slot_bytes run each) into
+// miss_rows[i], from the host pool or from the staging copy of step t - 1.
+// Workgroup `part` of `nparts`, blockDim.x threads each.
+__device__ __forceinline__ void prefetch_misses(const GroupDev& g, FastDiv per_slot, int part,
+                                                int nparts) {
+  const int m = g.ctr->n_miss;
+  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
+  const uint32_t total = (uint32_t)m * chunks;
+  const uint32_t stride = (uint32_t)nparts * blockDim.x;
+  constexpr int U = 4;
+  for (uint32_t base = (uint32_t)part * blockDim.x + threadIdx.x; base < total; base += U * stride) {
+    vec4u v[U];
+    vec4u* dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t idx = base + u * stride;
+      dst[u] = nullptr;
+      if (idx < total) {
+        const uint32_t i = per_slot.div(idx);
+        const uint32_t c = idx - i * chunks;
+        const uint32_t from = g.miss_stage[i];
+        const uint8_t* src = from != kAbsent ? g.evict_rows + (size_t)from * g.slot_bytes
+                                             : g.host + (size_t)g.miss_h[i] * g.slot_bytes;
+        v[u] = reinterpret_cast<const vec4u*>(src)[c];
+        dst[u] = reinterpret_cast<vec4u*>(g.miss_rows + (size_t)i * g.slot_bytes) + c;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (dst[u]) *dst[u] = v[u];
+  }
+}
+
+// The rows staged by the swap of step `t` go to the host slots their misses
+// vacated (wb_h; absent for a victim that was free). Does nothing unless the
+// staging buffer holds step t's rows.
+__device__ __forceinline__ void writeback_rows(const GroupDev& g, uint32_t t, FastDiv per_slot,
+                                               int part, int nparts) {
+  if (g.ctr->wb_step != t) return;
+  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
+  const uint32_t total = (uint32_t)g.ctr->wb_n * chunks;
+  const uint32_t stride = (uint32_t)nparts * blockDim.x;
+  constexpr int U = 4;
+  for (uint32_t base = (uint32_t)part * blockDim.x + threadIdx.x; base < total; base += U * stride) {
+    vec4u v[U];
+    vec4u* hp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t idx = base + u * stride;
+      hp[u] = nullptr;
+      if (idx < total) {
+        const uint32_t i = per_slot.div(idx);
+        const uint32_t c = idx - i * chunks;
+        const uint32_t h = g.wb_h[i];
+        if (h != kAbsent) {
+          hp[u] = reinterpret_cast<vec4u*>(g.host + (size_t)h * g.slot_bytes) + c;
+          v[u] = reinterpret_cast<const vec4u*>(g.evict_rows + (size_t)i * g.slot_bytes)[c];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (hp[u]) *hp[u] = v[u];
+  }
+}
+
+}  // namespace ula

@@ -77,7 +77,8 @@ bool check_config(const ula_config* c, Dims* d) {
 
 struct Layout {
   size_t map, tag, gown, stamp, dirty, hown, bm, tcnt, hbm, htcnt, hits, mla, mh, vict, blk,
-      partial, items, app_la, app_dst, app_rows, evict_rows, wb_h, miss_e, res, pool, group_bytes;
+      partial, items, app_la, app_dst, app_rows, evict_rows, wb_h, miss_e, miss_stage, miss_rows,
+      hs_stage, res, pool, group_bytes;
   size_t counters_bytes, total;
 };
 
@@ -112,6 +113,9 @@ Layout layout_of(const ula_config* c, const Dims& d) {
   L.evict_rows = take((size_t)d.maxU * d.slot_bytes);
   L.wb_h = take(4 * d.maxU);
   L.miss_e = take(4 * d.maxU);
+  L.miss_stage = take(4 * d.maxU);
+  L.miss_rows = take((size_t)d.maxU * d.slot_bytes);
+  L.hs_stage = take(8 * d.H);
   L.res = take(8 * d.nsel);
   L.pool = take((size_t)d.P * d.slot_bytes);
   L.group_bytes = o;
@@ -144,12 +148,9 @@ struct GroupHost {
   hipEvent_t stage_ev[kStageSlots] = {};
   bool stage_used[kStageSlots] = {};
   int stage_next = 0;
-  hipEvent_t ev[6] = {};
-  hipStream_t wb_stream = nullptr;   // side stream of the deferred eviction write-back
-  hipEvent_t ev_fork = nullptr, ev_wb = nullptr, ev_wb0 = nullptr, ev_wb1 = nullptr;
-  bool wb_staged = false;    // evicted rows staged by the last swap, write-back not launched yet
-  bool wb_pending = false;   // write-back launched on the side stream, not yet waited for
-  bool wb_timed = false;     // ev_wb0 / ev_wb1 hold a measured write-back
+  hipEvent_t ev[5] = {};
+  int32_t last_pairs = 0;           // most miss pairs the last step could have staged
+  int64_t written_back = 0;         // last step whose staged rows a flush wrote to the host
   hipStream_t last_stream = nullptr;   // stream of the group's last step
 };
 
@@ -203,12 +204,8 @@ static void destroy_ctx(ula_ctx* ctx) {
       if (g.stage_ev[i]) (void)hipEventDestroy(g.stage_ev[i]);
       if (g.stage[i]) (void)hipHostFree(g.stage[i]);
     }
-    if (g.wb_stream) (void)hipStreamSynchronize(g.wb_stream);
     for (auto& e : g.ev)
       if (e) (void)hipEventDestroy(e);
-    for (hipEvent_t e : {g.ev_fork, g.ev_wb, g.ev_wb0, g.ev_wb1})
-      if (e) (void)hipEventDestroy(e);
-    if (g.wb_stream) (void)hipStreamDestroy(g.wb_stream);
   }
   delete ctx;
 }
@@ -272,6 +269,9 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     g.evict_rows = b + L.evict_rows;
     g.wb_h = reinterpret_cast<uint32_t*>(b + L.wb_h);
     g.miss_e = reinterpret_cast<int32_t*>(b + L.miss_e);
+    g.miss_stage = reinterpret_cast<uint32_t*>(b + L.miss_stage);
+    g.miss_rows = b + L.miss_rows;
+    g.hs_stage = reinterpret_cast<unsigned long long*>(b + L.hs_stage);
     g.res = reinterpret_cast<uint2*>(b + L.res);
     g.pool = b + L.pool;
     g.host = hdev ? hdev + (size_t)gi * d.H * d.slot_bytes : nullptr;
@@ -300,6 +300,8 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.dirty), d.T, 0u, s);
     if (e == hipSuccess) e = launch_fill_u64(g.desc, 2 * g.maxBlk, 0ull, s);
     if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.hown), d.H, 0xFFFFFFFFu, s);
+    // no host slot has a staged row: step 0xFFFFFFFF is never the previous step
+    if (e == hipSuccess) e = launch_fill_u64(g.hs_stage, d.H, ~0ull, s);
     if (e == hipSuccess) e = launch_fill_u32(g.bm, d.NB * d.W, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(g.tcnt, d.NB * d.T, 0u, s);
     if (e == hipSuccess) e = launch_init_bitmap(g.bm + kFree * d.W, g.W, d.P, g.tcnt + kFree * d.T, g.T, s);
@@ -309,12 +311,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
                         hipHostMallocDefault);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.stage_ev[i], hipEventDisableTiming);
     }
-    for (int i = 0; i < 6 && e == hipSuccess; ++i) e = hipEventCreate(&gh.ev[i]);
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&gh.wb_stream, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.ev_fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.ev_wb, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreate(&gh.ev_wb0);
-    if (e == hipSuccess) e = hipEventCreate(&gh.ev_wb1);
+    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventCreate(&gh.ev[i]);
     if (e != hipSuccess) rc = hip_fail(e, "ula_init");
   }
   if (rc == ULA_OK) {
@@ -360,6 +357,11 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const GroupDev& g = gh.d;
+  // An append needs no wait for a pending eviction write-back: it writes only
+  // free host slots, and a host slot is freed only by a miss whose victim was a
+  // free GPU slot. That never happens: an entry reaches the host pool only when
+  // no GPU slot is free, and nothing makes a GPU slot free again, so once a step
+  // can miss the free bucket stays empty.
   if (n <= kSmallAppend && n <= d.maxApp && rows_on_device) {
     // decode-time appends: one workgroup, addresses passed by value
     SmallAppend a{};
@@ -402,35 +404,17 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
   return ULA_OK;
 }
 
-// The write-back of a step's evicted rows is launched at the start of the
-// group's next step, on the side stream, so that it overlaps that step's
-// latency-bound lookup and selection kernels and not the HBM-bound gathers
-// (host-link writes slow concurrent HBM traffic). The next swap waits for it.
-static int fork_writeback(ula_ctx* ctx, GroupHost& gh, hipStream_t s) {
-  if (!gh.wb_staged) return ULA_OK;
-  const int32_t max_pairs = (int32_t)ctx->dims.maxU;
-  HIP_TRY(hipEventRecord(gh.ev_fork, s));
-  HIP_TRY(hipStreamWaitEvent(gh.wb_stream, gh.ev_fork, 0));
-  if (ctx->timing) HIP_TRY(hipEventRecord(gh.ev_wb0, gh.wb_stream));
-  HIP_TRY(launch_writeback(gh.d, max_pairs, gh.wb_stream));
-  if (ctx->timing) {
-    HIP_TRY(hipEventRecord(gh.ev_wb1, gh.wb_stream));
-    gh.wb_timed = true;
-  }
-  HIP_TRY(hipEventRecord(gh.ev_wb, gh.wb_stream));
-  gh.wb_staged = false;
-  gh.wb_pending = true;
-  return ULA_OK;
-}
-
-// Finish every group's outstanding write-back (before the host looks at state).
+// The evicted rows a step stages reach the host in the group's next step (the
+// write-back workgroups of its mark launch). Before the host reads state, a
+// stand-alone write-back puts the staged rows there too (those of the last
+// step, or of an earlier one if a device error stopped the steps after it).
 static int flush_writebacks(ula_ctx* ctx) {
   for (auto& gh : ctx->groups) {
-    int rc = fork_writeback(ctx, gh, gh.last_stream);
-    if (rc) return rc;
+    if (gh.steps == 0 || gh.written_back == gh.steps) continue;
+    HIP_TRY(launch_writeback(gh.d, std::max<int32_t>(gh.last_pairs, 1), gh.last_stream));
+    gh.written_back = gh.steps;
   }
   HIP_TRY(hipDeviceSynchronize());
-  for (auto& gh : ctx->groups) gh.wb_pending = false;
   return ULA_OK;
 }
 
@@ -448,16 +432,15 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   const int64_t t = gh.steps + 1;
   const int32_t cur = (int32_t)(t % ctx->dims.B);
   const bool tm = ctx->timing != 0;
+  const int32_t max_pairs = (int32_t)std::min<int64_t>(n, ctx->dims.maxU);
+  // the previous step's evicted rows, unless a flush already wrote them out
+  const int32_t wb_pairs = (gh.steps > 0 && gh.written_back != gh.steps) ? gh.last_pairs : 0;
 
-  {
-    int rc = fork_writeback(ctx, gh, s);
-    if (rc) return rc;
-  }
   gh.last_stream = s;
   if (tm) HIP_TRY(hipEventRecord(gh.ev[0], s));
   HIP_TRY(launch_tag(g, sel_dev, n, (uint32_t)t, s));
-  if (tm) HIP_TRY(hipEventRecord(gh.ev[1], s));
   HIP_TRY(launch_compact(g, sel_dev, n, (uint32_t)t, s));
+  if (tm) HIP_TRY(hipEventRecord(gh.ev[1], s));
   PlanArgs a{};
   a.mode = kPlanStep;
   a.dest = ring_id(cur);
@@ -465,23 +448,17 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   a.order[1] = kCold;
   a.norder = 2;
   for (int j = 1; j < ctx->dims.B; ++j) a.order[a.norder++] = (int8_t)ring_id((cur + j) % ctx->dims.B);
-  HIP_TRY(launch_mark(g, (uint32_t)t, cur, a, s));   // ends with the victim plan
+  // marking and victim plan, with the missed rows read in and the previous
+  // step's evicted rows written out, in one launch
+  HIP_TRY(launch_mark(g, (uint32_t)t, cur, a, max_pairs, wb_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
-  const int32_t max_pairs = (int32_t)std::min<int64_t>(n, ctx->dims.maxU);
   HIP_TRY(launch_extract(g, kPlanStep, a.dest, max_pairs, s));
-  // the previous step's write-back must land before host slots are read again
-  if (gh.wb_pending) {
-    HIP_TRY(hipStreamWaitEvent(s, gh.ev_wb, 0));
-    gh.wb_pending = false;
-  }
   if (tm) HIP_TRY(hipEventRecord(gh.ev[3], s));
-  HIP_TRY(launch_swap_in(g, max_pairs, s));
+  HIP_TRY(launch_swap_commit(g, (uint32_t)t, max_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[4], s));
-  gh.wb_staged = true;
-  HIP_TRY(launch_commit(g, (long long)t, max_pairs, s));
-  if (tm) HIP_TRY(hipEventRecord(gh.ev[5], s));
   gh.steps = t;
   gh.last_n = n;
+  gh.last_pairs = max_pairs;
   return ULA_OK;
 }
 
@@ -519,10 +496,6 @@ static void fill_stats(const Counters& c, ula_step_stats* s) {
 int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out) {
   if (!ctx) return ULA_EINVAL;
   HIP_TRY(hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream)));
-  {
-    int rc = flush_writebacks(ctx);
-    if (rc) return rc;
-  }
   std::vector<Counters> c;
   int rc = read_counters(ctx, c);
   if (rc) return rc;
@@ -602,17 +575,12 @@ int ula_set_timing(ula_ctx* ctx, int32_t enable) {
   return ULA_OK;
 }
 
-int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out6) {
-  if (!ctx || !ms_out6) return ULA_EINVAL;
+int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out4) {
+  if (!ctx || !ms_out4) return ULA_EINVAL;
   if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
   GroupHost& gh = ctx->groups[group];
-  HIP_TRY(hipEventSynchronize(gh.ev[5]));
-  for (int i = 0; i < 5; ++i) HIP_TRY(hipEventElapsedTime(&ms_out6[i], gh.ev[i], gh.ev[i + 1]));
-  ms_out6[5] = 0.f;
-  if (gh.wb_timed) {
-    HIP_TRY(hipEventSynchronize(gh.ev_wb1));
-    HIP_TRY(hipEventElapsedTime(&ms_out6[5], gh.ev_wb0, gh.ev_wb1));
-  }
+  HIP_TRY(hipEventSynchronize(gh.ev[4]));
+  for (int i = 0; i < 4; ++i) HIP_TRY(hipEventElapsedTime(&ms_out4[i], gh.ev[i], gh.ev[i + 1]));
   return ULA_OK;
 }
 

@@ -19,8 +19,10 @@
 //   res    the step's selection resolved to GPU slots, entry by entry, so that
 //          every per-layer gather reads slots sequentially instead of looking
 //          each address up in the mapping table again
-//   stage  append addresses, destinations and (host-sourced) rows; evicted rows
-//          awaiting their write-back to the host, with their host slots
+//   stage  append addresses, destinations and (host-sourced) rows; missed rows
+//          prefetched into HBM; evicted rows awaiting their write-back to the
+//          host, with their host slots, and per host slot the step and staging
+//          row of the last row evicted into it
 //   pool   u8[P][Lg][row_bytes]   the GPU pool, slot-major: one slot holds all
 //                        layers of its group contiguously
 // The host pool is u8[H][Lg][row_bytes] per group in pinned, device-mapped memory.
@@ -43,7 +45,9 @@ constexpr int kTileShift = 11;                  // 2048 slots per span
 constexpr int kScanBlock = 1024;                // selection entries per de-dup block
 constexpr int kMaxRing = 64;                    // B <= 64
 constexpr int kMaxBuckets = kMaxRing + 2;
-constexpr int kMarkBlocks = 32;                 // fixed grid (1024 threads each) of the mark kernel
+constexpr int kMarkBlocks = 32;                 // mark workgroups (1024 threads each) of the mark kernel
+constexpr int kPrefetchBlocks = 32;             // its prefetch workgroups (missed rows into HBM)
+constexpr int kWritebackBlocks = 16;            // its write-back workgroups (last step's evictions out)
 
 // bucket ids
 constexpr int kFree = 0;
@@ -59,11 +63,12 @@ struct alignas(64) Counters {
   int32_t n_items;       // work items written by the last selection plan
   int32_t hfree;         // free host slots
   int32_t bcnt[kMaxBuckets];  // slots per bucket
-  int32_t wb_n;          // pairs of the last swap, for its deferred write-back
+  int32_t wb_n;          // pairs of the last swap, for the deferred write-back of its victims
   int32_t done_mark;     // ticket of the mark kernel's last-workgroup plan
   int32_t lb_ticket;     // order in which compaction workgroups start (look-back scan)
-  int32_t pad_acc;       // padding entries counted by the compaction workgroups
-  int32_t pad[2];
+  int32_t pad_acc;       // padding entries counted by the tag kernel
+  uint32_t wb_step;      // step whose swap staged the rows in evict_rows (0 = none)
+  int32_t pad[1];
 };
 static_assert(sizeof(Counters) % 64 == 0, "counter block alignment");
 
@@ -91,6 +96,10 @@ struct GroupDev {        // device view of one group, passed by value to kernels
   int32_t* miss_la;
   uint32_t* miss_h;
   int32_t* miss_e;       // [maxU] selection entry of each miss's first occurrence
+  uint32_t* miss_stage;  // [maxU] staging row of the previous step holding the missed row, or absent
+  uint8_t* miss_rows;    // [maxU][slot_bytes] missed rows prefetched into HBM
+  unsigned long long* hs_stage;  // [H] (step << 32) | staging row of the row last evicted into
+                                 //   each host slot (until that step's write-back lands)
   uint2* res;            // [max_sets * max_k] per selection entry of the last step:
                          //   (address, GPU slot), or (address, 0x80000000 | entry of the
                          //   first occurrence) for a repeated miss; (-1, absent) for padding
@@ -155,7 +164,8 @@ hipError_t launch_init_bitmap(uint32_t* words, int32_t nwords, int64_t nbits, ui
 hipError_t launch_init_counters(Counters* c, int32_t P, int32_t H, hipStream_t s);
 
 hipError_t launch_tag(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
-hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArgs& a, hipStream_t s);
+hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArgs& a,
+                       int32_t max_pairs, int32_t wb_pairs, hipStream_t s);
 hipError_t launch_compact(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
 hipError_t launch_plan(const GroupDev& g, const PlanArgs& a, hipStream_t s);
 hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, int32_t max_items,
@@ -163,9 +173,8 @@ hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, int32_t
 hipError_t launch_append_small(const GroupDev& g, const SmallAppend& a, const uint8_t* rows,
                               hipStream_t s);
 hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s);
-hipError_t launch_swap_in(const GroupDev& g, int32_t max_pairs, hipStream_t s);
+hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s);
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s);
-hipError_t launch_commit(const GroupDev& g, long long t, int32_t max_pairs, hipStream_t s);
 hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
                          uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s);
 
