@@ -217,7 +217,7 @@ def gpu_run(tr, W: int, K: int, phases: bool) -> dict:
         initial_load(eng, tr, groups, rows)
         eng.set_timing(True)
         torch.cuda.synchronize()
-        ph = np.zeros(4)
+        ph = np.zeros(3)
         h2d = d2h = 0
         n = 0
         prev_evict = {g: 0 for g in groups}
@@ -282,7 +282,7 @@ def main():
         rnd = lambda x, d: None if x is None else round(x, d)
         miss = {"bound": "host-link", "peak": round(LINK_PEAK_GBS, 1), "unit": "GB/s per direction",
                 "note": "both directions run concurrently in the k_mark launch (prefetch and "
-                        "write-back workgroups beside the hit marking and victim planning); rates "
+                        "write-back workgroups beside the hit marking and victim selection); rates "
                         "are bytes over that launch's duration, a lower bound on the link rate",
                 "h2d": {"kernel": "k_mark (prefetch workgroups)", "achieved": rnd(gin, 2),
                         "frac": rnd(None if gin is None else gin / LINK_PEAK_GBS, 4),
@@ -291,7 +291,7 @@ def main():
                         "frac": rnd(None if gout is None else gout / LINK_PEAK_GBS, 4),
                         "bytes_per_step": down / r["group_steps"]},
                 "phase_ms_per_group_step": {k: round(v, 5) for k, v in zip(
-                    ["lookup_dedup", "mark_plan_link", "victims", "swap_commit"],
+                    ["lookup_dedup", "mark_select_link", "swap_commit"],
                     r["phase_ms"])}}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K,

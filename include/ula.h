@@ -193,12 +193,12 @@ int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr);
 
 /* Per-phase timing of the last step of group g, in milliseconds, when enabled
  * with ula_set_timing: [0] lookup + de-duplication, [1] hit marking + fold +
- * victim planning, with the missed rows read in and the previous step's
- * evicted rows written out over the host link in the same launch, [2] victim
- * extraction, [3] rows into the victim slots + commit + signal.
- * ula_read_timing synchronises on the step's last event. */
+ * victim selection, with the missed rows read in and the previous step's
+ * evicted rows written out over the host link in the same launch, [2] rows into
+ * the victim slots + commit + signal. ula_read_timing synchronises on the
+ * step's last event. */
 int ula_set_timing(ula_ctx* ctx, int32_t enable);
-int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out4);
+int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out3);
 
 /* Release the context (not the caller's buffers). Waits for no stream. */
 int ula_destroy(ula_ctx* ctx);

@@ -55,6 +55,7 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     g.ctr->wb_n = m;
     g.ctr->wb_step = t;
+    g.ctr->mark_role = 0;   // the mark launch has ended: every workgroup took its role
   }
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
   const uint32_t total = (uint32_t)m * chunks;

@@ -119,6 +119,42 @@ __global__ __launch_bounds__(1024) void k_plan(GroupDev g, PlanArgs a) {
   plan_body(g, a, scratch, s_nonempty);
 }
 
+// One wavefront takes the lowest `take` set bits of one span of one bitmap.
+// STEP: taken GPU slots join ring[cur] (dest); the output list is the victims,
+// and victims taken from the free bucket carry the top bit (their slot holds no
+// row to evict). APPEND: taken GPU slots join cold (dest), taken host slots
+// leave the free-host bitmap; the output list is the destinations (host slots
+// carry the host bit).
+__device__ __forceinline__ void extract_item(const GroupDev& g, const SelItem it, int32_t mode,
+                                             int32_t dest, uint32_t* out) {
+  const int lane = lane_id();
+  const bool host = it.src == kHostFreeId;
+  const uint32_t flag = (host || (mode == kPlanStep && it.src == kFree)) ? kHostBit : 0u;
+  uint32_t* words = bucket_words(g, it.src);
+  const int w = it.tile * kTileWords + lane;
+  const uint32_t x = w < bucket_nwords(g, it.src) ? words[w] : 0u;
+  const int cnt = __popc(x);
+  const int ex = wave_inclusive_sum(cnt) - cnt;
+  int mine = it.take - ex;                    // lowest set bits this lane gives
+  mine = mine < 0 ? 0 : (mine > cnt ? cnt : mine);
+  uint32_t y = x, taken = 0;
+  for (int r = 0; r < mine; ++r) {
+    const uint32_t low = y & (0u - y);
+    const uint32_t slot = (uint32_t)w * 32u + (uint32_t)(__ffs(y) - 1);
+    y ^= low;
+    taken |= low;
+    out[it.out_off + ex + r] = flag | slot;
+  }
+  if (taken) {
+    words[w] = x & ~taken;
+    if (!host) atomicOr(&g.bm[(size_t)dest * g.W + w], taken);
+  }
+  if (lane == 0) {
+    bucket_tcnt(g, it.src)[it.tile] -= (uint32_t)it.take;
+    if (!host) atomicAdd(&g.tcnt[(size_t)dest * g.T + it.tile], (uint32_t)it.take);
+  }
+}
+
 // Fold and hit marking, word-parallel and free of global atomics. One
 // wavefront per 2048-slot span, lane = bitmap word. A span is visited only if
 // it holds hits of this step (dirty == t) or survivors in ring[cur] to fold;
@@ -131,25 +167,69 @@ __global__ __launch_bounds__(1024) void k_plan(GroupDev g, PlanArgs a) {
 // sums; bucket-count changes go to per-workgroup partials, which the last
 // workgroup adds up when it plans the step's victims.
 //
-// The same launch carries the host-link work of the miss path in extra
-// workgroups: `pf` prefetch workgroups read the step's missed rows into HBM
-// (victims are not known yet; the swap kernel moves them into the victim slots
-// over HBM), and the rest write the previous step's evicted rows out, when
-// wb_step names that step. Both link directions then run concurrently, and only
-// beside this kernel's own marking and planning.
+// The same launch carries the rest of the step's selection and the host-link
+// work of the miss path in extra workgroups:
+//   - `pf` prefetch workgroups read the step's missed rows into HBM (victims
+//     are not known yet; the swap kernel moves them into the victim slots over
+//     HBM);
+//   - `wbb` write-back workgroups write the previous step's evicted rows out,
+//     when wb_step names that step; both link directions then run concurrently,
+//     and only beside this launch's own marking and planning;
+//   - `nh` extraction workgroups wait for the victim plan, then take one work
+//     item per wavefront, together with the planning workgroup.
+// Roles follow the order in which workgroups start (a ticket), so every
+// workgroup that waits started after all the workgroups it waits for, which
+// are resident and never wait themselves.
+__device__ __forceinline__ void extract_part(const GroupDev& g, int32_t dest, int part, int nparts) {
+  const int nitems = g.ctr->n_items;
+  const int wpb = blockDim.x / kWave;
+  for (int i = part * wpb + threadIdx.x / kWave; i < nitems; i += nparts * wpb)
+    extract_item(g, g.items[i], kPlanStep, dest, g.victims);
+}
+
+constexpr int kPlanWaitLimit = 1 << 20;
+
 __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t cur, PlanArgs a,
-                                               FastDiv per_slot, int32_t pf, uint32_t wb_step) {
+                                               FastDiv per_slot, int32_t pf, int32_t wbb, int32_t nh,
+                                               uint32_t wb_step) {
   __shared__ int s_delta[kMaxBuckets];
-  __shared__ int s_last;
+  __shared__ int s_last, s_role, s_fail;
   __shared__ int scratch[1024 / kWave + 1];
   __shared__ unsigned long long s_nonempty[1024 / kWave];
   if (block_failed(g.ctr)) return;
-  if (blockIdx.x >= kMarkBlocks + pf) {
-    writeback_rows(g, wb_step, per_slot, blockIdx.x - kMarkBlocks - pf, gridDim.x - kMarkBlocks - pf);
+  if (threadIdx.x == 0) {
+    s_role = atomicAdd(&g.ctr->mark_role, 1);
+    s_fail = 0;
+  }
+  __syncthreads();
+  const int role = s_role;
+  if (role < 0 || role >= (int)gridDim.x) {   // a corrupt ticket: never index with it
+    if (threadIdx.x == 0) latch(g.ctr, ULA_ESTATE);
     return;
   }
-  if (blockIdx.x >= kMarkBlocks) {
-    prefetch_misses(g, per_slot, blockIdx.x - kMarkBlocks, pf);
+  if (role >= kMarkBlocks + pf + wbb) {
+    // extraction: wait until the planning workgroup publishes the plan
+    if (threadIdx.x == 0) {
+      int spins = 0;
+      while (__hip_atomic_load(&g.ctr->plan_done, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) != t) {
+        if (++spins > kPlanWaitLimit || status_of(g.ctr)) {
+          s_fail = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (s_fail && !status_of(g.ctr)) latch(g.ctr, ULA_ESTATE);   // a wait that never ended
+    }
+    __syncthreads();
+    if (!s_fail) extract_part(g, a.dest, role - (kMarkBlocks + pf + wbb), nh + 1);
+    return;
+  }
+  if (role >= kMarkBlocks + pf) {
+    writeback_rows(g, wb_step, per_slot, role - kMarkBlocks - pf, wbb);
+    return;
+  }
+  if (role >= kMarkBlocks) {
+    prefetch_misses(g, per_slot, role - kMarkBlocks, pf);
     return;
   }
   for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x) s_delta[i] = 0;
@@ -161,8 +241,7 @@ __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t c
   uint32_t* ring = g.bm + (size_t)rc * g.W;
   uint32_t* ct = g.tcnt + (size_t)kCold * g.T;
   uint32_t* rt = g.tcnt + (size_t)rc * g.T;
-  for (int tile = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave; tile < g.T;
-       tile += nwaves) {
+  for (int tile = role * (blockDim.x / kWave) + threadIdx.x / kWave; tile < g.T; tile += nwaves) {
     const bool hits = g.dirty[tile] == (int32_t)t;
     const int fold_cnt = (int)rt[tile];
     if (!hits && fold_cnt == 0) continue;     // nothing to fold, no hit: skip the span
@@ -224,7 +303,7 @@ __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t c
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x)
-    g.partial[blockIdx.x * kMaxBuckets + i] = s_delta[i];
+    g.partial[role * kMaxBuckets + i] = s_delta[i];
   // The last workgroup to finish plans the victims: one release per workgroup
   // before its ticket, the acquire-release ticket, and an acquire in the last
   // workgroup make every workgroup's bitmaps, span counts and partials visible.
@@ -243,44 +322,15 @@ __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t c
   __syncthreads();
   if (!s_last) return;
   plan_body(g, a, scratch, s_nonempty);
+  // publish the plan (items, counts) to the extraction workgroups, then join them
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    __hip_atomic_store(&g.ctr->plan_done, t, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  extract_part(g, a.dest, nh, nh + 1);
 }
 
-
-// One wavefront takes the lowest `take` set bits of one span of one bitmap.
-// STEP: taken GPU slots join ring[cur] (dest); the output list is the victims,
-// and victims taken from the free bucket carry the top bit (their slot holds no
-// row to evict). APPEND: taken GPU slots join cold (dest), taken host slots
-// leave the free-host bitmap; the output list is the destinations (host slots
-// carry the host bit).
-__device__ __forceinline__ void extract_item(const GroupDev& g, const SelItem it, int32_t mode,
-                                             int32_t dest, uint32_t* out) {
-  const int lane = lane_id();
-  const bool host = it.src == kHostFreeId;
-  const uint32_t flag = (host || (mode == kPlanStep && it.src == kFree)) ? kHostBit : 0u;
-  uint32_t* words = bucket_words(g, it.src);
-  const int w = it.tile * kTileWords + lane;
-  const uint32_t x = w < bucket_nwords(g, it.src) ? words[w] : 0u;
-  const int cnt = __popc(x);
-  const int ex = wave_inclusive_sum(cnt) - cnt;
-  int mine = it.take - ex;                    // lowest set bits this lane gives
-  mine = mine < 0 ? 0 : (mine > cnt ? cnt : mine);
-  uint32_t y = x, taken = 0;
-  for (int r = 0; r < mine; ++r) {
-    const uint32_t low = y & (0u - y);
-    const uint32_t slot = (uint32_t)w * 32u + (uint32_t)(__ffs(y) - 1);
-    y ^= low;
-    taken |= low;
-    out[it.out_off + ex + r] = flag | slot;
-  }
-  if (taken) {
-    words[w] = x & ~taken;
-    if (!host) atomicOr(&g.bm[(size_t)dest * g.W + w], taken);
-  }
-  if (lane == 0) {
-    bucket_tcnt(g, it.src)[it.tile] -= (uint32_t)it.take;
-    if (!host) atomicAdd(&g.tcnt[(size_t)dest * g.T + it.tile], (uint32_t)it.take);
-  }
-}
 
 __global__ __launch_bounds__(256) void k_extract(GroupDev g, int32_t mode, int32_t dest) {
   if (status_of(g.ctr)) return;
@@ -334,9 +384,10 @@ hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArg
     return (int)std::min<int64_t>(n, cap);
   };
   const int pf = g.H > 0 ? blocks_for(max_pairs, kPrefetchBlocks) : 0;
-  const int wb = g.H > 0 ? blocks_for(wb_pairs, kWritebackBlocks) : 0;
-  k_mark<<<kMarkBlocks + pf + wb, 1024, 0, s>>>(g, t, cur, a, FastDiv(chunks), pf,
-                                                wb > 0 ? t - 1u : 0u);
+  const int wbb = g.H > 0 ? blocks_for(wb_pairs, kWritebackBlocks) : 0;
+  const int nh = kExtractHelpers;
+  k_mark<<<kMarkBlocks + pf + wbb + nh, 1024, 0, s>>>(g, t, cur, a, FastDiv(chunks), pf, wbb, nh,
+                                                      wbb > 0 ? t - 1u : 0u);
   return hipGetLastError();
 }
 

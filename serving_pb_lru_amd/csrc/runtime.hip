@@ -148,7 +148,7 @@ struct GroupHost {
   hipEvent_t stage_ev[kStageSlots] = {};
   bool stage_used[kStageSlots] = {};
   int stage_next = 0;
-  hipEvent_t ev[5] = {};
+  hipEvent_t ev[4] = {};
   int32_t last_pairs = 0;           // most miss pairs the last step could have staged
   int64_t written_back = 0;         // last step whose staged rows a flush wrote to the host
   hipStream_t last_stream = nullptr;   // stream of the group's last step
@@ -311,7 +311,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
                         hipHostMallocDefault);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.stage_ev[i], hipEventDisableTiming);
     }
-    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = hipEventCreate(&gh.ev[i]);
+    for (int i = 0; i < 4 && e == hipSuccess; ++i) e = hipEventCreate(&gh.ev[i]);
     if (e != hipSuccess) rc = hip_fail(e, "ula_init");
   }
   if (rc == ULA_OK) {
@@ -448,14 +448,12 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   a.order[1] = kCold;
   a.norder = 2;
   for (int j = 1; j < ctx->dims.B; ++j) a.order[a.norder++] = (int8_t)ring_id((cur + j) % ctx->dims.B);
-  // marking and victim plan, with the missed rows read in and the previous
-  // step's evicted rows written out, in one launch
+  // marking, victim plan and extraction, with the missed rows read in and the
+  // previous step's evicted rows written out, in one launch
   HIP_TRY(launch_mark(g, (uint32_t)t, cur, a, max_pairs, wb_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
-  HIP_TRY(launch_extract(g, kPlanStep, a.dest, max_pairs, s));
-  if (tm) HIP_TRY(hipEventRecord(gh.ev[3], s));
   HIP_TRY(launch_swap_commit(g, (uint32_t)t, max_pairs, s));
-  if (tm) HIP_TRY(hipEventRecord(gh.ev[4], s));
+  if (tm) HIP_TRY(hipEventRecord(gh.ev[3], s));
   gh.steps = t;
   gh.last_n = n;
   gh.last_pairs = max_pairs;
@@ -575,12 +573,12 @@ int ula_set_timing(ula_ctx* ctx, int32_t enable) {
   return ULA_OK;
 }
 
-int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out4) {
-  if (!ctx || !ms_out4) return ULA_EINVAL;
+int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out3) {
+  if (!ctx || !ms_out3) return ULA_EINVAL;
   if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
   GroupHost& gh = ctx->groups[group];
-  HIP_TRY(hipEventSynchronize(gh.ev[4]));
-  for (int i = 0; i < 4; ++i) HIP_TRY(hipEventElapsedTime(&ms_out4[i], gh.ev[i], gh.ev[i + 1]));
+  HIP_TRY(hipEventSynchronize(gh.ev[3]));
+  for (int i = 0; i < 3; ++i) HIP_TRY(hipEventElapsedTime(&ms_out3[i], gh.ev[i], gh.ev[i + 1]));
   return ULA_OK;
 }
 

@@ -48,6 +48,7 @@ constexpr int kMaxBuckets = kMaxRing + 2;
 constexpr int kMarkBlocks = 32;                 // mark workgroups (1024 threads each) of the mark kernel
 constexpr int kPrefetchBlocks = 32;             // its prefetch workgroups (missed rows into HBM)
 constexpr int kWritebackBlocks = 16;            // its write-back workgroups (last step's evictions out)
+constexpr int kExtractHelpers = 8;              // its extraction workgroups (besides the planning one)
 
 // bucket ids
 constexpr int kFree = 0;
@@ -68,7 +69,8 @@ struct alignas(64) Counters {
   int32_t lb_ticket;     // order in which compaction workgroups start (look-back scan)
   int32_t pad_acc;       // padding entries counted by the tag kernel
   uint32_t wb_step;      // step whose swap staged the rows in evict_rows (0 = none)
-  int32_t pad[1];
+  int32_t mark_role;     // order in which the mark launch's workgroups start (their roles)
+  uint32_t plan_done;    // step whose victim plan is published (extraction may start)
 };
 static_assert(sizeof(Counters) % 64 == 0, "counter block alignment");
 

@@ -204,7 +204,7 @@ class Engine:
         _check(lib().ula_set_timing(self.ctx, 1 if enable else 0), "ula_set_timing")
 
     def read_timing(self, group: int) -> List[float]:
-        ms = (ctypes.c_float * 4)()
+        ms = (ctypes.c_float * 3)()
         _check(lib().ula_read_timing(self.ctx, group, ms), "ula_read_timing")
         return list(ms)
 

@@ -38,7 +38,13 @@ def assert_same_state(st: dict, ref: dict, where: str) -> None:
 
 
 def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, check_every=1):
-    """selections: optional {g: list of int32 [n_sets][k]} overriding the trace's."""
+    """selections: optional {g: list of int32 [n_sets][k]} overriding the trace's.
+
+    The state is exported (which writes any staged evicted rows out to the host
+    pool) every `check_every` steps and after the last; in between, evicted rows
+    reach the host pool only through the next step's own write-back. Gathered
+    rows are checked after every step.
+    """
     import torch
     tr = Trace(wl, steps)
     groups = list(range(wl.groups)) if groups is None else groups
@@ -74,6 +80,15 @@ def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, ch
                         bad = np.argwhere((got != ref).any(axis=-1))
                         raise AssertionError(f"group {g} step {t} layer {l}: gathered rows differ at "
                                              f"{len(bad)} rows, first {bad[:5].tolist()}")
+        # stored rows of every entry, from whichever pool holds them (the host
+        # pool after the last step's evicted rows are written out)
+        known = np.concatenate([tr.initial_load_order()] + [tr.appends(t) for t in range(1, tr.steps + 1)])
+        rng = np.random.default_rng([tr.N, 11])
+        probe = known if known.size <= 4096 else rng.choice(known, size=4096, replace=False)
+        for g in groups:
+            got = eng.read_rows(g, probe)
+            want = rows_for(wl.seed, g, probe, wl.layers, wl.row_bytes)
+            assert np.array_equal(got, want), f"group {g}: stored rows differ after the last step"
         return ora
     finally:
         eng.close()

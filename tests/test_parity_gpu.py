@@ -76,17 +76,40 @@ def test_ring_lengths_parity(ring):
     run_parity(wl)
 
 
-@pytest.mark.parametrize("name,factor,steps", [
-    ("r16_64k_g1x3", 16, 10),
-    ("r64_64k128k_g24x3", 32, 5),
-    ("spec3_r128_64k128k_g4", 32, 6),
-    ("evict_r256_128k_g2", 32, 8),
-    ("evict_r256_128k_g2_ctl98", 32, 6),
+@pytest.mark.parametrize("name,factor,steps,check_every", [
+    ("r16_64k_g1x3", 16, 10, 1),
+    ("r16_64k_g1x3", 16, 10, 4),
+    ("r64_64k128k_g24x3", 32, 5, 1),
+    ("spec3_r128_64k128k_g4", 32, 6, 1),
+    ("spec3_r128_64k128k_g4", 32, 6, 100),
+    ("evict_r256_128k_g2", 32, 8, 1),
+    ("evict_r256_128k_g2", 32, 8, 3),
+    ("evict_r256_128k_g2_ctl98", 32, 6, 1),
 ])
-def test_scaled_workload_parity(name, factor, steps):
+def test_scaled_workload_parity(name, factor, steps, check_every):
     wl = scaled(preset(name), factor)
     groups = None if wl.groups <= 4 else [0, 7, 23]
-    run_parity(wl, steps=steps, groups=groups, max_append=1 << 15)
+    run_parity(wl, steps=steps, groups=groups, max_append=1 << 15, check_every=check_every)
+
+
+def _pingpong():
+    """One request of 64 positions, a pool of 8 slots, 2 ring buckets and k = 8:
+    alternating disjoint sets miss every entry and evict the previous set, so
+    most misses ask for rows evicted by the step just before."""
+    from synth.configs import Workload
+    wl = Workload(name="pingpong", requests=1, ctx_fixed=64, ctx_range=None, sets_per_request=1,
+                  draft_keep=0.0, groups=1, layers=2, k=8, pool_frac=0.0, pool_slots=8, ring=2,
+                  steps=12, appends=0, overlap=0.0, p_recent=0.0, window=8, row_bytes=64, seed=3)
+    A, B, C = (np.arange(8 * i, 8 * i + 8, dtype=np.int32)[None, :] for i in range(3))
+    mix = np.concatenate([A[:, :4], B[:, 4:]], axis=1)
+    return wl, [A, B, A, B, C, A, B, mix, C, A, B, A]
+
+
+@pytest.mark.parametrize("check_every", [1, 2, 5, 100])
+def test_evicted_rows_missed_next_step(check_every):
+    wl, sels = _pingpong()
+    ora = run_parity(wl, selections={0: sels}, check_every=check_every)
+    assert ora[0].last.as_tuple()[2:4] == (8, 8)   # the last step still swaps every entry
 
 
 def test_pool_holds_everything_parity():
