@@ -9,34 +9,41 @@
 // step already resolved its selection to slots entry by entry (the lookup is
 // done once per group); a gather of that selection reads those slots in order
 // and only entries that differ fall back to the mapping table. A
-// workgroup takes 32 output rows at a time: 32 lanes look the rows up once
-// (selection entry, then mapping table) into LDS, then all 256 lanes stream
-// the rows in 16-byte pieces, C = row_bytes / 16 pieces per row, lane i taking
-// piece (i mod C) of row (i div C): consecutive lanes write consecutive 16
-// bytes (fully coalesced, non-temporal stores) and read one contiguous source
-// row. Six pieces per lane are in flight (one round for 656-byte rows). Bound
-// by HBM bandwidth.
+// workgroup takes ROWS output rows at a time: ROWS lanes look the rows up once
+// (selection entry and resolved slot in one round trip, else the mapping
+// table) into LDS, then all lanes stream the rows in 16-byte pieces,
+// C = row_bytes / 16 pieces per row, lane i taking piece (i mod C) of row
+// (i div C): consecutive lanes write consecutive 16 bytes (fully coalesced,
+// non-temporal stores) and read one contiguous source row. UNROLL pieces per
+// lane are in flight; for 656-byte rows both tilings below cover all staged
+// rows in one round. Bound by HBM bandwidth.
+//
+// Tilings (measured on MI355X with 656-byte rows): a small gather (tens of
+// thousands of rows, a few workgroups per compute unit) is fastest with 64
+// rows and 11 pieces in flight per lane of 256; a large one with 32 rows and 3
+// pieces per lane of 512, which keeps more workgroups resident.
 #include "device_util.h"
 
 namespace ula {
 
-constexpr int kGatherRows = 32;   // output rows staged per workgroup iteration
-constexpr int kGatherUnroll = 6;  // 16-byte pieces in flight per lane
+constexpr int kSmallGatherRows = 1 << 17;   // up to this many rows: the small-gather tiling
 
 // Rows are read with plain (cached) loads: repeated entries of one step (the
 // speculative sets) and the heavy overlap between consecutive steps both hit the
 // caches; non-temporal loads measured 18% slower on the speculative workload and
 // only 3% faster where nothing repeats.
-__global__ __launch_bounds__(256) void k_gather(GroupDev g, const int32_t* __restrict__ sel, int32_t n,
-                                                int32_t layer, uint8_t* __restrict__ out,
-                                                long long want_flag, int32_t n_res, FastDiv per_row) {
-  __shared__ long long s_off[kGatherRows];   // source byte offset of each staged row, -1 = zero row
+template <int ROWS, int UNROLL, int THREADS>
+__global__ __launch_bounds__(THREADS) void k_gather(GroupDev g, const int32_t* __restrict__ sel, int32_t n,
+                                                    int32_t layer, uint8_t* __restrict__ out,
+                                                    long long want_flag, int32_t n_res, FastDiv per_row) {
+  static_assert(ROWS < THREADS, "one lane per staged row plus the checking lane");
+  __shared__ long long s_off[ROWS];   // source byte offset of each staged row, -1 = zero row
   __shared__ int s_ok;
   const uint32_t C = (uint32_t)g.row_bytes / 16u;
   const size_t layer_off = (size_t)layer * g.row_bytes;
   int err = 0;
   bool first_round = true;
-  for (int row0 = blockIdx.x * kGatherRows; row0 < n; row0 += gridDim.x * kGatherRows) {
+  for (int row0 = blockIdx.x * ROWS; row0 < n; row0 += gridDim.x * ROWS) {
     // 1. resolve the block's rows once: the step already resolved its own
     //    selection entry by entry (res); an entry that differs from it, or lies
     //    beyond it, goes through the mapping table. In the first round thread 0
@@ -46,7 +53,7 @@ __global__ __launch_bounds__(256) void k_gather(GroupDev g, const int32_t* __res
     //    kernel-boundary acquire already makes the moved rows visible; this
     //    check only catches a gather issued without that ordering (an acquire
     //    here would invalidate caches in every workgroup).
-    if (first_round && threadIdx.x == kGatherRows) {
+    if (first_round && threadIdx.x == ROWS) {
       int ok = status_of(g.ctr) == 0;
       const long long f = __hip_atomic_load(&g.ctr->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (ok && f != want_flag) {
@@ -55,15 +62,16 @@ __global__ __launch_bounds__(256) void k_gather(GroupDev g, const int32_t* __res
       }
       s_ok = ok;
     }
-    if (threadIdx.x < kGatherRows) {
+    if (threadIdx.x < ROWS) {
       const int r = row0 + threadIdx.x;
       long long off = -1;
       if (r < n) {
+        // the selection entry and its resolved slot are loaded together (one round trip)
+        const uint2 rs = r < n_res ? g.res[r] : make_uint2(kAbsent, kAbsent);
         const int32_t la = sel[r];
         if (la != -1) {
           uint32_t slot = kAbsent;
           if (r < n_res) {
-            const uint2 rs = g.res[r];
             if (rs.x == (uint32_t)la) {
               slot = rs.y;
               if ((slot & kHostBit) && slot != kAbsent && (int32_t)(slot & ~kHostBit) < n_res) {
@@ -92,14 +100,14 @@ __global__ __launch_bounds__(256) void k_gather(GroupDev g, const int32_t* __res
       first_round = false;
     }
     // 2. stream the staged rows: piece i of the block is piece (i mod C) of row (i div C)
-    const int nrows = min(kGatherRows, n - row0);
+    const int nrows = min(ROWS, n - row0);
     const uint32_t pieces = (uint32_t)nrows * C;
     vec4u* o = reinterpret_cast<vec4u*>(out) + (size_t)row0 * C;
-    for (uint32_t i0 = threadIdx.x; i0 < pieces; i0 += blockDim.x * kGatherUnroll) {
-      vec4u v[kGatherUnroll];
+    for (uint32_t i0 = threadIdx.x; i0 < pieces; i0 += THREADS * UNROLL) {
+      vec4u v[UNROLL];
 #pragma unroll
-      for (int u = 0; u < kGatherUnroll; ++u) {
-        const uint32_t i = i0 + u * blockDim.x;
+      for (int u = 0; u < UNROLL; ++u) {
+        const uint32_t i = i0 + u * THREADS;
         v[u] = vec4u{0u, 0u, 0u, 0u};
         if (i < pieces) {
           const uint32_t r = per_row.div(i);
@@ -111,8 +119,8 @@ __global__ __launch_bounds__(256) void k_gather(GroupDev g, const int32_t* __res
         }
       }
 #pragma unroll
-      for (int u = 0; u < kGatherUnroll; ++u) {
-        const uint32_t i = i0 + u * blockDim.x;
+      for (int u = 0; u < UNROLL; ++u) {
+        const uint32_t i = i0 + u * THREADS;
         if (i < pieces) __builtin_nontemporal_store(v[u], o + i);
       }
     }
@@ -121,14 +129,21 @@ __global__ __launch_bounds__(256) void k_gather(GroupDev g, const int32_t* __res
   if (err) latch(g.ctr, err);
 }
 
+template <int ROWS, int UNROLL, int THREADS>
+static hipError_t launch_tiled(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer, uint8_t* out,
+                               long long want_flag, int32_t n_res, hipStream_t s) {
+  int blocks = (n + ROWS - 1) / ROWS;
+  if (blocks > 32768) blocks = 32768;
+  k_gather<ROWS, UNROLL, THREADS><<<blocks, THREADS, 0, s>>>(g, sel, n, layer, out, want_flag, n_res,
+                                                             FastDiv((uint32_t)g.row_bytes / 16u));
+  return hipGetLastError();
+}
+
 hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
                          uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  int blocks = (n + kGatherRows - 1) / kGatherRows;
-  if (blocks > 32768) blocks = 32768;
-  k_gather<<<blocks, 256, 0, s>>>(g, sel, n, layer, out, want_flag, n_res,
-                                  FastDiv((uint32_t)g.row_bytes / 16u));
-  return hipGetLastError();
+  if (n <= kSmallGatherRows) return launch_tiled<64, 11, 256>(g, sel, n, layer, out, want_flag, n_res, s);
+  return launch_tiled<32, 3, 512>(g, sel, n, layer, out, want_flag, n_res, s);
 }
 
 }  // namespace ula
