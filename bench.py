@@ -16,8 +16,10 @@ value = selected row-layers resolved and gathered per second
 
 Printed as one JSON line, with:
   roofline      the gather kernel against HBM peak (1312 algorithmic bytes per
-                gathered row-layer: 656 read + 656 written), its launch duration
-                measured with HIP events on the engine's stream;
+                gathered row-layer: 656 read + 656 written), its average kernel
+                duration over the timed region from HIP events that every gather
+                records in its own dispatch on the engine's stream (the kernel's
+                execution, as rocprofv3 reports it);
   miss_path     the miss path against the host link, per direction: missed rows
                 in (656 * layers bytes per miss) and the previous step's
                 evicted rows out (656 * layers bytes per eviction), both moved
@@ -170,22 +172,14 @@ def gpu_run(tr, W: int, K: int, phases: bool) -> dict:
     outs = {g: [torch.empty((tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
                 for _ in range(wl.layers)] for g in groups}
 
-    def run_step(eng, t, gather_events=None):
+    def run_step(eng, t):
         for g in groups:
             if apps[t - 1].size:
                 eng.append(g, apps[t - 1], app_rows[g][t - 1])
             sel = sels[g][t - 1]
             eng.step(g, sel)
             for l in range(wl.layers):
-                if gather_events is not None:
-                    a = torch.cuda.Event(enable_timing=True)
-                    b = torch.cuda.Event(enable_timing=True)
-                    a.record()
-                    eng.gather(g, l, sel, out=outs[g][l])
-                    b.record()
-                    gather_events.append((a, b))
-                else:
-                    eng.gather(g, l, sel, out=outs[g][l])
+                eng.gather(g, l, sel, out=outs[g][l])
 
     # ---- timed replay ----------------------------------------------------
     eng = engine_for(tr, max_append=1 << 16)
@@ -194,22 +188,27 @@ def gpu_run(tr, W: int, K: int, phases: bool) -> dict:
     for t in range(1, W + 1):
         run_step(eng, t)
     torch.cuda.synchronize()
-    gev = []
+    # every gather of the timed region records its kernel's start and end in its
+    # own dispatch (HIP events on the engine's stream, no launch overhead inside)
+    eng.set_timing(eng.TIMING_GATHER)
+    eng.read_gather_timing()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     t0 = time.perf_counter()
     for t in range(W + 1, W + K + 1):
-        run_step(eng, t, gev)
+        run_step(eng, t)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     eng.sync()   # raises if the device latched an error
     ev_ms = start.elapsed_time(end)
-    gather_ms = [a.elapsed_time(b) for a, b in gev]
+    g_total_ms, g_launches = eng.read_gather_timing()
+    eng.set_timing(0)
     eng.close()
     del eng
-    res = dict(wall_s=wall, event_ms=ev_ms, gather_ms=gather_ms)
+    res = dict(wall_s=wall, event_ms=ev_ms, gather_ms=g_total_ms / max(g_launches, 1),
+               gather_launches=g_launches)
 
     # ---- per-phase replay (diagnostic, synchronises every step) --------------
     if phases:
@@ -264,9 +263,9 @@ def main():
     value = per_step * K / r["wall_s"]
     ms_per_step = r["event_ms"] / K
 
-    g_ms = float(np.mean(r["gather_ms"]))
+    g_ms = float(r["gather_ms"])
     rows_per_gather = tr.n_sets * tr.k
-    g_bytes = 1312 * rows_per_gather
+    g_bytes = 2 * wl.row_bytes * rows_per_gather
     g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": "k_gather", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": gather_traffic(wl.name),

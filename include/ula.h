@@ -191,14 +191,22 @@ int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host
  * completed step), for hipStreamWaitValue64 on another stream. */
 int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr);
 
-/* Per-phase timing of the last step of group g, in milliseconds, when enabled
- * with ula_set_timing: [0] lookup + de-duplication, [1] hit marking + fold +
- * victim selection, with the missed rows read in and the previous step's
- * evicted rows written out over the host link in the same launch, [2] rows into
- * the victim slots + commit + signal. ula_read_timing synchronises on the
- * step's last event. */
-int ula_set_timing(ula_ctx* ctx, int32_t enable);
+/* Timing, off by default; ula_set_timing takes an OR of these flags (ULA_EINVAL
+ * for unknown bits).
+ *  - ULA_TIMING_STEP: events between the phases of every step. ula_read_timing
+ *    gives, for the last step of group g, in milliseconds: [0] lookup +
+ *    de-duplication, [1] hit marking + fold + victim selection, with the missed
+ *    rows read in and the previous step's evicted rows written out over the
+ *    host link in the same launch, [2] rows into the victim slots + commit +
+ *    signal. It synchronises on the step's last event.
+ *  - ULA_TIMING_GATHER: every gather launch records events in its own dispatch,
+ *    so their interval is the kernel's execution alone (no launch overhead).
+ *    ula_read_gather_timing synchronises on them and returns the summed kernel
+ *    time and the number of launches since the last read (then resets both). */
+enum { ULA_TIMING_STEP = 1, ULA_TIMING_GATHER = 2 };
+int ula_set_timing(ula_ctx* ctx, int32_t flags);
 int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out3);
+int ula_read_gather_timing(ula_ctx* ctx, double* kernel_ms, int64_t* launches);
 
 /* Release the context (not the caller's buffers). Waits for no stream. */
 int ula_destroy(ula_ctx* ctx);

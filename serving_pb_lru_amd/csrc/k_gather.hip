@@ -22,6 +22,8 @@
 // thousands of rows, a few workgroups per compute unit) is fastest with 64
 // rows and 11 pieces in flight per lane of 256; a large one with 32 rows and 3
 // pieces per lane of 512, which keeps more workgroups resident.
+#include <hip/hip_ext.h>
+
 #include "device_util.h"
 
 namespace ula {
@@ -131,19 +133,26 @@ __global__ __launch_bounds__(THREADS) void k_gather(GroupDev g, const int32_t* _
 
 template <int ROWS, int UNROLL, int THREADS>
 static hipError_t launch_tiled(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer, uint8_t* out,
-                               long long want_flag, int32_t n_res, hipStream_t s) {
+                               long long want_flag, int32_t n_res, hipStream_t s, hipEvent_t start,
+                               hipEvent_t stop) {
   int blocks = (n + ROWS - 1) / ROWS;
   if (blocks > 32768) blocks = 32768;
-  k_gather<ROWS, UNROLL, THREADS><<<blocks, THREADS, 0, s>>>(g, sel, n, layer, out, want_flag, n_res,
-                                                             FastDiv((uint32_t)g.row_bytes / 16u));
+  const FastDiv per_row((uint32_t)g.row_bytes / 16u);
+  if (start)
+    hipExtLaunchKernelGGL(k_gather<ROWS, UNROLL, THREADS>, dim3(blocks), dim3(THREADS), 0, s, start, stop, 0,
+                          g, sel, n, layer, out, want_flag, n_res, per_row);
+  else
+    k_gather<ROWS, UNROLL, THREADS><<<blocks, THREADS, 0, s>>>(g, sel, n, layer, out, want_flag, n_res, per_row);
   return hipGetLastError();
 }
 
 hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
-                         uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s) {
+                         uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s,
+                         hipEvent_t start, hipEvent_t stop) {
   if (n <= 0) return hipSuccess;
-  if (n <= kSmallGatherRows) return launch_tiled<64, 11, 256>(g, sel, n, layer, out, want_flag, n_res, s);
-  return launch_tiled<32, 3, 512>(g, sel, n, layer, out, want_flag, n_res, s);
+  if (n <= kSmallGatherRows)
+    return launch_tiled<64, 11, 256>(g, sel, n, layer, out, want_flag, n_res, s, start, stop);
+  return launch_tiled<32, 3, 512>(g, sel, n, layer, out, want_flag, n_res, s, start, stop);
 }
 
 }  // namespace ula

@@ -163,8 +163,28 @@ struct ula_ctx {
   Counters* ctrs = nullptr;
   std::vector<GroupHost> groups;
   int poisoned = 0;
-  int timing = 0;
+  int timing = 0;                    // ULA_TIMING_* flags
+  // gather kernel durations: a ring of dispatch-recorded event pairs, summed
+  // lazily (when the ring wraps, and by ula_read_gather_timing)
+  std::vector<hipEvent_t> gt_ev;     // 2 * kGatherTimingRing events
+  int gt_head = 0, gt_pending = 0;
+  double gt_ms = 0.0;
+  int64_t gt_launches = 0;
 };
+
+static constexpr int kGatherTimingRing = 256;
+
+// Add the oldest pending gather's kernel time to the total.
+static int retire_gather_timing(ula_ctx* ctx) {
+  const int i = (ctx->gt_head - ctx->gt_pending + kGatherTimingRing) % kGatherTimingRing;
+  HIP_TRY(hipEventSynchronize(ctx->gt_ev[2 * i + 1]));
+  float ms = 0.f;
+  HIP_TRY(hipEventElapsedTime(&ms, ctx->gt_ev[2 * i], ctx->gt_ev[2 * i + 1]));
+  ctx->gt_ms += ms;
+  ctx->gt_launches += 1;
+  ctx->gt_pending -= 1;
+  return ULA_OK;
+}
 
 extern "C" {
 
@@ -199,6 +219,8 @@ int ula_host_free(void* p) {
 }
 
 static void destroy_ctx(ula_ctx* ctx) {
+  for (hipEvent_t e : ctx->gt_ev)
+    if (e) (void)hipEventDestroy(e);
   for (auto& g : ctx->groups) {
     for (int i = 0; i < kStageSlots; ++i) {
       if (g.stage_ev[i]) (void)hipEventDestroy(g.stage_ev[i]);
@@ -431,7 +453,7 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t t = gh.steps + 1;
   const int32_t cur = (int32_t)(t % ctx->dims.B);
-  const bool tm = ctx->timing != 0;
+  const bool tm = (ctx->timing & ULA_TIMING_STEP) != 0;
   const int32_t max_pairs = (int32_t)std::min<int64_t>(n, ctx->dims.maxU);
   // the previous step's evicted rows, unless a flush already wrote them out
   const int32_t wb_pairs = (gh.steps > 0 && gh.written_back != gh.steps) ? gh.last_pairs : 0;
@@ -471,8 +493,23 @@ int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32
   if (n > 0 && (!sel_dev || !out_dev)) return ULA_EINVAL;
   GroupHost& gh = ctx->groups[group];
   if (gh.steps == 0) return ULA_ENOTRESIDENT;
+  hipEvent_t start = nullptr, stop = nullptr;
+  if ((ctx->timing & ULA_TIMING_GATHER) && n > 0) {
+    if (ctx->gt_ev.empty()) {
+      ctx->gt_ev.assign(2 * kGatherTimingRing, nullptr);
+      for (auto& e : ctx->gt_ev) HIP_TRY(hipEventCreate(&e));
+    }
+    if (ctx->gt_pending == kGatherTimingRing) {
+      int rc = retire_gather_timing(ctx);
+      if (rc) return rc;
+    }
+    start = ctx->gt_ev[2 * ctx->gt_head];
+    stop = ctx->gt_ev[2 * ctx->gt_head + 1];
+    ctx->gt_head = (ctx->gt_head + 1) % kGatherTimingRing;
+    ctx->gt_pending += 1;
+  }
   HIP_TRY(launch_gather(gh.d, sel_dev, n, layer, static_cast<uint8_t*>(out_dev), (long long)gh.steps,
-                        gh.last_n, reinterpret_cast<hipStream_t>(stream)));
+                        gh.last_n, reinterpret_cast<hipStream_t>(stream), start, stop));
   return ULA_OK;
 }
 
@@ -567,9 +604,22 @@ int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr) {
   return ULA_OK;
 }
 
-int ula_set_timing(ula_ctx* ctx, int32_t enable) {
-  if (!ctx) return ULA_EINVAL;
-  ctx->timing = enable ? 1 : 0;
+int ula_set_timing(ula_ctx* ctx, int32_t flags) {
+  if (!ctx || (flags & ~(ULA_TIMING_STEP | ULA_TIMING_GATHER))) return ULA_EINVAL;
+  ctx->timing = flags;
+  return ULA_OK;
+}
+
+int ula_read_gather_timing(ula_ctx* ctx, double* kernel_ms, int64_t* launches) {
+  if (!ctx || !kernel_ms || !launches) return ULA_EINVAL;
+  while (ctx->gt_pending > 0) {
+    int rc = retire_gather_timing(ctx);
+    if (rc) return rc;
+  }
+  *kernel_ms = ctx->gt_ms;
+  *launches = ctx->gt_launches;
+  ctx->gt_ms = 0.0;
+  ctx->gt_launches = 0;
   return ULA_OK;
 }
 

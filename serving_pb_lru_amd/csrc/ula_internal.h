@@ -177,7 +177,10 @@ hipError_t launch_append_small(const GroupDev& g, const SmallAppend& a, const ui
 hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s);
 hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s);
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s);
+// start / stop (both or neither): events recorded by the dispatch itself, so
+// that their interval is the kernel's execution
 hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
-                         uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s);
+                         uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s,
+                         hipEvent_t start, hipEvent_t stop);
 
 }  // namespace ula

@@ -73,6 +73,8 @@ SIGNATURES = [
                                         ctypes.POINTER(ctypes.c_void_p)]),
     ("ula_set_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32]),
     ("ula_read_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
+    ("ula_read_gather_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
+                                              ctypes.POINTER(ctypes.c_int64)]),
     ("ula_destroy", ctypes.c_int, [ctypes.c_void_p]),
     ("ula_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("ula_host_alloc", ctypes.c_void_p, [ctypes.c_size_t]),
@@ -200,13 +202,25 @@ class Engine:
         _check(lib().ula_flag_address(self.ctx, group, ctypes.byref(p)), "ula_flag_address")
         return p.value
 
-    def set_timing(self, enable: bool) -> None:
-        _check(lib().ula_set_timing(self.ctx, 1 if enable else 0), "ula_set_timing")
+    TIMING_STEP = 1      # phase events of every step (read_timing)
+    TIMING_GATHER = 2    # kernel time of every gather (read_gather_timing)
+
+    def set_timing(self, flags) -> None:
+        """flags: an OR of TIMING_STEP and TIMING_GATHER (True means TIMING_STEP)."""
+        flags = self.TIMING_STEP if flags is True else int(flags)
+        _check(lib().ula_set_timing(self.ctx, flags), "ula_set_timing")
 
     def read_timing(self, group: int) -> List[float]:
         ms = (ctypes.c_float * 3)()
         _check(lib().ula_read_timing(self.ctx, group, ms), "ula_read_timing")
         return list(ms)
+
+    def read_gather_timing(self) -> tuple:
+        """(summed gather kernel milliseconds, launches) since the last read."""
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(lib().ula_read_gather_timing(self.ctx, ctypes.byref(ms), ctypes.byref(n)),
+               "ula_read_gather_timing")
+        return ms.value, n.value
 
     def close(self) -> None:
         if getattr(self, "ctx", None) is not None and self.ctx.value:

@@ -262,3 +262,39 @@ def test_engine_on_dirty_workspace_matches_oracle():
     torch.cuda.synchronize()
     del junk                      # the caching allocator hands this block to the engine
     run_parity(wl, max_append=4096)
+
+
+def test_timing_modes_count_and_change_nothing():
+    """Gather timing records one kernel duration per launch; neither timing mode
+    changes any state or gathered byte."""
+    from serving_pb_lru_amd import UlaError
+    tr, eng, rows = _engine()
+    tr2, ref, _ = _engine()
+    try:
+        with pytest.raises(UlaError) as e:
+            eng.set_timing(4)
+        assert e.value.name == "EINVAL"
+        eng.set_timing(eng.TIMING_STEP | eng.TIMING_GATHER)
+        assert eng.read_gather_timing() == (0.0, 0)
+        sels = tr.selections(0)
+        launches = 0
+        for t in range(1, 4):
+            sel = _cuda(next(sels))
+            app = tr.appends(t)   # the step's selection may pick the positions appended with it
+            for e in (eng, ref):
+                e.append(0, app, rows(app, 0))
+                e.step(0, sel)
+            for l in range(tr.wl.layers):
+                a, b = eng.gather(0, l, sel), ref.gather(0, l, sel)
+                launches += 1
+                assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+            ms3 = eng.read_timing(0)
+            assert len(ms3) == 3 and all(x >= 0 for x in ms3)
+        ms, n = eng.read_gather_timing()
+        assert n == launches and ms > 0
+        assert eng.read_gather_timing() == (0.0, 0)   # reset by the read
+        eng.sync(), ref.sync()
+        assert _state(eng) == _state(ref)
+    finally:
+        eng.close()
+        ref.close()
