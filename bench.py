@@ -63,6 +63,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="timed CPU work of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-phases", action="store_true", help="skip the per-phase replay")
+    p.add_argument("--policy", choices=("pblru", "lru"), default="pblru",
+                   help="replacement policy: PB-LRU (the pages' policy) or exact LRU (the one it is "
+                        "compared against); the CPU baseline is reported for PB-LRU only")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run 5 plain device-to-device copies of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -152,7 +155,7 @@ def cpu_baseline(tr, W: int, K: int, seconds: float) -> dict:
 
 
 # ---------------------------------------------------------------------------
-def gpu_run(tr, W: int, K: int, phases: bool) -> dict:
+def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
     import torch
 
     from serving_pb_lru_amd.replay import engine_for, initial_load
@@ -182,7 +185,7 @@ def gpu_run(tr, W: int, K: int, phases: bool) -> dict:
                 eng.gather(g, l, sel, out=outs[g][l])
 
     # ---- timed replay ----------------------------------------------------
-    eng = engine_for(tr, max_append=1 << 16)
+    eng = engine_for(tr, max_append=1 << 16, policy=policy)
     initial_load(eng, tr, groups, rows)
     torch.cuda.synchronize()
     for t in range(1, W + 1):
@@ -212,7 +215,7 @@ def gpu_run(tr, W: int, K: int, phases: bool) -> dict:
 
     # ---- per-phase replay (diagnostic, synchronises every step) --------------
     if phases:
-        eng = engine_for(tr, max_append=1 << 16)
+        eng = engine_for(tr, max_append=1 << 16, policy=policy)
         initial_load(eng, tr, groups, rows)
         eng.set_timing(True)
         torch.cuda.synchronize()
@@ -255,11 +258,12 @@ def main():
     tr = Trace(wl, steps=max(W + K, 1))
     per_step = rows_per_step(tr)
 
+    policy = 1 if args.policy == "lru" else 0
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and policy == 0:
         cpu = cpu_baseline(tr, W, K, args.cpu_seconds)
 
-    r = gpu_run(tr, W, K, not args.no_phases)
+    r = gpu_run(tr, W, K, not args.no_phases, policy)
     value = per_step * K / r["wall_s"]
     ms_per_step = r["event_ms"] / K
 
@@ -301,6 +305,7 @@ def main():
                    "sets_per_request": wl.sets_per_request, "groups": wl.groups,
                    "layers_per_group": wl.layers, "k": wl.k, "gpu_slots": tr.P, "host_slots": tr.H,
                    "ring": wl.ring, "row_bytes": wl.row_bytes, "overlap": wl.overlap,
+                   "policy": "exact LRU" if policy else "PB-LRU",
                    "row_layers_per_step": per_step},
         "roofline": roofline,
         "miss_path": miss,

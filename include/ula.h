@@ -90,7 +90,18 @@ typedef struct {
   int32_t max_sets;          /* most selection sets per step */
   int32_t max_k;             /* most entries per selection set; max_sets * max_k < 2^31 */
   int32_t max_append;        /* most addresses staged per append chunk, >= 1 */
+  int32_t policy;            /* ULA_POLICY_PBLRU (0, default) or ULA_POLICY_LRU (1) */
 } ula_config;
+
+/* Replacement policies. PB-LRU is the pages' policy (UlaCache summary, section 3).
+ * Exact LRU is the standard policy the pages compare it against (sections 3 and 4):
+ * one timestamp per GPU slot (a hit or a load at step t sets it to t; an
+ * appended slot s counts as s - P, so older than any step and ordered by slot)
+ * and a scan of the whole pool each step; victims are the free slots in
+ * ascending order, then the occupied slots by (timestamp, slot), never a slot
+ * stamped with the current step. Everything else (lookup, pairing, data moves,
+ * commit, signal, appends) is shared. */
+enum { ULA_POLICY_PBLRU = 0, ULA_POLICY_LRU = 1 };
 
 typedef struct {
   int64_t unique;     /* distinct valid addresses selected by the step */
@@ -105,10 +116,13 @@ typedef struct {             /* caller-allocated host buffers filled by ula_expo
   uint32_t* map;             /* [N] mapping table */
   int32_t* gown;             /* [P] owner logical address of each GPU slot, -1 = empty */
   int32_t* hown;             /* [H] owner logical address of each host slot, -1 = empty */
-  uint32_t* bitsets;         /* [(B + 2)][ceil(P / 32)]: free, cold, ring[0..B-1] */
+  uint32_t* bitsets;         /* [(B + 2)][ceil(P / 32)]: free, cold, ring[0..B-1]; under exact
+                                LRU only the free set is kept (the others read as empty) */
   int32_t cur;               /* current ring bucket */
   int64_t flag;              /* last completed step (completion counter) */
   ula_step_stats last;       /* statistics of that step */
+  int32_t* stamps;           /* nullable, [P]: exact LRU timestamps (appended slot s: s - P,
+                                free slot: 0); under PB-LRU left untouched */
 } ula_state_host;
 
 /* Bytes of device workspace / pinned host pool a configuration needs; 0 for an

@@ -17,7 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libula.so")
-SOURCES = ["k_init.hip", "k_lookup.hip", "k_select.hip", "k_move.hip", "k_gather.hip", "runtime.hip"]
+SOURCES = ["k_init.hip", "k_lookup.hip", "k_select.hip", "k_lru.hip", "k_move.hip", "k_gather.hip",
+           "runtime.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -88,6 +88,8 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
           const int32_t old = g.gown[v];
           g.map[la] = v;
           g.gown[v] = la;
+          g.stamp[v] = (int32_t)t;       // loaded this step (exact LRU's timestamp; PB-LRU reads
+                                         // stamps only to find the next step's hits)
           g.res[g.miss_e[i]].y = v;      // the step's selection now resolves to the loaded slot
           if (old != -1) {
             g.map[old] = kHostBit | h;

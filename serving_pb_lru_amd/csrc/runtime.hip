@@ -36,7 +36,8 @@ int hip_fail(hipError_t e, const char* what) {
 
 struct Dims {
   int64_t N, P, H, B, NB, W, T, WH, TH, Lg, row_bytes, slot_bytes;
-  int64_t maxU, maxBlk, maxItems, maxApp, nsel;
+  int64_t maxU, maxBlk, maxItems, maxApp, nsel, maxRs;
+  int policy;
 };
 
 bool check_config(const ula_config* c, Dims* d) {
@@ -49,6 +50,7 @@ bool check_config(const ula_config* c, Dims* d) {
   if (c->gpu_slots < 1 || c->host_slots < 0) return false;
   if ((int64_t)c->gpu_slots + c->host_slots >= (1ll << 31)) return false;
   if (c->max_sets < 1 || c->max_k < 1 || c->max_append < 1) return false;
+  if (c->policy != ULA_POLICY_PBLRU && c->policy != ULA_POLICY_LRU) return false;
   const int64_t nsel = (int64_t)c->max_sets * c->max_k;
   if (nsel >= (1ll << 31)) return false;
   d->N = c->logical_capacity;
@@ -68,6 +70,8 @@ bool check_config(const ula_config* c, Dims* d) {
   d->maxBlk = (nsel + kScanBlock - 1) / kScanBlock;
   d->maxApp = c->max_append;
   d->maxItems = std::max<int64_t>(d->maxU, d->maxApp) + 2;
+  d->maxRs = (d->maxU + 1023) / 1024;
+  d->policy = c->policy;
   // 16-byte piece counts handled with 32-bit indices and FastDiv (< 2^31)
   if (nsel * (d->row_bytes / 16) >= (1ll << 31)) return false;
   if (d->maxU * (d->slot_bytes / 16) >= (1ll << 31)) return false;
@@ -78,7 +82,8 @@ bool check_config(const ula_config* c, Dims* d) {
 struct Layout {
   size_t map, tag, gown, stamp, dirty, hown, bm, tcnt, hbm, htcnt, hits, mla, mh, vict, blk,
       partial, items, app_la, app_dst, app_rows, evict_rows, wb_h, miss_e, miss_stage, miss_rows,
-      hs_stage, res, pool, group_bytes;
+      hs_stage, res, lru_hist, span_a, span_b, sort_key[2], sort_slot[2], rs_hist, rs_base, pool,
+      group_bytes;
   size_t counters_bytes, total;
 };
 
@@ -117,6 +122,17 @@ Layout layout_of(const ula_config* c, const Dims& d) {
   L.miss_rows = take((size_t)d.maxU * d.slot_bytes);
   L.hs_stage = take(8 * d.H);
   L.res = take(8 * d.nsel);
+  if (d.policy == ULA_POLICY_LRU) {   // exact-LRU selection scratch
+    L.lru_hist = take(4 * 2048);
+    L.span_a = take(4 * d.T);
+    L.span_b = take(4 * d.T);
+    for (int i = 0; i < 2; ++i) {
+      L.sort_key[i] = take(4 * d.maxU);
+      L.sort_slot[i] = take(4 * d.maxU);
+    }
+    L.rs_hist = take(4 * 256 * d.maxRs);
+    L.rs_base = take(4 * 256);
+  }
   L.pool = take((size_t)d.P * d.slot_bytes);
   L.group_bytes = o;
   L.counters_bytes = align_up(sizeof(Counters) * c->num_groups);
@@ -295,6 +311,19 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     g.miss_rows = b + L.miss_rows;
     g.hs_stage = reinterpret_cast<unsigned long long*>(b + L.hs_stage);
     g.res = reinterpret_cast<uint2*>(b + L.res);
+    if (d.policy == ULA_POLICY_LRU) {
+      g.lru_hist = reinterpret_cast<uint32_t*>(b + L.lru_hist);
+      g.span_a = reinterpret_cast<uint32_t*>(b + L.span_a);
+      g.span_b = reinterpret_cast<uint32_t*>(b + L.span_b);
+      for (int i = 0; i < 2; ++i) {
+        g.sort_key[i] = reinterpret_cast<uint32_t*>(b + L.sort_key[i]);
+        g.sort_slot[i] = reinterpret_cast<uint32_t*>(b + L.sort_slot[i]);
+      }
+      g.rs_hist = reinterpret_cast<uint32_t*>(b + L.rs_hist);
+      g.rs_base = reinterpret_cast<uint32_t*>(b + L.rs_base);
+    }
+    g.policy = d.policy;
+    g.maxRs = (int32_t)std::max<int64_t>(d.maxRs, 1);
     g.pool = b + L.pool;
     g.host = hdev ? hdev + (size_t)gi * d.H * d.slot_bytes : nullptr;
     g.N = (int32_t)d.N;
@@ -324,6 +353,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     if (e == hipSuccess) e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.hown), d.H, 0xFFFFFFFFu, s);
     // no host slot has a staged row: step 0xFFFFFFFF is never the previous step
     if (e == hipSuccess) e = launch_fill_u64(g.hs_stage, d.H, ~0ull, s);
+    if (e == hipSuccess && g.lru_hist) e = launch_fill_u32(g.lru_hist, 2048, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(g.bm, d.NB * d.W, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(g.tcnt, d.NB * d.T, 0u, s);
     if (e == hipSuccess) e = launch_init_bitmap(g.bm + kFree * d.W, g.W, d.P, g.tcnt + kFree * d.T, g.T, s);
@@ -470,9 +500,16 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   a.order[1] = kCold;
   a.norder = 2;
   for (int j = 1; j < ctx->dims.B; ++j) a.order[a.norder++] = (int8_t)ring_id((cur + j) % ctx->dims.B);
-  // marking, victim plan and extraction, with the missed rows read in and the
-  // previous step's evicted rows written out, in one launch
-  HIP_TRY(launch_mark(g, (uint32_t)t, cur, a, max_pairs, wb_pairs, s));
+  if (g.policy == ULA_POLICY_LRU) {
+    // exact LRU: select passes over the whole pool (the first launch also carries
+    // the host-link work), then the victim list in order
+    HIP_TRY(launch_lru_select(g, (uint32_t)t, max_pairs, wb_pairs, s));
+    HIP_TRY(launch_lru_order(g, (uint32_t)t, max_pairs, s));
+  } else {
+    // marking, victim plan and extraction, with the missed rows read in and the
+    // previous step's evicted rows written out, in one launch
+    HIP_TRY(launch_mark(g, (uint32_t)t, cur, a, max_pairs, wb_pairs, s));
+  }
   if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
   HIP_TRY(launch_swap_commit(g, (uint32_t)t, max_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[3], s));
@@ -557,6 +594,16 @@ int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out) {
   HIP_TRY(hipMemcpy(out->gown, g.gown, 4 * d.P, hipMemcpyDeviceToHost));
   if (d.H > 0) HIP_TRY(hipMemcpy(out->hown, g.hown, 4 * d.H, hipMemcpyDeviceToHost));
   HIP_TRY(hipMemcpy(out->bitsets, g.bm, 4 * d.NB * d.W, hipMemcpyDeviceToHost));
+  if (d.policy == ULA_POLICY_LRU) {
+    // exact LRU keeps only the free set; its timestamps, in the textbook form:
+    // an occupied slot that no step stamped counts as s - P
+    std::fill(out->bitsets + d.W, out->bitsets + d.NB * d.W, 0u);
+    if (out->stamps) {
+      HIP_TRY(hipMemcpy(out->stamps, g.stamp, 4 * d.P, hipMemcpyDeviceToHost));
+      for (int64_t s = 0; s < d.P; ++s)
+        if (out->gown[s] != -1 && out->stamps[s] < 1) out->stamps[s] = (int32_t)(s - d.P);
+    }
+  }
   Counters c;
   HIP_TRY(hipMemcpy(&c, g.ctr, sizeof(Counters), hipMemcpyDeviceToHost));
   out->flag = c.flag;

@@ -71,6 +71,14 @@ struct alignas(64) Counters {
   uint32_t wb_step;      // step whose swap staged the rows in evict_rows (0 = none)
   int32_t mark_role;     // order in which the mark launch's workgroups start (their roles)
   uint32_t plan_done;    // step whose victim plan is published (extraction may start)
+  // exact-LRU selection (policy ULA_POLICY_LRU)
+  uint32_t lru_prefix;   // high key bits fixed by the select passes so far
+  int32_t lru_below;     // candidate slots whose key lies below that prefix
+  int32_t lru_nfree;     // free slots seen by the first select pass
+  int32_t lru_ticket;    // last-workgroup ticket of the select, count and sort-count kernels
+  uint32_t lru_kstar;    // key of the last victim
+  int32_t lru_c;         // victims with a key below it (they need sorting by key)
+  int32_t lru_r;         // victims with that key (taken in slot order)
 };
 static_assert(sizeof(Counters) % 64 == 0, "counter block alignment");
 
@@ -114,9 +122,19 @@ struct GroupDev {        // device view of one group, passed by value to kernels
   uint8_t* app_rows;
   uint8_t* evict_rows;   // [maxU][slot_bytes] evicted rows staged for the write-back
   uint32_t* wb_h;        // [maxU] host slot each staged row goes to, or absent
+  // exact-LRU scratch (allocated only for that policy)
+  uint32_t* lru_hist;    // [2048] histogram of one select pass
+  uint32_t* span_a;      // [T] per 2048-slot span: victims below the last key, then their offsets
+  uint32_t* span_b;      // [T] per span: slots with the last key, then their offsets
+  uint32_t* sort_key[2]; // [maxU] keys of the victims below the last key, ping-pong
+  uint32_t* sort_slot[2];// [maxU] their slots
+  uint32_t* rs_hist;     // [256][maxRs] per-block digit counts of a sort pass, then offsets
+  uint32_t* rs_base;     // [256] first position of each digit
   uint8_t* pool;
   uint8_t* host;
   int32_t N, P, H, B, NB, W, T, WH, TH, Lg, row_bytes, slot_bytes;
+  int32_t policy;        // ULA_POLICY_PBLRU or ULA_POLICY_LRU
+  int32_t maxRs;         // sort blocks of 1024 victims
   int32_t maxU, maxBlk;  // capacity of the hit / miss / victim lists; compaction workgroups
 };
 
@@ -179,6 +197,11 @@ hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, 
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s);
 // start / stop (both or neither): events recorded by the dispatch itself, so
 // that their interval is the kernel's execution
+// exact-LRU victim selection (k_lru.hip)
+hipError_t launch_lru_select(const GroupDev& g, uint32_t t, int32_t max_pairs, int32_t wb_pairs,
+                             hipStream_t s);
+hipError_t launch_lru_order(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s);
+
 hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
                          uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop);

@@ -22,12 +22,15 @@ ERROR_NAMES = {0: "OK", -1: "EINVAL", -2: "ERANGE", -3: "EDUP", -4: "EHOSTFULL",
                -5: "ECAPACITY", -6: "ENOTRESIDENT", -7: "ESTATE", -8: "EHIP"}
 
 
+POLICY_PBLRU, POLICY_LRU = 0, 1
+
+
 class UlaConfig(ctypes.Structure):
     _fields_ = [("num_groups", ctypes.c_int32), ("layers_per_group", ctypes.c_int32),
                 ("row_bytes", ctypes.c_int32), ("ring_buckets", ctypes.c_int32),
                 ("logical_capacity", ctypes.c_int32), ("gpu_slots", ctypes.c_int32),
                 ("host_slots", ctypes.c_int32), ("max_sets", ctypes.c_int32),
-                ("max_k", ctypes.c_int32), ("max_append", ctypes.c_int32)]
+                ("max_k", ctypes.c_int32), ("max_append", ctypes.c_int32), ("policy", ctypes.c_int32)]
 
 
 class UlaStepStats(ctypes.Structure):
@@ -41,7 +44,7 @@ class UlaStepStats(ctypes.Structure):
 class UlaStateHost(ctypes.Structure):
     _fields_ = [("map", ctypes.c_void_p), ("gown", ctypes.c_void_p), ("hown", ctypes.c_void_p),
                 ("bitsets", ctypes.c_void_p), ("cur", ctypes.c_int32), ("flag", ctypes.c_int64),
-                ("last", UlaStepStats)]
+                ("last", UlaStepStats), ("stamps", ctypes.c_void_p)]
 
 
 class UlaError(RuntimeError):
@@ -121,10 +124,12 @@ class Engine:
 
     def __init__(self, num_groups: int, layers: int, row_bytes: int, ring: int, logical_capacity: int,
                  gpu_slots: int, host_slots: int, max_sets: int, max_k: int, max_append: int = 4096,
-                 device: str = "cuda", stream=None):
+                 device: str = "cuda", stream=None, policy: int = 0):
+        """policy: POLICY_PBLRU (0) or POLICY_LRU (1)."""
         import torch
         self.cfg = UlaConfig(num_groups, layers, row_bytes, ring, logical_capacity, gpu_slots,
-                             host_slots, max_sets, max_k, max_append)
+                             host_slots, max_sets, max_k, max_append, policy)
+        self.policy = policy
         L = lib()
         nbytes = L.ula_device_bytes(ctypes.byref(self.cfg))
         if nbytes == 0:
@@ -181,13 +186,17 @@ class Engine:
         out = dict(map=np.empty(self.N, np.uint32), gown=np.empty(self.P, np.int32),
                    hown=np.empty(max(self.H, 1), np.int32),
                    bitsets=np.empty((self.ring + 2, W), np.uint32))
+        stamps = np.empty(self.P, np.int32) if self.policy == POLICY_LRU else None
         sh = UlaStateHost(out["map"].ctypes.data, out["gown"].ctypes.data, out["hown"].ctypes.data,
-                          out["bitsets"].ctypes.data, 0, 0, UlaStepStats())
+                          out["bitsets"].ctypes.data, 0, 0, UlaStepStats(),
+                          stamps.ctypes.data if stamps is not None else None)
         _check(lib().ula_export_state(self.ctx, group, ctypes.byref(sh)), "ula_export_state")
         out["hown"] = out["hown"][: self.H]
         out["cur"] = int(sh.cur)
         out["flag"] = int(sh.flag)
         out["stats"] = sh.last.as_tuple()
+        if stamps is not None:
+            out["stamps"] = stamps
         return out
 
     def read_rows(self, group: int, las: np.ndarray) -> np.ndarray:
