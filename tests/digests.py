@@ -19,4 +19,7 @@ def digest(st: dict) -> dict:
     out["cur"] = int(st["cur"])
     out["flag"] = int(st["flag"])
     out["stats"] = [int(x) for x in st["stats"]]
+    if "stamps" in st:   # exact LRU's timestamps
+        out["stamps"] = xxhash.xxh3_64_hexdigest(np.ascontiguousarray(
+            np.asarray(st["stamps"]).astype("<i4", copy=False)).tobytes())
     return out

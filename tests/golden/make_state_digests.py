@@ -4,9 +4,11 @@ For every workload preset, every layer group and every step, the oracle (in
 metadata mode: mapping table, owners, buckets, no row bytes) replays the seeded
 synthetic trace and the digest of its exported state is stored: after the
 initial load (step 0) and after each step. The GPU parity tests replay the same
-inputs through the engine and compare digests. Usage:
+inputs through the engine and compare digests. With --lru the exact-LRU oracle
+(array form) replays the same traces into digests_lru_<workload>.json, with the
+timestamps in the digest. Usage:
 
-    python tests/golden/make_state_digests.py [workload ...]
+    python tests/golden/make_state_digests.py [--lru] [workload ...]
 """
 
 import json
@@ -24,6 +26,20 @@ from oracle.replay import initial_load, new_group  # noqa: E402
 from synth import PRESETS, Trace, preset  # noqa: E402
 
 
+def lru_group_digests(name: str, g: int) -> list:
+    from oracle.exact_lru_np import ExactLRUArrays
+    tr = Trace(preset(name))
+    grp = ExactLRUArrays(tr.N, tr.P, tr.H, tr.wl.ring)
+    grp.append(tr.initial_load_order())
+    out = [digest(grp.export_state())]
+    sels = tr.selections(g)
+    for t in range(1, tr.steps + 1):
+        grp.append(tr.appends(t))
+        grp.step(next(sels))
+        out.append(digest(grp.export_state()))
+    return out
+
+
 def group_digests(name: str, g: int) -> list:
     tr = Trace(preset(name))
     grp = new_group(tr, full_data=False)
@@ -37,22 +53,30 @@ def group_digests(name: str, g: int) -> list:
     return out
 
 
-def main(names):
+def main(names, lru=False):
     jobs = [(n, g) for n in names for g in range(preset(n).groups)]
+    fn = lru_group_digests if lru else group_digests
     with ProcessPoolExecutor(max_workers=min(6, len(jobs))) as ex:
-        res = list(ex.map(group_digests, [j[0] for j in jobs], [j[1] for j in jobs]))
+        res = list(ex.map(fn, [j[0] for j in jobs], [j[1] for j in jobs]))
     by = {}
     for (n, g), d in zip(jobs, res):
         by.setdefault(n, {})[g] = d
     for n in names:
         wl = preset(n)
-        doc = {"workload": n, "source": "oracle/ (metadata mode) via tests/golden/make_state_digests.py",
-               "digest": "xxh3_64 of the little-endian bytes of map, gown, hown, bitsets",
+        doc = {"workload": n, "policy": "exact LRU" if lru else "PB-LRU",
+               "source": ("oracle/exact_lru_np.py" if lru else "oracle/ (metadata mode)")
+               + " via tests/golden/make_state_digests.py",
+               "digest": "xxh3_64 of the little-endian bytes of map, gown, hown, bitsets"
+               + (", stamps" if lru else ""),
                "steps": wl.steps, "groups": [by[n][g] for g in range(wl.groups)]}
-        with open(os.path.join(HERE, f"digests_{n}.json"), "w") as f:
+        fname = f"digests_lru_{n}.json" if lru else f"digests_{n}.json"
+        with open(os.path.join(HERE, fname), "w") as f:
             json.dump(doc, f, separators=(",", ":"))
         print("wrote", n, flush=True)
 
 
 if __name__ == "__main__":
-    main(sys.argv[1:] or list(PRESETS))
+    args = sys.argv[1:]
+    lru = "--lru" in args
+    names = [a for a in args if a != "--lru"]
+    main(names or list(PRESETS), lru=lru)

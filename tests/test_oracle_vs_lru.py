@@ -83,3 +83,53 @@ def test_tiny_hit_rate_spread_over_seeds():
         gaps.append((pb - lru) * 100)
     print("PB-LRU minus exact-LRU hit rate (pp) over seeds 0-19:", np.round(gaps, 3))
     assert max(abs(g) for g in gaps) <= 0.1
+
+
+def _lru_pair(trace, sels):
+    from oracle.exact_lru_np import ExactLRUArrays
+    wl = trace.wl
+    brute = ExactLRUGroup(trace.N, trace.P, trace.H)
+    arr = ExactLRUArrays(trace.N, trace.P, trace.H, wl.ring)
+    load = trace.initial_load_order()
+    brute.append(load)
+    arr.append(load)
+    for t, sel in enumerate(sels, 1):
+        app = trace.appends(t)
+        brute.append(app)
+        arr.append(app)
+        brute.step(sel)
+        arr.step(sel)
+        yield t, brute, arr
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_array_lru_equals_brute_force_lru(seed):
+    """The array form of exact LRU (for full sizes) against the brute-force one:
+    same victims in the same order, map, owners, stamps and statistics, every step.
+    Small pools, many steps, padding: victims span many timestamps."""
+    wl = tiny_workload(seed, steps=40)
+    if seed % 2:
+        wl = dataclasses.replace(wl, pool_slots=2 * wl.requests * wl.sets_per_request * wl.k)
+    tr = Trace(wl)
+    for t, brute, arr in _lru_pair(tr, padded_selections(tr, 0, seed)):
+        assert [int(v) for v in arr.last_victims] == brute.last_victims, f"step {t}"
+        assert arr.last == brute.last, f"step {t}"
+        assert [int(x) for x in arr.map] == brute.map_array()
+        assert list(arr.gown) == brute.gown and list(arr.hown) == brute.hown
+        st = arr.export_state()["stamps"]
+        want = [brute.stamp[s] if brute.gown[s] != -1 else 0 for s in range(tr.P)]
+        assert list(st) == want, f"step {t}"
+
+
+def test_array_lru_worked_example():
+    """The array form on the hand-worked example: the victims the pages' ordering gives."""
+    import json
+    import os
+    from oracle.exact_lru_np import ExactLRUArrays
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+    z = ex["sizes"]
+    g = ExactLRUArrays(z["N"], z["P"], z["H"], z["B"])
+    g.append(ex["appends"])
+    for s, want in zip(ex["steps"], ex["exact_lru_victims"]):
+        g.step(np.array(s["sel"]))
+        assert [int(v) for v in g.last_victims] == want

@@ -11,6 +11,10 @@ sampled addresses (wherever they live, GPU or host pool) at the exported steps.
 Exporting writes staged evicted rows out to the host pool, so the unexported
 steps exercise the write-back inside the following step.
 
+The exact-LRU policy is checked the same way against the array form of the
+oracle's exact LRU (tests/golden/digests_lru_<workload>.json, timestamps
+included), on every workload and on three of the 24 groups of the largest.
+
 Layer groups are independent (their own pools, maps and buckets), so each
 group runs in an engine of its own; that keeps the pinned host pool of the
 24-group workload within one group's share at a time.
@@ -30,27 +34,29 @@ pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def _golden(name):
-    with open(os.path.join(HERE, "golden", f"digests_{name}.json")) as f:
+def _golden(name, policy=0):
+    fname = f"digests_lru_{name}.json" if policy else f"digests_{name}.json"
+    with open(os.path.join(HERE, "golden", fname)) as f:
         return json.load(f)
 
 
 def _cmp(got, want, where):
-    for k in ("map", "gown", "hown", "bitsets", "cur", "flag", "stats"):
-        assert got[k] == want[k], f"{where}: {k} differs (engine {got[k]}, oracle {want[k]})"
+    for k in ("map", "gown", "hown", "bitsets", "cur", "flag", "stats", "stamps"):
+        if k in want:
+            assert got[k] == want[k], f"{where}: {k} differs (engine {got[k]}, oracle {want[k]})"
 
 
-def run_group(name: str, g: int, samples: int = 1024):
+def run_group(name: str, g: int, samples: int = 1024, policy: int = 0):
     import torch
     from serving_pb_lru_amd import Engine
     from synth.device import rows_device
 
     wl = preset(name)
     tr = Trace(wl)
-    gold = _golden(name)["groups"][g]
-    say(f"full parity {name} group {g}: N={tr.N} P={tr.P} H={tr.H} steps={tr.steps}")
+    gold = _golden(name, policy)["groups"][g]
+    say(f"full parity {name} group {g} policy {policy}: N={tr.N} P={tr.P} H={tr.H} steps={tr.steps}")
     eng = Engine(1, wl.layers, wl.row_bytes, wl.ring, tr.N, tr.P, tr.H, tr.n_sets, tr.k,
-                 max_append=1 << 16)
+                 max_append=1 << 16, policy=policy)
     rows = lambda las: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
     rng = np.random.default_rng([g, 2024])
     try:
@@ -104,3 +110,16 @@ CASES = ([("tiny_4x4k", 0), ("r16_64k_g1x3", 0)]
 @pytest.mark.parametrize("name,g", CASES, ids=[f"{n}-g{g}" for n, g in CASES])
 def test_full_size_parity(name, g):
     run_group(name, g)
+
+
+# exact LRU against the array form of the oracle's exact LRU (digests with timestamps)
+LRU_CASES = ([("tiny_4x4k", 0), ("r16_64k_g1x3", 0)]
+             + [("r64_64k128k_g24x3", g) for g in (0, 11, 23)]
+             + [("spec3_r128_64k128k_g4", g) for g in range(4)]
+             + [("evict_r256_128k_g2", g) for g in range(2)]
+             + [("evict_r256_128k_g2_ctl98", g) for g in range(2)])
+
+
+@pytest.mark.parametrize("name,g", LRU_CASES, ids=[f"lru-{n}-g{g}" for n, g in LRU_CASES])
+def test_full_size_lru_parity(name, g):
+    run_group(name, g, policy=1)
