@@ -72,29 +72,39 @@ __device__ __forceinline__ void word_keys(const GroupDev& g, int w, uint32_t t, 
 
 // Last workgroup of a select pass: find the digit where the running count of
 // candidates reaches `need`, extend the prefix, count what lies below, and clear
-// the histogram for the next pass. 1024 threads, two bins each.
+// the histogram for the next pass. kLruThreads threads, consecutive bins each.
+constexpr int kLruThreads = 512;    // select passes
+constexpr int kSpanThreads = 256;   // count and emit (one wavefront per span)
+constexpr int kBinsPerThread = kLruBins / kLruThreads;
+
 __device__ void lru_find(const GroupDev& g, int nbins, int bits, int pass, int* scratch) {
   __shared__ int s_bin, s_add;
   Counters* c = g.ctr;
   const int m = c->n_miss;
   const int below = pass == 0 ? 0 : c->lru_below;
   const int need = m - below;   // >= 1
-  const int i0 = 2 * threadIdx.x, i1 = i0 + 1;
-  const int h0 = i0 < nbins ? (int)g.lru_hist[i0] : 0;
-  const int h1 = i1 < nbins ? (int)g.lru_hist[i1] : 0;
+  const int i0 = kBinsPerThread * threadIdx.x;
+  int h[kBinsPerThread], sum = 0;
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; ++j) {
+    h[j] = i0 + j < nbins ? (int)g.lru_hist[i0 + j] : 0;
+    sum += h[j];
+  }
   if (threadIdx.x == 0) s_bin = -1;
   int total;
-  const int pre = block_exclusive_sum<1024>(h0 + h1, scratch, total);   // has barriers
-  if (pre < need && pre + h0 >= need) {
-    s_bin = i0;
-    s_add = pre;
-  } else if (pre + h0 < need && pre + h0 + h1 >= need) {
-    s_bin = i1;
-    s_add = pre + h0;
+  int pre = block_exclusive_sum<kLruThreads>(sum, scratch, total);   // has barriers
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; ++j) {
+    if (pre < need && pre + h[j] >= need) {
+      s_bin = i0 + j;
+      s_add = pre;
+    }
+    pre += h[j];
   }
   __syncthreads();
-  if (i0 < nbins) g.lru_hist[i0] = 0u;
-  if (i1 < nbins) g.lru_hist[i1] = 0u;
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; ++j)
+    if (i0 + j < nbins) g.lru_hist[i0 + j] = 0u;
   if (threadIdx.x == 0) {
     if (s_bin < 0) {
       latch(c, ULA_ESTATE);   // fewer candidates than misses: inconsistent state
@@ -121,12 +131,12 @@ __device__ void lru_find(const GroupDev& g, int nbins, int bits, int pass, int* 
 // One select pass. Workgroups [0, nsel) histogram; in the first pass the next
 // pf workgroups prefetch the missed rows and the wbb after them write the
 // previous step's evicted rows out (they wait for nothing).
-__global__ __launch_bounds__(1024) void k_lru_pass(GroupDev g, uint32_t t, int32_t pass, int32_t nsel,
+__global__ __launch_bounds__(kLruThreads) void k_lru_pass(GroupDev g, uint32_t t, int32_t pass, int32_t nsel,
                                                    FastDiv per_slot, int32_t pf, int32_t wbb,
                                                    uint32_t wb_step) {
   __shared__ uint32_t s_hist[kLruBins];
   __shared__ int s_free, s_last;
-  __shared__ int scratch[1024 / kWave + 1];
+  __shared__ int scratch[kLruThreads / kWave + 1];
   if (block_failed(g.ctr)) return;
   if ((int)blockIdx.x >= nsel + pf) {
     writeback_rows(g, wb_step, per_slot, blockIdx.x - nsel - pf, wbb);
@@ -213,23 +223,23 @@ __device__ __forceinline__ void word_masks(const GroupDev& g, int w, uint32_t t,
   }
 }
 
-// Exclusive prefix of span counts in place (one 1024-thread workgroup).
+// Exclusive prefix of span counts in place (one kSpanThreads-thread workgroup).
 __device__ void spans_to_offsets(uint32_t* a, int n, int* scratch, int& total_out) {
   int carry = 0;
-  for (int base = 0; base < n; base += 1024) {
+  for (int base = 0; base < n; base += kSpanThreads) {
     const int i = base + threadIdx.x;
     const int v = i < n ? (int)a[i] : 0;
     int total;
-    const int ex = block_exclusive_sum<1024>(v, scratch, total);
+    const int ex = block_exclusive_sum<kSpanThreads>(v, scratch, total);
     if (i < n) a[i] = (uint32_t)(carry + ex);
     carry += total;
   }
   total_out = carry;
 }
 
-__global__ __launch_bounds__(1024) void k_lru_count(GroupDev g, uint32_t t) {
+__global__ __launch_bounds__(kSpanThreads) void k_lru_count(GroupDev g, uint32_t t) {
   __shared__ int s_last;
-  __shared__ int scratch[1024 / kWave + 1];
+  __shared__ int scratch[kSpanThreads / kWave + 1];
   if (block_failed(g.ctr)) return;
   if (g.ctr->n_miss == 0) return;
   const uint32_t kstar = g.ctr->lru_kstar;
@@ -266,7 +276,7 @@ __global__ __launch_bounds__(1024) void k_lru_count(GroupDev g, uint32_t t) {
     latch(g.ctr, ULA_ESTATE);   // the counts disagree with the select passes
 }
 
-__global__ __launch_bounds__(1024) void k_lru_emit(GroupDev g, uint32_t t) {
+__global__ __launch_bounds__(kSpanThreads) void k_lru_emit(GroupDev g, uint32_t t) {
   if (block_failed(g.ctr)) return;
   if (g.ctr->n_miss == 0) return;
   const uint32_t kstar = g.ctr->lru_kstar;
@@ -422,30 +432,38 @@ __global__ __launch_bounds__(1024) void k_rs_scatter(GroupDev g, int32_t pass) {
 
 hipError_t launch_lru_select(const GroupDev& g, uint32_t t, int32_t max_pairs, int32_t wb_pairs,
                              hipStream_t s) {
+  // host-link workgroups of kLruThreads lanes, four 16-byte pieces per lane per
+  // round: as many bytes in flight as the mark launch's prefetch and write-back
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
+  constexpr int kScale = 1024 / kLruThreads;
   auto blocks_for = [&](int32_t pairs, int cap) {
-    const int64_t n = ((int64_t)pairs * chunks + 4 * 1024 - 1) / (4 * 1024);
-    return (int)std::min<int64_t>(n, cap);
+    const int64_t n = ((int64_t)pairs * chunks + 4 * kLruThreads - 1) / (4 * kLruThreads);
+    return (int)std::min<int64_t>(n, (int64_t)cap * kScale);
   };
   const int pf = g.H > 0 ? blocks_for(max_pairs, kPrefetchBlocks) : 0;
   const int wbb = g.H > 0 ? blocks_for(wb_pairs, kWritebackBlocks) : 0;
-  const int nsel = (int)std::min<int64_t>(std::max<int64_t>((g.W + 1023) / 1024, 1), 128);
+  // one bitmap word (32 slots) per lane: enough workgroups to spread the scan over
+  // the compute units
+  const int nsel = (int)std::min<int64_t>(std::max<int64_t>((g.W + kLruThreads - 1) / kLruThreads, 1), 1024);
   const FastDiv per_slot(chunks);
-  k_lru_pass<<<nsel + pf + wbb, 1024, 0, s>>>(g, t, 0, nsel, per_slot, pf, wbb, wbb > 0 ? t - 1u : 0u);
+  k_lru_pass<<<nsel + pf + wbb, kLruThreads, 0, s>>>(g, t, 0, nsel, per_slot, pf, wbb,
+                                                       wbb > 0 ? t - 1u : 0u);
   hipError_t e = hipGetLastError();
   for (int pass = 1; pass < 3 && e == hipSuccess; ++pass) {
-    k_lru_pass<<<nsel, 1024, 0, s>>>(g, t, pass, nsel, per_slot, 0, 0, 0u);
+    k_lru_pass<<<nsel, kLruThreads, 0, s>>>(g, t, pass, nsel, per_slot, 0, 0, 0u);
     e = hipGetLastError();
   }
   return e;
 }
 
 hipError_t launch_lru_order(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s) {
-  const int spans = (int)std::min<int64_t>(std::max<int64_t>((g.T + 15) / 16, 1), 1024);
-  k_lru_count<<<spans, 1024, 0, s>>>(g, t);
+  constexpr int kWavesPerGroup = kSpanThreads / kWave;
+  const int spans = (int)std::min<int64_t>(std::max<int64_t>((g.T + kWavesPerGroup - 1) / kWavesPerGroup, 1),
+                                           4096);
+  k_lru_count<<<spans, kSpanThreads, 0, s>>>(g, t);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_lru_emit<<<spans, 1024, 0, s>>>(g, t);
+  k_lru_emit<<<spans, kSpanThreads, 0, s>>>(g, t);
   e = hipGetLastError();
   // keys are at most t + 1: enough 8-bit passes for that (idle passes exit at once)
   int passes = 0;
