@@ -66,6 +66,9 @@ def parse():
     p.add_argument("--policy", choices=("pblru", "lru"), default="pblru",
                    help="replacement policy: PB-LRU (the pages' policy) or exact LRU (the one it is "
                         "compared against); the CPU baseline is reported for PB-LRU only")
+    p.add_argument("--layer-prefetch", type=float, default=0.0, metavar="US",
+                   help="only run the later-layer prefetch experiment with US microseconds of "
+                        "synthetic compute per layer, and print its own JSON line")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run 5 plain device-to-device copies of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -242,10 +245,139 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
     return res
 
 
+def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
+    """Later-layer prefetch on a second stream (UlaCache summary, section 2: the
+    lookup and de-duplication run once per layer group, and while the current
+    layer computes a separate stream fetches the data of the group's later
+    layers). Here a step moves every layer of a missed entry at once, so the
+    later layers' gathers are what a second stream can take off the critical path.
+
+    Two schedules of the same steps, each group's layers followed by a synthetic
+    per-layer compute of `compute_us`:
+      serial    one stream: step, then per layer gather and compute;
+      prefetch  the step and layer 0's gather on the main stream; layers 1.. gathered
+                on a second stream ordered after the step by an event; layer l's
+                compute waits for its gather's event.
+    Two stand-ins for the compute: a single-lane spin (occupies no resources: the
+    upper bound of what overlap can hide) and a bf16 matrix product sized to the
+    same duration (occupies the matrix cores of the whole chip, like attention
+    math). Returns one result per stand-in."""
+    import torch
+
+    from serving_pb_lru_amd.replay import engine_for, initial_load
+    from synth.device import rows_device
+
+    wl = tr.wl
+    groups = list(range(wl.groups))
+    torch.cuda.set_device(0)
+    main_s = torch.cuda.Stream()
+    side_s = torch.cuda.Stream()
+    torch.cuda.set_stream(main_s)
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    sels = {g: [torch.from_numpy(s).cuda() for s in tr.selections(g)] for g in groups}
+    apps = [tr.appends(t) for t in range(1, tr.steps + 1)]
+    app_rows = {g: [rows(a, g) for a in apps] for g in groups}
+    outs = {g: [torch.empty((tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
+                for _ in range(wl.layers)] for g in groups}
+
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    # stand-ins calibrated to compute_us
+    spin_us_per_kcycle = timed(lambda: torch.cuda._sleep(100000)) / 100.0
+    spin_cycles = int(compute_us / spin_us_per_kcycle * 1000)
+    best = None
+    for n in (512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192):
+        x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        y = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+        us = timed(lambda: torch.mm(x, y))
+        if best is None or abs(us - compute_us) < abs(best[1] - compute_us):
+            best = (n, us, x, y)
+    n_mm, mm_us, xa, xb = best
+    stand_ins = {"spin": (lambda: torch.cuda._sleep(spin_cycles), timed(lambda: torch.cuda._sleep(spin_cycles))),
+                 "bf16_matmul": (lambda: torch.mm(xa, xb), mm_us)}
+
+    results = []
+    for kind, (compute, c_us) in stand_ins.items():
+        per = {}
+        for sched in ("serial", "prefetch"):
+            eng = engine_for(tr, max_append=1 << 16)
+            initial_load(eng, tr, groups, rows)
+            torch.cuda.synchronize()
+
+            def step(t):
+                for g in groups:
+                    if apps[t - 1].size:
+                        eng.append(g, apps[t - 1], app_rows[g][t - 1])
+                    sel = sels[g][t - 1]
+                    eng.step(g, sel)
+                    if sched == "serial":
+                        for l in range(wl.layers):
+                            eng.gather(g, l, sel, out=outs[g][l])
+                            compute()
+                        continue
+                    eng.gather(g, 0, sel, out=outs[g][0])
+                    after_step = torch.cuda.Event()
+                    after_step.record(main_s)
+                    side_s.wait_event(after_step)
+                    ready = []
+                    for l in range(1, wl.layers):
+                        eng.gather(g, l, sel, out=outs[g][l], stream=side_s)
+                        ev = torch.cuda.Event()
+                        ev.record(side_s)
+                        ready.append(ev)
+                    compute()
+                    for ev in ready:
+                        main_s.wait_event(ev)
+                        compute()
+
+            for t in range(1, W + 1):
+                step(t)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            t0 = time.perf_counter()
+            for t in range(W + 1, W + K + 1):
+                step(t)
+            host = (time.perf_counter() - t0) / K
+            b.record()
+            torch.cuda.synchronize()
+            eng.sync()
+            per[sched] = a.elapsed_time(b) / K
+            per[sched + "_host"] = host * 1e3
+            eng.close()
+        results.append({
+            "experiment": "later-layer prefetch on a second stream", "workload": wl.name,
+            "compute": kind, "compute_us_per_layer": round(c_us, 2),
+            "matmul_n": n_mm if kind == "bf16_matmul" else None,
+            "layers_per_group": wl.layers, "groups": wl.groups, "steps": K, "warmup": W,
+            "serial_ms_per_step": round(per["serial"], 5), "prefetch_ms_per_step": round(per["prefetch"], 5),
+            "hidden_us_per_step": round((per["serial"] - per["prefetch"]) * 1e3, 2),
+            "host_enqueue_ms_per_step": {"serial": round(per["serial_host"], 5),
+                                         "prefetch": round(per["prefetch_host"], 5)},
+            "compute_only_ms_per_step": round(c_us * wl.layers * wl.groups * 1e-3, 5)})
+    return results
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.layer_prefetch:
+        wl = preset(args.workload)
+        tr = Trace(wl, steps=max(args.warmup + args.steps, 1))
+        for r in layer_prefetch(tr, args.warmup, args.steps, args.layer_prefetch):
+            print(json.dumps(r), flush=True)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
