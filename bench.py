@@ -28,6 +28,10 @@ Printed as one JSON line, with:
                 from a second replay with per-phase events;
   cpu_baseline  the CPU oracle timed on this host's cores over the same steps
                 (a bounded sample; a baseline, not the target).
+Also: selections_per_s (selection entries resolved per second, all groups),
+first_step_ms (step 1, the cold start with the most misses, timed alone), and
+hipMemcpyAsync pinned-host peaks (each direction and both at once) next to the
+miss-path rates.
 """
 
 from __future__ import annotations
@@ -191,8 +195,17 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
     eng = engine_for(tr, max_append=1 << 16, policy=policy)
     initial_load(eng, tr, groups, rows)
     torch.cuda.synchronize()
+    # the first step (cold start: the most misses) is timed on its own
+    s1, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    first_ms = None
     for t in range(1, W + 1):
+        if t == 1:
+            s1.record()
         run_step(eng, t)
+        if t == 1:
+            e1.record()
+            torch.cuda.synchronize()
+            first_ms = s1.elapsed_time(e1)
     torch.cuda.synchronize()
     # every gather of the timed region records its kernel's start and end in its
     # own dispatch (HIP events on the engine's stream, no launch overhead inside)
@@ -214,7 +227,7 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
     eng.close()
     del eng
     res = dict(wall_s=wall, event_ms=ev_ms, gather_ms=g_total_ms / max(g_launches, 1),
-               gather_launches=g_launches)
+               gather_launches=g_launches, first_step_ms=first_ms)
 
     # ---- per-phase replay (diagnostic, synchronises every step) --------------
     if phases:
@@ -243,6 +256,37 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
         res.update(phase_ms=(ph / max(n, 1)).tolist(), link_ms_total=float(ph[1]),
                    h2d_rows=int(h2d), d2h_rows=int(d2h), group_steps=n)
     return res
+
+
+def copy_peaks(gib: float = 1.0) -> dict:
+    """hipMemcpyAsync between pinned host memory and HBM: GB/s host-to-device,
+    device-to-host, and each direction when both run at once (two streams)."""
+    import torch
+    n = int(gib * (1 << 30))
+    h_in = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    h_out = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    d_in = torch.empty(n, dtype=torch.uint8, device="cuda")
+    d_out = torch.empty(n, dtype=torch.uint8, device="cuda")
+    s_a, s_b = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def run(copies):
+        for _ in range(2):   # the first copies page the buffers in
+            for s, fn in copies:
+                with torch.cuda.stream(s):
+                    fn()
+            torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s, fn in copies:
+            with torch.cuda.stream(s):
+                fn()
+        torch.cuda.synchronize()
+        return n / (time.perf_counter() - t0) / 1e9
+
+    h2d = run([(s_a, lambda: d_in.copy_(h_in, non_blocking=True))])
+    d2h = run([(s_a, lambda: h_out.copy_(d_out, non_blocking=True))])
+    both = run([(s_a, lambda: d_in.copy_(h_in, non_blocking=True)),
+                (s_b, lambda: h_out.copy_(d_out, non_blocking=True))])
+    return {"bytes": n, "h2d": round(h2d, 2), "d2h": round(d2h, 2), "bidirectional_each": round(both, 2)}
 
 
 def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
@@ -428,8 +472,19 @@ def main():
                 "phase_ms_per_group_step": {k: round(v, 5) for k, v in zip(
                     ["lookup_dedup", "mark_select_link", "swap_commit"],
                     r["phase_ms"])}}
+        try:
+            peaks = copy_peaks()
+            miss["measured_copy_peak_GBps"] = peaks
+            if gin is not None and peaks["bidirectional_each"]:
+                miss["frac_of_measured_bidirectional"] = {
+                    "h2d": round(gin / peaks["bidirectional_each"], 4),
+                    "d2h": round(gout / peaks["bidirectional_each"], 4) if gout else None}
+        except RuntimeError as e:   # pinned memory refused: report without the measured peaks
+            miss["measured_copy_peak_GBps"] = f"not measured: {e}"
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K,
+        "selections_per_s": round(value / wl.layers, 1),
+        "first_step_ms": None if r.get("first_step_ms") is None else round(r["first_step_ms"], 5),
         "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u8", "data": "synthetic",
         "config": {"workload": wl.name, "requests": wl.requests,
