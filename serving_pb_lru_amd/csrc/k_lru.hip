@@ -9,11 +9,11 @@
 // PB-LRU; only the choice and order of the victims differ.
 //
 // Victim order: free slots ascending, then occupied slots by (timestamp, slot),
-// never a slot stamped with the current step t. A hit (compaction) or a load
-// (commit) at step t stamps t; an appended slot keeps stamp 0, standing for its
-// textbook stamp s - P: older than every step and, among such slots, ordered by
-// slot. So with the key
-//   K(s) = 0 (free), 1 (stamp < 1), stamp + 1 (1 <= stamp < t), excluded (stamp t)
+// never a slot hit by the current step t. The commit gives the step's hits and
+// loads timestamp t (so a failed step changes none); an appended slot keeps 0,
+// standing for its textbook stamp s - P: older than every step and, among such
+// slots, ordered by slot. So with the key
+//   K(s) = 0 (free), excluded (hit this step), 1 (timestamp 0), timestamp + 1
 // the order is (K, slot) ascending, exactly.
 //
 // Per step, with M misses:
@@ -43,23 +43,28 @@ constexpr uint32_t kExcludedKey = 0xFFFFFFFFu;
 constexpr int kLruBins = 2048;
 
 // Keys of the 32 slots of bitmap word w (slot 32 w + j in k[j]); slots >= P are
-// excluded. Stamps are padded to whole words; the owner array is read in the
-// same 16-byte pieces (its region is padded to 64 entries).
+// excluded. The compaction marks this step's hits (stamp == t); the timestamps
+// proper (lru_ts) change only at the commit. Both are padded to whole words;
+// the owner array is read in the same 16-byte pieces (its region is padded to
+// 64 entries).
 __device__ __forceinline__ void word_keys(const GroupDev& g, int w, uint32_t t, uint32_t k[32]) {
-  const vec4u* sp = reinterpret_cast<const vec4u*>(g.stamp + (size_t)w * 32);
+  const vec4u* hp = reinterpret_cast<const vec4u*>(g.stamp + (size_t)w * 32);
+  const vec4u* tp = reinterpret_cast<const vec4u*>(g.lru_ts + (size_t)w * 32);
   const vec4u* op = reinterpret_cast<const vec4u*>(g.gown + (size_t)w * 32);
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
-    const vec4u s4 = sp[q];
+    const vec4u h4 = hp[q];
+    const vec4u t4 = tp[q];
     const vec4u o4 = op[q];
-    const uint32_t st[4] = {s4.x, s4.y, s4.z, s4.w};
+    const uint32_t hm[4] = {h4.x, h4.y, h4.z, h4.w};
+    const uint32_t ts[4] = {t4.x, t4.y, t4.z, t4.w};
     const uint32_t ow[4] = {o4.x, o4.y, o4.z, o4.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int32_t stamp = (int32_t)st[j];
+      const int32_t stamp = (int32_t)ts[j];
       uint32_t key;
       if ((int32_t)ow[j] == -1) key = 0u;
-      else if (stamp == (int32_t)t) key = kExcludedKey;
+      else if ((int32_t)hm[j] == (int32_t)t) key = kExcludedKey;   // a hit of this step
       else key = stamp < 1 ? 1u : (uint32_t)stamp + 1u;
       k[4 * q + j] = key;
     }

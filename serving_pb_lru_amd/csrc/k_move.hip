@@ -88,8 +88,7 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
           const int32_t old = g.gown[v];
           g.map[la] = v;
           g.gown[v] = la;
-          g.stamp[v] = (int32_t)t;       // loaded this step (exact LRU's timestamp; PB-LRU reads
-                                         // stamps only to find the next step's hits)
+          if (g.lru_ts) g.lru_ts[v] = (int32_t)t;   // exact LRU: loaded this step
           g.res[g.miss_e[i]].y = v;      // the step's selection now resolves to the loaded slot
           if (old != -1) {
             g.map[old] = kHostBit | h;
@@ -113,6 +112,12 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
         *gp[u] = mv[u];
       }
     }
+  }
+  if (g.lru_ts) {
+    // exact LRU: the step's hits take its timestamp now that it has succeeded
+    const int nh = g.ctr->n_hits;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nh; i += gridDim.x * blockDim.x)
+      g.lru_ts[g.hit_slots[i]] = (int32_t)t;
   }
   if (freed) atomicAdd(&s_freed, freed);
   __syncthreads();

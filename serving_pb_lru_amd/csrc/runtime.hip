@@ -82,7 +82,7 @@ bool check_config(const ula_config* c, Dims* d) {
 struct Layout {
   size_t map, tag, gown, stamp, dirty, hown, bm, tcnt, hbm, htcnt, hits, mla, mh, vict, blk,
       partial, items, app_la, app_dst, app_rows, evict_rows, wb_h, miss_e, miss_stage, miss_rows,
-      hs_stage, res, lru_hist, span_a, span_b, sort_key[2], sort_slot[2], rs_hist, rs_base, pool,
+      hs_stage, res, lru_ts, lru_hist, span_a, span_b, sort_key[2], sort_slot[2], rs_hist, rs_base, pool,
       group_bytes;
   size_t counters_bytes, total;
 };
@@ -122,7 +122,8 @@ Layout layout_of(const ula_config* c, const Dims& d) {
   L.miss_rows = take((size_t)d.maxU * d.slot_bytes);
   L.hs_stage = take(8 * d.H);
   L.res = take(8 * d.nsel);
-  if (d.policy == ULA_POLICY_LRU) {   // exact-LRU selection scratch
+  if (d.policy == ULA_POLICY_LRU) {   // exact-LRU timestamps and selection scratch
+    L.lru_ts = take(4 * 32 * d.W);
     L.lru_hist = take(4 * 2048);
     L.span_a = take(4 * d.T);
     L.span_b = take(4 * d.T);
@@ -312,6 +313,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     g.hs_stage = reinterpret_cast<unsigned long long*>(b + L.hs_stage);
     g.res = reinterpret_cast<uint2*>(b + L.res);
     if (d.policy == ULA_POLICY_LRU) {
+      g.lru_ts = reinterpret_cast<int32_t*>(b + L.lru_ts);
       g.lru_hist = reinterpret_cast<uint32_t*>(b + L.lru_hist);
       g.span_a = reinterpret_cast<uint32_t*>(b + L.span_a);
       g.span_b = reinterpret_cast<uint32_t*>(b + L.span_b);
@@ -354,6 +356,8 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     // no host slot has a staged row: step 0xFFFFFFFF is never the previous step
     if (e == hipSuccess) e = launch_fill_u64(g.hs_stage, d.H, ~0ull, s);
     if (e == hipSuccess && g.lru_hist) e = launch_fill_u32(g.lru_hist, 2048, 0u, s);
+    if (e == hipSuccess && g.lru_ts)
+      e = launch_fill_u32(reinterpret_cast<uint32_t*>(g.lru_ts), 32 * d.W, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(g.bm, d.NB * d.W, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32(g.tcnt, d.NB * d.T, 0u, s);
     if (e == hipSuccess) e = launch_init_bitmap(g.bm + kFree * d.W, g.W, d.P, g.tcnt + kFree * d.T, g.T, s);
@@ -599,7 +603,7 @@ int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out) {
     // an occupied slot that no step stamped counts as s - P
     std::fill(out->bitsets + d.W, out->bitsets + d.NB * d.W, 0u);
     if (out->stamps) {
-      HIP_TRY(hipMemcpy(out->stamps, g.stamp, 4 * d.P, hipMemcpyDeviceToHost));
+      HIP_TRY(hipMemcpy(out->stamps, g.lru_ts, 4 * d.P, hipMemcpyDeviceToHost));
       for (int64_t s = 0; s < d.P; ++s)
         if (out->gown[s] != -1 && out->stamps[s] < 1) out->stamps[s] = (int32_t)(s - d.P);
     }

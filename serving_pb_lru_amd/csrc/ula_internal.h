@@ -122,7 +122,9 @@ struct GroupDev {        // device view of one group, passed by value to kernels
   uint8_t* app_rows;
   uint8_t* evict_rows;   // [maxU][slot_bytes] evicted rows staged for the write-back
   uint32_t* wb_h;        // [maxU] host slot each staged row goes to, or absent
-  // exact-LRU scratch (allocated only for that policy)
+  // exact-LRU state and scratch (allocated only for that policy)
+  int32_t* lru_ts;       // [32 W] timestamp of each slot (hit or load step; 0 = never), written
+                         //   only by the commit, so a failed step leaves it unchanged
   uint32_t* lru_hist;    // [2048] histogram of one select pass
   uint32_t* span_a;      // [T] per 2048-slot span: victims below the last key, then their offsets
   uint32_t* span_b;      // [T] per span: slots with the last key, then their offsets

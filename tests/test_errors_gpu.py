@@ -42,15 +42,16 @@ def _state(eng):
     return digest(eng.export_state(0))
 
 
+@pytest.mark.parametrize("policy", [0, 1], ids=["pblru", "lru"])
 @pytest.mark.parametrize("bad", ["range", "never_appended", "negative", "capacity"])
-def test_device_errors_latch_and_change_nothing(bad):
+def test_device_errors_latch_and_change_nothing(bad, policy):
     from serving_pb_lru_amd import Engine, UlaError
     from synth.device import rows_device
     tr = Trace(preset("tiny_4x4k"))
     wl = tr.wl
     # max_k wide enough for a step with more distinct entries than GPU slots
     eng = Engine(1, wl.layers, wl.row_bytes, wl.ring, tr.N, tr.P, tr.H, max_sets=tr.n_sets,
-                 max_k=tr.P + 1, max_append=4096)
+                 max_k=tr.P + 1, max_append=4096, policy=policy)
     rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
     try:
         order = tr.initial_load_order()
@@ -298,3 +299,55 @@ def test_timing_modes_count_and_change_nothing():
     finally:
         eng.close()
         ref.close()
+
+
+def test_lru_empty_padding_and_dirty_workspace():
+    """Exact LRU: an empty step and an all-padding step change nothing but the counter
+    and statistics; an engine built on a workspace full of set bits matches the
+    oracle over a whole trace (every counter and histogram the LRU kernels use is
+    initialised by ula_init)."""
+    import torch
+    from oracle.exact_lru_np import ExactLRUArrays
+    from serving_pb_lru_amd.replay import engine_for, initial_load
+    from serving_pb_lru_amd import lib
+    from serving_pb_lru_amd.ula import UlaConfig
+    from synth.device import rows_device
+    import ctypes
+    wl = tiny_workload(5, steps=12)
+    wl = dataclasses.replace(wl, pool_slots=2 * wl.requests * wl.sets_per_request * wl.k)
+    tr = Trace(wl)
+    cfg = UlaConfig(1, wl.layers, wl.row_bytes, wl.ring, tr.N, tr.P, tr.H, tr.n_sets, tr.k, 4096, 1)
+    junk = torch.full((lib().ula_device_bytes(ctypes.byref(cfg)),), 0xFF, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    del junk                      # the caching allocator hands this block to the engine
+    eng = engine_for(tr, max_append=4096, policy=1)
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    ora = ExactLRUArrays(tr.N, tr.P, tr.H, wl.ring)
+    try:
+        initial_load(eng, tr, [0], rows)
+        ora.append(tr.initial_load_order())
+        sels = list(tr.selections(0))
+        plan = [np.zeros((0, tr.k), np.int32), np.full((tr.n_sets, 5), -1, np.int32)] + sels
+        t_app = 0
+        for i, sel in enumerate(plan):
+            if i >= 2:
+                t_app += 1
+                app = tr.appends(t_app)
+                eng.append(0, app, rows(app, 0))
+                ora.append(app)
+            d = _cuda(sel)
+            eng.step(0, d)
+            outs = [eng.gather(0, l, d) for l in range(wl.layers)]
+            eng.sync()
+            ora.step(sel)
+            st, ref = eng.export_state(0), ora.export_state()
+            for k in ("map", "gown", "hown", "bitsets", "stamps"):
+                assert np.array_equal(np.asarray(st[k]), np.asarray(ref[k])), (i, k)
+            assert st["flag"] == ref["flag"] and tuple(st["stats"]) == tuple(ref["stats"]), i
+            flat = sel.reshape(-1)
+            want = rows_for(wl.seed, 0, np.where(flat < 0, 0, flat), wl.layers, wl.row_bytes)
+            want[flat < 0] = 0
+            for l in range(wl.layers):
+                assert np.array_equal(outs[l].cpu().numpy().reshape(flat.size, wl.row_bytes), want[:, l])
+    finally:
+        eng.close()
