@@ -100,6 +100,7 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
             wbh[i] = kAbsent;
             atomicOr(&g.hbm[h >> 5], 1u << (h & 31));
             atomicAdd(&g.htcnt[h >> kTileShift], 1u);
+            atomicMin(&g.ctr->hfree_lo, (int32_t)(h >> kTileShift));
             ++freed;
           }
         }

@@ -70,8 +70,10 @@ __device__ void plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
     if (q <= 0) continue;
     const uint32_t* tc = bucket_tcnt(g, id);
     const int T = bucket_ntiles(g, id);
+    // the free sets start at their hint: every span before it is empty
+    int32_t* hint = id == kFree ? &c->free_lo : (id == kHostFreeId ? &c->hfree_lo : nullptr);
     int pre = 0;   // set bits of this bucket in spans before the chunk
-    for (int base = 0; base < T && pre < q; base += 1024) {
+    for (int base = hint ? min(max(*hint, 0), T) : 0; base < T && pre < q; base += 1024) {
       const int tile = base + tid;
       const int cnt = tile < T ? (int)tc[tile] : 0;
       const unsigned long long ne = __ballot(cnt > 0);
@@ -92,6 +94,8 @@ __device__ void plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
         it.out_off = off + pre + ex;
         it.take = min(cnt, q - pre - ex);
         g.items[nitems + rank] = it;
+        // the span where the quota is reached: everything before it is taken
+        if (hint && pre + ex + cnt >= q) *hint = tile;
       }
       nitems += __syncthreads_count(emit);
       pre += total;

@@ -79,6 +79,10 @@ struct alignas(64) Counters {
   uint32_t lru_kstar;    // key of the last victim
   int32_t lru_c;         // victims with a key below it (they need sorting by key)
   int32_t lru_r;         // victims with that key (taken in slot order)
+  // first span of the free GPU set / free host set that may hold a set bit: both
+  // are taken lowest first, so every span before the hint is empty (a freed host
+  // slot lowers its hint)
+  int32_t free_lo, hfree_lo;
 };
 static_assert(sizeof(Counters) % 64 == 0, "counter block alignment");
 
