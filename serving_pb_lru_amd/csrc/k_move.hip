@@ -38,12 +38,38 @@ __global__ __launch_bounds__(256) void k_place(GroupDev g, int32_t n, const uint
 // already prefetched into miss_rows[i], into victim slot victims[i]; a victim
 // that holds an entry first copies its rows to the staging buffer, from which
 // the next step's mark launch (or a stand-alone write-back before the host
-// reads state) writes them to the host slot the miss vacated. The thread of piece 0 of a pair also commits it: mapping table,
-// owners, the step's resolved selection, and the staging record of its host
-// slot (so that a miss of the evicted entry in the next step reads the staged
-// copy instead of a host slot whose write may still be in flight). A victim
-// that was free releases its host slot instead. Every workgroup then releases
-// its writes and takes a ticket; the last one raises the completion counter.
+// reads state) writes them to the host slot the miss vacated. Each pair is also
+// committed (commit_pair): beside its first piece when one round of the data
+// loop covers every piece, else one lane per pair after the loop. Every
+// workgroup then releases its writes and takes a ticket; the last one raises the
+// completion counter.
+// Commit of pair i: mapping table, owners, the step's resolved selection, and
+// the staging record of the host slot; a victim that was free releases its host
+// slot instead (counted in `freed`).
+__device__ __forceinline__ void commit_pair(const GroupDev& g, uint32_t t, int i, int& freed) {
+  const uint32_t v = g.victims[i] & ~kHostBit;
+  const int32_t la = g.miss_la[i];
+  const uint32_t h = g.miss_h[i];
+  const int32_t old = g.gown[v];
+  g.map[la] = v;
+  g.gown[v] = la;
+  if (g.lru_ts) g.lru_ts[v] = (int32_t)t;   // exact LRU: loaded this step
+  g.res[g.miss_e[i]].y = v;      // the step's selection now resolves to the loaded slot
+  if (old != -1) {
+    g.map[old] = kHostBit | h;
+    g.hown[h] = old;
+    g.wb_h[i] = h;
+    g.hs_stage[h] = ((unsigned long long)t << 32) | (uint32_t)i;
+  } else {
+    g.hown[h] = -1;
+    g.wb_h[i] = kAbsent;
+    atomicOr(&g.hbm[h >> 5], 1u << (h & 31));
+    atomicAdd(&g.htcnt[h >> kTileShift], 1u);
+    atomicMin(&g.ctr->hfree_lo, (int32_t)(h >> kTileShift));
+    ++freed;
+  }
+}
+
 __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, FastDiv per_slot) {
   __shared__ int s_freed;
   if (block_failed(g.ctr)) return;
@@ -51,7 +77,6 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
   __syncthreads();
   const int m = g.ctr->n_miss;
   uint8_t* stage = g.evict_rows;
-  uint32_t* wbh = g.wb_h;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     g.ctr->wb_n = m;
     g.ctr->wb_step = t;
@@ -62,6 +87,7 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
   const uint32_t stride = gridDim.x * blockDim.x;
   int freed = 0;
   constexpr int U = 4;
+  const bool one_round = total <= U * stride;
   for (uint32_t base = blockIdx.x * blockDim.x + threadIdx.x; base < total; base += U * stride) {
     vec4u mv[U], gv[U];
     vec4u* gp[U];
@@ -82,28 +108,9 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
         sp[u] = reinterpret_cast<vec4u*>(stage + (size_t)i * g.slot_bytes) + c;
         if (ev[u]) gv[u] = *gp[u];
         mv[u] = reinterpret_cast<const vec4u*>(g.miss_rows + (size_t)i * g.slot_bytes)[c];
-        if (c == 0) {
-          const int32_t la = g.miss_la[i];
-          const uint32_t h = g.miss_h[i];
-          const int32_t old = g.gown[v];
-          g.map[la] = v;
-          g.gown[v] = la;
-          if (g.lru_ts) g.lru_ts[v] = (int32_t)t;   // exact LRU: loaded this step
-          g.res[g.miss_e[i]].y = v;      // the step's selection now resolves to the loaded slot
-          if (old != -1) {
-            g.map[old] = kHostBit | h;
-            g.hown[h] = old;
-            wbh[i] = h;
-            g.hs_stage[h] = ((unsigned long long)t << 32) | i;
-          } else {
-            g.hown[h] = -1;
-            wbh[i] = kAbsent;
-            atomicOr(&g.hbm[h >> 5], 1u << (h & 31));
-            atomicAdd(&g.htcnt[h >> kTileShift], 1u);
-            atomicMin(&g.ctr->hfree_lo, (int32_t)(h >> kTileShift));
-            ++freed;
-          }
-        }
+        // one data round covers every piece: commit beside the first piece, so
+        // the commit's dependent loads overlap the row loads
+        if (one_round && c == 0) commit_pair(g, t, (int)i, freed);
       }
     }
 #pragma unroll
@@ -114,6 +121,11 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
       }
     }
   }
+  // More rounds: commit one lane per pair after the data loop (interleaved, the
+  // commit's chain of dependent loads would stall a wavefront in every round).
+  if (!one_round)
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < m; i += gridDim.x * blockDim.x)
+      commit_pair(g, t, i, freed);
   if (g.lru_ts) {
     // exact LRU: the step's hits take its timestamp now that it has succeeded
     const int nh = g.ctr->n_hits;
