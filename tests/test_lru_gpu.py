@@ -47,42 +47,47 @@ def _compare(st: dict, ref: dict, where: str) -> None:
         assert tuple(st["stats"]) == tuple(ref["stats"]), f"{where}: stats {st['stats']} vs {ref['stats']}"
 
 
-def run_lru_parity(wl, steps=None, selections=None, check_every=1, max_append=4096):
+def run_lru_parity(wl, steps=None, selections=None, check_every=1, max_append=4096, groups=None):
+    """Every group of one engine against its own oracle, steps interleaved group by group."""
     import torch
     from serving_pb_lru_amd.replay import engine_for, initial_load
     from synth.device import rows_device
     tr = Trace(wl, steps)
-    say(f"lru parity {wl.name}: N={tr.N} P={tr.P} H={tr.H} steps={tr.steps}")
+    groups = [0] if groups is None else groups
+    say(f"lru parity {wl.name}: N={tr.N} P={tr.P} H={tr.H} steps={tr.steps} groups={groups}")
     eng = engine_for(tr, max_append=max_append, policy=1)
     rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
-    lru = ExactLRUGroup(tr.N, tr.P, tr.H)
+    lru = {g: ExactLRUGroup(tr.N, tr.P, tr.H) for g in groups}
     try:
-        initial_load(eng, tr, [0], rows)
-        lru.append(tr.initial_load_order())
-        _compare(eng.export_state(0), _lru_state(lru, tr.P), "after load")
-        sels = iter(selections) if selections is not None else tr.selections(0)
+        initial_load(eng, tr, groups, rows)
+        for g in groups:
+            lru[g].append(tr.initial_load_order())
+            _compare(eng.export_state(g), _lru_state(lru[g], tr.P), f"group {g} after load")
+        sels = {g: (iter(selections) if selections is not None else tr.selections(g)) for g in groups}
         for t in range(1, tr.steps + 1):
-            sel = next(sels)
             app = tr.appends(t)
-            if app.size:
-                eng.append(0, app, rows(app, 0))
-                lru.append(app)
-            dsel = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
-            eng.step(0, dsel)
-            outs = [eng.gather(0, l, dsel) for l in range(wl.layers)]
-            eng.sync()
-            lru.step(sel)
-            if t % check_every == 0 or t == tr.steps:
-                _compare(eng.export_state(0), _lru_state(lru, tr.P), f"step {t}")
-            flat = np.asarray(sel, dtype=np.int32).reshape(-1)
-            want = rows_for(wl.seed, 0, np.where(flat < 0, 0, flat), wl.layers, wl.row_bytes)
-            want[flat < 0] = 0
-            for l in range(wl.layers):
-                got = outs[l].cpu().numpy().reshape(flat.size, wl.row_bytes)
-                assert np.array_equal(got, want[:, l]), f"step {t} layer {l}: gathered rows differ"
+            for g in groups:
+                sel = next(sels[g])
+                if app.size:
+                    eng.append(g, app, rows(app, g))
+                    lru[g].append(app)
+                dsel = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
+                eng.step(g, dsel)
+                outs = [eng.gather(g, l, dsel) for l in range(wl.layers)]
+                eng.sync()
+                lru[g].step(sel)
+                if t % check_every == 0 or t == tr.steps:
+                    _compare(eng.export_state(g), _lru_state(lru[g], tr.P), f"group {g} step {t}")
+                flat = np.asarray(sel, dtype=np.int32).reshape(-1)
+                want = rows_for(wl.seed, g, np.where(flat < 0, 0, flat), wl.layers, wl.row_bytes)
+                want[flat < 0] = 0
+                for l in range(wl.layers):
+                    got = outs[l].cpu().numpy().reshape(flat.size, wl.row_bytes)
+                    assert np.array_equal(got, want[:, l]), f"group {g} step {t} layer {l}: gathered rows differ"
         known = np.concatenate([tr.initial_load_order()] + [tr.appends(t) for t in range(1, tr.steps + 1)])
-        assert np.array_equal(eng.read_rows(0, known), rows_for(wl.seed, 0, known, wl.layers, wl.row_bytes))
-        return lru
+        for g in groups:
+            assert np.array_equal(eng.read_rows(g, known), rows_for(wl.seed, g, known, wl.layers, wl.row_bytes))
+        return lru[groups[0]]
     finally:
         eng.close()
 
@@ -118,7 +123,7 @@ def test_lru_long_trace_two_sort_passes():
 ])
 def test_lru_scaled(name, factor, steps):
     wl = scaled(preset(name), factor)
-    run_lru_parity(wl, steps=steps, check_every=2, max_append=1 << 15)
+    run_lru_parity(wl, steps=steps, check_every=2, max_append=1 << 15, groups=list(range(wl.groups)))
 
 
 def test_lru_equals_long_ring_pblru_on_gpu():
