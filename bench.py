@@ -37,6 +37,7 @@ miss-path rates.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -67,6 +68,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="timed CPU work of the oracle sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-phases", action="store_true", help="skip the per-phase replay")
+    p.add_argument("--groups", type=int, default=0,
+                   help="run only the first N layer groups of the workload (groups are independent; "
+                        "for workloads whose pinned host pools exceed one host's memory)")
     p.add_argument("--policy", choices=("pblru", "lru"), default="pblru",
                    help="replacement policy: PB-LRU (the pages' policy) or exact LRU (the one it is "
                         "compared against); the CPU baseline is reported for PB-LRU only")
@@ -431,6 +435,11 @@ def main():
         sys.exit(2)
     W, K = args.warmup, args.steps
     wl = preset(args.workload)
+    groups_total = wl.groups
+    if args.groups:
+        # the first N groups are the same traces as in the full workload (each
+        # group's selections come from its own seeded stream)
+        wl = dataclasses.replace(wl, groups=min(args.groups, wl.groups))
     tr = Trace(wl, steps=max(W + K, 1))
     per_step = rows_per_step(tr)
 
@@ -490,6 +499,7 @@ def main():
         "config": {"workload": wl.name, "requests": wl.requests,
                    "context": wl.ctx_fixed if wl.ctx_fixed else list(wl.ctx_range),
                    "sets_per_request": wl.sets_per_request, "groups": wl.groups,
+                   "groups_of_workload": groups_total,
                    "layers_per_group": wl.layers, "k": wl.k, "gpu_slots": tr.P, "host_slots": tr.H,
                    "ring": wl.ring, "row_bytes": wl.row_bytes, "overlap": wl.overlap,
                    "policy": "exact LRU" if policy else "PB-LRU",

@@ -18,9 +18,9 @@
 // lane are in flight; for 656-byte rows both tilings below cover all staged
 // rows in one round. Bound by HBM bandwidth.
 //
-// Tilings (measured on MI355X with 656-byte rows): a small gather (tens of
-// thousands of rows, a few workgroups per compute unit) is fastest with 64
-// rows and 11 pieces in flight per lane of 256; a large one with 32 rows and 3
+// Tilings (measured on MI355X with 656-byte rows): a small gather (up to 64K
+// rows, a few workgroups per compute unit) is fastest with 64 rows and 11 pieces
+// in flight per lane of 256; a large one (131K rows and more) with 32 rows and 3
 // pieces per lane of 512, which keeps more workgroups resident.
 #include <hip/hip_ext.h>
 
@@ -28,7 +28,7 @@
 
 namespace ula {
 
-constexpr int kSmallGatherRows = 1 << 17;   // up to this many rows: the small-gather tiling
+constexpr int kSmallGatherRows = 1 << 16;   // up to this many rows: the small-gather tiling
 
 // Rows are read with plain (cached) loads: repeated entries of one step (the
 // speculative sets) and the heavy overlap between consecutive steps both hit the
