@@ -55,6 +55,19 @@ class ExactLRUGroup:
                 self.hown[h] = la
                 self.where[la] = ("host", h)
 
+    def release(self, las) -> None:
+        """The released entries' slots become free (GPU: back on the free list,
+        stamp cleared; host: back on the free list); the addresses become absent."""
+        for la in [int(x) for x in las]:
+            kind, s = self.where.pop(la)
+            if kind == "gpu":
+                self.gown[s] = -1
+                self.stamp[s] = 0
+                heapq.heappush(self.free_gpu, s)
+            else:
+                self.hown[s] = -1
+                heapq.heappush(self.free_host, s)
+
     def step(self, sel) -> None:
         self.t += 1
         t = self.t

@@ -67,6 +67,23 @@ class ExactLRUArrays:
         self.hown[hslots] = h_las
         self.free_host[hslots] = False
 
+    def release(self, las) -> None:
+        """The released entries' slots become free; the addresses become absent."""
+        las = np.asarray(las, dtype=np.int64).reshape(-1)
+        if las.size == 0:
+            return
+        assert np.unique(las).size == las.size and np.all(self.map[las] != ABSENT)
+        loc = self.map[las].astype(np.int64)
+        on_gpu = (loc & HOST) == 0
+        s = loc[on_gpu]
+        self.gown[s] = -1
+        self.stamp[s] = 0
+        self.free_gpu[s] = True
+        h = loc[~on_gpu] & ~HOST
+        self.hown[h] = -1
+        self.free_host[h] = True
+        self.map[las] = ABSENT
+
     def step(self, sel) -> None:
         flat = np.asarray(sel, dtype=np.int64).reshape(-1)
         valid = flat != -1

@@ -149,6 +149,37 @@ class PBLRUGroup:
             self.host[h] = rows[n_gpu:]
 
     # ------------------------------------------------------------------
+    def release(self, las: np.ndarray) -> None:
+        """Give back the slots of finished entries (section 1: in a shared pool the
+        space one request frees serves the others; section 2: placement is the
+        library's).
+
+        Reading: every released address must be appended and listed once; it
+        becomes absent (it may be appended again); its GPU slot leaves whatever
+        bucket holds it and becomes free, or its host slot becomes free. Nothing
+        else changes (the ring, ``cur``, ``flag`` and the statistics stay).
+        """
+        las = np.asarray(las, dtype=np.int64).reshape(-1)
+        if las.size == 0:
+            return
+        if las.min() < 0 or las.max() >= self.N:
+            raise OracleError("ERANGE", "address out of range")
+        if np.unique(las).size != las.size:
+            raise OracleError("EDUP", "address repeated in one release")
+        loc = self.map[las]
+        if (loc == ABSENT).any():
+            raise OracleError("ERANGE", "address not appended")
+        on_gpu = (loc & HOST_BIT) == 0
+        s = loc[on_gpu].astype(np.int64)
+        self.cold[s] = False
+        self.ring[:, s] = False
+        self.free[s] = True
+        self.gown[s] = -1
+        h = (loc[~on_gpu] & ~HOST_BIT).astype(np.int64)
+        self.hown[h] = -1
+        self.map[las] = ABSENT
+
+    # ------------------------------------------------------------------
     def step(self, sel: np.ndarray) -> StepStats:
         """One scheduling round of this group over its selection sets."""
         sel = np.asarray(sel, dtype=np.int64)

@@ -48,3 +48,55 @@ def test_invariants_random(seed):
             assert (out[~valid] == 0).all()
             ref = rows_for(wl.seed, 0, sel[valid], wl.layers, wl.row_bytes)[:, layer]
             assert (out[valid] == ref).all()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_invariants_hold_with_releases(seed):
+    """I1-I9 after every step of traces whose finished entries are released between
+    steps (released addresses are absent; their slots are free, so later misses take
+    free GPU slots first and free host slots are reused by appends)."""
+    from tracegen import release_plan
+    wl = tiny_workload(seed, steps=10)
+    tr = Trace(wl)
+    sels = padded_selections(tr, 0, seed)
+    plan = release_plan(tr, sels, seed, frac=0.4)
+    g = PBLRUGroup(tr.N, tr.P, tr.H, wl.ring, wl.layers, wl.row_bytes, full_data=True)
+    load = tr.initial_load_order()
+    g.append(load, rows_for(wl.seed, 0, load, wl.layers, wl.row_bytes))
+    for t, sel in enumerate(sels, 1):
+        app = tr.appends(t)
+        g.append(app, rows_for(wl.seed, 0, app, wl.layers, wl.row_bytes))
+        prev = g.export_state()
+        g.step(sel)
+        st = g.export_state()
+        U, hit_slots, _, _, victims = g.last_lists
+        check_step(prev, st, tr.P, tr.H, U=U, victims=victims, hit_slots=hit_slots)
+        appended = np.flatnonzero(g.map != 0xFFFFFFFF)
+        want = rows_for(wl.seed, 0, appended, wl.layers, wl.row_bytes)
+        assert (np.stack([g.read_row(int(la)) for la in appended]) == want).all()
+        for layer in range(wl.layers):
+            out = g.gather(sel, layer, step=t)
+            valid = sel != -1
+            assert (out[valid] == rows_for(wl.seed, 0, sel[valid], wl.layers, wl.row_bytes)[:, layer]).all()
+        rel = plan.get(t, np.zeros(0, np.int32))
+        g.release(rel)
+        assert (g.map[rel] == 0xFFFFFFFF).all()
+        check_state(g.export_state(), tr.P, tr.H)
+
+
+def test_release_errors_change_nothing():
+    from oracle.pblru import OracleError
+    wl = tiny_workload(1)
+    tr = Trace(wl)
+    g = PBLRUGroup(tr.N, tr.P, tr.H, wl.ring, wl.layers, wl.row_bytes, full_data=False)
+    g.append(tr.initial_load_order(), None)
+    st = g.export_state()
+    first = int(tr.initial_load_order()[0])
+    never = int(tr.appends(1)[0]) if tr.appends(1).size else tr.N
+    for bad, name in [([tr.N], "ERANGE"), ([-1], "ERANGE"), ([never], "ERANGE"), ([first, first], "EDUP")]:
+        with pytest.raises(OracleError) as e:
+            g.release(np.array(bad, dtype=np.int64))
+        assert e.value.name == name
+        after = g.export_state()
+        for k in ("map", "gown", "hown", "bitsets"):
+            assert np.array_equal(after[k], st[k])

@@ -133,3 +133,64 @@ def test_array_lru_worked_example():
     for s, want in zip(ex["steps"], ex["exact_lru_victims"]):
         g.step(np.array(s["sel"]))
         assert [int(v) for v in g.last_victims] == want
+
+
+def _with_releases(trace, sels, plan):
+    wl = trace.wl
+    from oracle.exact_lru_np import ExactLRUArrays
+    pb = PBLRUGroup(trace.N, trace.P, trace.H, wl.ring, wl.layers, wl.row_bytes, full_data=False)
+    brute = ExactLRUGroup(trace.N, trace.P, trace.H)
+    arr = ExactLRUArrays(trace.N, trace.P, trace.H, wl.ring)
+    load = trace.initial_load_order()
+    pb.append(load, None)
+    brute.append(load)
+    arr.append(load)
+    for t, sel in enumerate(sels, 1):
+        app = trace.appends(t)
+        pb.append(app, None)
+        brute.append(app)
+        arr.append(app)
+        pb.step(sel)
+        brute.step(sel)
+        arr.step(sel)
+        yield t, pb, brute, arr
+        rel = plan.get(t, np.zeros(0, np.int32))
+        pb.release(rel)
+        brute.release(rel)
+        arr.release(rel)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_releases_keep_long_ring_equal_to_exact_lru(seed):
+    """Released entries free their slots (GPU slots leave their bucket); later steps
+    take those free slots first. With a ring longer than the trace PB-LRU must still
+    equal exact LRU, and the array LRU the brute-force one, step by step."""
+    from tracegen import release_plan
+    wl = tiny_workload(seed, steps=12)
+    wl = dataclasses.replace(wl, ring=wl.steps + 1)
+    tr = Trace(wl)
+    sels = padded_selections(tr, 0, seed)
+    plan = release_plan(tr, sels, seed)
+    saw_free_victims = False
+    for t, pb, brute, arr in _with_releases(tr, sels, plan):
+        assert list(pb.last_lists[4]) == brute.last_victims == [int(v) for v in arr.last_victims], f"step {t}"
+        assert pb.last.as_tuple() == brute.last == arr.last
+        assert [int(x) for x in pb.map] == brute.map_array() == [int(x) for x in arr.map]
+        assert list(pb.gown) == brute.gown and list(pb.hown) == brute.hown
+        saw_free_victims |= pb.last.from_free > 0
+    if seed in (0, 1, 2):
+        assert any(plan[t].size for t in plan)
+
+
+def test_releases_reach_free_victims():
+    """After releases, misses take free GPU slots (the from-free path) and free host slots."""
+    from tracegen import release_plan
+    total_free = 0
+    for seed in range(10):
+        wl = tiny_workload(seed, steps=12)
+        tr = Trace(wl)
+        sels = padded_selections(tr, 0, seed)
+        plan = release_plan(tr, sels, seed, frac=0.5)
+        for t, pb, brute, arr in _with_releases(tr, sels, plan):
+            total_free += pb.last.from_free
+    assert total_free > 0

@@ -35,3 +35,25 @@ def with_padding(sel: np.ndarray, rng, frac: float = 0.1) -> np.ndarray:
 def padded_selections(trace: Trace, g: int, seed: int, frac: float = 0.1):
     rng = np.random.default_rng([seed, 99])
     return [with_padding(s, rng, frac) for s in trace.selections(g)]
+
+
+def release_plan(trace: Trace, sels, seed: int, frac: float = 0.3) -> dict:
+    """Addresses to release after each step t (before step t+1's appends): a random
+    share `frac` of the entries appended so far that no later step selects, so
+    that every later selection stays valid. {t: int32 array}."""
+    rng = np.random.default_rng([seed, 123])
+    sels = [np.asarray(s).reshape(-1) for s in sels]
+    later = [set() for _ in range(len(sels) + 1)]
+    for t in range(len(sels) - 1, -1, -1):        # later[t]: selected by step t+1 or after
+        later[t] = later[t + 1] | set(int(x) for x in sels[t] if x >= 0)
+    alive = set(int(x) for x in trace.initial_load_order())
+    plan = {}
+    for t in range(1, len(sels)):
+        alive |= set(int(x) for x in trace.appends(t))
+        cand = sorted(alive - later[t])
+        k = int(frac * len(cand))
+        pick = rng.choice(np.array(cand, dtype=np.int64), size=k, replace=False) if k else np.zeros(0, np.int64)
+        rng.shuffle(pick)
+        plan[t] = pick.astype(np.int32)
+        alive -= set(int(x) for x in pick)
+    return plan
