@@ -150,6 +150,23 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
 int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host,
                const void* rows, int32_t rows_on_device, uint64_t stream);
 
+/* Release n finished entries of group g (a request has ended; section 1: in a
+ * shared pool the space one request frees serves the others). Each address must
+ * be appended and listed once; it becomes absent and may be appended again. Its
+ * GPU slot leaves whatever bucket holds it and joins the free slots, which later
+ * steps take first for their misses and appends take before host slots; or its
+ * host slot joins the free host slots. The ring, the current bucket, the
+ * completion counter and the statistics do not change. Staged evicted rows of
+ * the last step are written to the host pool first (a released host slot may be
+ * waiting for one). Gathers of the last step's selection after a release resolve
+ * through the mapping table (a released entry is then ULA_ERANGE). la_host: n
+ * addresses in host memory. Enqueued on `stream`, ordered after the group's
+ * earlier calls like ula_append.
+ * Validated on the host first: ULA_EINVAL (bad g or n < 0), ULA_ERANGE (address
+ * outside [0, N) or not appended), ULA_EDUP (repeated), ULA_ESTATE; nothing
+ * changes on error. */
+int ula_release(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, uint64_t stream);
+
 /* One decode step (one scheduling round) of group g over n_sets x k selected
  * addresses (device memory, row-major, -1 = padding), section 3: de-duplicate
  * (first occurrence in row-major order) and look up once for the group; advance

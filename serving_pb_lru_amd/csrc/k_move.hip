@@ -160,6 +160,60 @@ __global__ __launch_bounds__(256) void k_writeback(GroupDev g, FastDiv per_slot)
   if (t != 0) writeback_rows(g, t, per_slot, blockIdx.x, gridDim.x);
 }
 
+// Release of finished entries (app_la[0..n), validated on the host): a GPU slot
+// leaves whichever bucket holds it and joins the free set, a host slot joins the
+// free host set (its staging record cleared, so no later miss reads a staged
+// copy of the released row); the address becomes absent. Bucket words and span
+// counts are shared between threads, hence atomics. Any staged write-back has
+// been written out before this kernel runs.
+__global__ __launch_bounds__(256) void k_release(GroupDev g, int32_t n) {
+  if (status_of(g.ctr)) return;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const int32_t la = g.app_la[i];
+    const uint32_t loc = g.map[la];
+    if (loc == kAbsent) {          // the host checked this: an inconsistent state
+      latch(g.ctr, ULA_ESTATE);
+      continue;
+    }
+    g.map[la] = kAbsent;
+    if (loc & kHostBit) {
+      const uint32_t h = loc & ~kHostBit;
+      g.hown[h] = -1;
+      g.hs_stage[h] = ~0ull;
+      atomicOr(&g.hbm[h >> 5], 1u << (h & 31));
+      atomicAdd(&g.htcnt[h >> kTileShift], 1u);
+      atomicAdd(&g.ctr->hfree, 1);
+      atomicMin(&g.ctr->hfree_lo, (int32_t)(h >> kTileShift));
+      continue;
+    }
+    const uint32_t s = loc;
+    const uint32_t bit = 1u << (s & 31);
+    const int w = (int)(s >> 5), tile = (int)(s >> kTileShift);
+    for (int id = kCold; id < g.NB; ++id) {     // the bucket holding the slot, if any
+      if (g.bm[(size_t)id * g.W + w] & bit) {
+        atomicAnd(&g.bm[(size_t)id * g.W + w], ~bit);
+        atomicSub(&g.tcnt[(size_t)id * g.T + tile], 1u);
+        atomicSub(&g.ctr->bcnt[id], 1);
+        break;
+      }
+    }
+    atomicOr(&g.bm[(size_t)kFree * g.W + w], bit);
+    atomicAdd(&g.tcnt[(size_t)kFree * g.T + tile], 1u);
+    atomicAdd(&g.ctr->bcnt[kFree], 1);
+    atomicMin(&g.ctr->free_lo, tile);
+    g.gown[s] = -1;
+    if (g.lru_ts) g.lru_ts[s] = 0;   // exact LRU: a slot appended later counts as never stamped
+  }
+}
+
+hipError_t launch_release(const GroupDev& g, int32_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  k_release<<<blocks, 256, 0, s>>>(g, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;

@@ -414,10 +414,11 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const GroupDev& g = gh.d;
   // An append needs no wait for a pending eviction write-back: it writes only
-  // free host slots, and a host slot is freed only by a miss whose victim was a
-  // free GPU slot. That never happens: an entry reaches the host pool only when
-  // no GPU slot is free, and nothing makes a GPU slot free again, so once a step
-  // can miss the free bucket stays empty.
+  // free host slots, and no free host slot has one. A step's evicted rows go to
+  // slots its misses vacated, which the evicted entries then occupy; a release
+  // writes every staged row out before it frees a slot; and the host slot a miss
+  // vacates when its victim was a free GPU slot receives no evicted row (nor had
+  // one pending: its entry was in it during the previous step).
   if (n <= kSmallAppend && n <= d.maxApp && rows_on_device) {
     // decode-time appends: one workgroup, addresses passed by value
     SmallAppend a{};
@@ -457,6 +458,54 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
     gh.appended[la >> 6] |= 1ull << (la & 63);
   }
   gh.n_appended += n;
+  return ULA_OK;
+}
+
+int ula_release(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, uint64_t stream) {
+  if (!ctx) return ULA_EINVAL;
+  if (ctx->poisoned) return ULA_ESTATE;
+  if (group < 0 || group >= ctx->cfg.num_groups || n < 0) return ULA_EINVAL;
+  if (n == 0) return ULA_OK;
+  if (!la_host) return ULA_EINVAL;
+  GroupHost& gh = ctx->groups[group];
+  const Dims& d = ctx->dims;
+  // validate the whole batch first; nothing changes on error
+  for (int32_t i = 0; i < n; ++i)
+    if (la_host[i] < 0 || la_host[i] >= d.N) return ULA_ERANGE;
+  {
+    std::vector<int32_t> sorted(la_host, la_host + n);
+    std::sort(sorted.begin(), sorted.end());
+    if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return ULA_EDUP;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t la = (uint32_t)la_host[i];
+    if (!(gh.appended[la >> 6] >> (la & 63) & 1ull)) return ULA_ERANGE;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const GroupDev& g = gh.d;
+  // A released host slot may be waiting for the last step's evicted row, and an
+  // append may take it next: write the staged rows out first.
+  if (gh.steps > 0 && gh.written_back != gh.steps) {
+    HIP_TRY(launch_writeback(g, std::max<int32_t>(gh.last_pairs, 1), s));
+    gh.written_back = gh.steps;
+  }
+  for (int32_t off = 0; off < n; off += (int32_t)d.maxApp) {
+    const int32_t cnt = (int32_t)std::min<int64_t>(n - off, d.maxApp);
+    const int k = gh.stage_next;
+    gh.stage_next = (k + 1) % kStageSlots;
+    if (gh.stage_used[k]) HIP_TRY(hipEventSynchronize(gh.stage_ev[k]));
+    gh.stage_used[k] = true;
+    std::memcpy(gh.stage[k], la_host + off, sizeof(int32_t) * cnt);
+    HIP_TRY(hipMemcpyAsync(g.app_la, gh.stage[k], sizeof(int32_t) * cnt, hipMemcpyHostToDevice, s));
+    HIP_TRY(hipEventRecord(gh.stage_ev[k], s));
+    HIP_TRY(launch_release(g, cnt, s));
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t la = (uint32_t)la_host[i];
+    gh.appended[la >> 6] &= ~(1ull << (la & 63));
+  }
+  gh.n_appended -= n;
+  gh.last_n = 0;   // the last step's resolved selection may name released entries
   return ULA_OK;
 }
 

@@ -199,6 +199,7 @@ hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, int32_t
 hipError_t launch_append_small(const GroupDev& g, const SmallAppend& a, const uint8_t* rows,
                               hipStream_t s);
 hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s);
+hipError_t launch_release(const GroupDev& g, int32_t n, hipStream_t s);
 hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s);
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s);
 // start / stop (both or neither): events recorded by the dispatch itself, so

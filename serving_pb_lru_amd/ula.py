@@ -64,6 +64,8 @@ SIGNATURES = [
                                 ctypes.c_uint64, ctypes.POINTER(ctypes.c_void_p)]),
     ("ula_append", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64]),
+    ("ula_release", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                   ctypes.c_uint64]),
     ("ula_step", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                 ctypes.c_void_p, ctypes.c_uint64]),
     ("ula_gather", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -157,6 +159,12 @@ class Engine:
             rows = np.ascontiguousarray(rows, dtype=np.uint8)
         _check(lib().ula_append(self.ctx, group, las.size, las.ctypes.data, _ptr(rows), on_dev,
                                 _stream(stream)), "ula_append")
+
+    def release(self, group: int, las: np.ndarray, stream=None) -> None:
+        """Give back the slots of finished entries (they become absent)."""
+        las = np.ascontiguousarray(las, dtype=np.int32)
+        _check(lib().ula_release(self.ctx, group, las.size, las.ctypes.data, _stream(stream)),
+               "ula_release")
 
     def step(self, group: int, sel, stream=None) -> None:
         """sel: torch CUDA int32 tensor [n_sets][k] (or [k] for one set)."""

@@ -37,13 +37,15 @@ def assert_same_state(st: dict, ref: dict, where: str) -> None:
     assert tuple(st["stats"]) == tuple(ref["stats"]), f"{where}: stats {st['stats']} vs {ref['stats']}"
 
 
-def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, check_every=1):
+def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, check_every=1,
+               releases=None):
     """selections: optional {g: list of int32 [n_sets][k]} overriding the trace's.
 
     The state is exported (which writes any staged evicted rows out to the host
     pool) every `check_every` steps and after the last; in between, evicted rows
     reach the host pool only through the next step's own write-back. Gathered
-    rows are checked after every step.
+    rows are checked after every step. releases: optional {t: int32 addresses}
+    released after step t (engine and oracle), before step t+1's appends.
     """
     import torch
     tr = Trace(wl, steps)
@@ -80,9 +82,18 @@ def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, ch
                         bad = np.argwhere((got != ref).any(axis=-1))
                         raise AssertionError(f"group {g} step {t} layer {l}: gathered rows differ at "
                                              f"{len(bad)} rows, first {bad[:5].tolist()}")
+                if releases is not None and t in releases and releases[t].size:
+                    eng.release(g, releases[t])
+                    ora[g].release(releases[t])
+                    if t % check_every == 0:
+                        assert_same_state(eng.export_state(g), ora[g].export_state(),
+                                          f"group {g} after the release of step {t}")
         # stored rows of every entry, from whichever pool holds them (the host
         # pool after the last step's evicted rows are written out)
         known = np.concatenate([tr.initial_load_order()] + [tr.appends(t) for t in range(1, tr.steps + 1)])
+        if releases is not None:
+            gone = np.concatenate([np.zeros(0, np.int32)] + list(releases.values()))
+            known = np.setdiff1d(known, gone)
         rng = np.random.default_rng([tr.N, 11])
         probe = known if known.size <= 4096 else rng.choice(known, size=4096, replace=False)
         for g in groups:

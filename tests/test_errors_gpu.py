@@ -351,3 +351,31 @@ def test_lru_empty_padding_and_dirty_workspace():
                 assert np.array_equal(outs[l].cpu().numpy().reshape(flat.size, wl.row_bytes), want[:, l])
     finally:
         eng.close()
+
+
+def test_release_host_errors_change_nothing():
+    from serving_pb_lru_amd import UlaError
+    tr, eng, rows = _engine()
+    try:
+        before = _state(eng)
+        first = int(tr.initial_load_order()[0])
+        never = int(tr.appends(2)[0])
+        for bad, name in [([tr.N], "ERANGE"), ([-3], "ERANGE"), ([never], "ERANGE"), ([first, first], "EDUP")]:
+            with pytest.raises(UlaError) as e:
+                eng.release(0, np.array(bad, dtype=np.int32))
+            assert e.value.name == name
+        assert _state(eng) == before
+        # a valid release, then the same address again: not appended any more
+        eng.release(0, np.array([first], dtype=np.int32))
+        with pytest.raises(UlaError) as e:
+            eng.release(0, np.array([first], dtype=np.int32))
+        assert e.value.name == "ERANGE"
+        st = eng.export_state(0)
+        assert st["map"][first] == 0xFFFFFFFF
+        # appended again, it takes the slot it freed (the lowest free GPU slot)
+        eng.append(0, np.array([first], dtype=np.int32), rows(np.array([first], dtype=np.int32), 0))
+        assert eng.export_state(0)["map"][first] == 0
+        assert np.array_equal(eng.read_rows(0, np.array([first], np.int32)),
+                              rows_for(tr.wl.seed, 0, np.array([first]), tr.wl.layers, tr.wl.row_bytes))
+    finally:
+        eng.close()

@@ -47,7 +47,8 @@ def _compare(st: dict, ref: dict, where: str) -> None:
         assert tuple(st["stats"]) == tuple(ref["stats"]), f"{where}: stats {st['stats']} vs {ref['stats']}"
 
 
-def run_lru_parity(wl, steps=None, selections=None, check_every=1, max_append=4096, groups=None):
+def run_lru_parity(wl, steps=None, selections=None, check_every=1, max_append=4096, groups=None,
+                   releases=None):
     """Every group of one engine against its own oracle, steps interleaved group by group."""
     import torch
     from serving_pb_lru_amd.replay import engine_for, initial_load
@@ -84,7 +85,13 @@ def run_lru_parity(wl, steps=None, selections=None, check_every=1, max_append=40
                 for l in range(wl.layers):
                     got = outs[l].cpu().numpy().reshape(flat.size, wl.row_bytes)
                     assert np.array_equal(got, want[:, l]), f"group {g} step {t} layer {l}: gathered rows differ"
+                if releases is not None and t in releases and releases[t].size:
+                    eng.release(g, releases[t])
+                    lru[g].release(releases[t])
+                    _compare(eng.export_state(g), _lru_state(lru[g], tr.P), f"group {g} after release {t}")
         known = np.concatenate([tr.initial_load_order()] + [tr.appends(t) for t in range(1, tr.steps + 1)])
+        if releases is not None:
+            known = np.setdiff1d(known, np.concatenate([np.zeros(0, np.int32)] + list(releases.values())))
         for g in groups:
             assert np.array_equal(eng.read_rows(g, known), rows_for(wl.seed, g, known, wl.layers, wl.row_bytes))
         return lru[groups[0]]
@@ -154,3 +161,14 @@ def test_lru_equals_long_ring_pblru_on_gpu():
     finally:
         for e in engs:
             e.close()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_lru_release_random(seed):
+    """Released entries' slots become free: exact LRU takes freed GPU slots first
+    (ascending), and a slot appended after its release counts as never stamped."""
+    from tracegen import release_plan
+    wl = tiny_workload(seed, steps=10)
+    tr = Trace(wl)
+    sels = padded_selections(tr, 0, seed)
+    run_lru_parity(wl, selections=sels, max_append=7, releases=release_plan(tr, sels, seed, frac=0.4))

@@ -117,3 +117,32 @@ def test_pool_holds_everything_parity():
     tr = Trace(wl)
     wl = dataclasses.replace(wl, pool_slots=tr.N)
     run_parity(wl)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_release_parity_random(seed):
+    """Finished entries released between steps (their GPU slots join the free set,
+    their host slots the free host set); later misses take the freed GPU slots first
+    and appends reuse freed slots. State and gathered bytes match the oracle."""
+    from tracegen import release_plan
+    wl = tiny_workload(seed, steps=10)
+    tr = Trace(wl)
+    sels = padded_selections(tr, 0, seed)
+    ora = run_parity(wl, selections={0: sels}, max_append=7, check_every=1 if seed % 2 else 3,
+                     releases=release_plan(tr, sels, seed, frac=0.4))
+    assert ora[0].flag == tr.steps
+
+
+@pytest.mark.parametrize("name,factor,steps", [
+    ("r16_64k_g1x3", 16, 8),
+    ("evict_r256_128k_g2", 32, 6),
+])
+def test_release_parity_scaled(name, factor, steps):
+    from tracegen import release_plan
+    wl = scaled(preset(name), factor)
+    tr = Trace(wl, steps)
+    sels = {g: list(tr.selections(g)) for g in range(wl.groups)}
+    # one release plan for every group: addresses no group's later steps select
+    merged = [np.concatenate([sels[g][t].reshape(-1) for g in sels]) for t in range(steps)]
+    plan = release_plan(tr, merged, 7, frac=0.3)
+    run_parity(wl, steps=steps, selections=sels, max_append=1 << 15, check_every=2, releases=plan)
