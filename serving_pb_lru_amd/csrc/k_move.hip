@@ -40,9 +40,12 @@ __global__ __launch_bounds__(256) void k_place(GroupDev g, int32_t n, const uint
 // the next step's mark launch (or a stand-alone write-back before the host
 // reads state) writes them to the host slot the miss vacated. Each pair is also
 // committed (commit_pair): beside its first piece when one round of the data
-// loop covers every piece, else one lane per pair after the loop. Every
-// workgroup then releases its writes and takes a ticket; the last one raises the
-// completion counter.
+// loop covers every piece, else one lane per pair after the loop. The
+// completion counter is raised by k_publish, launched right after on the same
+// stream: the kernel boundary makes every workgroup's writes visible first. (A
+// release fence and a ticket in every workgroup, so that the last one could
+// raise it, wrote each compute die's L2 back once per workgroup and cost about a
+// third of this kernel.)
 // Commit of pair i: mapping table, owners, the step's resolved selection, and
 // the staging record of the host slot; a victim that was free releases its host
 // slot instead (counted in `freed`).
@@ -134,19 +137,14 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
   }
   if (freed) atomicAdd(&s_freed, freed);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    if (s_freed) atomicAdd(&g.ctr->hfree, s_freed);
-    // The barrier ordered the workgroup's writes before this thread; one
-    // release per workgroup publishes them (a fence per thread would write the
-    // cache back once per thread). The ticket is acquire-release, so the last
-    // workgroup's release of the counter covers every workgroup's writes.
-    __threadfence();
-    const int ticket = __hip_atomic_fetch_add(&g.ctr->done, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (ticket == (int)gridDim.x - 1) {
-      g.ctr->done = 0;
-      __hip_atomic_store(&g.ctr->flag, (long long)t, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  if (threadIdx.x == 0 && s_freed) atomicAdd(&g.ctr->hfree, s_freed);
+}
+
+// The step's signal (section 3: readers wait for it): completion counter = t,
+// unless an error was latched, in which case the step did not take effect.
+__global__ __launch_bounds__(64) void k_publish(GroupDev g, uint32_t t) {
+  if (threadIdx.x == 0 && !status_of(g.ctr))
+    __hip_atomic_store(&g.ctr->flag, (long long)t, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Stand-alone write-back of whatever rows the last swap staged, for when the
@@ -232,10 +230,11 @@ static int grid_for_pairs(int32_t max_pairs, uint32_t chunks, int threads, int c
 }
 
 hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s) {
-  // At most 128 workgroups: HBM-to-HBM copies need no more to reach full
-  // bandwidth, and each workgroup costs one ticket on the completion counter.
+  // At most 256 workgroups (one per compute unit): one round of the data loop
+  // then covers about 1000 three-layer pairs, so those steps commit beside it.
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
-  k_swap_commit<<<grid_for_pairs(max_pairs, chunks, 512, 128), 512, 0, s>>>(g, t, FastDiv(chunks));
+  k_swap_commit<<<grid_for_pairs(max_pairs, chunks, 512, 256), 512, 0, s>>>(g, t, FastDiv(chunks));
+  k_publish<<<1, 64, 0, s>>>(g, t);
   return hipGetLastError();
 }
 

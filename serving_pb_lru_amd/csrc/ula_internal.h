@@ -57,7 +57,7 @@ __host__ __device__ constexpr int ring_id(int b) { return 2 + b; }
 
 struct alignas(64) Counters {
   int32_t status;        // first latched device error of the group, 0 = none
-  int32_t done;          // ticket of the commit kernel's last-block signal
+  int32_t pad0;          // keeps flag 8-byte aligned
   long long flag;        // completion counter: last completed step
   long long stats[6];    // unique, hits, misses, evictions, from_free, invalid
   int32_t n_unique, n_hits, n_miss, n_invalid;
