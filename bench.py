@@ -79,6 +79,9 @@ def parse():
                         "synthetic compute per layer, and print its own JSON line")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run 5 plain device-to-device copies of MIB MiB (counter calibration) and exit")
+    p.add_argument("--copy-ceiling", type=int, default=0, metavar="BYTES",
+                   help="only run plain device-to-device copies moving BYTES each (half read, half "
+                        "written), from buffers larger than the memory-side cache, and exit")
     return p.parse_args()
 
 
@@ -93,6 +96,33 @@ def calibrate_copy(mib: int) -> None:
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"calibration_copy_bytes": mib << 20, "copies": 5}), flush=True)
+
+
+def copy_ceiling(nbytes: int, copies: int = 64) -> None:
+    """Plain device-to-device copies moving `nbytes` per copy (half read, half
+    written: the algorithmic bytes of one gather launch), rotating over slices
+    of buffers larger than the memory-side cache so that every copy reads from
+    HBM, as the gathers do. Run under rocprofv3 --kernel-trace --stats for the
+    copy kernel's duration: the practical HBM rate at the gather's size."""
+    import torch
+    torch.cuda.set_device(0)
+    half = nbytes // 2
+    slices = max(4, -(-(1 << 30) // half))   # more than 1 GiB in each buffer
+    src = torch.empty(slices * half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.fill_(0)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(copies):
+        j = (i % slices) * half
+        dst[j:j + half].copy_(src[j:j + half])
+    b.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_ceiling_bytes_per_copy": 2 * half, "copies": copies, "slices": slices,
+                      "batch_ms_per_copy_incl_launch_gaps": round(a.elapsed_time(b) / copies, 5)}),
+          flush=True)
 
 
 def gather_traffic(workload: str):
@@ -420,6 +450,9 @@ def main():
     args = parse()
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.copy_ceiling:
+        copy_ceiling(args.copy_ceiling)
         return
     if args.layer_prefetch:
         wl = preset(args.workload)

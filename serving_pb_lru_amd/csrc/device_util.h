@@ -95,13 +95,11 @@ __device__ __forceinline__ int32_t* bucket_count(const GroupDev& g, int id) {
   return id == kHostFreeId ? &g.ctr->hfree : &g.ctr->bcnt[id];
 }
 
-// Piece c of appended entry i: copy 16 bytes of its rows to the destination
-// chosen for it (app_dst: a GPU slot, or a host slot with the host bit); the
-// lane of piece 0 also publishes the mapping and owner entries of `la`.
-__device__ __forceinline__ void place_piece(const GroupDev& g, uint32_t i, uint32_t c, int32_t la,
-                                            const uint8_t* __restrict__ rows) {
-  const uint32_t d = g.app_dst[i];
-  const vec4u v = reinterpret_cast<const vec4u*>(rows + (size_t)i * g.slot_bytes)[c];
+// Piece c (16 bytes, value v) of appended entry `la` goes to the destination
+// chosen for it (d: a GPU slot, or a host slot with the host bit); the lane of
+// piece 0 also publishes the mapping and owner entries of `la`.
+__device__ __forceinline__ void place_piece(const GroupDev& g, uint32_t d, uint32_t c, int32_t la,
+                                            const vec4u v) {
   uint8_t* dst = (d & kHostBit) ? g.host + (size_t)(d & ~kHostBit) * g.slot_bytes
                                 : g.pool + (size_t)d * g.slot_bytes;
   reinterpret_cast<vec4u*>(dst)[c] = v;

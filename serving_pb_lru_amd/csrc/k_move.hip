@@ -30,7 +30,8 @@ __global__ __launch_bounds__(256) void k_place(GroupDev g, int32_t n, const uint
        idx += gridDim.x * blockDim.x) {
     const uint32_t i = per_slot.div(idx);
     const uint32_t c = idx - i * chunks;
-    place_piece(g, i, c, c == 0 ? g.app_la[i] : 0, rows);
+    const vec4u v = reinterpret_cast<const vec4u*>(rows + (size_t)i * g.slot_bytes)[c];
+    place_piece(g, g.app_dst[i], c, c == 0 ? g.app_la[i] : 0, v);
   }
 }
 
@@ -141,10 +142,13 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
 }
 
 // The step's signal (section 3: readers wait for it): completion counter = t,
-// unless an error was latched, in which case the step did not take effect.
+// unless an error was latched, in which case the step did not take effect. The
+// store needs no release of its own: the swap's writes were made visible at
+// the end of its kernel, before this one started, and this kernel's end makes
+// the counter visible to other streams and the host.
 __global__ __launch_bounds__(64) void k_publish(GroupDev g, uint32_t t) {
   if (threadIdx.x == 0 && !status_of(g.ctr))
-    __hip_atomic_store(&g.ctr->flag, (long long)t, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&g.ctr->flag, (long long)t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Stand-alone write-back of whatever rows the last swap staged, for when the

@@ -43,9 +43,13 @@ namespace ula {
 // Selection plan (one 1024-thread workgroup). STEP mode: m = misses of the
 // step, sources in eviction order, destination ring[cur]. APPEND mode: m = n,
 // sources [free, free host slots]: the first min(n, free GPU slots) entries take
-// free GPU slots (joining cold), the rest free host slots.
-__device__ void plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
-                          unsigned long long* s_nonempty) {
+// free GPU slots (joining cold), the rest free host slots. Work items go to
+// `items`; returns their number (in every thread). pre_avail / pre_hint
+// (nullable, LDS): the order's bucket counts and the free sets' span hints
+// (GPU, host), already loaded by the caller.
+__device__ int plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
+                         unsigned long long* s_nonempty, SelItem* items,
+                         const int* pre_avail = nullptr, const int* pre_hint = nullptr) {
   Counters* c = g.ctr;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -65,15 +69,16 @@ __device__ void plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
   int q_free = 0;
   for (int j = 0; j < a.norder && off < m; ++j) {
     const int id = a.order[j];
-    const int avail = *bucket_count(g, id);
+    const int avail = pre_avail ? pre_avail[j] : *bucket_count(g, id);
     const int q = min(m - off, avail);
     if (q <= 0) continue;
     const uint32_t* tc = bucket_tcnt(g, id);
     const int T = bucket_ntiles(g, id);
     // the free sets start at their hint: every span before it is empty
     int32_t* hint = id == kFree ? &c->free_lo : (id == kHostFreeId ? &c->hfree_lo : nullptr);
+    const int start = hint ? (pre_hint ? pre_hint[id == kFree ? 0 : 1] : *hint) : 0;
     int pre = 0;   // set bits of this bucket in spans before the chunk
-    for (int base = hint ? min(max(*hint, 0), T) : 0; base < T && pre < q; base += 1024) {
+    for (int base = min(max(start, 0), T); base < T && pre < q; base += 1024) {
       const int tile = base + tid;
       const int cnt = tile < T ? (int)tc[tile] : 0;
       const unsigned long long ne = __ballot(cnt > 0);
@@ -93,7 +98,7 @@ __device__ void plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
         it.tile = tile;
         it.out_off = off + pre + ex;
         it.take = min(cnt, q - pre - ex);
-        g.items[nitems + rank] = it;
+        items[nitems + rank] = it;
         // the span where the quota is reached: everything before it is taken
         if (hint && pre + ex + cnt >= q) *hint = tile;
       }
@@ -114,13 +119,14 @@ __device__ void plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
       c->bcnt[a.dest] += q_free;
     }
   }
+  return nitems;
 }
 
 __global__ __launch_bounds__(1024) void k_plan(GroupDev g, PlanArgs a) {
   __shared__ int scratch[1024 / kWave + 1];
   __shared__ unsigned long long s_nonempty[1024 / kWave];  // level-2 summary of a 1024-span chunk
   if (block_failed(g.ctr)) return;
-  plan_body(g, a, scratch, s_nonempty);
+  plan_body(g, a, scratch, s_nonempty, g.items);
 }
 
 // One wavefront takes the lowest `take` set bits of one span of one bitmap.
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t c
   }
   __syncthreads();
   if (!s_last) return;
-  plan_body(g, a, scratch, s_nonempty);
+  plan_body(g, a, scratch, s_nonempty, g.items);
   // publish the plan (items, counts) to the extraction workgroups, then join them
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -346,14 +352,39 @@ __global__ __launch_bounds__(256) void k_extract(GroupDev g, int32_t mode, int32
 }
 
 // A small append in one workgroup: plan, extraction and placement back to back
-// (the same steps as the plan / extract / place kernels), with the addresses
-// passed by value so that no copy precedes the launch.
+// (the same steps as the plan / extract / place kernels) with the work items and
+// destinations in LDS, the addresses passed by value so that no copy precedes
+// the launch, and the counters, span hints and first pieces of the rows loaded
+// together before the plan: the chain of dependent memory accesses is the
+// span counts, the bitmap words, then the stores.
 __global__ __launch_bounds__(1024) void k_append_small(GroupDev g, SmallAppend a,
                                                        const uint8_t* __restrict__ rows,
                                                        FastDiv per_slot) {
   __shared__ int scratch[1024 / kWave + 1];
   __shared__ unsigned long long s_nonempty[1024 / kWave];
-  if (block_failed(g.ctr)) return;
+  __shared__ SelItem s_items[kSmallAppend];   // each item takes at least one entry
+  __shared__ uint32_t s_dst[kSmallAppend];
+  __shared__ int s_status, s_avail[2], s_hint[2];
+  const int tid = threadIdx.x;
+  if (tid == 0) s_status = status_of(g.ctr);
+  else if (tid == kWave) s_avail[0] = g.ctr->bcnt[kFree];
+  else if (tid == 2 * kWave) s_avail[1] = g.ctr->hfree;
+  else if (tid == 3 * kWave) s_hint[0] = g.ctr->free_lo;
+  else if (tid == 4 * kWave) s_hint[1] = g.ctr->hfree_lo;
+  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
+  const uint32_t total = (uint32_t)a.n * chunks;
+  constexpr int kEarly = 2;   // pieces per lane loaded before the plan
+  vec4u early[kEarly];
+#pragma unroll
+  for (int r = 0; r < kEarly; ++r) {
+    const uint32_t idx = (uint32_t)tid + (uint32_t)r * 1024u;
+    if (idx < total) {
+      const uint32_t i = per_slot.div(idx);
+      early[r] = reinterpret_cast<const vec4u*>(rows + (size_t)i * g.slot_bytes)[idx - i * chunks];
+    }
+  }
+  __syncthreads();
+  if (s_status) return;
   PlanArgs p{};
   p.mode = kPlanAppend;
   p.n = a.n;
@@ -361,17 +392,22 @@ __global__ __launch_bounds__(1024) void k_append_small(GroupDev g, SmallAppend a
   p.dest = kCold;
   p.order[0] = kFree;
   p.order[1] = kHostFreeId;
-  plan_body(g, p, scratch, s_nonempty);
+  const int nitems = plan_body(g, p, scratch, s_nonempty, s_items, s_avail, s_hint);
+  for (int i = tid / kWave; i < nitems; i += blockDim.x / kWave)
+    extract_item(g, s_items[i], kPlanAppend, kCold, s_dst);
   __syncthreads();
-  const int nitems = g.ctr->n_items;
-  for (int i = threadIdx.x / kWave; i < nitems; i += blockDim.x / kWave)
-    extract_item(g, g.items[i], kPlanAppend, kCold, g.app_dst);
-  __syncthreads();
-  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
-  const uint32_t total = (uint32_t)a.n * chunks;
-  for (uint32_t idx = threadIdx.x; idx < total; idx += blockDim.x) {
+#pragma unroll
+  for (int r = 0; r < kEarly; ++r) {
+    const uint32_t idx = (uint32_t)tid + (uint32_t)r * 1024u;
+    if (idx < total) {
+      const uint32_t i = per_slot.div(idx);
+      place_piece(g, s_dst[i], idx - i * chunks, a.las[i], early[r]);
+    }
+  }
+  for (uint32_t idx = (uint32_t)tid + kEarly * 1024u; idx < total; idx += blockDim.x) {
     const uint32_t i = per_slot.div(idx);
-    place_piece(g, i, idx - i * chunks, a.las[i], rows);
+    const uint32_t c = idx - i * chunks;
+    place_piece(g, s_dst[i], c, a.las[i], reinterpret_cast<const vec4u*>(rows + (size_t)i * g.slot_bytes)[c]);
   }
 }
 

@@ -200,6 +200,53 @@ def test_gather_on_second_stream_ordered_by_event():
         eng.close()
 
 
+def test_gather_on_second_stream_ordered_by_counter_wait():
+    """The other ordering the boundary offers: a second stream waits on the
+    group's completion counter (hipStreamWaitValue64 on ula_flag_address) until it
+    reaches the step, then gathers. The first step checks, with the device idle,
+    that the counter reaches its step number, so the wait of the second step
+    (same kernels, valid inputs) is known to end."""
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch has already loaded
+    hip.hipStreamWaitValue64.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                         ctypes.c_uint, ctypes.c_uint64]
+    hip.hipStreamWaitValue64.restype = ctypes.c_int
+    wait_gte = 0x0
+    tr, eng, rows = _engine()
+    wl = tr.wl
+    try:
+        sels = tr.selections(0)
+        sel = next(sels)
+        app = tr.appends(1)
+        eng.append(0, app, rows(app, 0))
+        eng.step(0, _cuda(sel))
+        eng.sync()
+        assert eng.export_state(0)["flag"] == 1
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        busy = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        sel = next(sels)
+        d = _cuda(sel)
+        app = tr.appends(2)
+        app_rows = rows(app, 0)
+        torch.cuda.synchronize()
+        busy.fill_(3)                              # keeps the main stream busy for a while
+        eng.append(0, app, app_rows)
+        eng.step(0, d)
+        rc = hip.hipStreamWaitValue64(ctypes.c_void_p(side.cuda_stream), ctypes.c_void_p(eng.flag_address(0)),
+                                      2, wait_gte, 0xFFFFFFFFFFFFFFFF)
+        assert rc == 0, rc
+        out = eng.gather(0, 0, d, stream=side)
+        torch.cuda.synchronize()
+        eng.sync()
+        want = rows_for(wl.seed, 0, sel.reshape(-1), wl.layers, wl.row_bytes)[:, 0]
+        assert np.array_equal(out.cpu().numpy().reshape(-1, wl.row_bytes), want)
+        assert eng.export_state(0)["flag"] == 2
+    finally:
+        eng.close()
+
+
 def test_unordered_gather_is_correct_or_refused():
     """A gather issued on another stream without ordering either runs after
     the step completed (correct rows) or sees the completion counter behind and
