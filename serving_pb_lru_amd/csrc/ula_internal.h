@@ -202,13 +202,13 @@ hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipSt
 hipError_t launch_release(const GroupDev& g, int32_t n, hipStream_t s);
 hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s);
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s);
-// start / stop (both or neither): events recorded by the dispatch itself, so
-// that their interval is the kernel's execution
 // exact-LRU victim selection (k_lru.hip)
 hipError_t launch_lru_select(const GroupDev& g, uint32_t t, int32_t max_pairs, int32_t wb_pairs,
                              hipStream_t s);
 hipError_t launch_lru_order(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s);
 
+// start / stop (both or neither): events recorded by the dispatch itself, so
+// that their interval is the kernel's execution
 hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
                          uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop);

@@ -76,13 +76,16 @@ def test_tiny_hit_rate_within_a_tenth_of_a_point():
 
 @pytest.mark.slow
 def test_tiny_hit_rate_spread_over_seeds():
-    """The PB-LRU - LRU hit-rate gap stays within the pages' 0.1 point on 20 seeds."""
+    """The PB-LRU - LRU hit-rate gap stays within the pages' 0.1 point on seeds
+    0-99 of the tiny workload (largest gap measured: 0.061 pp)."""
     gaps = []
-    for seed in range(20):
+    for seed in range(100):
         pb, lru = _hit_rates(dataclasses.replace(preset("tiny_4x4k"), seed=seed))
         gaps.append((pb - lru) * 100)
-    print("PB-LRU minus exact-LRU hit rate (pp) over seeds 0-19:", np.round(gaps, 3))
-    assert max(abs(g) for g in gaps) <= 0.1
+    g = np.array(gaps)
+    print(f"PB-LRU minus exact-LRU hit rate (pp) over seeds 0-99: mean {g.mean():.4f}, "
+          f"max |gap| {np.abs(g).max():.3f}, median |gap| {np.median(np.abs(g)):.3f}")
+    assert np.abs(g).max() <= 0.1
 
 
 def _lru_pair(trace, sels):
