@@ -70,10 +70,21 @@ def test_random_tiny_parity(seed):
     run_parity(wl, selections={0: padded_selections(tr, 0, seed)}, max_append=7)
 
 
-@pytest.mark.parametrize("ring", [1, 2, 9])
+@pytest.mark.parametrize("ring", [1, 2, 9, 64])   # 64: the longest ring the engine takes
 def test_ring_lengths_parity(ring):
     wl = dataclasses.replace(preset("tiny_4x4k"), ring=ring, name=f"tiny_ring{ring}")
     run_parity(wl)
+
+
+@pytest.mark.parametrize("row_bytes,layers", [(16, 1), (16, 3), (1024, 2)])
+def test_row_sizes_parity(row_bytes, layers):
+    """The smallest row (one 16-byte piece), a three-layer slot of such rows, and the
+    largest row the synthetic generator makes (64 pieces): the gather, swap, prefetch,
+    write-back and append loops with unusual piece counts per row and per slot."""
+    base = tiny_workload(5)
+    wl = dataclasses.replace(base, row_bytes=row_bytes, layers=layers, name=f"rows{row_bytes}x{layers}")
+    tr = Trace(wl)
+    run_parity(wl, selections={0: padded_selections(tr, 0, 5)}, max_append=7)
 
 
 @pytest.mark.parametrize("name,factor,steps,check_every", [
