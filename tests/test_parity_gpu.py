@@ -103,6 +103,17 @@ def test_scaled_workload_parity(name, factor, steps, check_every):
     run_parity(wl, steps=steps, groups=groups, max_append=1 << 15, check_every=check_every)
 
 
+def test_large_gather_ragged_parity():
+    """A selection of 70,001 entries: the large-gather tiling (above 65,536 rows) with a
+    partial last block, and a lookup with a partial last workgroup, against the oracle."""
+    from synth.configs import Workload
+    wl = Workload(name="ragged70001", requests=1, ctx_fixed=200_000, ctx_range=None, sets_per_request=1,
+                  draft_keep=0.0, groups=1, layers=2, k=70_001, pool_frac=0.0, pool_slots=100_000, ring=4,
+                  steps=3, appends=1, overlap=0.85, p_recent=0.7, window=4096, row_bytes=64, seed=9)
+    ora = run_parity(wl, max_append=1 << 12)
+    assert ora[0].last.misses > 0
+
+
 def _pingpong():
     """One request of 64 positions, a pool of 8 slots, 2 ring buckets and k = 8:
     alternating disjoint sets miss every entry and evict the previous set, so
