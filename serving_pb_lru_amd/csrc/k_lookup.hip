@@ -33,7 +33,9 @@ __device__ __forceinline__ unsigned long long dedup_key(uint32_t t, uint32_t e) 
 
 __global__ __launch_bounds__(256) void k_tag(GroupDev g, const int32_t* __restrict__ sel,
                                              int32_t n, uint32_t t) {
-  if (status_of(g.ctr)) return;
+  // No error check up front: this kernel writes only scratch (tags, this
+  // step's look-back descriptors, the padding count), and a latched error
+  // stops the compaction, which is where the step's results are written.
   // the compaction of this step uses the descriptors of parity t & 1, last used
   // two steps ago
   unsigned long long* desc = g.desc + (size_t)(t & 1u) * g.maxBlk;
@@ -75,16 +77,20 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
                                                         int32_t n, uint32_t t, int32_t nblk) {
   constexpr int NW = kScanBlock / kWave;
   __shared__ int s_h[NW], s_m[NW];
-  __shared__ int s_vid, s_fail;
+  __shared__ int s_vid, s_fail, s_status;
   __shared__ uint32_t s_eh, s_em;
-  if (block_failed(g.ctr)) return;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
+  // the error status and the ticket in one round trip (a workgroup that then
+  // stops has taken a ticket; the step has failed, so the order no longer matters)
   if (threadIdx.x == 0) {
-    s_vid = atomicAdd(&g.ctr->lb_ticket, 1);
+    s_status = status_of(g.ctr);
     s_fail = 0;
+  } else if (threadIdx.x == kWave) {
+    s_vid = atomicAdd(&g.ctr->lb_ticket, 1);
   }
   __syncthreads();
+  if (s_status) return;
   const int vid = s_vid;
   if (vid < 0 || vid >= nblk) {            // a corrupt ticket: never index with it
     if (threadIdx.x == 0) latch(g.ctr, ULA_ESTATE);
@@ -97,6 +103,7 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
   int c = 0;
   int32_t la = -1;
   uint32_t loc = 0;
+  unsigned long long stage_rec = ~0ull;
   if (e < n) {
     la = sel[e];
     if (la == -1) {
@@ -108,6 +115,8 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
       if (key == dedup_key(t, (uint32_t)e)) {
         c = (loc & kHostBit) ? 2 : 1;
         g.res[e] = make_uint2((uint32_t)la, c == 1 ? loc : kAbsent);   // a miss's slot comes at commit
+        // a miss's staging record, loaded now so that it arrives during the look-back
+        if (c == 2) stage_rec = g.hs_stage[loc & ~kHostBit];
       } else {
         // a repeat: a hit resolves to its slot, a missed entry to its first occurrence
         const uint32_t first = ~(uint32_t)key;
@@ -215,7 +224,7 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
       g.miss_e[pos] = e;
       // a row evicted by the previous step may still be on its way to the host:
       // read it from its staging copy instead
-      const unsigned long long st = g.hs_stage[h];
+      const unsigned long long st = stage_rec;
       uint32_t from = kAbsent;
       if ((uint32_t)(st >> 32) == t - 1u) {
         from = (uint32_t)st;

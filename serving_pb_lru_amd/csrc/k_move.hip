@@ -75,11 +75,17 @@ __device__ __forceinline__ void commit_pair(const GroupDev& g, uint32_t t, int i
 }
 
 __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, FastDiv per_slot) {
-  __shared__ int s_freed;
-  if (block_failed(g.ctr)) return;
-  if (threadIdx.x == 0) s_freed = 0;
+  __shared__ int s_freed, s_status, s_m;
+  // the error status and the pair count in one round trip
+  if (threadIdx.x == 0) {
+    s_status = status_of(g.ctr);
+    s_freed = 0;
+  } else if (threadIdx.x == kWave) {
+    s_m = g.ctr->n_miss;
+  }
   __syncthreads();
-  const int m = g.ctr->n_miss;
+  if (s_status) return;
+  const int m = s_m;
   uint8_t* stage = g.evict_rows;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     g.ctr->wb_n = m;

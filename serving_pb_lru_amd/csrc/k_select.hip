@@ -203,15 +203,19 @@ __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t c
                                                FastDiv per_slot, int32_t pf, int32_t wbb, int32_t nh,
                                                uint32_t wb_step) {
   __shared__ int s_delta[kMaxBuckets];
-  __shared__ int s_last, s_role, s_fail;
+  __shared__ int s_last, s_role, s_fail, s_status;
   __shared__ int scratch[1024 / kWave + 1];
   __shared__ unsigned long long s_nonempty[1024 / kWave];
-  if (block_failed(g.ctr)) return;
+  // the error status and the role ticket in one round trip (a workgroup that
+  // then stops has taken a role; the step has failed, so no role is waited for)
   if (threadIdx.x == 0) {
-    s_role = atomicAdd(&g.ctr->mark_role, 1);
+    s_status = status_of(g.ctr);
     s_fail = 0;
+  } else if (threadIdx.x == kWave) {
+    s_role = atomicAdd(&g.ctr->mark_role, 1);
   }
   __syncthreads();
+  if (s_status) return;
   const int role = s_role;
   if (role < 0 || role >= (int)gridDim.x) {   // a corrupt ticket: never index with it
     if (threadIdx.x == 0) latch(g.ctr, ULA_ESTATE);
