@@ -140,18 +140,25 @@ __global__ __launch_bounds__(kLruThreads) void k_lru_pass(GroupDev g, uint32_t t
                                                    FastDiv per_slot, int32_t pf, int32_t wbb,
                                                    uint32_t wb_step) {
   __shared__ uint32_t s_hist[kLruBins];
-  __shared__ int s_free, s_last;
+  __shared__ int s_free, s_last, s_status, s_nmiss, s_wbn;
+  __shared__ uint32_t s_wbstep;
   __shared__ int scratch[kLruThreads / kWave + 1];
-  if (block_failed(g.ctr)) return;
+  // the error status and the counts every role needs, in one round trip
+  if (threadIdx.x == 0) s_status = status_of(g.ctr);
+  else if (threadIdx.x == kWave) s_nmiss = g.ctr->n_miss;
+  else if (threadIdx.x == 2 * kWave) s_wbstep = g.ctr->wb_step;
+  else if (threadIdx.x == 3 * kWave) s_wbn = g.ctr->wb_n;
+  __syncthreads();
+  if (s_status) return;
   if ((int)blockIdx.x >= nsel + pf) {
-    writeback_rows(g, wb_step, per_slot, blockIdx.x - nsel - pf, wbb);
+    writeback_rows(g, s_wbstep, s_wbn, wb_step, per_slot, blockIdx.x - nsel - pf, wbb);
     return;
   }
   if ((int)blockIdx.x >= nsel) {
-    prefetch_misses(g, per_slot, blockIdx.x - nsel, pf);
+    prefetch_misses(g, s_nmiss, per_slot, blockIdx.x - nsel, pf);
     return;
   }
-  if (g.ctr->n_miss == 0) return;   // no victims to choose (uniform over the launch)
+  if (s_nmiss == 0) return;   // no victims to choose (uniform over the launch)
   const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
   const int bits = pass == 2 ? 10 : 11;
   const int nbins = 1 << bits;

@@ -170,7 +170,8 @@ __global__ __launch_bounds__(64) void k_publish(GroupDev g, uint32_t t) {
 // slots meanwhile.
 __global__ __launch_bounds__(256) void k_writeback(GroupDev g, FastDiv per_slot) {
   const uint32_t t = g.ctr->wb_step;
-  if (t != 0) writeback_rows(g, t, per_slot, blockIdx.x, gridDim.x);
+  const int n = g.ctr->wb_n;
+  if (t != 0) writeback_rows(g, t, n, t, per_slot, blockIdx.x, gridDim.x);
 }
 
 // Release of finished entries (app_la[0..n), validated on the host): a GPU slot

@@ -203,16 +203,24 @@ __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t c
                                                FastDiv per_slot, int32_t pf, int32_t wbb, int32_t nh,
                                                uint32_t wb_step) {
   __shared__ int s_delta[kMaxBuckets];
-  __shared__ int s_last, s_role, s_fail, s_status;
+  __shared__ int s_last, s_role, s_fail, s_status, s_nmiss, s_wbn;
+  __shared__ uint32_t s_wbstep;
   __shared__ int scratch[1024 / kWave + 1];
   __shared__ unsigned long long s_nonempty[1024 / kWave];
-  // the error status and the role ticket in one round trip (a workgroup that
-  // then stops has taken a role; the step has failed, so no role is waited for)
+  // the error status, the role ticket and the link roles' counts in one round
+  // trip (a workgroup that then stops has taken a role; the step has failed, so
+  // no role is waited for)
   if (threadIdx.x == 0) {
     s_status = status_of(g.ctr);
     s_fail = 0;
   } else if (threadIdx.x == kWave) {
     s_role = atomicAdd(&g.ctr->mark_role, 1);
+  } else if (threadIdx.x == 2 * kWave) {
+    s_nmiss = g.ctr->n_miss;
+  } else if (threadIdx.x == 3 * kWave) {
+    s_wbstep = g.ctr->wb_step;
+  } else if (threadIdx.x == 4 * kWave) {
+    s_wbn = g.ctr->wb_n;
   }
   __syncthreads();
   if (s_status) return;
@@ -239,11 +247,11 @@ __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t c
     return;
   }
   if (role >= kMarkBlocks + pf) {
-    writeback_rows(g, wb_step, per_slot, role - kMarkBlocks - pf, wbb);
+    writeback_rows(g, s_wbstep, s_wbn, wb_step, per_slot, role - kMarkBlocks - pf, wbb);
     return;
   }
   if (role >= kMarkBlocks) {
-    prefetch_misses(g, per_slot, role - kMarkBlocks, pf);
+    prefetch_misses(g, s_nmiss, per_slot, role - kMarkBlocks, pf);
     return;
   }
   for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x) s_delta[i] = 0;

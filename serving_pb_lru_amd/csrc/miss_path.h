@@ -19,11 +19,11 @@
 namespace ula {
 
 // Missed rows of step t (all layers, one contiguous slot_bytes run each) into
-// miss_rows[i], from the host pool or from the staging copy of step t - 1.
+// miss_rows[i], from the host pool or from the staging copy of step t - 1. m is
+// the step's miss count (the caller loads it with its other first loads).
 // Workgroup `part` of `nparts`, blockDim.x threads each.
-__device__ __forceinline__ void prefetch_misses(const GroupDev& g, FastDiv per_slot, int part,
+__device__ __forceinline__ void prefetch_misses(const GroupDev& g, int m, FastDiv per_slot, int part,
                                                 int nparts) {
-  const int m = g.ctr->n_miss;
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
   const uint32_t total = (uint32_t)m * chunks;
   const uint32_t stride = (uint32_t)nparts * blockDim.x;
@@ -52,13 +52,15 @@ __device__ __forceinline__ void prefetch_misses(const GroupDev& g, FastDiv per_s
 }
 
 // The rows staged by the swap of step `t` go to the host slots their misses
-// vacated (wb_h; absent for a victim that was free). Does nothing unless the
-// staging buffer holds step t's rows.
-__device__ __forceinline__ void writeback_rows(const GroupDev& g, uint32_t t, FastDiv per_slot,
-                                               int part, int nparts) {
-  if (g.ctr->wb_step != t) return;
+// vacated (wb_h; absent for a victim that was free). staged_step and staged_n
+// are the counter block's record of what the staging buffer holds (the caller
+// loads them with its other first loads); nothing happens unless it holds
+// step t's rows.
+__device__ __forceinline__ void writeback_rows(const GroupDev& g, uint32_t staged_step, int staged_n,
+                                               uint32_t t, FastDiv per_slot, int part, int nparts) {
+  if (staged_step != t) return;
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
-  const uint32_t total = (uint32_t)g.ctr->wb_n * chunks;
+  const uint32_t total = (uint32_t)staged_n * chunks;
   const uint32_t stride = (uint32_t)nparts * blockDim.x;
   constexpr int U = 4;
   for (uint32_t base = (uint32_t)part * blockDim.x + threadIdx.x; base < total; base += U * stride) {
