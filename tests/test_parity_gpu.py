@@ -114,6 +114,79 @@ def test_large_gather_ragged_parity():
     assert ora[0].last.misses > 0
 
 
+@pytest.mark.parametrize("policy", [0, 1], ids=["pblru", "lru"])
+def test_groups_on_separate_streams(policy):
+    """Layer groups are independent and may be driven on different streams: each
+    group's appends, steps and gathers go to a stream of its own, interleaved with
+    no synchronisation between the groups; every group matches its own oracle
+    (every gathered byte of every step, and the state after the last step)."""
+    import torch
+    from oracle.exact_lru_np import ExactLRUArrays
+    from oracle.replay import initial_load as oracle_load, new_group
+    from serving_pb_lru_amd.replay import engine_for, initial_load
+    from synth.device import rows_device
+    wl = scaled(preset("spec3_r128_64k128k_g4"), 32)
+    tr = Trace(wl, 6)
+    G = wl.groups
+    say(f"separate streams {wl.name} policy {policy}: groups={G} steps={tr.steps}")
+    eng = engine_for(tr, max_append=1 << 15, policy=policy)
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    try:
+        initial_load(eng, tr, range(G), rows)
+        sels = {g: list(tr.selections(g)) for g in range(G)}
+        dsel = {g: [torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda() for x in sels[g]]
+                for g in range(G)}
+        app_rows = {(g, t): rows(tr.appends(t), g) for g in range(G) for t in range(1, tr.steps + 1)
+                    if tr.appends(t).size}
+        torch.cuda.synchronize()
+        streams = [torch.cuda.Stream() for _ in range(G)]
+        outs = {}
+        for t in range(1, tr.steps + 1):
+            app = tr.appends(t)
+            for g in range(G):
+                if app.size:
+                    eng.append(g, app, app_rows[(g, t)], stream=streams[g])
+                eng.step(g, dsel[g][t - 1], stream=streams[g])
+                outs[(g, t)] = [eng.gather(g, l, dsel[g][t - 1], stream=streams[g]) for l in range(wl.layers)]
+        torch.cuda.synchronize()
+        eng.sync()
+        for g in range(G):
+            if policy == 0:
+                ora = new_group(tr, full_data=True)
+                oracle_load(ora, tr, g)
+            else:
+                ora = ExactLRUArrays(tr.N, tr.P, tr.H, wl.ring)
+                ora.append(tr.initial_load_order())
+            for t in range(1, tr.steps + 1):
+                app = tr.appends(t)
+                sel = sels[g][t - 1]
+                if policy == 0:
+                    ora.append(app, rows_for(wl.seed, g, app, wl.layers, wl.row_bytes))
+                    ora.step(sel)
+                else:
+                    ora.append(app)
+                    ora.step(sel)
+                for l in range(wl.layers):
+                    got = outs[(g, t)][l].cpu().numpy()
+                    flat = sel.reshape(-1)
+                    want = np.zeros((flat.size, wl.row_bytes), np.uint8)
+                    ok = flat >= 0
+                    want[ok] = rows_for(wl.seed, g, flat[ok], wl.layers, wl.row_bytes)[:, l]
+                    assert np.array_equal(got.reshape(flat.size, wl.row_bytes), want), \
+                        f"group {g} step {t} layer {l}: gathered rows differ"
+            st = eng.export_state(g)
+            ref = ora.export_state()
+            for key in ("map", "gown", "hown"):
+                assert np.array_equal(np.asarray(st[key]), np.asarray(ref[key])), f"group {g}: {key} differs"
+            assert st["flag"] == ref["flag"] and tuple(st["stats"]) == tuple(ref["stats"]), f"group {g}"
+            if policy == 0:
+                assert np.array_equal(np.asarray(st["bitsets"]), np.asarray(ref["bitsets"])), f"group {g}: bitsets"
+            else:
+                assert np.array_equal(np.asarray(st["stamps"]), np.asarray(ref["stamps"])), f"group {g}: stamps"
+    finally:
+        eng.close()
+
+
 def _pingpong():
     """One request of 64 positions, a pool of 8 slots, 2 ring buckets and k = 8:
     alternating disjoint sets miss every entry and evict the previous set, so
