@@ -17,12 +17,15 @@
 // the order is (K, slot) ascending, exactly.
 //
 // Per step, with M misses:
-//   select  three passes over every slot, each a histogram of the next key digit
-//           (bits 21-31, 10-20, 0-9) among the slots whose higher digits match the
-//           prefix found so far; the last workgroup of a pass finds the digit where
-//           the running count reaches M. After the third, K* is the key of the
-//           M-th victim, C the number of victims with a smaller key and R = M - C
-//           the number taken from the slots with key K* (the lowest slots first).
+//   select  up to three passes over every slot, each a histogram of the next key
+//           digit (bits 21-31, 10-20, 0-9) among the slots whose higher digits
+//           match the prefix found so far; the last workgroup of a pass finds the
+//           digit where the running count reaches M. After the last, K* is the key
+//           of the M-th victim, C the number of victims with a smaller key and
+//           R = M - C the number taken from the slots with key K* (the lowest
+//           slots first). No key exceeds the step number t (a timestamp is at
+//           most t - 1), so the passes whose digits are zero for every key below
+//           2^21 or 2^10 are skipped: before step 1024 a single pass decides.
 //           The first pass's launch also carries the miss path's host-link
 //           workgroups (prefetch and write-back), as the mark launch does under
 //           PB-LRU.
@@ -82,11 +85,11 @@ constexpr int kLruThreads = 512;    // select passes
 constexpr int kSpanThreads = 256;   // count and emit (one wavefront per span)
 constexpr int kBinsPerThread = kLruBins / kLruThreads;
 
-__device__ void lru_find(const GroupDev& g, int nbins, int bits, int pass, int* scratch) {
+__device__ void lru_find(const GroupDev& g, int nbins, int bits, int pass, int first, int* scratch) {
   __shared__ int s_bin, s_add;
   Counters* c = g.ctr;
   const int m = c->n_miss;
-  const int below = pass == 0 ? 0 : c->lru_below;
+  const int below = pass == first ? 0 : c->lru_below;
   const int need = m - below;   // >= 1
   const int i0 = kBinsPerThread * threadIdx.x;
   int h[kBinsPerThread], sum = 0;
@@ -114,11 +117,11 @@ __device__ void lru_find(const GroupDev& g, int nbins, int bits, int pass, int* 
     if (s_bin < 0) {
       latch(c, ULA_ESTATE);   // fewer candidates than misses: inconsistent state
     } else {
-      const uint32_t prefix = pass == 0 ? (uint32_t)s_bin : (c->lru_prefix << bits) | (uint32_t)s_bin;
+      const uint32_t prefix = pass == first ? (uint32_t)s_bin : (c->lru_prefix << bits) | (uint32_t)s_bin;
       const int nb = below + s_add;
       c->lru_prefix = prefix;
       c->lru_below = nb;
-      if (pass == 0) {
+      if (pass == first) {
         const int ff = min(m, c->lru_nfree);
         c->stats[3] = m - ff;   // evictions
         c->stats[4] = ff;       // from free slots
@@ -133,10 +136,12 @@ __device__ void lru_find(const GroupDev& g, int nbins, int bits, int pass, int* 
   }
 }
 
-// One select pass. Workgroups [0, nsel) histogram; in the first pass the next
-// pf workgroups prefetch the missed rows and the wbb after them write the
-// previous step's evicted rows out (they wait for nothing).
-__global__ __launch_bounds__(kLruThreads) void k_lru_pass(GroupDev g, uint32_t t, int32_t pass, int32_t nsel,
+// One select pass. Workgroups [0, nsel) histogram; in the first pass launched
+// (`first`: the higher digits of every key are zero) the next pf workgroups
+// prefetch the missed rows and the wbb after them write the previous step's
+// evicted rows out (they wait for nothing).
+__global__ __launch_bounds__(kLruThreads) void k_lru_pass(GroupDev g, uint32_t t, int32_t pass, int32_t first,
+                                                   int32_t nsel,
                                                    FastDiv per_slot, int32_t pf, int32_t wbb,
                                                    uint32_t wb_step) {
   __shared__ uint32_t s_hist[kLruBins];
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kLruThreads) void k_lru_pass(GroupDev g, uint32_t t
   const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
   const int bits = pass == 2 ? 10 : 11;
   const int nbins = 1 << bits;
-  const uint32_t prefix = pass == 0 ? 0u : g.ctr->lru_prefix;
+  const uint32_t prefix = pass == first ? 0u : g.ctr->lru_prefix;
   for (int i = threadIdx.x; i < nbins; i += blockDim.x) s_hist[i] = 0u;
   if (threadIdx.x == 0) s_free = 0;
   __syncthreads();
@@ -189,14 +194,14 @@ __global__ __launch_bounds__(kLruThreads) void k_lru_pass(GroupDev g, uint32_t t
     }
     if (run) atomicAdd(&s_hist[run_bin], (uint32_t)run);
   }
-  if (pass == 0) {
+  if (pass == first) {
     nfree = wave_sum(nfree);
     if (lane_id() == 0 && nfree) atomicAdd(&s_free, nfree);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nbins; i += blockDim.x)
     if (s_hist[i]) atomicAdd(&g.lru_hist[i], s_hist[i]);
-  if (threadIdx.x == 0 && pass == 0 && s_free) atomicAdd(&g.ctr->lru_nfree, s_free);
+  if (threadIdx.x == 0 && pass == first && s_free) atomicAdd(&g.ctr->lru_nfree, s_free);
   // the last workgroup to finish finds the digit (release per workgroup, then an
   // acquire-release ticket, as in the mark kernel)
   __syncthreads();
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(kLruThreads) void k_lru_pass(GroupDev g, uint32_t t
   }
   __syncthreads();
   if (!s_last) return;
-  lru_find(g, nbins, bits, pass, scratch);
+  lru_find(g, nbins, bits, pass, first, scratch);
 }
 
 // Masks of the 32 slots of word w: below K*, and equal to K*; free slots among them.
@@ -458,11 +463,14 @@ hipError_t launch_lru_select(const GroupDev& g, uint32_t t, int32_t max_pairs, i
   // the compute units
   const int nsel = (int)std::min<int64_t>(std::max<int64_t>((g.W + kLruThreads - 1) / kLruThreads, 1), 1024);
   const FastDiv per_slot(chunks);
-  k_lru_pass<<<nsel + pf + wbb, kLruThreads, 0, s>>>(g, t, 0, nsel, per_slot, pf, wbb,
+  // keys are at most t: the digits of bits 21-31 (and 10-20) are zero for every
+  // key while t < 2^21 (2^10), and those passes would pick digit 0
+  const int first = t >= (1u << 21) ? 0 : (t >= (1u << 10) ? 1 : 2);
+  k_lru_pass<<<nsel + pf + wbb, kLruThreads, 0, s>>>(g, t, first, first, nsel, per_slot, pf, wbb,
                                                        wbb > 0 ? t - 1u : 0u);
   hipError_t e = hipGetLastError();
-  for (int pass = 1; pass < 3 && e == hipSuccess; ++pass) {
-    k_lru_pass<<<nsel, kLruThreads, 0, s>>>(g, t, pass, nsel, per_slot, 0, 0, 0u);
+  for (int pass = first + 1; pass < 3 && e == hipSuccess; ++pass) {
+    k_lru_pass<<<nsel, kLruThreads, 0, s>>>(g, t, pass, first, nsel, per_slot, 0, 0, 0u);
     e = hipGetLastError();
   }
   return e;

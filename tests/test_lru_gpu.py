@@ -123,6 +123,16 @@ def test_lru_long_trace_two_sort_passes():
     assert lru.t == 300
 
 
+def test_lru_long_trace_two_select_passes():
+    # keys never exceed the step number, so the selection runs one 10-bit pass up
+    # to step 1023 and two from step 1024 (bits 10-20, then 0-9): a 1100-step
+    # trace crosses over, with state checked every 25 steps around the crossing
+    wl = tiny_workload(2, steps=1100, sets=1, layers=1)
+    wl = dataclasses.replace(wl, pool_slots=2 * wl.requests * wl.k, name="long1100")
+    lru = run_lru_parity(wl, check_every=25)
+    assert lru.t == 1100
+
+
 @pytest.mark.parametrize("name,factor,steps", [
     ("r16_64k_g1x3", 16, 8),
     ("evict_r256_128k_g2", 64, 6),
