@@ -1,0 +1,103 @@
+"""Randomised parity across the engine's paths at once (GPU).
+
+Each seed draws a small workload with one to three layer groups, one of the two
+policies, a random ring, and per step and group a random way to append: rows in
+device memory or in host memory, with a per-call append limit small enough that
+most appends run in several chunks (the plan / extract / place kernels) and the
+rest in the one-workgroup path. Finished entries are released between steps.
+After every step (and every release) each group's exported state must equal its
+oracle's, and every gathered byte must equal the closed form of its row.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+
+from gpu_harness import say
+from synth import Trace, rows_for
+from tracegen import padded_selections, release_plan, tiny_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(tr, g, policy):
+    from oracle.exact_lru_np import ExactLRUArrays
+    from oracle.replay import initial_load, new_group
+    if policy == 0:
+        o = new_group(tr, full_data=True)
+        initial_load(o, tr, g)
+    else:
+        o = ExactLRUArrays(tr.N, tr.P, tr.H, tr.wl.ring)
+        o.append(tr.initial_load_order())
+    return o
+
+
+def _same(st, ref, policy, where):
+    for key in ("map", "gown", "hown"):
+        assert np.array_equal(np.asarray(st[key]), np.asarray(ref[key])), f"{where}: {key} differs"
+    assert st["flag"] == ref["flag"], f"{where}: flag"
+    assert tuple(st["stats"]) == tuple(ref["stats"]), f"{where}: stats {st['stats']} vs {ref['stats']}"
+    if policy == 0:
+        assert np.array_equal(np.asarray(st["bitsets"]), np.asarray(ref["bitsets"])), f"{where}: bitsets"
+        assert st["cur"] == ref["cur"], f"{where}: cur"
+    else:
+        assert np.array_equal(np.asarray(st["stamps"]), np.asarray(ref["stamps"])), f"{where}: stamps"
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_mixed_paths_random(seed):
+    import torch
+    from serving_pb_lru_amd.replay import engine_for, initial_load
+    from synth.device import rows_device
+    rng = np.random.default_rng([seed, 555])
+    policy = int(rng.integers(0, 2))
+    groups = int(rng.integers(1, 4))
+    wl = tiny_workload(seed, steps=int(rng.integers(4, 11)))
+    wl = dataclasses.replace(wl, groups=groups, appends=int(rng.integers(1, 4)), name=f"mixed{seed}")
+    tr = Trace(wl)
+    max_append = int(rng.integers(2, 6))
+    say(f"mixed {seed}: policy {policy} groups {groups} ring {wl.ring} steps {tr.steps} "
+        f"N={tr.N} P={tr.P} H={tr.H} max_append={max_append}")
+    eng = engine_for(tr, max_append=max_append, policy=policy)
+    rows_dev = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    try:
+        initial_load(eng, tr, range(groups), rows_dev)
+        ora = {g: _oracle(tr, g, policy) for g in range(groups)}
+        for g in range(groups):
+            _same(eng.export_state(g), ora[g].export_state(), policy, f"group {g} after load")
+        sels = {g: padded_selections(tr, g, seed + 7 * g) for g in range(groups)}
+        plans = {g: release_plan(tr, sels[g], seed + 11 * g, frac=0.3) for g in range(groups)}
+        for t in range(1, tr.steps + 1):
+            app = tr.appends(t)
+            for g in range(groups):
+                sel = sels[g][t - 1]
+                if app.size:
+                    host_rows = rng.random() < 0.5
+                    rows = (rows_for(wl.seed, g, app, wl.layers, wl.row_bytes) if host_rows
+                            else rows_dev(app, g))
+                    eng.append(g, app, rows)
+                    if policy == 0:
+                        ora[g].append(app, rows_for(wl.seed, g, app, wl.layers, wl.row_bytes))
+                    else:
+                        ora[g].append(app)
+                dsel = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
+                eng.step(g, dsel)
+                outs = [eng.gather(g, l, dsel) for l in range(wl.layers)]
+                ora[g].step(sel)
+                eng.sync()
+                _same(eng.export_state(g), ora[g].export_state(), policy, f"group {g} step {t}")
+                flat = np.asarray(sel, dtype=np.int64).reshape(-1)
+                want = np.zeros((flat.size, wl.layers, wl.row_bytes), np.uint8)
+                ok = flat >= 0
+                want[ok] = rows_for(wl.seed, g, flat[ok], wl.layers, wl.row_bytes)
+                for l in range(wl.layers):
+                    got = outs[l].cpu().numpy().reshape(flat.size, wl.row_bytes)
+                    assert np.array_equal(got, want[:, l]), f"group {g} step {t} layer {l}: gathered rows differ"
+                rel = plans[g].get(t, np.zeros(0, np.int32))
+                if rel.size:
+                    eng.release(g, rel)
+                    ora[g].release(rel)
+                    _same(eng.export_state(g), ora[g].export_state(), policy, f"group {g} release {t}")
+    finally:
+        eng.close()
