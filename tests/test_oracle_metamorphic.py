@@ -123,3 +123,38 @@ def test_padding_changes_only_the_padding_count(seed):
             assert np.array_equal(a[k], b[k]), f"step {t}: {k}"
         sa, sb = a["stats"], b["stats"]
         assert sa[:5] == sb[:5] and sb[5] == sa[5] + added[t - 1], f"step {t}: stats {sa} vs {sb}"
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_exact_lru_relabelling_addresses(seed):
+    """The same relabelling property for the array form of exact LRU (victims by
+    timestamp and slot, never by address), releases included."""
+    from oracle.exact_lru_np import ExactLRUArrays
+    wl = tiny_workload(seed, steps=10)
+    tr = Trace(wl)
+    sels = padded_selections(tr, 0, seed)
+    rel = release_plan(tr, sels, seed, frac=0.3)
+    load = tr.initial_load_order()
+    apps = [tr.appends(t) for t in range(1, tr.steps + 1)]
+    perm = np.random.default_rng([seed, 34]).permutation(tr.N)
+    f = lambda a: np.where(np.asarray(a) >= 0, perm[np.maximum(np.asarray(a), 0)], -1).astype(np.int32)
+
+    def run(fn):
+        g = ExactLRUArrays(tr.N, tr.P, tr.H, wl.ring)
+        g.append(fn(load))
+        out = []
+        for t, sel in enumerate(sels, 1):
+            g.append(fn(apps[t - 1]))
+            g.step(fn(sel))
+            out.append((g.export_state(), [int(v) for v in g.last_victims]))
+            r = rel.get(t)
+            if r is not None and r.size:
+                g.release(fn(r))
+        return out
+
+    for t, ((a, va), (b, vb)) in enumerate(zip(run(lambda x: np.asarray(x, np.int32)), run(f)), 1):
+        assert va == vb, f"step {t}: victims"
+        assert np.array_equal(_relabel_map(a["map"], perm), b["map"]), f"step {t}: map"
+        assert np.array_equal(_relabel_owners(a["gown"], perm), b["gown"]), f"step {t}: gown"
+        assert np.array_equal(_relabel_owners(a["hown"], perm), b["hown"]), f"step {t}: hown"
+        assert np.array_equal(a["stamps"], b["stamps"]) and a["stats"] == b["stats"], f"step {t}"
