@@ -6,10 +6,12 @@
 // threads. The selection is n = n_sets * k logical addresses, row-major; -1 is
 // padding. The distinct addresses are kept in first-occurrence order.
 //
-//   tag      every valid entry e stores key(t, e) = (t << 32) | ~e into tag[la]
-//            with a 64-bit atomic max, so after the kernel tag[la] holds the key
-//            of la's first occurrence in step t (a smaller e gives a larger ~e;
-//            tags of earlier steps have a smaller t and never match).
+//   tag      every in-range entry e stores key(t, e) = (t << 32) | ~e into
+//            tag[la] with a 64-bit atomic max, so after the kernel tag[la] holds
+//            the key of la's first occurrence in step t (a smaller e gives a
+//            larger ~e; tags of earlier steps have a smaller t and never match).
+//            An address outside [0, N) is an error here; one never appended is
+//            found by the compaction, which reads the mapping table anyway.
 //   compact  single pass with a decoupled look-back: workgroups take tickets in
 //            start order; each classifies its 1024 entries (first occurrence on
 //            the GPU = hit, on the host = miss, padding) with wavefront ballots,
@@ -20,7 +22,9 @@
 //            so every wait ends; waits are bounded all the same. Padding entries
 //            are counted by the tag kernel. The last
 //            workgroup knows the totals: more distinct entries than GPU slots is
-//            a capacity error raised before any state changes. Each hit is
+//            a capacity error raised before any state changes, and a never
+//            appended entry anywhere (its flag travels in the counts) leaves the
+//            statistics as they were. Each hit is
 //            stamped with the step and its span marked dirty; every entry is
 //            resolved for the gathers.
 #include "device_util.h"
@@ -49,7 +53,7 @@ __global__ __launch_bounds__(256) void k_tag(GroupDev g, const int32_t* __restri
       ++pad;
       continue;
     }
-    if (la < 0 || la >= g.N || g.map[la] == kAbsent) {
+    if (la < 0 || la >= g.N) {
       bad = true;
       continue;
     }
@@ -62,22 +66,28 @@ __global__ __launch_bounds__(256) void k_tag(GroupDev g, const int32_t* __restri
 }
 
 // Look-back descriptor of a workgroup: status in bits 62-63 (0 = not yet, 1 =
-// its own counts, 2 = inclusive prefix), misses in bits 31-61, hits in bits 0-30.
-// The counts travel inside the descriptor, so relaxed atomics suffice.
+// its own counts, 2 = inclusive prefix), bit 61 set if a never appended entry
+// was seen (in the workgroup, or for a prefix anywhere up to it), misses in bits
+// 31-60, hits in bits 0-30. The counts travel inside the descriptor, so relaxed
+// atomics suffice.
 constexpr unsigned long long kDescAgg = 1ull << 62;
 constexpr unsigned long long kDescPre = 2ull << 62;
+constexpr unsigned long long kDescStatus = 3ull << 62;
+constexpr unsigned long long kDescBad = 1ull << 61;
 constexpr uint32_t kCount31 = 0x7FFFFFFFu;
+constexpr uint32_t kCount30 = 0x3FFFFFFFu;
 constexpr int kSpinLimit = 1 << 16;
 
-__device__ __forceinline__ unsigned long long desc_pack(unsigned long long status, uint32_t h, uint32_t m) {
-  return status | ((unsigned long long)m << 31) | (unsigned long long)h;
+__device__ __forceinline__ unsigned long long desc_pack(unsigned long long status, bool bad, uint32_t h,
+                                                        uint32_t m) {
+  return status | (bad ? kDescBad : 0ull) | ((unsigned long long)m << 31) | (unsigned long long)h;
 }
 
 __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_t* __restrict__ sel,
                                                         int32_t n, uint32_t t, int32_t nblk) {
   constexpr int NW = kScanBlock / kWave;
   __shared__ int s_h[NW], s_m[NW];
-  __shared__ int s_vid, s_fail, s_status;
+  __shared__ int s_vid, s_fail, s_status, s_bad;
   __shared__ uint32_t s_eh, s_em;
   const int wave = threadIdx.x / kWave;
   const int lane = lane_id();
@@ -86,6 +96,7 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
   if (threadIdx.x == 0) {
     s_status = status_of(g.ctr);
     s_fail = 0;
+    s_bad = 0;
   } else if (threadIdx.x == kWave) {
     s_vid = atomicAdd(&g.ctr->lb_ticket, 1);
   }
@@ -109,9 +120,12 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
     if (la == -1) {
       c = 3;
       g.res[e] = make_uint2(0xFFFFFFFFu, kAbsent);
+    } else if (la < 0 || la >= g.N || (loc = g.map[la]) == kAbsent) {
+      // never appended (out-of-range addresses were stopped by the tag kernel)
+      s_bad = 1;
+      latch(g.ctr, ULA_ERANGE);
     } else {
       const unsigned long long key = g.tag[la];
-      loc = g.map[la];
       if (key == dedup_key(t, (uint32_t)e)) {
         c = (loc & kHostBit) ? 2 : 1;
         g.res[e] = make_uint2((uint32_t)la, c == 1 ? loc : kAbsent);   // a miss's slot comes at commit
@@ -133,22 +147,24 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
 
   // publish this workgroup's counts, then look back for its offsets (wave 0)
   if (wave == 0) {
+    const bool bad = s_bad != 0;
     uint32_t ah = 0, am = 0;
     for (int w = 0; w < NW; ++w) {
       ah += s_h[w];
       am += s_m[w];
     }
     if (lane == 0)
-      __hip_atomic_store(&desc[vid], desc_pack(vid == 0 ? kDescPre : kDescAgg, ah, am), __ATOMIC_RELAXED,
+      __hip_atomic_store(&desc[vid], desc_pack(vid == 0 ? kDescPre : kDescAgg, bad, ah, am), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     uint32_t eh = 0, em = 0;
+    bool ebad = false;   // a never appended entry before this workgroup
     int j = vid - 1;     // predecessor examined by lane 0
     int spins = 0;
     while (j >= 0) {
       const int k = j - lane;
       const unsigned long long d =
           k >= 0 ? __hip_atomic_load(&desc[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : kDescPre;
-      const unsigned long long st = d & (3ull << 62);
+      const unsigned long long st = d & kDescStatus;
       const unsigned long long pre = __ballot(st == kDescPre);
       const unsigned long long zero = __ballot(st == 0ull);
       // lanes up to the nearest inclusive prefix must all have published
@@ -163,15 +179,16 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
       }
       const bool take = (upto >> lane) & 1ull;
       int vh = take ? (int)(d & kCount31) : 0;
-      int vm = take ? (int)((d >> 31) & kCount31) : 0;
+      int vm = take ? (int)((d >> 31) & kCount30) : 0;
       eh += (uint32_t)wave_sum(vh);
       em += (uint32_t)wave_sum(vm);
+      ebad |= __ballot(take && (d & kDescBad) != 0ull) != 0ull;
       if (pre) break;
       j -= kWave;
     }
     if (lane == 0) {
       if (vid > 0 && !s_fail)
-        __hip_atomic_store(&desc[vid], desc_pack(kDescPre, eh + ah, em + am), __ATOMIC_RELAXED,
+        __hip_atomic_store(&desc[vid], desc_pack(kDescPre, ebad || bad, eh + ah, em + am), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       s_eh = eh;
       s_em = em;
@@ -183,7 +200,9 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
         const int u = th + tm;
         cs->lb_ticket = 0;
         cs->pad_acc = 0;
-        if (u > g.P) {
+        if (ebad || bad) {
+          // a never appended entry (already latched): the statistics stay as they were
+        } else if (u > g.P) {
           latch(cs, ULA_ECAPACITY);   // before anything changes, statistics included
         } else {
           cs->n_hits = th;

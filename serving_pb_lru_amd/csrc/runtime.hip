@@ -72,6 +72,8 @@ bool check_config(const ula_config* c, Dims* d) {
   d->maxItems = std::max<int64_t>(d->maxU, d->maxApp) + 2;
   d->maxRs = (d->maxU + 1023) / 1024;
   d->policy = c->policy;
+  // selection entries (and so misses) fit the look-back descriptors' 30-bit counts
+  if (nsel >= (1ll << 30)) return false;
   // 16-byte piece counts handled with 32-bit indices and FastDiv (< 2^31)
   if (nsel * (d->row_bytes / 16) >= (1ll << 31)) return false;
   if (d->maxU * (d->slot_bytes / 16) >= (1ll << 31)) return false;
