@@ -2,10 +2,10 @@
 """Throughput of the PB-LRU KV residency engine on one MI355X.
 
 One step = the whole per-decode-step path for every layer group of the
-workload: the step's appends, ula_step (de-duplication and lookup, fold and hit
-marking, victim selection, the miss path over the host link, commit and
-completion signal) and
-one ula_gather per layer of the group. Inputs (selection sets for every step
+workload: the step's appends and the step in one ula_append_step call (the
+appends, de-duplication and lookup, fold and hit marking, victim selection, the
+miss path over the host link, commit and completion signal) and one ula_gather
+per layer of the group. Inputs (selection sets for every step
 and the appended rows) are resident in HBM before the timed region; the GPU
 pool starts full (initial load untimed). W warm-up steps run first (they carry
 the cold-start misses), then exactly K steps are timed between two device
@@ -218,10 +218,10 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
 
     def run_step(eng, t):
         for g in groups:
-            if apps[t - 1].size:
-                eng.append(g, apps[t - 1], app_rows[g][t - 1])
             sel = sels[g][t - 1]
-            eng.step(g, sel)
+            # the step's appends and the step in one call (the appends run in the
+            # step's first launch when they are small)
+            eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel)
             for l in range(wl.layers):
                 eng.gather(g, l, sel, out=outs[g][l])
 
@@ -275,10 +275,10 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
         prev_evict = {g: 0 for g in groups}
         for t in range(1, W + K + 1):
             for g in groups:
-                if apps[t - 1].size:
-                    eng.append(g, apps[t - 1], app_rows[g][t - 1])
-                eng.step(g, sels[g][t - 1])
-                ms = eng.read_timing(g)   # [1] also moves this step's misses in, last step's evictions out
+                eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sels[g][t - 1])
+                # [0] includes a small append (it runs in the lookup's first launch);
+                # [1] also moves this step's misses in, last step's evictions out
+                ms = eng.read_timing(g)
                 st = eng.sync()[g]
                 if t > W:
                     ph += ms

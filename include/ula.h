@@ -187,6 +187,22 @@ int ula_release(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, 
 int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
              uint64_t stream);
 
+/* One decode step of group g with its appends (section 2: the new positions a
+ * step produces are appended, then the step selects among all entries):
+ * exactly ula_append(ctx, group, n_app, la_host, rows, rows_on_device, stream)
+ * followed by ula_step(ctx, group, n_sets, k, sel_dev, stream), with the same
+ * arguments, placement and results, in fewer launches: an append of at most 256
+ * entries (and at most max_append) with rows in device memory runs in the
+ * step's first launch, beside the de-duplication, which does not read the
+ * mapping table; other appends run as ula_append does, before the step.
+ * n_app = 0 is a plain step. Both parts are validated on the host before
+ * anything is enqueued: any host error of ula_append or ula_step is returned
+ * with nothing changed. Device errors of the step are reported by ula_sync as
+ * for ula_step; the appended entries stay appended. */
+int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* la_host,
+                    const void* rows, int32_t rows_on_device, int32_t n_sets, int32_t k,
+                    const int32_t* sel_dev, uint64_t stream);
+
 /* Gather layer `layer` of every selected entry of group g into out_dev
  * (device memory, n_sets x k x row_bytes bytes, packed; a -1 entry gives a zero
  * row). Reads the GPU pool through the mapping table after checking that the

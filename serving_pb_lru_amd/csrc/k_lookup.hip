@@ -7,11 +7,11 @@
 // padding. The distinct addresses are kept in first-occurrence order.
 //
 //   tag      every in-range entry e stores key(t, e) = (t << 32) | ~e into
-//            tag[la] with a 64-bit atomic max, so after the kernel tag[la] holds
-//            the key of la's first occurrence in step t (a smaller e gives a
-//            larger ~e; tags of earlier steps have a smaller t and never match).
-//            An address outside [0, N) is an error here; one never appended is
-//            found by the compaction, which reads the mapping table anyway.
+//            tag[la] with a 64-bit atomic max (tag_part.h), so after the pass
+//            tag[la] holds the key of la's first occurrence in step t. An
+//            address outside [0, N) is an error there; one never appended is
+//            found by the compaction, which reads the mapping table anyway. A
+//            step's small append may run in the same launch (k_select.hip).
 //   compact  single pass with a decoupled look-back: workgroups take tickets in
 //            start order; each classifies its 1024 entries (first occurrence on
 //            the GPU = hit, on the host = miss, padding) with wavefront ballots,
@@ -27,42 +27,13 @@
 //            statistics as they were. Each hit is
 //            stamped with the step and its span marked dirty; every entry is
 //            resolved for the gathers.
-#include "device_util.h"
+#include "tag_part.h"
 
 namespace ula {
 
-__device__ __forceinline__ unsigned long long dedup_key(uint32_t t, uint32_t e) {
-  return ((unsigned long long)t << 32) | (unsigned long long)(~e);
-}
-
 __global__ __launch_bounds__(256) void k_tag(GroupDev g, const int32_t* __restrict__ sel,
                                              int32_t n, uint32_t t) {
-  // No error check up front: this kernel writes only scratch (tags, this
-  // step's look-back descriptors, the padding count), and a latched error
-  // stops the compaction, which is where the step's results are written.
-  // the compaction of this step uses the descriptors of parity t & 1, last used
-  // two steps ago
-  unsigned long long* desc = g.desc + (size_t)(t & 1u) * g.maxBlk;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < g.maxBlk; i += gridDim.x * blockDim.x)
-    desc[i] = 0ull;
-  bool bad = false;
-  int pad = 0;
-  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < n; e += gridDim.x * blockDim.x) {
-    int32_t la = sel[e];
-    if (la == -1) {
-      ++pad;
-      continue;
-    }
-    if (la < 0 || la >= g.N) {
-      bad = true;
-      continue;
-    }
-    atomicMax(&g.tag[la], dedup_key(t, (uint32_t)e));
-  }
-  if (bad) latch(g.ctr, ULA_ERANGE);
-  // padding entries of the step (statistics); one atomic per wavefront that saw any
-  pad = wave_sum(pad);
-  if (pad && lane_id() == 0) atomicAdd(&g.ctr->pad_acc, pad);
+  tag_entries(g, sel, n, t, blockIdx.x, gridDim.x);
 }
 
 // Look-back descriptor of a workgroup: status in bits 62-63 (0 = not yet, 1 =

@@ -37,6 +37,7 @@
 #include <algorithm>
 
 #include "miss_path.h"
+#include "tag_part.h"
 
 namespace ula {
 
@@ -368,10 +369,9 @@ __global__ __launch_bounds__(256) void k_extract(GroupDev g, int32_t mode, int32
 // destinations in LDS, the addresses passed by value so that no copy precedes
 // the launch, and the counters, span hints and first pieces of the rows loaded
 // together before the plan: the chain of dependent memory accesses is the
-// span counts, the bitmap words, then the stores.
-__global__ __launch_bounds__(1024) void k_append_small(GroupDev g, SmallAppend a,
-                                                       const uint8_t* __restrict__ rows,
-                                                       FastDiv per_slot) {
+// span counts, the bitmap words, then the stores. One 1024-lane workgroup.
+__device__ void append_small_body(const GroupDev& g, const SmallAppend& a, const uint8_t* __restrict__ rows,
+                                  FastDiv per_slot) {
   __shared__ int scratch[1024 / kWave + 1];
   __shared__ unsigned long long s_nonempty[1024 / kWave];
   __shared__ SelItem s_items[kSmallAppend];   // each item takes at least one entry
@@ -423,6 +423,27 @@ __global__ __launch_bounds__(1024) void k_append_small(GroupDev g, SmallAppend a
   }
 }
 
+__global__ __launch_bounds__(1024) void k_append_small(GroupDev g, SmallAppend a,
+                                                       const uint8_t* __restrict__ rows,
+                                                       FastDiv per_slot) {
+  append_small_body(g, a, rows, per_slot);
+}
+
+// A step's first launch with the step's small append beside it: the last
+// workgroup appends, the others run the de-duplication tag pass, which reads
+// only the selection; the two write disjoint data (tags, descriptors and the
+// padding count; the mapping table, owners, buckets and rows of the appended
+// entries). The compaction, in the next launch, sees both.
+__global__ __launch_bounds__(1024) void k_tag_append(GroupDev g, SmallAppend a, const uint8_t* __restrict__ rows,
+                                                     FastDiv per_slot, const int32_t* __restrict__ sel,
+                                                     int32_t n, uint32_t t) {
+  if ((int)blockIdx.x == (int)gridDim.x - 1) {
+    append_small_body(g, a, rows, per_slot);
+    return;
+  }
+  tag_entries(g, sel, n, t, blockIdx.x, gridDim.x - 1);
+}
+
 hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArgs& a,
                        int32_t max_pairs, int32_t wb_pairs, hipStream_t s) {
   // Prefetch workgroups: enough for the largest possible miss list, at most
@@ -451,6 +472,15 @@ hipError_t launch_plan(const GroupDev& g, const PlanArgs& a, hipStream_t s) {
 hipError_t launch_append_small(const GroupDev& g, const SmallAppend& a, const uint8_t* rows,
                               hipStream_t s) {
   k_append_small<<<1, 1024, 0, s>>>(g, a, rows, FastDiv((uint32_t)g.slot_bytes / 16u));
+  return hipGetLastError();
+}
+
+hipError_t launch_tag_append(const GroupDev& g, const SmallAppend& a, const uint8_t* rows,
+                             const int32_t* sel, int32_t n, uint32_t t, hipStream_t s) {
+  int blocks = (n + 1023) / 1024;
+  if (blocks > 2048) blocks = 2048;
+  if (blocks < 1) blocks = 1;   // also clears the look-back descriptors
+  k_tag_append<<<blocks + 1, 1024, 0, s>>>(g, a, rows, FastDiv((uint32_t)g.slot_bytes / 16u), sel, n, t);
   return hipGetLastError();
 }
 

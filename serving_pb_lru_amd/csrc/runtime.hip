@@ -390,16 +390,9 @@ int ula_destroy(ula_ctx* ctx) {
   return ULA_OK;
 }
 
-int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, const void* rows,
-               int32_t rows_on_device, uint64_t stream) {
-  if (!ctx) return ULA_EINVAL;
-  if (ctx->poisoned) return ULA_ESTATE;
-  if (group < 0 || group >= ctx->cfg.num_groups || n < 0) return ULA_EINVAL;
-  if (n == 0) return ULA_OK;
-  if (!la_host || !rows) return ULA_EINVAL;
-  GroupHost& gh = ctx->groups[group];
+// Host validation of an append batch (nothing changes on error).
+static int validate_append(const ula_ctx* ctx, const GroupHost& gh, int32_t n, const int32_t* la_host) {
   const Dims& d = ctx->dims;
-  // validate the whole batch first; nothing changes on error
   for (int32_t i = 0; i < n; ++i)
     if (la_host[i] < 0 || la_host[i] >= d.N) return ULA_ERANGE;
   {
@@ -412,6 +405,30 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
     if (gh.appended[la >> 6] >> (la & 63) & 1ull) return ULA_EDUP;
   }
   if (gh.n_appended + n > d.P + d.H) return ULA_EHOSTFULL;
+  return ULA_OK;
+}
+
+static void note_appended(GroupHost& gh, int32_t n, const int32_t* la_host) {
+  for (int32_t i = 0; i < n; ++i) {
+    const uint32_t la = (uint32_t)la_host[i];
+    gh.appended[la >> 6] |= 1ull << (la & 63);
+  }
+  gh.n_appended += n;
+}
+
+int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, const void* rows,
+               int32_t rows_on_device, uint64_t stream) {
+  if (!ctx) return ULA_EINVAL;
+  if (ctx->poisoned) return ULA_ESTATE;
+  if (group < 0 || group >= ctx->cfg.num_groups || n < 0) return ULA_EINVAL;
+  if (n == 0) return ULA_OK;
+  if (!la_host || !rows) return ULA_EINVAL;
+  GroupHost& gh = ctx->groups[group];
+  const Dims& d = ctx->dims;
+  {
+    const int rc = validate_append(ctx, gh, n, la_host);   // the whole batch first
+    if (rc) return rc;
+  }
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const GroupDev& g = gh.d;
@@ -455,11 +472,7 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
       HIP_TRY(launch_place(g, cnt, src, s));
     }
   }
-  for (int32_t i = 0; i < n; ++i) {
-    const uint32_t la = (uint32_t)la_host[i];
-    gh.appended[la >> 6] |= 1ull << (la & 63);
-  }
-  gh.n_appended += n;
+  note_appended(gh, n, la_host);
   return ULA_OK;
 }
 
@@ -525,14 +538,20 @@ static int flush_writebacks(ula_ctx* ctx) {
   return ULA_OK;
 }
 
-int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
-             uint64_t stream) {
-  if (!ctx) return ULA_EINVAL;
+// Host checks of a step's arguments (nothing is enqueued on error).
+static int validate_step(const ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev) {
   if (ctx->poisoned) return ULA_ESTATE;
   if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
   if (n_sets < 0 || k < 0 || n_sets > ctx->cfg.max_sets || k > ctx->cfg.max_k) return ULA_EINVAL;
+  if (n_sets * k > 0 && !sel_dev) return ULA_EINVAL;
+  return ULA_OK;
+}
+
+// A validated step; `app` (nullable): a small append whose rows are in device
+// memory, run in the step's first launch beside the tag pass.
+static int step_impl(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
+                     uint64_t stream, const SmallAppend* app, const uint8_t* app_rows) {
   const int32_t n = n_sets * k;
-  if (n > 0 && !sel_dev) return ULA_EINVAL;
   GroupHost& gh = ctx->groups[group];
   const GroupDev& g = gh.d;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -545,7 +564,8 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
 
   gh.last_stream = s;
   if (tm) HIP_TRY(hipEventRecord(gh.ev[0], s));
-  HIP_TRY(launch_tag(g, sel_dev, n, (uint32_t)t, s));
+  if (app) HIP_TRY(launch_tag_append(g, *app, app_rows, sel_dev, n, (uint32_t)t, s));
+  else HIP_TRY(launch_tag(g, sel_dev, n, (uint32_t)t, s));
   HIP_TRY(launch_compact(g, sel_dev, n, (uint32_t)t, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[1], s));
   PlanArgs a{};
@@ -572,6 +592,44 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
   gh.last_n = n;
   gh.last_pairs = max_pairs;
   return ULA_OK;
+}
+
+int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32_t* sel_dev,
+             uint64_t stream) {
+  if (!ctx) return ULA_EINVAL;
+  const int rc = validate_step(ctx, group, n_sets, k, sel_dev);
+  if (rc) return rc;
+  return step_impl(ctx, group, n_sets, k, sel_dev, stream, nullptr, nullptr);
+}
+
+int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* la_host, const void* rows,
+                    int32_t rows_on_device, int32_t n_sets, int32_t k, const int32_t* sel_dev,
+                    uint64_t stream) {
+  if (!ctx) return ULA_EINVAL;
+  {
+    const int rc = validate_step(ctx, group, n_sets, k, sel_dev);
+    if (rc) return rc;
+  }
+  if (n_app < 0) return ULA_EINVAL;
+  if (n_app > 0) {
+    if (!la_host || !rows) return ULA_EINVAL;
+    const int rc = validate_append(ctx, ctx->groups[group], n_app, la_host);
+    if (rc) return rc;
+  }
+  if (n_app > 0 && n_app <= kSmallAppend && n_app <= ctx->dims.maxApp && rows_on_device) {
+    SmallAppend a{};
+    a.n = n_app;
+    std::memcpy(a.las, la_host, sizeof(int32_t) * n_app);
+    const int rc = step_impl(ctx, group, n_sets, k, sel_dev, stream, &a, static_cast<const uint8_t*>(rows));
+    if (rc) return rc;
+    note_appended(ctx->groups[group], n_app, la_host);
+    return ULA_OK;
+  }
+  if (n_app > 0) {
+    const int rc = ula_append(ctx, group, n_app, la_host, rows, rows_on_device, stream);
+    if (rc) return rc;
+  }
+  return step_impl(ctx, group, n_sets, k, sel_dev, stream, nullptr, nullptr);
 }
 
 int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32_t k,

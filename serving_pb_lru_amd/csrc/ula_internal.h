@@ -198,6 +198,9 @@ hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, int32_t
                           hipStream_t s);
 hipError_t launch_append_small(const GroupDev& g, const SmallAppend& a, const uint8_t* rows,
                               hipStream_t s);
+// the step's tag pass with a small append in the same launch (ula_append_step)
+hipError_t launch_tag_append(const GroupDev& g, const SmallAppend& a, const uint8_t* rows,
+                             const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
 hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s);
 hipError_t launch_release(const GroupDev& g, int32_t n, hipStream_t s);
 hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s);

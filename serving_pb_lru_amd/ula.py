@@ -68,6 +68,9 @@ SIGNATURES = [
                                    ctypes.c_uint64]),
     ("ula_step", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                 ctypes.c_void_p, ctypes.c_uint64]),
+    ("ula_append_step", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.c_uint64]),
     ("ula_gather", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64]),
     ("ula_sync", ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
@@ -170,6 +173,17 @@ class Engine:
         """sel: torch CUDA int32 tensor [n_sets][k] (or [k] for one set)."""
         n_sets, k = (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
         _check(lib().ula_step(self.ctx, group, n_sets, k, sel.data_ptr(), _stream(stream)), "ula_step")
+
+    def append_step(self, group: int, las: np.ndarray, rows, sel, stream=None) -> None:
+        """append(group, las, rows) then step(group, sel), in fewer launches."""
+        las = np.ascontiguousarray(las, dtype=np.int32)
+        on_dev = 1 if hasattr(rows, "is_cuda") and rows.is_cuda else 0
+        if not on_dev:
+            rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        n_sets, k = (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
+        _check(lib().ula_append_step(self.ctx, group, las.size, las.ctypes.data if las.size else None,
+                                     _ptr(rows) if las.size else None, on_dev, n_sets, k, sel.data_ptr(),
+                                     _stream(stream)), "ula_append_step")
 
     def gather(self, group: int, layer: int, sel, out=None, stream=None):
         import torch

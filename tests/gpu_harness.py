@@ -38,7 +38,7 @@ def assert_same_state(st: dict, ref: dict, where: str) -> None:
 
 
 def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, check_every=1,
-               releases=None):
+               releases=None, combined=False):
     """selections: optional {g: list of int32 [n_sets][k]} overriding the trace's.
 
     The state is exported (which writes any staged evicted rows out to the host
@@ -46,6 +46,7 @@ def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, ch
     reach the host pool only through the next step's own write-back. Gathered
     rows are checked after every step. releases: optional {t: int32 addresses}
     released after step t (engine and oracle), before step t+1's appends.
+    combined: each step's appends go with the step in one ula_append_step call.
     """
     import torch
     tr = Trace(wl, steps)
@@ -66,9 +67,12 @@ def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, ch
             for g in groups:
                 sel = next(sels[g])
                 dsel = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
-                if app.size:
-                    eng.append(g, app, rows(app, g))
-                eng.step(g, dsel)
+                if combined:
+                    eng.append_step(g, app, rows(app, g), dsel)
+                else:
+                    if app.size:
+                        eng.append(g, app, rows(app, g))
+                    eng.step(g, dsel)
                 outs = [eng.gather(g, l, dsel) for l in range(wl.layers)]
                 ora[g].append(app, rows_for(wl.seed, g, app, wl.layers, wl.row_bytes))
                 ora[g].step(sel)

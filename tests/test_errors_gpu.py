@@ -99,6 +99,12 @@ def test_host_errors_change_nothing():
             ("EINVAL", lambda: eng.step(1, sel)),
             ("EINVAL", lambda: eng.step(0, _cuda(np.zeros((tr.n_sets + 1, tr.k))))),
             ("EINVAL", lambda: eng.gather(0, 1, sel)),
+            # ula_append_step: a host error in either part enqueues nothing
+            ("ERANGE", lambda: eng.append_step(0, np.array([tr.N]), rows(np.array([0]), 0), sel)),
+            ("EDUP", lambda: eng.append_step(0, np.array([0]), rows(np.array([0]), 0), sel)),
+            ("EINVAL", lambda: eng.append_step(1, app, rows(app, 0), sel)),
+            ("EINVAL", lambda: eng.append_step(0, app, rows(app, 0),
+                                               _cuda(np.zeros((tr.n_sets + 1, tr.k))))),
         ]
         for name, fn in cases:
             with pytest.raises(UlaError) as e:
@@ -106,6 +112,45 @@ def test_host_errors_change_nothing():
             assert e.value.name == name
         eng.sync()
         assert _state(eng) == before
+        eng.append(0, app, rows(app, 0))   # none of the failed calls recorded these addresses
+    finally:
+        eng.close()
+
+
+@pytest.mark.parametrize("policy", [0, 1], ids=["pblru", "lru"])
+def test_append_step_device_error_keeps_the_append(policy):
+    """A step that selects a never appended address fails on the device (ERANGE at
+    ula_sync) and changes nothing; the append that came with it in ula_append_step
+    has taken place, as it would have with ula_append before ula_step."""
+    from oracle.replay import initial_load as oracle_load, new_group
+    from serving_pb_lru_amd import UlaError
+    from serving_pb_lru_amd.replay import engine_for, initial_load
+    from synth.device import rows_device
+    tr = Trace(preset("tiny_4x4k"))
+    wl = tr.wl
+    eng = engine_for(tr, max_append=4096, policy=policy)
+    rows = lambda las: rows_device(las, wl.layers, wl.row_bytes, wl.seed, 0)
+    try:
+        initial_load(eng, tr, [0], lambda las, g: rows(las))
+        sel = next(tr.selections(0)).copy()
+        app = tr.appends(1)
+        sel[0, 3] = tr.appends(2)[0]               # appended only at step 2
+        eng.append_step(0, app, rows(app), _cuda(sel))
+        with pytest.raises(UlaError) as e:
+            eng.sync()
+        assert e.value.name == "ERANGE"
+        st = eng.export_state(0)
+        if policy == 0:
+            ora = new_group(tr, full_data=False)
+            oracle_load(ora, tr, 0)
+            ora.append(app, None)
+            ref = ora.export_state()
+            for key in ("map", "gown", "hown", "bitsets"):
+                assert np.array_equal(np.asarray(st[key]), np.asarray(ref[key])), key
+            assert (st["flag"], tuple(st["stats"])) == (ref["flag"], tuple(ref["stats"]))
+        else:
+            assert st["flag"] == 0
+        assert all(st["map"][la] != 0xFFFFFFFF for la in app)
     finally:
         eng.close()
 

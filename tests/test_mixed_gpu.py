@@ -4,7 +4,9 @@ Each seed draws a small workload with one to three layer groups, one of the two
 policies, a random ring, and per step and group a random way to append: rows in
 device memory or in host memory, with a per-call append limit small enough that
 most appends run in several chunks (the plan / extract / place kernels) and the
-rest in the one-workgroup path. Finished entries are released between steps.
+rest in the one-workgroup path, through ula_append before ula_step or through
+ula_append_step (which runs a small device-memory append in the step's first
+launch). Finished entries are released between steps.
 After every step (and every release) each group's exported state must equal its
 oracle's, and every gathered byte must equal the closed form of its row.
 """
@@ -72,17 +74,23 @@ def test_mixed_paths_random(seed):
             app = tr.appends(t)
             for g in range(groups):
                 sel = sels[g][t - 1]
+                dsel = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
+                combined = rng.random() < 0.5     # ula_append_step, else ula_append + ula_step
+                rows = np.zeros((0, wl.layers, wl.row_bytes), np.uint8)
                 if app.size:
                     host_rows = rng.random() < 0.5
                     rows = (rows_for(wl.seed, g, app, wl.layers, wl.row_bytes) if host_rows
                             else rows_dev(app, g))
-                    eng.append(g, app, rows)
                     if policy == 0:
                         ora[g].append(app, rows_for(wl.seed, g, app, wl.layers, wl.row_bytes))
                     else:
                         ora[g].append(app)
-                dsel = torch.from_numpy(np.ascontiguousarray(sel, dtype=np.int32)).cuda()
-                eng.step(g, dsel)
+                if combined:
+                    eng.append_step(g, app, rows, dsel)
+                else:
+                    if app.size:
+                        eng.append(g, app, rows)
+                    eng.step(g, dsel)
                 outs = [eng.gather(g, l, dsel) for l in range(wl.layers)]
                 ora[g].step(sel)
                 eng.sync()

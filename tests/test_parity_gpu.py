@@ -70,6 +70,24 @@ def test_random_tiny_parity(seed):
     run_parity(wl, selections={0: padded_selections(tr, 0, seed)}, max_append=7)
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_append_step_parity(seed):
+    """ula_append_step (the step's appends in its first launch beside the tag pass)
+    gives the same state and gathered bytes as ula_append then ula_step."""
+    wl = dataclasses.replace(tiny_workload(seed), appends=1 + seed % 3)
+    tr = Trace(wl)
+    run_parity(wl, selections={0: padded_selections(tr, 0, seed)}, max_append=64, combined=True)
+
+
+@pytest.mark.parametrize("name,factor,steps", [
+    ("r16_64k_g1x3", 16, 8),
+    ("spec3_r128_64k128k_g4", 32, 5),
+])
+def test_append_step_scaled_parity(name, factor, steps):
+    wl = scaled(preset(name), factor)
+    run_parity(wl, steps=steps, max_append=1 << 15, check_every=2, combined=True)
+
+
 @pytest.mark.parametrize("ring", [1, 2, 9, 64])   # 64: the longest ring the engine takes
 def test_ring_lengths_parity(ring):
     wl = dataclasses.replace(preset("tiny_4x4k"), ring=ring, name=f"tiny_ring{ring}")
