@@ -4,8 +4,12 @@
 One step = the whole per-decode-step path for every layer group of the
 workload: the step's appends and the step in one ula_append_step call (the
 appends, de-duplication and lookup, fold and hit marking, victim selection, the
-miss path over the host link, commit and completion signal) and one ula_gather
-per layer of the group. Inputs (selection sets for every step
+miss path over the host link, commit and completion signal), then the gather
+of the group's first layer (ula_gather) and of its later layers in one
+ula_gather_layers launch (the layers of a group share the selection, and the
+later ones are fetched together while the first is in use; --gather layer
+gathers each layer by its own ula_gather call, --gather all every layer in one
+launch). Inputs (selection sets for every step
 and the appended rows) are resident in HBM before the timed region; the GPU
 pool starts full (initial load untimed). W warm-up steps run first (they carry
 the cold-start misses), then exactly K steps are timed between two device
@@ -16,10 +20,12 @@ value = selected row-layers resolved and gathered per second
 
 Printed as one JSON line, with:
   roofline      the gather kernel against HBM peak (1312 algorithmic bytes per
-                gathered row-layer: 656 read + 656 written), its average kernel
-                duration over the timed region from HIP events that every gather
-                records in its own dispatch on the engine's stream (the kernel's
-                execution, as rocprofv3 reports it);
+                gathered row-layer: 656 read + 656 written; bytes per launch =
+                the timed region's row-layers over its gather launches, which
+                on the default split are 1 and layers - 1 layers each), its
+                average kernel duration over the timed region from HIP events
+                that every gather records in its own dispatch on the engine's
+                stream (the kernel's execution, as rocprofv3 reports it);
   miss_path     the miss path against the host link, per direction: missed rows
                 in (656 * layers bytes per miss) and the previous step's
                 evicted rows out (656 * layers bytes per eviction), both moved
@@ -74,6 +80,10 @@ def parse():
     p.add_argument("--policy", choices=("pblru", "lru"), default="pblru",
                    help="replacement policy: PB-LRU (the pages' policy) or exact LRU (the one it is "
                         "compared against); the CPU baseline is reported for PB-LRU only")
+    p.add_argument("--gather", choices=("layer", "split", "all"), default="split",
+                   help="gathers per group step: one per layer (ula_gather); layer 0 alone, then the "
+                        "later layers in one ula_gather_layers launch (default); or every layer in "
+                        "one launch")
     p.add_argument("--layer-prefetch", type=float, default=0.0, metavar="US",
                    help="only run the later-layer prefetch experiment with US microseconds of "
                         "synthetic compute per layer, and print its own JSON line")
@@ -125,13 +135,14 @@ def copy_ceiling(nbytes: int, copies: int = 64) -> None:
           flush=True)
 
 
-def gather_traffic(workload: str):
+def gather_traffic(workload: str, mode: str = "layer"):
     """HBM bytes per gather launch from the committed rocprofv3 counter record
     (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or
-    None when there is no record for this workload or the kernel source changed
-    since the counters were taken."""
+    None when there is no record for this workload and gather mode or the kernel
+    source changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_k_gather_{workload}.json")
+    suffix = "" if mode == "layer" else f"_{mode}"
+    path = os.path.join(ROOT, "profiles", f"traffic_k_gather_{workload}{suffix}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -196,7 +207,22 @@ def cpu_baseline(tr, W: int, K: int, seconds: float) -> dict:
 
 
 # ---------------------------------------------------------------------------
-def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
+def gather_all_layers(eng, g, sel, outs, layers, mode, stream=None):
+    """Every layer of group g's selection into outs ([layers][n_sets][k][row_bytes]):
+    one ula_gather per layer, layer 0 alone and the later layers in one
+    ula_gather_layers launch ("split"), or all layers in one launch ("all")."""
+    if mode == "layer":
+        for l in range(layers):
+            eng.gather(g, l, sel, out=outs[l], stream=stream)
+    elif mode == "all":
+        eng.gather_layers(g, 0, layers, sel, out=outs, stream=stream)
+    else:
+        eng.gather(g, 0, sel, out=outs[0], stream=stream)
+        if layers > 1:
+            eng.gather_layers(g, 1, layers - 1, sel, out=outs[1:], stream=stream)
+
+
+def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str = "layer") -> dict:
     import torch
 
     from serving_pb_lru_amd.replay import engine_for, initial_load
@@ -213,8 +239,9 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
     sels = {g: [torch.from_numpy(s).cuda() for s in tr.selections(g)] for g in groups}
     apps = [tr.appends(t) for t in range(1, tr.steps + 1)]
     app_rows = {g: [rows(a, g) for a in apps] for g in groups}
-    outs = {g: [torch.empty((tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
-                for _ in range(wl.layers)] for g in groups}
+    # one buffer per group: its layers' gathered rows one after the other
+    outs = {g: torch.empty((wl.layers, tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
+            for g in groups}
 
     def run_step(eng, t):
         for g in groups:
@@ -222,8 +249,7 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0) -> dict:
             # the step's appends and the step in one call (the appends run in the
             # step's first launch when they are small)
             eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel)
-            for l in range(wl.layers):
-                eng.gather(g, l, sel, out=outs[g][l])
+            gather_all_layers(eng, g, sel, outs[g], wl.layers, gather_mode)
 
     # ---- timed replay ----------------------------------------------------
     eng = engine_for(tr, max_append=1 << 16, policy=policy)
@@ -335,7 +361,9 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
       serial    one stream: step, then per layer gather and compute;
       prefetch  the step and layer 0's gather on the main stream; layers 1.. gathered
                 on a second stream ordered after the step by an event; layer l's
-                compute waits for its gather's event.
+                compute waits for its gather's event;
+      prefetch_one_launch  as prefetch, with layers 1.. gathered by one
+                ula_gather_layers launch (one event for all of them).
     Two stand-ins for the compute: a single-lane spin (occupies no resources: the
     upper bound of what overlap can hide) and a bf16 matrix product sized to the
     same duration (occupies the matrix cores of the whole chip, like attention
@@ -355,8 +383,8 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
     sels = {g: [torch.from_numpy(s).cuda() for s in tr.selections(g)] for g in groups}
     apps = [tr.appends(t) for t in range(1, tr.steps + 1)]
     app_rows = {g: [rows(a, g) for a in apps] for g in groups}
-    outs = {g: [torch.empty((tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
-                for _ in range(wl.layers)] for g in groups}
+    outs = {g: torch.empty((wl.layers, tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
+            for g in groups}
 
     def timed(fn, reps=20):
         for _ in range(3):
@@ -387,7 +415,7 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
     results = []
     for kind, (compute, c_us) in stand_ins.items():
         per = {}
-        for sched in ("serial", "prefetch"):
+        for sched in ("serial", "prefetch", "prefetch_one_launch"):
             eng = engine_for(tr, max_append=1 << 16)
             initial_load(eng, tr, groups, rows)
             torch.cuda.synchronize()
@@ -408,14 +436,21 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
                     after_step.record(main_s)
                     side_s.wait_event(after_step)
                     ready = []
-                    for l in range(1, wl.layers):
-                        eng.gather(g, l, sel, out=outs[g][l], stream=side_s)
+                    if sched == "prefetch_one_launch" and wl.layers > 1:
+                        eng.gather_layers(g, 1, wl.layers - 1, sel, out=outs[g][1:], stream=side_s)
                         ev = torch.cuda.Event()
                         ev.record(side_s)
-                        ready.append(ev)
+                        ready = [ev] + [None] * (wl.layers - 2)
+                    else:
+                        for l in range(1, wl.layers):
+                            eng.gather(g, l, sel, out=outs[g][l], stream=side_s)
+                            ev = torch.cuda.Event()
+                            ev.record(side_s)
+                            ready.append(ev)
                     compute()
                     for ev in ready:
-                        main_s.wait_event(ev)
+                        if ev is not None:
+                            main_s.wait_event(ev)
                         compute()
 
             for t in range(1, W + 1):
@@ -439,9 +474,11 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
             "matmul_n": n_mm if kind == "bf16_matmul" else None,
             "layers_per_group": wl.layers, "groups": wl.groups, "steps": K, "warmup": W,
             "serial_ms_per_step": round(per["serial"], 5), "prefetch_ms_per_step": round(per["prefetch"], 5),
+            "prefetch_one_launch_ms_per_step": round(per["prefetch_one_launch"], 5),
             "hidden_us_per_step": round((per["serial"] - per["prefetch"]) * 1e3, 2),
-            "host_enqueue_ms_per_step": {"serial": round(per["serial_host"], 5),
-                                         "prefetch": round(per["prefetch_host"], 5)},
+            "hidden_us_per_step_one_launch": round((per["serial"] - per["prefetch_one_launch"]) * 1e3, 2),
+            "host_enqueue_ms_per_step": {k: round(per[k + "_host"], 5)
+                                         for k in ("serial", "prefetch", "prefetch_one_launch")},
             "compute_only_ms_per_step": round(c_us * wl.layers * wl.groups * 1e-3, 5)})
     return results
 
@@ -481,17 +518,23 @@ def main():
     if not args.no_cpu_baseline and policy == 0:
         cpu = cpu_baseline(tr, W, K, args.cpu_seconds)
 
-    r = gpu_run(tr, W, K, not args.no_phases, policy)
+    gather_mode = args.gather if wl.layers > 1 else "layer"   # one layer: the same launch
+    r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode)
     value = per_step * K / r["wall_s"]
     ms_per_step = r["event_ms"] / K
 
     g_ms = float(r["gather_ms"])
-    rows_per_gather = tr.n_sets * tr.k
-    g_bytes = 2 * wl.row_bytes * rows_per_gather
+    # algorithmic bytes per launch: every gathered row-layer of the timed region
+    # over the gather launches that moved them
+    launches_per_group_step = {"layer": wl.layers, "all": 1, "split": 2}[gather_mode]
+    g_bytes = 2 * wl.row_bytes * tr.n_sets * tr.k * wl.layers / launches_per_group_step
+    assert r["gather_launches"] == K * wl.groups * launches_per_group_step, r["gather_launches"]
     g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "kernel": "k_gather", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4), "traffic": gather_traffic(wl.name),
-                "bytes_per_launch": g_bytes, "launch_ms": round(g_ms, 5)}
+                "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                "traffic": gather_traffic(wl.name, gather_mode),
+                "bytes_per_launch": round(g_bytes), "launch_ms": round(g_ms, 5),
+                "layers_per_launch": round(wl.layers / launches_per_group_step, 3)}
     miss = None
     if "phase_ms" in r:
         slot = wl.layers * wl.row_bytes
@@ -535,7 +578,7 @@ def main():
                    "groups_of_workload": groups_total,
                    "layers_per_group": wl.layers, "k": wl.k, "gpu_slots": tr.P, "host_slots": tr.H,
                    "ring": wl.ring, "row_bytes": wl.row_bytes, "overlap": wl.overlap,
-                   "policy": "exact LRU" if policy else "PB-LRU",
+                   "policy": "exact LRU" if policy else "PB-LRU", "gather": gather_mode,
                    "row_layers_per_step": per_step},
         "roofline": roofline,
         "miss_path": miss,

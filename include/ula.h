@@ -216,6 +216,19 @@ int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* l
 int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32_t k,
                const int32_t* sel_dev, void* out_dev, uint64_t stream);
 
+/* Gather layers layer0 .. layer0 + n_layers - 1 of every selected entry of
+ * group g in one launch (section 2: the layers of a group share one selection,
+ * and the later layers are fetched while an earlier one is in use). out_dev
+ * (device memory) holds n_layers per-layer buffers one after the other, each
+ * n_sets x k x row_bytes bytes laid out as ula_gather writes it: the result is
+ * exactly that of ula_gather(layer0 + i, out_dev + i * n_sets * k * row_bytes)
+ * for each i. Since a slot keeps its layers side by side, each entry's layers
+ * are read as one contiguous run. Same checks and errors as ula_gather, plus
+ * ULA_EINVAL unless 0 <= layer0, 1 <= n_layers and layer0 + n_layers <=
+ * layers_per_group. */
+int ula_gather_layers(ula_ctx* ctx, int32_t group, int32_t layer0, int32_t n_layers, int32_t n_sets,
+                      int32_t k, const int32_t* sel_dev, void* out_dev, uint64_t stream);
+
 /* Wait for `stream`, then report the first latched device error of any group
  * (poisoning the context) or ULA_OK. per_group_out (nullable, num_groups
  * entries) receives each group's last step statistics. */

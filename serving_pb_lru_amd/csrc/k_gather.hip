@@ -5,7 +5,11 @@
 // reading the new locations (section 3); layers sharing one selection read the
 // same entries (section 2), so this kernel runs once per layer of a group.
 //
-// out[j][i][:] = pool[map[sel[j][i]]][layer][:], or zeros for -1 padding. The
+// out[l][j][i][:] = pool[map[sel[j][i]]][layer0 + l][:] for the nl layers of
+// one launch (one per-layer buffer each, layer_stride apart), or zeros for -1
+// padding. A slot keeps its layers side by side, so the nl rows of one entry
+// are one contiguous source run; the later layers of a group can be fetched
+// together while the first one is in use (section 2). The
 // step already resolved its selection to slots entry by entry (the lookup is
 // done once per group); a gather of that selection reads those slots in order
 // and only entries that differ fall back to the mapping table. A
@@ -13,32 +17,79 @@
 // (selection entry and resolved slot in one round trip, else the mapping
 // table) into LDS, then all lanes stream the rows in 16-byte pieces,
 // C = row_bytes / 16 pieces per row, lane i taking piece (i mod C) of row
-// (i div C): consecutive lanes write consecutive 16 bytes (fully coalesced,
-// non-temporal stores) and read one contiguous source row. UNROLL pieces per
-// lane are in flight; for 656-byte rows both tilings below cover all staged
-// rows in one round. Bound by HBM bandwidth.
+// (i div C), layer by layer: consecutive lanes write consecutive 16 bytes
+// (fully coalesced, non-temporal stores) and read one contiguous source row.
+// UNROLL pieces per lane are in flight; for 656-byte rows both tilings below
+// cover all staged rows of one layer in one round. Bound by HBM bandwidth.
 //
 // Tilings (measured on MI355X with 656-byte rows): a small gather (up to 64K
-// rows, a few workgroups per compute unit) is fastest with 64 rows and 11 pieces
-// in flight per lane of 256; a large one (131K rows and more) with 32 rows and 3
-// pieces per lane of 512, which keeps more workgroups resident.
+// row-layers, a few workgroups per compute unit) is fastest with 64 rows and 11
+// pieces in flight per lane of 256; a large one (131K row-layers and more) with
+// 32 rows and 3 pieces per lane of 512, which keeps more workgroups resident.
 #include <hip/hip_ext.h>
 
 #include "device_util.h"
 
 namespace ula {
 
-constexpr int kSmallGatherRows = 1 << 16;   // up to this many rows: the small-gather tiling
+constexpr int kSmallGatherRows = 1 << 16;   // up to this many row-layers: the small-gather tiling
 
+// Streams the staged rows of one block, layer by layer: piece i is piece
+// (i mod C) of staged row q = i div C, which is row (q mod nrows) of layer
+// (q div nrows); layer l's output rows start layer_stride pieces after layer
+// l - 1's. s_off[r]: source offset of row r's first layer (-1: zero row).
+// MULTI = false is the one-layer case, without the layer arithmetic.
 // Rows are read with plain (cached) loads: repeated entries of one step (the
 // speculative sets) and the heavy overlap between consecutive steps both hit the
 // caches; non-temporal loads measured 18% slower on the speculative workload and
 // only 3% faster where nothing repeats.
+template <int ROWS, int UNROLL, int THREADS, bool MULTI>
+__device__ __forceinline__ void stream_rows(const GroupDev& g, const long long* s_off, int nrows, int nl,
+                                            size_t layer_stride, vec4u* o, uint32_t C, FastDiv per_row) {
+  const uint32_t per_layer = (uint32_t)nrows * C;
+  const uint32_t pieces = MULTI ? per_layer * (uint32_t)nl : per_layer;
+  for (uint32_t i0 = threadIdx.x; i0 < pieces; i0 += THREADS * UNROLL) {
+    vec4u v[UNROLL];
+    vec4u* dst[UNROLL];
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
+      const uint32_t i = i0 + u * THREADS;
+      v[u] = vec4u{0u, 0u, 0u, 0u};
+      dst[u] = nullptr;
+      if (i < pieces) {
+        const uint32_t q = per_row.div(i);
+        uint32_t l = 0, r = q;
+        if (MULTI) {
+          if (nrows == ROWS) {   // block-uniform: every block but the last
+            l = q / ROWS;
+            r = q % ROWS;
+          } else {
+            l = q / (uint32_t)nrows;
+            r = q - l * (uint32_t)nrows;
+          }
+        }
+        const long long off = s_off[r];
+        if (off >= 0) {
+          const vec4u* p = reinterpret_cast<const vec4u*>(g.pool + off + (size_t)l * g.row_bytes +
+                                                          (size_t)(i - q * C) * 16);
+          v[u] = *p;
+        }
+        dst[u] = MULTI ? o + (size_t)l * layer_stride + (i - l * per_layer) : o + i;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u)
+      if (dst[u]) __builtin_nontemporal_store(v[u], dst[u]);
+  }
+}
+
 template <int ROWS, int UNROLL, int THREADS>
 __global__ __launch_bounds__(THREADS) void k_gather(GroupDev g, const int32_t* __restrict__ sel, int32_t n,
-                                                    int32_t layer, uint8_t* __restrict__ out,
-                                                    long long want_flag, int32_t n_res, FastDiv per_row) {
+                                                    int32_t layer, int32_t nl, size_t layer_stride,
+                                                    uint8_t* __restrict__ out, long long want_flag,
+                                                    int32_t n_res, FastDiv per_row) {
   static_assert(ROWS < THREADS, "one lane per staged row plus the checking lane");
+  static_assert((ROWS & (ROWS - 1)) == 0, "full blocks split piece indexes with shifts");
   __shared__ long long s_off[ROWS];   // source byte offset of each staged row, -1 = zero row
   __shared__ int s_ok;
   const uint32_t C = (uint32_t)g.row_bytes / 16u;
@@ -101,58 +152,43 @@ __global__ __launch_bounds__(THREADS) void k_gather(GroupDev g, const int32_t* _
       if (!s_ok) return;   // block-uniform
       first_round = false;
     }
-    // 2. stream the staged rows: piece i of the block is piece (i mod C) of row (i div C)
+    // 2. stream the staged rows (one layer: no layer arithmetic per piece)
     const int nrows = min(ROWS, n - row0);
-    const uint32_t pieces = (uint32_t)nrows * C;
     vec4u* o = reinterpret_cast<vec4u*>(out) + (size_t)row0 * C;
-    for (uint32_t i0 = threadIdx.x; i0 < pieces; i0 += THREADS * UNROLL) {
-      vec4u v[UNROLL];
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const uint32_t i = i0 + u * THREADS;
-        v[u] = vec4u{0u, 0u, 0u, 0u};
-        if (i < pieces) {
-          const uint32_t r = per_row.div(i);
-          const long long off = s_off[r];
-          if (off >= 0) {
-            const vec4u* p = reinterpret_cast<const vec4u*>(g.pool + off + (size_t)(i - r * C) * 16);
-            v[u] = *p;
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u) {
-        const uint32_t i = i0 + u * THREADS;
-        if (i < pieces) __builtin_nontemporal_store(v[u], o + i);
-      }
-    }
+    if (nl == 1)   // kernel-uniform
+      stream_rows<ROWS, UNROLL, THREADS, false>(g, s_off, nrows, 1, 0, o, C, per_row);
+    else
+      stream_rows<ROWS, UNROLL, THREADS, true>(g, s_off, nrows, nl, layer_stride, o, C, per_row);
     __syncthreads();
   }
   if (err) latch(g.ctr, err);
 }
 
 template <int ROWS, int UNROLL, int THREADS>
-static hipError_t launch_tiled(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer, uint8_t* out,
-                               long long want_flag, int32_t n_res, hipStream_t s, hipEvent_t start,
-                               hipEvent_t stop) {
+static hipError_t launch_tiled(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer, int32_t nl,
+                               uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s,
+                               hipEvent_t start, hipEvent_t stop) {
   int blocks = (n + ROWS - 1) / ROWS;
   if (blocks > 32768) blocks = 32768;
-  const FastDiv per_row((uint32_t)g.row_bytes / 16u);
+  const uint32_t C = (uint32_t)g.row_bytes / 16u;
+  const size_t layer_stride = (size_t)n * C;
+  const FastDiv per_row(C);
   if (start)
     hipExtLaunchKernelGGL(k_gather<ROWS, UNROLL, THREADS>, dim3(blocks), dim3(THREADS), 0, s, start, stop, 0,
-                          g, sel, n, layer, out, want_flag, n_res, per_row);
+                          g, sel, n, layer, nl, layer_stride, out, want_flag, n_res, per_row);
   else
-    k_gather<ROWS, UNROLL, THREADS><<<blocks, THREADS, 0, s>>>(g, sel, n, layer, out, want_flag, n_res, per_row);
+    k_gather<ROWS, UNROLL, THREADS><<<blocks, THREADS, 0, s>>>(g, sel, n, layer, nl, layer_stride, out,
+                                                               want_flag, n_res, per_row);
   return hipGetLastError();
 }
 
-hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
+hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer, int32_t nl,
                          uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop) {
-  if (n <= 0) return hipSuccess;
-  if (n <= kSmallGatherRows)
-    return launch_tiled<64, 11, 256>(g, sel, n, layer, out, want_flag, n_res, s, start, stop);
-  return launch_tiled<32, 3, 512>(g, sel, n, layer, out, want_flag, n_res, s, start, stop);
+  if (n <= 0 || nl <= 0) return hipSuccess;
+  if ((int64_t)n * nl <= kSmallGatherRows)
+    return launch_tiled<64, 11, 256>(g, sel, n, layer, nl, out, want_flag, n_res, s, start, stop);
+  return launch_tiled<32, 3, 512>(g, sel, n, layer, nl, out, want_flag, n_res, s, start, stop);
 }
 
 }  // namespace ula

@@ -632,12 +632,14 @@ int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* l
   return step_impl(ctx, group, n_sets, k, sel_dev, stream, nullptr, nullptr);
 }
 
-int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32_t k,
-               const int32_t* sel_dev, void* out_dev, uint64_t stream) {
+// Layers layer0 .. layer0 + nl - 1 of the selection, one launch.
+static int gather_impl(ula_ctx* ctx, int32_t group, int32_t layer0, int32_t nl, int32_t n_sets, int32_t k,
+                       const int32_t* sel_dev, void* out_dev, uint64_t stream) {
   if (!ctx) return ULA_EINVAL;
   if (ctx->poisoned) return ULA_ESTATE;
   if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
-  if (layer < 0 || layer >= ctx->cfg.layers_per_group) return ULA_EINVAL;
+  if (layer0 < 0 || nl < 1 || layer0 >= ctx->cfg.layers_per_group || nl > ctx->cfg.layers_per_group - layer0)
+    return ULA_EINVAL;
   if (n_sets < 0 || k < 0 || n_sets > ctx->cfg.max_sets || k > ctx->cfg.max_k) return ULA_EINVAL;
   const int32_t n = n_sets * k;
   if (n > 0 && (!sel_dev || !out_dev)) return ULA_EINVAL;
@@ -658,9 +660,19 @@ int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32
     ctx->gt_head = (ctx->gt_head + 1) % kGatherTimingRing;
     ctx->gt_pending += 1;
   }
-  HIP_TRY(launch_gather(gh.d, sel_dev, n, layer, static_cast<uint8_t*>(out_dev), (long long)gh.steps,
+  HIP_TRY(launch_gather(gh.d, sel_dev, n, layer0, nl, static_cast<uint8_t*>(out_dev), (long long)gh.steps,
                         gh.last_n, reinterpret_cast<hipStream_t>(stream), start, stop));
   return ULA_OK;
+}
+
+int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32_t k,
+               const int32_t* sel_dev, void* out_dev, uint64_t stream) {
+  return gather_impl(ctx, group, layer, 1, n_sets, k, sel_dev, out_dev, stream);
+}
+
+int ula_gather_layers(ula_ctx* ctx, int32_t group, int32_t layer0, int32_t n_layers, int32_t n_sets,
+                      int32_t k, const int32_t* sel_dev, void* out_dev, uint64_t stream) {
+  return gather_impl(ctx, group, layer0, n_layers, n_sets, k, sel_dev, out_dev, stream);
 }
 
 static int read_counters(ula_ctx* ctx, std::vector<Counters>& out) {

@@ -212,7 +212,9 @@ hipError_t launch_lru_order(const GroupDev& g, uint32_t t, int32_t max_pairs, hi
 
 // start / stop (both or neither): events recorded by the dispatch itself, so
 // that their interval is the kernel's execution
-hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer,
+// layers layer .. layer + nl - 1, each into its own n-row buffer, one after
+// the other from out
+hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32_t layer, int32_t nl,
                          uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop);
 

@@ -1,5 +1,7 @@
-"""Drive a decode trace through the engine (initial load, then per step: appends,
-the group's step, one gather per layer). Used by the GPU tests and bench.py.
+"""Drive a decode trace through the engine (initial load, then per step: the
+step's appends and the step in one call, then the group's layers: the first
+gathered alone, the later ones in one launch). Used by the GPU tests, smoke()
+and bench.py.
 
 The trace object supplies the addresses (initial_load_order, appends(t),
 selections(g)); `rows(las, g)` supplies the appended rows as a CUDA tensor.
@@ -29,14 +31,16 @@ def initial_load(eng: Engine, trace, groups, rows) -> None:
             eng.append(g, las, rows(las, g))
 
 
-def step_all(eng: Engine, trace, t: int, sels, groups, rows, outs=None):
-    """Step t for the given groups. sels[g]: CUDA int32 [n_sets][k]. Returns gathered tensors."""
+def step_all(eng: Engine, trace, t: int, sels, groups, rows):
+    """Step t for the given groups. sels[g]: CUDA int32 [n_sets][k]. Returns, per
+    group, one gathered tensor per layer."""
     app = trace.appends(t)
+    layers = trace.wl.layers
     gathered = {}
     for g in groups:
-        if app.size:
-            eng.append(g, app, rows(app, g))
-        eng.step(g, sels[g])
-        gathered[g] = [eng.gather(g, l, sels[g], out=None if outs is None else outs[g][l])
-                       for l in range(trace.wl.layers)]
+        eng.append_step(g, app, rows(app, g), sels[g])
+        outs = [eng.gather(g, 0, sels[g])]
+        if layers > 1:
+            outs += list(eng.gather_layers(g, 1, layers - 1, sels[g]))
+        gathered[g] = outs
     return gathered

@@ -73,6 +73,9 @@ SIGNATURES = [
                                        ctypes.c_void_p, ctypes.c_uint64]),
     ("ula_gather", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64]),
+    ("ula_gather_layers", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_uint64]),
     ("ula_sync", ctypes.c_int, [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]),
     ("ula_export_state", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(UlaStateHost)]),
     ("ula_read_rows", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -192,6 +195,16 @@ class Engine:
             out = torch.empty((n_sets, k, self.row_bytes), dtype=torch.uint8, device=sel.device)
         _check(lib().ula_gather(self.ctx, group, layer, n_sets, k, sel.data_ptr(), out.data_ptr(),
                                 _stream(stream)), "ula_gather")
+        return out
+
+    def gather_layers(self, group: int, layer0: int, n_layers: int, sel, out=None, stream=None):
+        """Layers layer0 .. layer0 + n_layers - 1 in one launch: out[i] is gather(layer0 + i)."""
+        import torch
+        n_sets, k = (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
+        if out is None:
+            out = torch.empty((n_layers, n_sets, k, self.row_bytes), dtype=torch.uint8, device=sel.device)
+        _check(lib().ula_gather_layers(self.ctx, group, layer0, n_layers, n_sets, k, sel.data_ptr(),
+                                       out.data_ptr(), _stream(stream)), "ula_gather_layers")
         return out
 
     def sync(self, stream=None) -> List[tuple]:

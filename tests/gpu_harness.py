@@ -37,8 +37,23 @@ def assert_same_state(st: dict, ref: dict, where: str) -> None:
     assert tuple(st["stats"]) == tuple(ref["stats"]), f"{where}: stats {st['stats']} vs {ref['stats']}"
 
 
+def gather_layers_by(eng, g, layers, dsel, mode):
+    """Every layer of group g's selection, as one tensor per layer, gathered by
+    per-layer calls ("layer"), one call for all layers ("all"), or layer 0 alone
+    and the later layers in one call ("split")."""
+    if mode == "layer":
+        return [eng.gather(g, l, dsel) for l in range(layers)]
+    if mode == "all":
+        return list(eng.gather_layers(g, 0, layers, dsel))
+    assert mode == "split", mode
+    outs = [eng.gather(g, 0, dsel)]
+    if layers > 1:
+        outs += list(eng.gather_layers(g, 1, layers - 1, dsel))
+    return outs
+
+
 def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, check_every=1,
-               releases=None, combined=False):
+               releases=None, combined=False, gather_mode="layer"):
     """selections: optional {g: list of int32 [n_sets][k]} overriding the trace's.
 
     The state is exported (which writes any staged evicted rows out to the host
@@ -47,6 +62,9 @@ def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, ch
     rows are checked after every step. releases: optional {t: int32 addresses}
     released after step t (engine and oracle), before step t+1's appends.
     combined: each step's appends go with the step in one ula_append_step call.
+    gather_mode: "layer" (one ula_gather per layer), "all" (one ula_gather_layers
+    for every layer) or "split" (layer 0 alone, the later layers in one
+    ula_gather_layers call).
     """
     import torch
     tr = Trace(wl, steps)
@@ -73,7 +91,7 @@ def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, ch
                     if app.size:
                         eng.append(g, app, rows(app, g))
                     eng.step(g, dsel)
-                outs = [eng.gather(g, l, dsel) for l in range(wl.layers)]
+                outs = gather_layers_by(eng, g, wl.layers, dsel, gather_mode)
                 ora[g].append(app, rows_for(wl.seed, g, app, wl.layers, wl.row_bytes))
                 ora[g].step(sel)
                 eng.sync()

@@ -155,6 +155,49 @@ def test_append_step_device_error_keeps_the_append(policy):
         eng.close()
 
 
+def test_gather_layers_errors():
+    """ula_gather_layers: a window outside the group's layers or an empty one is
+    ULA_EINVAL, no step yet is ULA_ENOTRESIDENT, an empty selection is a no-op, and
+    a host-resident entry latches ULA_ENOTRESIDENT on the device as for ula_gather;
+    none of them changes the state."""
+    import torch
+    from serving_pb_lru_amd import UlaError
+    wl = dataclasses.replace(preset("tiny_4x4k"), layers=3, name="tiny_l3")
+    tr, eng, rows = _engine(wl)
+    try:
+        sel = next(tr.selections(0))
+        d = _cuda(sel)
+        with pytest.raises(UlaError) as e:
+            eng.gather_layers(0, 0, 3, d)         # no step yet
+        assert e.value.name == "ENOTRESIDENT"
+        app = tr.appends(1)
+        eng.append_step(0, app, rows(app, 0), d)
+        eng.sync()
+        before = _state(eng)
+        for l0, nl in [(-1, 1), (0, 0), (0, 4), (1, 3), (2, 2), (3, 1), (0, -1)]:
+            with pytest.raises(UlaError) as e:
+                eng.gather_layers(0, l0, nl, d, out=torch.empty((4, *sel.shape, wl.row_bytes),
+                                                                dtype=torch.uint8, device="cuda"))
+            assert e.value.name == "EINVAL", (l0, nl)
+        with pytest.raises(UlaError) as e:
+            eng.gather_layers(1, 0, 1, d)          # no such group
+        assert e.value.name == "EINVAL"
+        empty = _cuda(np.zeros((0, tr.k)))
+        out = eng.gather_layers(0, 0, 3, empty)
+        assert out.shape == (3, 0, tr.k, wl.row_bytes)
+        eng.sync()
+        assert _state(eng) == before
+        st = eng.export_state(0)
+        on_host = int(np.flatnonzero(st["map"] & 0x80000000 != 0)[0])
+        eng.gather_layers(0, 1, 2, _cuda([[on_host]]))
+        with pytest.raises(UlaError) as e:
+            eng.sync()
+        assert e.value.name == "ENOTRESIDENT"
+        assert _state(eng) == before
+    finally:
+        eng.close()
+
+
 def test_host_pool_full_rejected():
     from serving_pb_lru_amd import Engine, UlaError
     eng = Engine(1, 1, 64, 2, logical_capacity=16, gpu_slots=4, host_slots=4, max_sets=1, max_k=4)

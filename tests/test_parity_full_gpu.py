@@ -1,5 +1,10 @@
 """Full-size parity on the GPU: every workload preset at its real sizes.
 
+The PB-LRU cases drive the engine as bench.py does (each step's appends and
+the step in one ula_append_step call; layer 0 gathered alone, the later layers
+of the group in one ula_gather_layers launch); the exact-LRU cases use the
+separate calls (ula_append, ula_step, one ula_gather per layer).
+
 After the initial load and after every other step (and the last) the digest
 of the engine's exported state (mapping table, owners, bucket bitsets, current
 bucket, completion counter, step statistics) must equal the digest the CPU
@@ -27,7 +32,7 @@ import numpy as np
 import pytest
 
 from digests import digest
-from gpu_harness import say
+from gpu_harness import gather_layers_by, say
 from synth import Trace, preset, rows_for
 
 pytestmark = pytest.mark.gpu
@@ -46,7 +51,7 @@ def _cmp(got, want, where):
             assert got[k] == want[k], f"{where}: {k} differs (engine {got[k]}, oracle {want[k]})"
 
 
-def run_group(name: str, g: int, samples: int = 1024, policy: int = 0):
+def run_group(name: str, g: int, samples: int = 1024, policy: int = 0, bench_calls: bool = True):
     import torch
     from serving_pb_lru_amd import Engine
     from synth.device import rows_device
@@ -72,10 +77,14 @@ def run_group(name: str, g: int, samples: int = 1024, policy: int = 0):
             dsel = torch.from_numpy(sel).cuda()
             app = tr.appends(t)
             known.append(app)
-            if app.size:
-                eng.append(0, app, rows(app))
-            eng.step(0, dsel)
-            outs = [eng.gather(0, l, dsel) for l in range(wl.layers)]
+            if bench_calls:
+                eng.append_step(0, app, rows(app), dsel)
+                outs = gather_layers_by(eng, 0, wl.layers, dsel, "split")
+            else:
+                if app.size:
+                    eng.append(0, app, rows(app))
+                eng.step(0, dsel)
+                outs = gather_layers_by(eng, 0, wl.layers, dsel, "layer")
             eng.sync()
             # state and stored rows every other step: exporting writes the staged
             # evicted rows out, so the steps in between leave that to the next
@@ -122,4 +131,4 @@ LRU_CASES = ([("tiny_4x4k", 0), ("r16_64k_g1x3", 0)]
 
 @pytest.mark.parametrize("name,g", LRU_CASES, ids=[f"lru-{n}-g{g}" for n, g in LRU_CASES])
 def test_full_size_lru_parity(name, g):
-    run_group(name, g, policy=1)
+    run_group(name, g, policy=1, bench_calls=False)

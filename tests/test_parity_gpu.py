@@ -88,6 +88,75 @@ def test_append_step_scaled_parity(name, factor, steps):
     run_parity(wl, steps=steps, max_append=1 << 15, check_every=2, combined=True)
 
 
+@pytest.mark.parametrize("mode", ["all", "split"])
+@pytest.mark.parametrize("seed", range(6))
+def test_gather_layers_parity(seed, mode):
+    """ula_gather_layers (several layers of one selection in one launch) gives every
+    layer's rows as the oracle gathers them: ragged selections with padding, two to
+    four layers, both launch splits (all layers at once; layer 0, then the rest)."""
+    wl = dataclasses.replace(tiny_workload(seed), layers=2 + seed % 3)
+    tr = Trace(wl)
+    run_parity(wl, selections={0: padded_selections(tr, 0, seed)}, max_append=7, gather_mode=mode)
+
+
+@pytest.mark.parametrize("name,factor,steps,mode", [
+    ("r16_64k_g1x3", 16, 6, "all"),
+    ("r16_64k_g1x3", 16, 6, "split"),
+    ("spec3_r128_64k128k_g4", 32, 4, "all"),
+    ("evict_r256_128k_g2", 32, 5, "all"),
+])
+def test_gather_layers_scaled_parity(name, factor, steps, mode):
+    wl = scaled(preset(name), factor)
+    run_parity(wl, steps=steps, max_append=1 << 15, check_every=2, combined=True, gather_mode=mode)
+
+
+@pytest.mark.parametrize("k,layers", [(32_768, 2), (32_769, 2), (21_846, 3), (70_001, 2)])
+def test_gather_layers_tilings_parity(k, layers):
+    """Multi-layer launches on both sides of the tiling switch (65,536 row-layers per
+    launch: 32,768 x 2 is the last small one, 32,769 x 2 the first large one), with
+    partial last blocks, against the oracle."""
+    from synth.configs import Workload
+    wl = Workload(name=f"layers{k}x{layers}", requests=1, ctx_fixed=200_000, ctx_range=None,
+                  sets_per_request=1, draft_keep=0.0, groups=1, layers=layers, k=k, pool_frac=0.0,
+                  pool_slots=100_000, ring=4, steps=3, appends=1, overlap=0.85, p_recent=0.7,
+                  window=4096, row_bytes=64, seed=9)
+    run_parity(wl, max_append=1 << 12, gather_mode="all")
+
+
+def test_gather_layers_every_window():
+    """Every window (layer0, n_layers) of a four-layer group, including a selection
+    with padding and repeated entries, equals the per-layer gathers of its layers, and
+    bytes outside the window's buffers are left alone."""
+    import torch
+    from synth.device import rows_device
+    from serving_pb_lru_amd.replay import engine_for, initial_load
+    wl = dataclasses.replace(tiny_workload(3), layers=4, name="window4")
+    tr = Trace(wl, 3)
+    eng = engine_for(tr, max_append=64)
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    try:
+        initial_load(eng, tr, [0], rows)
+        sels = list(padded_selections(tr, 0, 3, frac=0.2))
+        for t in range(1, tr.steps + 1):
+            app = tr.appends(t)
+            eng.append_step(0, app, rows(app, 0), torch.from_numpy(sels[t - 1]).cuda())
+        sel = sels[-1].copy()
+        sel[0, -1] = sel[0, 0]                       # a repeated entry
+        dsel = torch.from_numpy(np.ascontiguousarray(sel)).cuda()
+        want = [eng.gather(0, l, dsel).cpu().numpy() for l in range(wl.layers)]
+        for l0 in range(wl.layers):
+            for nl in range(1, wl.layers - l0 + 1):
+                buf = torch.full((nl + 1, *sel.shape, wl.row_bytes), 0xA5, dtype=torch.uint8, device="cuda")
+                eng.gather_layers(0, l0, nl, dsel, out=buf)
+                got = buf.cpu().numpy()
+                for i in range(nl):
+                    assert np.array_equal(got[i], want[l0 + i]), (l0, nl, i)
+                assert (got[nl] == 0xA5).all(), (l0, nl)
+        eng.sync()
+    finally:
+        eng.close()
+
+
 @pytest.mark.parametrize("ring", [1, 2, 9, 64])   # 64: the longest ring the engine takes
 def test_ring_lengths_parity(ring):
     wl = dataclasses.replace(preset("tiny_4x4k"), ring=ring, name=f"tiny_ring{ring}")
