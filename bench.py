@@ -422,10 +422,8 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
 
             def step(t):
                 for g in groups:
-                    if apps[t - 1].size:
-                        eng.append(g, apps[t - 1], app_rows[g][t - 1])
                     sel = sels[g][t - 1]
-                    eng.step(g, sel)
+                    eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel)
                     if sched == "serial":
                         for l in range(wl.layers):
                             eng.gather(g, l, sel, out=outs[g][l])

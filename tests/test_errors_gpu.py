@@ -288,6 +288,46 @@ def test_gather_on_second_stream_ordered_by_event():
         eng.close()
 
 
+def test_gather_layers_on_second_stream_and_timed():
+    """Layer 0 gathered on the step's stream and the later layers by one
+    ula_gather_layers launch on a second stream ordered after the step by an
+    event (the prefetch of the later layers): every layer's rows match their
+    closed form; with gather timing on, each launch, one layer or several,
+    records one kernel duration."""
+    import torch
+    wl = dataclasses.replace(preset("tiny_4x4k"), layers=3, name="tiny_l3")
+    tr, eng, rows = _engine(wl)
+    try:
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        busy = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        eng.set_timing(eng.TIMING_GATHER)
+        sels = tr.selections(0)
+        for t in range(1, 4):
+            sel = next(sels)
+            d = _cuda(sel)
+            app = tr.appends(t)
+            app_rows = rows(app, 0)
+            torch.cuda.synchronize()
+            busy.fill_(t)                          # keeps the main stream busy for a while
+            eng.append_step(0, app, app_rows, d)
+            done = torch.cuda.Event()
+            done.record(main)
+            side.wait_event(done)
+            first = eng.gather(0, 0, d)
+            later = eng.gather_layers(0, 1, 2, d, stream=side)
+            torch.cuda.synchronize()
+            eng.sync()
+            want = rows_for(wl.seed, 0, sel.reshape(-1), wl.layers, wl.row_bytes)
+            assert np.array_equal(first.cpu().numpy().reshape(-1, wl.row_bytes), want[:, 0]), t
+            for i in range(2):
+                assert np.array_equal(later[i].cpu().numpy().reshape(-1, wl.row_bytes), want[:, 1 + i]), (t, i)
+        ms, n = eng.read_gather_timing()
+        assert n == 6 and ms > 0
+    finally:
+        eng.close()
+
+
 def test_gather_on_second_stream_ordered_by_counter_wait():
     """The other ordering the boundary offers: a second stream waits on the
     group's completion counter (hipStreamWaitValue64 on ula_flag_address) until it

@@ -6,7 +6,9 @@ device memory or in host memory, with a per-call append limit small enough that
 most appends run in several chunks (the plan / extract / place kernels) and the
 rest in the one-workgroup path, through ula_append before ula_step or through
 ula_append_step (which runs a small device-memory append in the step's first
-launch). Finished entries are released between steps.
+launch). Each group's layers are gathered one call per layer, all in one
+ula_gather_layers launch, or layer 0 alone and the rest in one launch, drawn per
+step. Finished entries are released between steps.
 After every step (and every release) each group's exported state must equal its
 oracle's, and every gathered byte must equal the closed form of its row.
 """
@@ -16,7 +18,7 @@ import dataclasses
 import numpy as np
 import pytest
 
-from gpu_harness import say
+from gpu_harness import gather_layers_by, say
 from synth import Trace, rows_for
 from tracegen import padded_selections, release_plan, tiny_workload
 
@@ -91,7 +93,7 @@ def test_mixed_paths_random(seed):
                     if app.size:
                         eng.append(g, app, rows)
                     eng.step(g, dsel)
-                outs = [eng.gather(g, l, dsel) for l in range(wl.layers)]
+                outs = gather_layers_by(eng, g, wl.layers, dsel, str(rng.choice(["layer", "all", "split"])))
                 ora[g].step(sel)
                 eng.sync()
                 _same(eng.export_state(g), ora[g].export_state(), policy, f"group {g} step {t}")
