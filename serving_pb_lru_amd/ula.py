@@ -113,11 +113,24 @@ def _check(rc: int, where: str) -> None:
         raise UlaError(rc, where, lib().ula_strerror(rc).decode())
 
 
-def _ptr(x) -> int:
-    """Device pointer of a torch tensor, or address of a numpy array."""
-    if hasattr(x, "data_ptr"):
-        return x.data_ptr()
-    return x.ctypes.data
+def _dev(t, dtype: str, count: int, what: str) -> int:
+    """Device pointer of a contiguous CUDA tensor of `dtype` holding at least
+    `count` elements; raises ValueError otherwise (the library takes plain
+    pointers and would read or write past a smaller buffer)."""
+    if not (hasattr(t, "is_cuda") and t.is_cuda):
+        raise ValueError(f"{what}: a CUDA tensor is required")
+    if str(t.dtype) != f"torch.{dtype}":
+        raise ValueError(f"{what}: dtype {t.dtype}, expected torch.{dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: the tensor must be contiguous")
+    if t.numel() < count:
+        raise ValueError(f"{what}: {t.numel()} elements, at least {count} needed")
+    return t.data_ptr()
+
+
+def _sets(sel):
+    """(n_sets, k) of a selection tensor [n_sets][k] or [k]."""
+    return (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
 
 
 def _stream(stream) -> int:
@@ -157,13 +170,21 @@ class Engine:
         self.N, self.P, self.H = logical_capacity, gpu_slots, host_slots
 
     # -- calls ---------------------------------------------------------------
+    def _rows(self, las, rows, what):
+        """(pointer, on_device) of the appended rows [n][layers][row_bytes]."""
+        n = las.size * self.layers * self.row_bytes
+        if hasattr(rows, "is_cuda") and rows.is_cuda:
+            return (_dev(rows, "uint8", n, what) if las.size else None), 1
+        rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        if rows.size < n:
+            raise ValueError(f"{what}: {rows.size} row bytes, at least {n} needed")
+        return (rows.ctypes.data if las.size else None), 0, rows
+
     def append(self, group: int, las: np.ndarray, rows, stream=None) -> None:
         """rows: torch CUDA uint8 tensor or numpy uint8 array [n][layers][row_bytes]."""
         las = np.ascontiguousarray(las, dtype=np.int32)
-        on_dev = 1 if hasattr(rows, "is_cuda") and rows.is_cuda else 0
-        if not on_dev:
-            rows = np.ascontiguousarray(rows, dtype=np.uint8)
-        _check(lib().ula_append(self.ctx, group, las.size, las.ctypes.data, _ptr(rows), on_dev,
+        ptr, on_dev, *keep = self._rows(las, rows, "ula_append rows")
+        _check(lib().ula_append(self.ctx, group, las.size, las.ctypes.data, ptr, on_dev,
                                 _stream(stream)), "ula_append")
 
     def release(self, group: int, las: np.ndarray, stream=None) -> None:
@@ -174,37 +195,43 @@ class Engine:
 
     def step(self, group: int, sel, stream=None) -> None:
         """sel: torch CUDA int32 tensor [n_sets][k] (or [k] for one set)."""
-        n_sets, k = (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
-        _check(lib().ula_step(self.ctx, group, n_sets, k, sel.data_ptr(), _stream(stream)), "ula_step")
+        n_sets, k = _sets(sel)
+        _check(lib().ula_step(self.ctx, group, n_sets, k, _dev(sel, "int32", n_sets * k, "ula_step sel"),
+                              _stream(stream)), "ula_step")
 
     def append_step(self, group: int, las: np.ndarray, rows, sel, stream=None) -> None:
         """append(group, las, rows) then step(group, sel), in fewer launches."""
         las = np.ascontiguousarray(las, dtype=np.int32)
-        on_dev = 1 if hasattr(rows, "is_cuda") and rows.is_cuda else 0
-        if not on_dev:
-            rows = np.ascontiguousarray(rows, dtype=np.uint8)
-        n_sets, k = (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
+        ptr, on_dev, *keep = self._rows(las, rows, "ula_append_step rows")
+        n_sets, k = _sets(sel)
         _check(lib().ula_append_step(self.ctx, group, las.size, las.ctypes.data if las.size else None,
-                                     _ptr(rows) if las.size else None, on_dev, n_sets, k, sel.data_ptr(),
+                                     ptr, on_dev, n_sets, k,
+                                     _dev(sel, "int32", n_sets * k, "ula_append_step sel"),
                                      _stream(stream)), "ula_append_step")
 
     def gather(self, group: int, layer: int, sel, out=None, stream=None):
         import torch
-        n_sets, k = (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
+        n_sets, k = _sets(sel)
         if out is None:
             out = torch.empty((n_sets, k, self.row_bytes), dtype=torch.uint8, device=sel.device)
-        _check(lib().ula_gather(self.ctx, group, layer, n_sets, k, sel.data_ptr(), out.data_ptr(),
+        _check(lib().ula_gather(self.ctx, group, layer, n_sets, k,
+                                _dev(sel, "int32", n_sets * k, "ula_gather sel"),
+                                _dev(out, "uint8", n_sets * k * self.row_bytes, "ula_gather out"),
                                 _stream(stream)), "ula_gather")
         return out
 
     def gather_layers(self, group: int, layer0: int, n_layers: int, sel, out=None, stream=None):
         """Layers layer0 .. layer0 + n_layers - 1 in one launch: out[i] is gather(layer0 + i)."""
         import torch
-        n_sets, k = (1, sel.shape[0]) if sel.dim() == 1 else tuple(sel.shape)
+        n_sets, k = _sets(sel)
         if out is None:
-            out = torch.empty((n_layers, n_sets, k, self.row_bytes), dtype=torch.uint8, device=sel.device)
-        _check(lib().ula_gather_layers(self.ctx, group, layer0, n_layers, n_sets, k, sel.data_ptr(),
-                                       out.data_ptr(), _stream(stream)), "ula_gather_layers")
+            out = torch.empty((max(n_layers, 0), n_sets, k, self.row_bytes), dtype=torch.uint8,
+                              device=sel.device)
+        _check(lib().ula_gather_layers(
+            self.ctx, group, layer0, n_layers, n_sets, k,
+            _dev(sel, "int32", n_sets * k, "ula_gather_layers sel"),
+            _dev(out, "uint8", max(n_layers, 0) * n_sets * k * self.row_bytes, "ula_gather_layers out"),
+            _stream(stream)), "ula_gather_layers")
         return out
 
     def sync(self, stream=None) -> List[tuple]:

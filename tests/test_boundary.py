@@ -82,3 +82,35 @@ def test_error_texts():
         assert L.ula_strerror(code)
     assert L.ula_strerror(-5).decode().startswith("a step selects more distinct")
     assert L.ula_destroy(None) == -1
+
+
+def test_binding_rejects_unusable_device_buffers():
+    """The binding passes plain pointers, so it checks every device buffer before a
+    call: a CUDA tensor of the right dtype, contiguous, and large enough for what
+    the call reads or writes."""
+    import torch
+
+    class FakeCuda:   # stands in for a CUDA tensor (no GPU here)
+        is_cuda = True
+
+        def __init__(self, dtype, n, contiguous=True):
+            self.dtype, self.n, self.contiguous = dtype, n, contiguous
+
+        def is_contiguous(self):
+            return self.contiguous
+
+        def numel(self):
+            return self.n
+
+        def data_ptr(self):
+            return 4096
+
+    assert ula._dev(FakeCuda(torch.int32, 8), "int32", 8, "sel") == 4096
+    assert ula._dev(FakeCuda(torch.uint8, 0), "uint8", 0, "out") == 4096
+    bad = [torch.zeros(8, dtype=torch.int32),            # host memory
+           FakeCuda(torch.int64, 8),                     # wrong dtype
+           FakeCuda(torch.int32, 7),                     # too small
+           FakeCuda(torch.int32, 8, contiguous=False)]   # strided view
+    for t in bad:
+        with pytest.raises(ValueError):
+            ula._dev(t, "int32", 8, "sel")
