@@ -135,12 +135,23 @@ def copy_ceiling(nbytes: int, copies: int = 64) -> None:
           flush=True)
 
 
+def code_digest(path: str) -> str:
+    """sha256 of a C/C++ source with its comments removed and whitespace runs
+    collapsed: it changes when the code changes, not when a comment does."""
+    import hashlib
+    import re
+    with open(path) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()
+
+
 def gather_traffic(workload: str, mode: str = "layer"):
     """HBM bytes per gather launch from the committed rocprofv3 counter record
     (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known size), or
     None when there is no record for this workload and gather mode or the kernel
-    source changed since the counters were taken."""
-    import hashlib
+    code changed since the counters were taken."""
     suffix = "" if mode == "layer" else f"_{mode}"
     path = os.path.join(ROOT, "profiles", f"traffic_k_gather_{workload}{suffix}.json")
     if not os.path.exists(path):
@@ -148,9 +159,8 @@ def gather_traffic(workload: str, mode: str = "layer"):
     with open(path) as f:
         rec = json.load(f)
     src = os.path.join(ROOT, "serving_pb_lru_amd", "csrc", "k_gather.hip")
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["k_gather_hip_sha256"]:
-            return None
+    if code_digest(src) != rec["k_gather_hip_code_sha256"]:
+        return None
     return rec["traffic_bytes_per_launch"]
 
 

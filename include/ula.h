@@ -207,7 +207,8 @@ int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* l
  * (device memory, n_sets x k x row_bytes bytes, packed; a -1 entry gives a zero
  * row). Reads the GPU pool through the mapping table after checking that the
  * group's completion counter equals the group's last step (section 3: readers
- * wait for the signal); call it once per layer of the group. On a stream other
+ * wait for the signal); call it once per layer of the group, or gather several
+ * layers in one launch with ula_gather_layers. On a stream other
  * than the step's, order it after the step first (event, or a stream wait on
  * ula_flag_address reaching the step number).
  * Host errors: ULA_EINVAL, ULA_ESTATE, ULA_ENOTRESIDENT (no step yet).

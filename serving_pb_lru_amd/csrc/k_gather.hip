@@ -1,24 +1,26 @@
-// Gather of the selected rows of one layer into contiguous per-set buffers.
+// Gather of the selected rows of one or more layers into contiguous per-set
+// buffers.
 //
 // UlaCache summary (paper-daily.com): attention reads only the KV rows at the
 // selected positions (introduction) and waits for the completion signal before
 // reading the new locations (section 3); layers sharing one selection read the
-// same entries (section 2), so this kernel runs once per layer of a group.
+// same entries (section 2), so a group's layers are gathered one launch per
+// layer, or several in one launch: the later layers of a group are fetched
+// together while the first one is in use (section 2).
 //
 // out[l][j][i][:] = pool[map[sel[j][i]]][layer0 + l][:] for the nl layers of
 // one launch (one per-layer buffer each, layer_stride apart), or zeros for -1
 // padding. A slot keeps its layers side by side, so the nl rows of one entry
-// are one contiguous source run; the later layers of a group can be fetched
-// together while the first one is in use (section 2). The
-// step already resolved its selection to slots entry by entry (the lookup is
-// done once per group); a gather of that selection reads those slots in order
-// and only entries that differ fall back to the mapping table. A
-// workgroup takes ROWS output rows at a time: ROWS lanes look the rows up once
-// (selection entry and resolved slot in one round trip, else the mapping
-// table) into LDS, then all lanes stream the rows in 16-byte pieces,
-// C = row_bytes / 16 pieces per row, lane i taking piece (i mod C) of row
-// (i div C), layer by layer: consecutive lanes write consecutive 16 bytes
-// (fully coalesced, non-temporal stores) and read one contiguous source row.
+// are one contiguous source run. The step already resolved its selection to
+// slots entry by entry (the lookup is done once per group); a gather of that
+// selection reads those slots in order and only entries that differ fall back
+// to the mapping table. A workgroup takes ROWS output rows at a time: ROWS
+// lanes look the rows up once (selection entry and resolved slot in one round
+// trip, else the mapping table) into LDS, then all lanes stream the rows in
+// 16-byte pieces, C = row_bytes / 16 pieces per row, lane i taking piece
+// (i mod C) of row (i div C), layer by layer: consecutive lanes write
+// consecutive 16 bytes (fully coalesced, non-temporal stores) and read one
+// contiguous source row.
 // UNROLL pieces per lane are in flight; for 656-byte rows both tilings below
 // cover all staged rows of one layer in one round. Bound by HBM bandwidth.
 //
