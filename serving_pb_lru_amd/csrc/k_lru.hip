@@ -155,12 +155,8 @@ __global__ __launch_bounds__(kLruThreads) void k_lru_pass(GroupDev g, uint32_t t
   else if (threadIdx.x == 3 * kWave) s_wbn = g.ctr->wb_n;
   __syncthreads();
   if (s_status) return;
-  if ((int)blockIdx.x >= nsel + pf) {
-    writeback_rows(g, s_wbstep, s_wbn, wb_step, per_slot, blockIdx.x - nsel - pf, wbb);
-    return;
-  }
   if ((int)blockIdx.x >= nsel) {
-    prefetch_misses(g, s_nmiss, per_slot, blockIdx.x - nsel, pf);
+    link_part(g, s_nmiss, s_wbstep, s_wbn, wb_step, per_slot, blockIdx.x - nsel, pf, wbb);
     return;
   }
   if (s_nmiss == 0) return;   // no victims to choose (uniform over the launch)

@@ -247,12 +247,8 @@ __global__ __launch_bounds__(1024) void k_mark(GroupDev g, uint32_t t, int32_t c
     if (!s_fail) extract_part(g, a.dest, role - (kMarkBlocks + pf + wbb), nh + 1);
     return;
   }
-  if (role >= kMarkBlocks + pf) {
-    writeback_rows(g, s_wbstep, s_wbn, wb_step, per_slot, role - kMarkBlocks - pf, wbb);
-    return;
-  }
   if (role >= kMarkBlocks) {
-    prefetch_misses(g, s_nmiss, per_slot, role - kMarkBlocks, pf);
+    link_part(g, s_nmiss, s_wbstep, s_wbn, wb_step, per_slot, role - kMarkBlocks, pf, wbb);
     return;
   }
   for (int i = threadIdx.x; i < kMaxBuckets; i += blockDim.x) s_delta[i] = 0;

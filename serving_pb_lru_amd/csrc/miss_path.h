@@ -94,4 +94,73 @@ __device__ __forceinline__ void writeback_rows(const GroupDev& g, uint32_t stage
   }
 }
 
+// Both directions in every link workgroup: each iteration loads U pieces of
+// missed rows and U pieces of staged rows, then stores both. m missed rows
+// come in; wb_rows staged rows (0: none) go out to their host slots.
+// Workgroup `part` of `nparts`.
+__device__ __forceinline__ void swap_rows_interleaved(const GroupDev& g, int m, int wb_rows, FastDiv per_slot,
+                                                      int part, int nparts) {
+  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
+  const uint32_t tp = (uint32_t)m * chunks;
+  const uint32_t tw = (uint32_t)wb_rows * chunks;
+  const uint32_t total = tp > tw ? tp : tw;
+  const uint32_t stride = (uint32_t)nparts * blockDim.x;
+  constexpr int U = 2;
+  for (uint32_t base = (uint32_t)part * blockDim.x + threadIdx.x; base < total; base += U * stride) {
+    vec4u pv[U], wv[U];
+    vec4u* pd[U];
+    vec4u* wd[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t idx = base + u * stride;
+      pd[u] = nullptr;
+      wd[u] = nullptr;
+      if (idx < tp) {
+        const uint32_t i = per_slot.div(idx);
+        const uint32_t c = idx - i * chunks;
+        const uint32_t from = g.miss_stage[i];
+        const uint8_t* src = from != kAbsent ? g.evict_rows + (size_t)from * g.slot_bytes
+                                             : g.host + (size_t)g.miss_h[i] * g.slot_bytes;
+        pv[u] = reinterpret_cast<const vec4u*>(src)[c];
+        pd[u] = reinterpret_cast<vec4u*>(g.miss_rows + (size_t)i * g.slot_bytes) + c;
+      }
+      if (idx < tw) {
+        const uint32_t i = per_slot.div(idx);
+        const uint32_t c = idx - i * chunks;
+        const uint32_t h = g.wb_h[i];
+        if (h != kAbsent) {
+          wd[u] = reinterpret_cast<vec4u*>(g.host + (size_t)h * g.slot_bytes) + c;
+          wv[u] = reinterpret_cast<const vec4u*>(g.evict_rows + (size_t)i * g.slot_bytes)[c];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (pd[u]) *pd[u] = pv[u];
+      if (wd[u]) *wd[u] = wv[u];
+    }
+  }
+}
+
+// The link work of a step's selection launch, workgroup `part` of its pf
+// prefetch and wbb write-back workgroups (m: the step's misses; staged_step /
+// staged_n: the counter block's record of the staging buffer; wb_step: the
+// step whose staged rows go out, meaningful when wbb > 0). A step that moves
+// at least kInterleavedLinkBytes in a direction runs both directions in every
+// link workgroup; a smaller one keeps them in separate workgroups (measured:
+// interleaving made the eviction-heavy workload's steps about 10% shorter,
+// but the default workload's link phase 10% longer, since a lane's next host
+// read then waits for its previous host write).
+__device__ __forceinline__ void link_part(const GroupDev& g, int m, uint32_t staged_step, int staged_n,
+                                          uint32_t wb_step, FastDiv per_slot, int part, int pf, int wbb) {
+  const int wb_rows = (wbb > 0 && staged_step == wb_step) ? staged_n : 0;
+  const int rows = m > wb_rows ? m : wb_rows;
+  if ((int64_t)rows * g.slot_bytes >= kInterleavedLinkBytes)   // uniform over the launch
+    swap_rows_interleaved(g, m, wb_rows, per_slot, part, pf + wbb);
+  else if (part >= pf)
+    writeback_rows(g, staged_step, staged_n, wb_step, per_slot, part - pf, wbb);
+  else
+    prefetch_misses(g, m, per_slot, part, pf);
+}
+
 }  // namespace ula

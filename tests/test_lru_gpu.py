@@ -137,6 +137,7 @@ def test_lru_long_trace_two_select_passes():
     ("r16_64k_g1x3", 16, 8),
     ("evict_r256_128k_g2", 64, 6),
     ("spec3_r128_64k128k_g4", 64, 4),
+    ("evict_r256_128k_g2", 8, 4),   # both link directions in every link workgroup
 ])
 def test_lru_scaled(name, factor, steps):
     wl = scaled(preset(name), factor)
