@@ -24,17 +24,19 @@
 // UNROLL pieces per lane are in flight; for 656-byte rows both tilings below
 // cover all staged rows of one layer in one round. Bound by HBM bandwidth.
 //
-// Tilings (measured on MI355X with 656-byte rows): a small gather (up to 64K
-// row-layers, a few workgroups per compute unit) is fastest with 64 rows and 11
-// pieces in flight per lane of 256; a large one (131K row-layers and more) with
-// 32 rows and 3 pieces per lane of 512, which keeps more workgroups resident.
+// Tilings (measured on MI355X with 656-byte rows): a small one-layer gather
+// (up to 64K rows, a few workgroups per compute unit) is fastest with 64 rows
+// and 11 pieces in flight per lane of 256; a small multi-layer one (up to 128K
+// row-layers) with 32 rows and 11 pieces per lane of 256 (the two-layer launch
+// of 32K rows 16.5 against 18.5 us with 64 rows); larger ones with 32 rows and
+// 3 pieces per lane of 512, which keeps more workgroups resident.
 #include <hip/hip_ext.h>
 
 #include "device_util.h"
 
 namespace ula {
 
-constexpr int kSmallGatherRows = 1 << 16;   // up to this many row-layers: the small-gather tiling
+constexpr int kSmallGatherRows = 1 << 16;   // up to this many rows (one layer): the small-gather tiling
 
 // Streams the staged rows of one block, layer by layer: piece i is piece
 // (i mod C) of staged row q = i div C, which is row (q mod nrows) of layer
@@ -189,8 +191,10 @@ hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32
                          uint8_t* out, long long want_flag, int32_t n_res, hipStream_t s,
                          hipEvent_t start, hipEvent_t stop) {
   if (n <= 0 || nl <= 0) return hipSuccess;
-  if ((int64_t)n * nl <= kSmallGatherRows)
+  if (nl == 1 && n <= kSmallGatherRows)
     return launch_tiled<64, 11, 256>(g, sel, n, layer, nl, out, want_flag, n_res, s, start, stop);
+  if (nl > 1 && (int64_t)n * nl <= 2 * kSmallGatherRows)
+    return launch_tiled<32, 11, 256>(g, sel, n, layer, nl, out, want_flag, n_res, s, start, stop);
   return launch_tiled<32, 3, 512>(g, sel, n, layer, nl, out, want_flag, n_res, s, start, stop);
 }
 

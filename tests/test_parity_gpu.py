@@ -110,17 +110,21 @@ def test_gather_layers_scaled_parity(name, factor, steps, mode):
     run_parity(wl, steps=steps, max_append=1 << 15, check_every=2, combined=True, gather_mode=mode)
 
 
-@pytest.mark.parametrize("k,layers", [(32_768, 2), (32_769, 2), (21_846, 3), (70_001, 2)])
+@pytest.mark.parametrize("k,layers", [(32_768, 2), (65_536, 2), (65_537, 2), (43_691, 3), (70_001, 2)])
 def test_gather_layers_tilings_parity(k, layers):
-    """Multi-layer launches on both sides of the tiling switch (65,536 row-layers per
-    launch: 32,768 x 2 is the last small one, 32,769 x 2 the first large one), with
-    partial last blocks, against the oracle."""
+    """Gathers on every side of the tiling switches, with partial last blocks, against
+    the oracle: one-layer launches up to 65,536 rows and multi-layer launches up to
+    131,072 row-layers take the small tilings (65,536 x 2 is the last small
+    multi-layer launch, 65,537 x 2 and 43,691 x 3 the first large ones), and the
+    one-layer launch of layer 0 beside them (32,768 and 65,536 rows small, 65,537 and
+    70,001 large)."""
     from synth.configs import Workload
     wl = Workload(name=f"layers{k}x{layers}", requests=1, ctx_fixed=200_000, ctx_range=None,
                   sets_per_request=1, draft_keep=0.0, groups=1, layers=layers, k=k, pool_frac=0.0,
                   pool_slots=100_000, ring=4, steps=3, appends=1, overlap=0.85, p_recent=0.7,
                   window=4096, row_bytes=64, seed=9)
     run_parity(wl, max_append=1 << 12, gather_mode="all")
+    run_parity(wl, max_append=1 << 12, gather_mode="split")
 
 
 def test_gather_layers_every_window():
