@@ -1,0 +1,54 @@
+"""bench.py's host-side contract, without a GPU: a request for more than one GPU
+exits with a message before touching a device, and the kernel-code digest that
+keys the committed counter records ignores comments but not code."""
+
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_code_digest_ignores_comments_only(tmp_path):
+    import bench
+    base = "int f(int a) {\n  return a + 1;  // one more\n}\n/* block\n   comment */\n"
+    same = "// header\nint f(int a) {\n    return a + 1;\n}\n"
+    other = "int f(int a) {\n  return a + 2;\n}\n"
+    paths = []
+    for i, text in enumerate((base, same, other)):
+        p = tmp_path / f"k{i}.hip"
+        p.write_text(text)
+        paths.append(str(p))
+    d = [bench.code_digest(p) for p in paths]
+    assert d[0] == d[1]
+    assert d[0] != d[2]
+
+
+def test_traffic_record_needs_matching_code(tmp_path, monkeypatch):
+    """A counter record is reported only for the kernel code it was taken on."""
+    import json
+    import bench
+    prof = tmp_path / "profiles"
+    csrc = tmp_path / "serving_pb_lru_amd" / "csrc"
+    prof.mkdir()
+    csrc.mkdir(parents=True)
+    (csrc / "k_gather.hip").write_text("int g() { return 1; }\n")
+    rec = {"k_gather_hip_code_sha256": bench.code_digest(str(csrc / "k_gather.hip")),
+           "traffic_bytes_per_launch": 12345}
+    (prof / "traffic_k_gather_w_split.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.gather_traffic("w", "split") == 12345
+    assert bench.gather_traffic("w", "layer") is None            # no record for that form
+    (csrc / "k_gather.hip").write_text("// note\nint g() { return 1; }\n")
+    assert bench.gather_traffic("w", "split") == 12345           # a comment changes nothing
+    (csrc / "k_gather.hip").write_text("int g() { return 2; }\n")
+    assert bench.gather_traffic("w", "split") is None            # the code changed
