@@ -171,10 +171,11 @@ class Engine:
 
     # -- calls ---------------------------------------------------------------
     def _rows(self, las, rows, what):
-        """(pointer, on_device) of the appended rows [n][layers][row_bytes]."""
+        """(pointer, on_device, keep) for the appended rows [n][layers][row_bytes];
+        `keep` holds a host copy alive for the duration of the call."""
         n = las.size * self.layers * self.row_bytes
         if hasattr(rows, "is_cuda") and rows.is_cuda:
-            return (_dev(rows, "uint8", n, what) if las.size else None), 1
+            return (_dev(rows, "uint8", n, what) if las.size else None), 1, None
         rows = np.ascontiguousarray(rows, dtype=np.uint8)
         if rows.size < n:
             raise ValueError(f"{what}: {rows.size} row bytes, at least {n} needed")
@@ -183,7 +184,7 @@ class Engine:
     def append(self, group: int, las: np.ndarray, rows, stream=None) -> None:
         """rows: torch CUDA uint8 tensor or numpy uint8 array [n][layers][row_bytes]."""
         las = np.ascontiguousarray(las, dtype=np.int32)
-        ptr, on_dev, *keep = self._rows(las, rows, "ula_append rows")
+        ptr, on_dev, _keep = self._rows(las, rows, "ula_append rows")
         _check(lib().ula_append(self.ctx, group, las.size, las.ctypes.data, ptr, on_dev,
                                 _stream(stream)), "ula_append")
 
@@ -202,7 +203,7 @@ class Engine:
     def append_step(self, group: int, las: np.ndarray, rows, sel, stream=None) -> None:
         """append(group, las, rows) then step(group, sel), in fewer launches."""
         las = np.ascontiguousarray(las, dtype=np.int32)
-        ptr, on_dev, *keep = self._rows(las, rows, "ula_append_step rows")
+        ptr, on_dev, _keep = self._rows(las, rows, "ula_append_step rows")
         n_sets, k = _sets(sel)
         _check(lib().ula_append_step(self.ctx, group, las.size, las.ctypes.data if las.size else None,
                                      ptr, on_dev, n_sets, k,
