@@ -35,7 +35,8 @@ Printed as one JSON line, with:
   cpu_baseline  the CPU oracle timed on this host's cores over the same steps
                 (a bounded sample; a baseline, not the target).
 Also: selections_per_s (selection entries resolved per second, all groups),
-first_step_ms (step 1, the cold start with the most misses, timed alone), and
+first_step_ms (step 1, the cold start with the most misses, timed alone, after
+every step kernel has run once on a tiny engine), and
 hipMemcpyAsync pinned-host peaks (each direction and both at once) next to the
 miss-path rates.
 """
