@@ -74,6 +74,8 @@ def test_device_errors_latch_and_change_nothing(bad, policy):
         assert e.value.name == want
         assert _state(eng) == before
         for call in (lambda: eng.step(0, d), lambda: eng.gather(0, 0, d),
+                     lambda: eng.gather_layers(0, 0, 1, d),
+                     lambda: eng.append_step(0, tr.appends(1), rows(tr.appends(1), 0), d),
                      lambda: eng.append(0, tr.appends(1), rows(tr.appends(1), 0))):
             with pytest.raises(UlaError) as e:
                 call()
