@@ -24,12 +24,13 @@
 // UNROLL pieces per lane are in flight; for 656-byte rows both tilings below
 // cover all staged rows of one layer in one round. Bound by HBM bandwidth.
 //
-// Tilings (measured on MI355X with 656-byte rows): a small one-layer gather
-// (up to 64K rows, a few workgroups per compute unit) is fastest with 64 rows
-// and 11 pieces in flight per lane of 256; a small multi-layer one (up to 128K
-// row-layers) with 32 rows and 11 pieces per lane of 256 (the two-layer launch
-// of 32K rows 16.5 against 18.5 us with 64 rows); larger ones with 32 rows and
-// 3 pieces per lane of 512, which keeps more workgroups resident.
+// Tilings (measured on MI355X with 656-byte rows): a small gather is fastest
+// when each workgroup's rows take one round of 11 pieces per lane of 256: 64
+// rows for one layer (up to 64K rows), 32 rows for two layers and 16 for three
+// or more (up to 128K row-layers; the two-layer launch of 32K rows 16.5 against
+// 18.5 us with 64 rows, the three-layer one 24.8 against 25.5 us with the large
+// tiling); larger launches take 32 rows and 3 pieces per lane of 512, which
+// keeps more workgroups resident.
 #include <hip/hip_ext.h>
 
 #include "device_util.h"
@@ -193,8 +194,10 @@ hipError_t launch_gather(const GroupDev& g, const int32_t* sel, int32_t n, int32
   if (n <= 0 || nl <= 0) return hipSuccess;
   if (nl == 1 && n <= kSmallGatherRows)
     return launch_tiled<64, 11, 256>(g, sel, n, layer, nl, out, want_flag, n_res, s, start, stop);
-  if (nl > 1 && (int64_t)n * nl <= 2 * kSmallGatherRows)
+  if (nl == 2 && (int64_t)n * nl <= 2 * kSmallGatherRows)
     return launch_tiled<32, 11, 256>(g, sel, n, layer, nl, out, want_flag, n_res, s, start, stop);
+  if (nl > 2 && (int64_t)n * nl <= 2 * kSmallGatherRows)
+    return launch_tiled<16, 11, 256>(g, sel, n, layer, nl, out, want_flag, n_res, s, start, stop);
   return launch_tiled<32, 3, 512>(g, sel, n, layer, nl, out, want_flag, n_res, s, start, stop);
 }
 

@@ -110,14 +110,15 @@ def test_gather_layers_scaled_parity(name, factor, steps, mode):
     run_parity(wl, steps=steps, max_append=1 << 15, check_every=2, combined=True, gather_mode=mode)
 
 
-@pytest.mark.parametrize("k,layers", [(32_768, 2), (65_536, 2), (65_537, 2), (43_691, 3), (70_001, 2)])
+@pytest.mark.parametrize("k,layers", [(32_768, 2), (65_536, 2), (65_537, 2), (43_690, 3), (43_691, 3),
+                                      (32_767, 4), (70_001, 2)])
 def test_gather_layers_tilings_parity(k, layers):
     """Gathers on every side of the tiling switches, with partial last blocks, against
     the oracle: one-layer launches up to 65,536 rows and multi-layer launches up to
-    131,072 row-layers take the small tilings (65,536 x 2 is the last small
-    multi-layer launch, 65,537 x 2 and 43,691 x 3 the first large ones), and the
-    one-layer launch of layer 0 beside them (32,768 and 65,536 rows small, 65,537 and
-    70,001 large)."""
+    131,072 row-layers take the small tilings (32 rows for two layers, 16 for three or
+    more: 65,536 x 2, 43,690 x 3 and 32,767 x 4 are small, 65,537 x 2 and 43,691 x 3
+    the first large ones), and the one-layer launch of layer 0 beside them (32,767,
+    32,768, 43,690 and 65,536 rows small, 65,537 and 70,001 large)."""
     from synth.configs import Workload
     wl = Workload(name=f"layers{k}x{layers}", requests=1, ctx_fixed=200_000, ctx_range=None,
                   sets_per_request=1, draft_keep=0.0, groups=1, layers=layers, k=k, pool_frac=0.0,
