@@ -100,9 +100,10 @@ __device__ __forceinline__ int32_t* bucket_count(const GroupDev& g, int id) {
 // piece 0 also publishes the mapping and owner entries of `la`.
 __device__ __forceinline__ void place_piece(const GroupDev& g, uint32_t d, uint32_t c, int32_t la,
                                             const vec4u v) {
-  uint8_t* dst = (d & kHostBit) ? g.host + (size_t)(d & ~kHostBit) * g.slot_bytes
-                                : g.pool + (size_t)d * g.slot_bytes;
-  reinterpret_cast<vec4u*>(dst)[c] = v;
+  if (d & kHostBit)   // host pool: non-temporal, as every store to it
+    __builtin_nontemporal_store(v, reinterpret_cast<vec4u*>(g.host + (size_t)(d & ~kHostBit) * g.slot_bytes) + c);
+  else
+    reinterpret_cast<vec4u*>(g.pool + (size_t)d * g.slot_bytes)[c] = v;
   if (c == 0) {
     g.map[la] = d;
     if (d & kHostBit) g.hown[d & ~kHostBit] = la;

@@ -18,6 +18,11 @@
 
 namespace ula {
 
+// Stores to the host pool are non-temporal: measured against plain stores of
+// the same bytes, the default workload's link phase went from 66-67 to 61-63
+// us and the speculative workload's steps became 3% shorter; the eviction
+// control and the eviction-heavy workload did not change.
+//
 // Request depth. In both loops below each of a lane's U pieces first loads a
 // small record (staging row or host slot) and then its data; loads complete in
 // order, so each record load also waits for the previous piece's host access,
@@ -90,7 +95,7 @@ __device__ __forceinline__ void writeback_rows(const GroupDev& g, uint32_t stage
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (hp[u]) *hp[u] = v[u];
+      if (hp[u]) __builtin_nontemporal_store(v[u], hp[u]);
   }
 }
 
@@ -137,7 +142,7 @@ __device__ __forceinline__ void swap_rows_interleaved(const GroupDev& g, int m, 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (pd[u]) *pd[u] = pv[u];
-      if (wd[u]) *wd[u] = wv[u];
+      if (wd[u]) __builtin_nontemporal_store(wv[u], wd[u]);
     }
   }
 }
