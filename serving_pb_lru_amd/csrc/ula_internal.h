@@ -48,7 +48,7 @@ constexpr int kMaxBuckets = kMaxRing + 2;
 constexpr int kMarkBlocks = 32;                 // mark workgroups (1024 threads each) of the mark kernel
 constexpr int kPrefetchBlocks = 32;             // its prefetch workgroups (missed rows into HBM)
 constexpr int kWritebackBlocks = 16;            // its write-back workgroups (last step's evictions out)
-constexpr int64_t kInterleavedLinkBytes = 16ll << 20;   // from this many bytes in a direction, every link
+constexpr int64_t kInterleavedLinkBytes = 4ll << 20;   // from this many bytes in a direction, every link
                                                         // workgroup moves both directions
 constexpr int kExtractHelpers = 8;              // its extraction workgroups (besides the planning one)
 

@@ -189,7 +189,7 @@ def test_row_sizes_parity(row_bytes, layers):
     ("evict_r256_128k_g2", 32, 8, 3),
     ("evict_r256_128k_g2_ctl98", 32, 6, 1),
     # ~19.5 MB each way per group step: the link moves both directions in every
-    # link workgroup (16 MB and more)
+    # link workgroup (4 MB and more)
     ("evict_r256_128k_g2", 8, 4, 1),
 ])
 def test_scaled_workload_parity(name, factor, steps, check_every):
