@@ -99,8 +99,8 @@ __device__ __forceinline__ void writeback_rows(const GroupDev& g, uint32_t stage
   }
 }
 
-// Both directions in every link workgroup: each iteration loads U pieces of
-// missed rows and U pieces of staged rows, then stores both. m missed rows
+// Both directions in every link workgroup: each iteration loads a piece of
+// missed rows and a piece of staged rows, then stores both. m missed rows
 // come in; wb_rows staged rows (0: none) go out to their host slots.
 // Workgroup `part` of `nparts`.
 __device__ __forceinline__ void swap_rows_interleaved(const GroupDev& g, int m, int wb_rows, FastDiv per_slot,
@@ -110,7 +110,7 @@ __device__ __forceinline__ void swap_rows_interleaved(const GroupDev& g, int m, 
   const uint32_t tw = (uint32_t)wb_rows * chunks;
   const uint32_t total = tp > tw ? tp : tw;
   const uint32_t stride = (uint32_t)nparts * blockDim.x;
-  constexpr int U = 2;
+  constexpr int U = 1;   // pieces per direction, lane and round (measured: 1-2% faster steps than 2, 4 slower)
   for (uint32_t base = (uint32_t)part * blockDim.x + threadIdx.x; base < total; base += U * stride) {
     vec4u pv[U], wv[U];
     vec4u* pd[U];
