@@ -162,6 +162,19 @@ def test_gather_layers_every_window():
         eng.close()
 
 
+@pytest.mark.parametrize("appends,pool_frac", [(1, 0.5), (2, 0.0)])
+def test_append_step_many_appends_parity(appends, pool_frac):
+    """ula_append_step with more appends per step (300 and 600) than the step's first
+    launch takes (256): they run as ula_append does, before the step; with room on the
+    GPU and with a full GPU pool (appends into host slots)."""
+    from synth.configs import Workload
+    wl = Workload(name=f"many_appends{appends}", requests=300, ctx_fixed=2048, ctx_range=None,
+                  sets_per_request=1, draft_keep=0.0, groups=1, layers=2, k=64, pool_frac=pool_frac,
+                  pool_slots=None if pool_frac else 40_000, ring=4, steps=4, appends=appends, overlap=0.8,
+                  p_recent=0.7, window=256, row_bytes=64, seed=3)
+    run_parity(wl, max_append=1024, combined=True)
+
+
 @pytest.mark.parametrize("ring", [1, 2, 9, 64])   # 64: the longest ring the engine takes
 def test_ring_lengths_parity(ring):
     wl = dataclasses.replace(preset("tiny_4x4k"), ring=ring, name=f"tiny_ring{ring}")
