@@ -29,7 +29,7 @@ def check_state(st: dict, P: int, H: int) -> None:
     m = np.asarray(st["map"], dtype=np.uint32).astype(np.int64)
     gown = np.asarray(st["gown"], dtype=np.int64)
     hown = np.asarray(st["hown"], dtype=np.int64)
-    assert gown.size == P and hown.size == H
+    assert gown.size == P and hown.size == H, "owner arrays of the wrong size"
 
     # I1: an entry is on the GPU or on the host, never both, and the mapping
     # table and the owners agree both ways
@@ -66,24 +66,26 @@ def check_step(prev: dict, st: dict, P: int, H: int, U: Optional[np.ndarray] = N
     unique, hits, misses, evictions, from_free, invalid = st["stats"]
     B = len(st["bitsets"]) - 2
     # I9: the completion counter is the step number
-    assert st["flag"] == prev["flag"] + 1
-    assert st["cur"] == (prev["cur"] + 1) % B
+    assert st["flag"] == prev["flag"] + 1, "I9: the completion counter is not the step number"
+    assert st["cur"] == (prev["cur"] + 1) % B, "the ring did not advance by one bucket"
     # I6: conservation
-    assert hits + misses == unique
-    assert from_free + evictions == misses
+    assert hits + misses == unique, "I6: hits + misses != unique"
+    assert from_free + evictions == misses, "I6: from_free + evictions != misses"
     occ_prev = int((np.asarray(prev["gown"]) != -1).sum())
     occ_now = int((np.asarray(st["gown"]) != -1).sum())
-    assert occ_now - occ_prev == from_free
+    assert occ_now - occ_prev == from_free, "I6: occupied GPU slots did not grow by from_free"
     # I5: eviction starts only once the pool is full
     free_prev = P - occ_prev
-    assert from_free == min(misses, free_prev), (from_free, misses, free_prev)
+    assert from_free == min(misses, free_prev), \
+        f"I5: eviction while free slots remained (from_free {from_free}, misses {misses}, free {free_prev})"
     # I3: the current bucket holds exactly this step's unique entries, all on the GPU
     cur_bits, _ = unpack(st["bitsets"][2 + st["cur"]], P)
-    assert int(cur_bits.sum()) == unique
+    assert int(cur_bits.sum()) == unique, "I3: the current bucket does not hold exactly the unique entries"
     if U is not None:
         m = np.asarray(st["map"], dtype=np.int64)[np.asarray(U, dtype=np.int64)]
         assert ((m & HOST_BIT) == 0).all(), "a selected entry is not GPU-resident"
-        assert cur_bits[m].all() and np.unique(m).size == unique
+        assert cur_bits[m].all() and np.unique(m).size == unique, \
+            "I3: a selected entry is outside the current bucket"
     # I4: no victim was taken from the current bucket
     if victims is not None and hit_slots is not None:
-        assert np.intersect1d(victims, hit_slots).size == 0
+        assert np.intersect1d(victims, hit_slots).size == 0, "I4: a victim was taken from the current bucket"

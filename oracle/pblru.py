@@ -194,10 +194,8 @@ class PBLRUGroup:
         if v.size and (self.map[v] == ABSENT).any():
             raise OracleError("ERANGE", "selected address never appended")
 
-        # S2 de-duplicate once for the whole group (section 2): first occurrence
-        # in row-major order
-        _, first = np.unique(v, return_index=True)
-        U = v[np.sort(first)]
+        # S2 de-duplicate once for the whole group (section 2)
+        U = self._dedup(v)
         invalid = int(flat.size - v.size)
 
         # S3 lookup through the mapping table (section 2)
@@ -224,11 +222,9 @@ class PBLRUGroup:
         self.ring[:, hit_slots] = False
         self.ring[self.cur, hit_slots] = True
 
-        # S7 victims: free, then cold, then ring oldest -> newest, never current,
-        # ascending slot order inside each bucket (section 3)
-        order = [self.free, self.cold]
-        order += [self.ring[(self.cur + j) % self.B] for j in range(1, self.B)]
-        candidates = np.concatenate([np.flatnonzero(b) for b in order])
+        # S7 victims: ascending slot order inside each bucket, buckets in the
+        # order of _victim_order (section 3)
+        candidates = np.concatenate([np.flatnonzero(b) for b in self._victim_order()])
         m = miss_la.size
         victims = candidates[:m]
         assert victims.size == m   # guaranteed by S4: |free|+|cold|+|other rings| >= P - |hits| >= m
@@ -262,6 +258,21 @@ class PBLRUGroup:
                               evictions=int(m - n_free), from_free=n_free, invalid=invalid)
         self.last_lists = (U, hit_slots, miss_la, miss_h, victims)
         return self.last
+
+    # ------------------------------------------------------------------
+    def _dedup(self, v: np.ndarray) -> np.ndarray:
+        """S2: the distinct valid addresses of a step in first-occurrence order
+        over (set, index), row-major (the reading of "once for such a group")."""
+        _, first = np.unique(v, return_index=True)
+        return v[np.sort(first)]
+
+    def _victim_order(self) -> list:
+        """S7: the buckets victims come from, in order: free, then cold, then the
+        ring from the oldest bucket (cur+1) to the newest (cur-1); the current
+        bucket never (section 3)."""
+        order = [self.free, self.cold]
+        order += [self.ring[(self.cur + j) % self.B] for j in range(1, self.B)]
+        return order
 
     # ------------------------------------------------------------------
     def gather(self, sel: np.ndarray, layer: int, step: Optional[int] = None) -> np.ndarray:
