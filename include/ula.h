@@ -45,10 +45,12 @@
  * Errors
  *  - Every call returns ULA_OK (0) or a negative code. Errors detected on the
  *    host are returned at once and change nothing. Errors detected on the
- *    device during an enqueued step or gather are latched per group; the
- *    remaining kernels of that call exit before changing any state, the next
- *    ula_sync returns the code and the context becomes unusable (ULA_ESTATE)
- *    for every call but ula_export_state, ula_sync and ula_destroy.
+ *    device during an enqueued step are latched per group and the remaining
+ *    kernels of that step exit before changing any state; errors a gather
+ *    detects are latched per group in a separate word that steps do not read,
+ *    so a gather never stops a step part-way. The next ula_sync returns the
+ *    first latched code and the context becomes unusable (ULA_ESTATE) for every
+ *    call but ula_export_state, ula_read_rows, ula_sync and ula_destroy.
  *  - ULA_ECAPACITY is detected before any state changes, so an exported state
  *    after it is the state before the failed step.
  *
@@ -180,7 +182,11 @@ int ula_release(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, 
  * replace them; the staged rows reach the host slots their misses vacated
  * during the group's next step, beside that step's reads from the host (a miss
  * of a row evicted by the previous step reads its staged copy), or when
- * ula_export_state or ula_read_rows needs the host pool current. Enqueued on
+ * ula_read_rows or ula_release needs the host pool current. So the mapping
+ * table can name a host slot for an evicted entry one step before its rows
+ * land there; every GPU reader is unaffected (a row in the host pool is read
+ * only by a later step of the group, which writes the staged rows first or
+ * reads the staged copy). Enqueued on
  * `stream` with no host synchronisation.
  * Host errors: ULA_EINVAL (bad g, n_sets > max_sets, k > max_k, negative sizes),
  * ULA_ESTATE. Device errors (reported by ula_sync): ULA_ERANGE, ULA_ECAPACITY. */
@@ -210,7 +216,11 @@ int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* l
  * wait for the signal); call it once per layer of the group, or gather several
  * layers in one launch with ula_gather_layers. On a stream other
  * than the step's, order it after the step first (event, or a stream wait on
- * ula_flag_address reaching the step number).
+ * ula_flag_address reaching the step number): the counter check inside the
+ * gather is a relaxed read that only catches a gather that runs before the
+ * counter is raised (ULA_ENOTRESIDENT); the rows of an unordered gather that
+ * finds the counter raised are undefined, since nothing orders its reads after
+ * the step's writes on another cache.
  * Host errors: ULA_EINVAL, ULA_ESTATE, ULA_ENOTRESIDENT (no step yet).
  * Device errors (reported by ula_sync): ULA_ENOTRESIDENT (counter not reached,
  * or an entry not on the GPU), ULA_ERANGE. */
@@ -235,9 +245,13 @@ int ula_gather_layers(ula_ctx* ctx, int32_t group, int32_t layer0, int32_t n_lay
  * entries) receives each group's last step statistics. */
 int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out);
 
-/* Copy group g's canonical state into caller host buffers (writes any staged
- * evicted rows to the host pool and synchronises the device first). Works on a
- * poisoned context. */
+/* Copy group g's canonical state (mapping table, owners, bucket bitsets, the
+ * current bucket, the completion counter and the last step's statistics) into
+ * caller host buffers, after synchronising the device. Staged evicted rows stay
+ * staged: none of these fields depends on the host pool's bytes. Works on a
+ * poisoned context. cur is derived from the counter (the ring advances once
+ * per step, section 3), not read from the device. Errors: ULA_EINVAL (null
+ * context or buffers, bad group), ULA_EHIP. */
 int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out);
 
 /* Read back the stored rows (all layers, layers_per_group x row_bytes bytes

@@ -66,6 +66,11 @@ __device__ __forceinline__ void latch(Counters* c, int code) {
   atomicCAS(&c->status, 0, code);
 }
 
+// Latch the first error a gather found, apart from the steps' status.
+__device__ __forceinline__ void latch_gather(Counters* c, int code) {
+  atomicCAS(&c->gstatus, 0, code);
+}
+
 __device__ __forceinline__ int status_of(const Counters* c) {
   return __hip_atomic_load(&c->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(THREADS) void k_gather(GroupDev g, const int32_t* _
       int ok = status_of(g.ctr) == 0;
       const long long f = __hip_atomic_load(&g.ctr->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (ok && f != want_flag) {
-        latch(g.ctr, ULA_ENOTRESIDENT);
+        latch_gather(g.ctr, ULA_ENOTRESIDENT);
         ok = 0;
       }
       s_ok = ok;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(THREADS) void k_gather(GroupDev g, const int32_t* _
       stream_rows<ROWS, UNROLL, THREADS, true>(g, s_off, nrows, nl, layer_stride, o, C, per_row);
     __syncthreads();
   }
-  if (err) latch(g.ctr, err);
+  if (err) latch_gather(g.ctr, err);
 }
 
 template <int ROWS, int UNROLL, int THREADS>

@@ -170,7 +170,6 @@ struct GroupHost {
   hipEvent_t ev[4] = {};
   int32_t last_pairs = 0;           // most miss pairs the last step could have staged
   int64_t written_back = 0;         // last step whose staged rows a flush wrote to the host
-  hipStream_t last_stream = nullptr;   // stream of the group's last step
 };
 
 struct ula_ctx {
@@ -525,16 +524,21 @@ int ula_release(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, 
 }
 
 // The evicted rows a step stages reach the host in the group's next step (the
-// write-back workgroups of its mark launch). Before the host reads state, a
+// write-back workgroups of its mark launch). Before the host reads rows, a
 // stand-alone write-back puts the staged rows there too (those of the last
 // step, or of an earlier one if a device error stopped the steps after it).
+// The device is idle first, so the write-back runs on the null stream: the
+// library never enqueues on a caller's stream outside a call that names it.
 static int flush_writebacks(ula_ctx* ctx) {
+  HIP_TRY(hipDeviceSynchronize());
+  bool any = false;
   for (auto& gh : ctx->groups) {
     if (gh.steps == 0 || gh.written_back == gh.steps) continue;
-    HIP_TRY(launch_writeback(gh.d, std::max<int32_t>(gh.last_pairs, 1), gh.last_stream));
+    HIP_TRY(launch_writeback(gh.d, std::max<int32_t>(gh.last_pairs, 1), nullptr));
     gh.written_back = gh.steps;
+    any = true;
   }
-  HIP_TRY(hipDeviceSynchronize());
+  if (any) HIP_TRY(hipDeviceSynchronize());
   return ULA_OK;
 }
 
@@ -562,7 +566,6 @@ static int step_impl(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, con
   // the previous step's evicted rows, unless a flush already wrote them out
   const int32_t wb_pairs = (gh.steps > 0 && gh.written_back != gh.steps) ? gh.last_pairs : 0;
 
-  gh.last_stream = s;
   if (tm) HIP_TRY(hipEventRecord(gh.ev[0], s));
   if (app) HIP_TRY(launch_tag_append(g, *app, app_rows, sel_dev, n, (uint32_t)t, s));
   else HIP_TRY(launch_tag(g, sel_dev, n, (uint32_t)t, s));
@@ -699,7 +702,8 @@ int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out) {
   int first = ULA_OK;
   for (size_t i = 0; i < c.size(); ++i) {
     if (per_group_out) fill_stats(c[i], &per_group_out[i]);
-    if (c[i].status && first == ULA_OK) first = c[i].status;
+    const int code = c[i].status ? c[i].status : c[i].gstatus;
+    if (code && first == ULA_OK) first = code;
   }
   if (first != ULA_OK) ctx->poisoned = first;
   return first;
@@ -709,10 +713,9 @@ int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out) {
   if (!ctx || !out) return ULA_EINVAL;
   if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
   if (!out->map || !out->gown || !out->bitsets || (ctx->dims.H > 0 && !out->hown)) return ULA_EINVAL;
-  {
-    int rc = flush_writebacks(ctx);
-    if (rc) return rc;
-  }
+  // the exported fields do not depend on the host pool's rows, so staged
+  // evicted rows stay staged (the group's next step writes them out as usual)
+  HIP_TRY(hipDeviceSynchronize());
   const GroupDev& g = ctx->groups[group].d;
   const Dims& d = ctx->dims;
   HIP_TRY(hipMemcpy(out->map, g.map, 4 * d.N, hipMemcpyDeviceToHost));
@@ -732,7 +735,9 @@ int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out) {
   Counters c;
   HIP_TRY(hipMemcpy(&c, g.ctr, sizeof(Counters), hipMemcpyDeviceToHost));
   out->flag = c.flag;
-  out->cur = (int32_t)(c.flag % d.B);   // the ring advances exactly once per completed step
+  // derived, not read back: the ring advances once per step, so after step t the
+  // current bucket is t mod B (the bucket bitsets show where the step's entries went)
+  out->cur = (int32_t)(c.flag % d.B);
   fill_stats(c, &out->last);
   return ULA_OK;
 }

@@ -58,8 +58,10 @@ constexpr int kCold = 1;
 __host__ __device__ constexpr int ring_id(int b) { return 2 + b; }
 
 struct alignas(64) Counters {
-  int32_t status;        // first latched device error of the group, 0 = none
-  int32_t pad0;          // keeps flag 8-byte aligned
+  int32_t status;        // first latched device error of the group's steps, 0 = none
+  int32_t gstatus;       // first device error a gather of the group found (kept apart
+                         //   from status: the step kernels poll status only, so a
+                         //   gather issued out of order cannot stop a step half-way)
   long long flag;        // completion counter: last completed step
   long long stats[6];    // unique, hits, misses, evictions, from_free, invalid
   int32_t n_unique, n_hits, n_miss, n_invalid;

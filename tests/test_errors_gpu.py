@@ -377,14 +377,20 @@ def test_gather_on_second_stream_ordered_by_counter_wait():
         eng.close()
 
 
-def test_unordered_gather_is_correct_or_refused():
-    """A gather issued on another stream without ordering either runs after
-    the step completed (correct rows) or sees the completion counter behind and
-    reports ENOTRESIDENT; it never returns rows of a half-finished step."""
+def test_unordered_gather_is_refused_or_leaves_the_step_intact():
+    """A gather issued on another stream without ordering after the step either
+    finds the completion counter behind and reports ENOTRESIDENT, or runs once the
+    counter has been raised. Its rows are guaranteed in neither case (ula.h: an
+    unordered gather is undefined; the counter check is a relaxed read), so what
+    is checked is what the design does guarantee: the gather's error never stops
+    the step it raced (gather errors are latched apart from the step's status),
+    so the group's state equals the oracle's after that step either way."""
     import torch
     from serving_pb_lru_amd import UlaError
     tr, eng, rows = _engine()
     wl = tr.wl
+    ora = new_group(tr, full_data=False)
+    oracle_load(ora, tr, 0)
     try:
         side = torch.cuda.Stream()
         busy = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -396,6 +402,8 @@ def test_unordered_gather_is_correct_or_refused():
             eng.append(0, app, rows(app, 0))
             eng.step(0, d)
             eng.sync()
+            ora.append(app, None)
+            ora.step(sel)
         sel = next(sels)
         d = _cuda(sel)
         app = tr.appends(3)
@@ -404,15 +412,18 @@ def test_unordered_gather_is_correct_or_refused():
         busy.fill_(1)
         eng.append(0, app, app_rows)
         eng.step(0, d)
-        out = eng.gather(0, 0, d, stream=side)
+        eng.gather(0, 0, d, stream=side)
         torch.cuda.synchronize()
+        ora.append(app, None)
+        ora.step(sel)
         try:
             eng.sync()
         except UlaError as e:
             assert e.name == "ENOTRESIDENT"
-            return
-        want = rows_for(wl.seed, 0, sel.reshape(-1), wl.layers, wl.row_bytes)[:, 0]
-        assert np.array_equal(out.cpu().numpy().reshape(-1, wl.row_bytes), want)
+        st, ref = eng.export_state(0), ora.export_state()
+        for key in ("map", "gown", "hown", "bitsets"):
+            assert np.array_equal(st[key], ref[key]), f"{key} differs after the raced step"
+        assert (st["flag"], tuple(st["stats"])) == (ref["flag"], ref["stats"])
     finally:
         eng.close()
 

@@ -5,16 +5,21 @@ the step in one ula_append_step call; layer 0 gathered alone, the later layers
 of the group in one ula_gather_layers launch); the exact-LRU cases use the
 separate calls (ula_append, ula_step, one ula_gather per layer).
 
-After the initial load and after every other step (and the last) the digest
-of the engine's exported state (mapping table, owners, bucket bitsets, current
-bucket, completion counter, step statistics) must equal the digest the CPU
-oracle produced for the same seeded inputs (tests/golden/digests_<workload>.json,
-written by tests/golden/make_state_digests.py from oracle/ alone). Gathered
-bytes are checked after every step on sampled rows against their closed form
-(row contents are a function of group, address and layer), and stored rows on
-sampled addresses (wherever they live, GPU or host pool) at the exported steps.
-Exporting writes staged evicted rows out to the host pool, so the unexported
-steps exercise the write-back inside the following step.
+After the initial load and after every step, the digest of the engine's
+exported state (mapping table, owners, bucket bitsets, completion counter, step
+statistics) must equal the digest the CPU oracle produced for the same seeded
+inputs (tests/golden/digests_<workload>.json, written by
+tests/golden/make_state_digests.py from oracle/ alone), and so must the step
+statistics ula_sync returns. The current bucket in the digest is derived from
+the counter on both sides (the ring advances once per step); which bucket the
+step's entries went to is in the bitsets. Every gathered byte of every layer
+is compared after every step with its closed form (row contents are a function
+of group, address and layer, generated on the device by synth's HIP generator,
+itself pinned to the numpy one), zeros for padding. Exporting leaves the staged
+evicted rows staged, so every step's write-back still happens inside the next
+step; the stored rows of sampled addresses (wherever they live, GPU or host
+pool) are read back every eighth step and after the last, which writes the
+staged rows out first.
 
 The exact-LRU policy is checked the same way against the array form of the
 oracle's exact LRU (tests/golden/digests_lru_<workload>.json, timestamps
@@ -51,7 +56,7 @@ def _cmp(got, want, where):
             assert got[k] == want[k], f"{where}: {k} differs (engine {got[k]}, oracle {want[k]})"
 
 
-def run_group(name: str, g: int, samples: int = 1024, policy: int = 0, bench_calls: bool = True):
+def run_group(name: str, g: int, samples: int = 128, policy: int = 0, bench_calls: bool = True):
     import torch
     from serving_pb_lru_amd import Engine
     from synth.device import rows_device
@@ -85,23 +90,23 @@ def run_group(name: str, g: int, samples: int = 1024, policy: int = 0, bench_cal
                     eng.append(0, app, rows(app))
                 eng.step(0, dsel)
                 outs = gather_layers_by(eng, 0, wl.layers, dsel, "layer")
-            eng.sync()
-            # state and stored rows every other step: exporting writes the staged
-            # evicted rows out, so the steps in between leave that to the next
-            # step's own write-back
-            exported = t % 2 == 0 or t == tr.steps
-            if exported:
-                _cmp(digest(eng.export_state(0)), gold[t], f"{name} g{g} step {t}")
-            flat = sel.reshape(-1)
-            idx = rng.choice(flat.size, size=min(samples, flat.size), replace=False)
-            want = rows_for(wl.seed, g, flat[idx], wl.layers, wl.row_bytes)
-            tidx = torch.from_numpy(idx).cuda()
+            stats = eng.sync()[0]
+            assert list(stats) == gold[t]["stats"], f"{name} g{g} step {t}: ula_sync stats {stats}"
+            _cmp(digest(eng.export_state(0)), gold[t], f"{name} g{g} step {t}")
+            # every gathered byte against its closed form, on the device
+            flat = dsel.reshape(-1)
+            want = rows(sel.reshape(-1))
+            want[flat == -1] = 0
             for l in range(wl.layers):
-                got = outs[l].view(-1, wl.row_bytes).index_select(0, tidx).cpu().numpy()
-                assert np.array_equal(got, want[:, l]), f"{name} g{g} step {t} layer {l}: gathered rows differ"
-            pool = np.concatenate(known)
-            probe = pool[rng.choice(pool.size, size=128, replace=False)]
-            if exported:
+                got = outs[l].reshape(-1, wl.row_bytes)
+                if not torch.equal(got, want[:, l]):
+                    bad = (got != want[:, l]).any(dim=1).nonzero().reshape(-1)[:5].tolist()
+                    raise AssertionError(f"{name} g{g} step {t} layer {l}: gathered rows differ, "
+                                         f"first rows {bad}")
+            del want
+            if t % 8 == 0 or t == tr.steps:
+                pool = np.concatenate(known)
+                probe = pool[rng.choice(pool.size, size=samples, replace=False)]
                 assert np.array_equal(eng.read_rows(0, probe),
                                       rows_for(wl.seed, g, probe, wl.layers, wl.row_bytes)), \
                     f"{name} g{g} step {t}: stored rows differ"
