@@ -76,7 +76,9 @@ enum {
   ULA_ECAPACITY = -5,    /* a step selects more distinct entries than the GPU pool holds */
   ULA_ENOTRESIDENT = -6, /* gather before its step completed, or of an entry not on the GPU */
   ULA_ESTATE = -7,       /* the context was poisoned by an earlier device error */
-  ULA_EHIP = -8          /* a HIP runtime call failed; ula_strerror gives its text */
+  ULA_EHIP = -8,         /* a HIP runtime call failed; ula_strerror gives its text */
+  ULA_EBUSY = -9,        /* ula_init_static: this device's static workspace is held by a live context */
+  ULA_ETOOBIG = -10      /* ula_init_static: the configuration needs more than the static workspace */
 };
 
 typedef struct ula_ctx ula_ctx;
@@ -139,6 +141,26 @@ size_t ula_host_bytes(const ula_config* cfg);
  * (may be NULL when host_slots == 0). Errors: ULA_EINVAL, ULA_EHIP. */
 int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t stream,
              ula_ctx** out);
+
+/* ula_init for callers that cannot allocate device memory (code that must not
+ * call hipMalloc or a caching allocator: tight serving loops, harnesses that
+ * forbid allocation). Exactly ula_init, with the device workspace taken from a
+ * static array the library holds on every device it runs on (32 MiB per device,
+ * kept until the process ends) instead of a dev_ws argument: the current
+ * device's array, resolved once per device. Only a configuration with
+ * ula_device_bytes(cfg) <= 32 MiB fits (ULA_ETOOBIG otherwise, nothing
+ * touched). One live context per device may hold the array: another call on the
+ * same device before that context's ula_destroy returns ULA_EBUSY (two contexts
+ * on one array would overwrite each other's state). Every call starts from a
+ * fully initialised workspace whatever an earlier context left in it.
+ * The call allocates no device memory and no pinned host memory (the context
+ * itself is ordinary host memory; host_pinned is still the caller's pool). Such
+ * a context has no pinned staging buffers, so ula_append of more than 256
+ * entries or of host-resident rows, and ula_release, copy addresses and rows
+ * from the caller's memory and wait for the copy before they return. Everything
+ * else behaves as for a context from ula_init.
+ * Errors: ULA_EINVAL, ULA_ETOOBIG, ULA_EBUSY, ULA_EHIP. */
+int ula_init_static(const ula_config* cfg, void* host_pinned, uint64_t stream, ula_ctx** out);
 
 /* Append n new logical entries to group g (section 2: the library decides the
  * pool). In list order each entry takes the lowest free GPU slot (joining the

@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -153,6 +154,8 @@ const char* kMessages[] = {
     "gathered entry not resident on the GPU, or its step has not completed",
     "context poisoned by an earlier device error",
     "HIP runtime error",
+    "the static device workspace of this device is held by a live context",
+    "the configuration needs more device workspace than the static workspace holds (32 MiB)",
 };
 
 }  // namespace
@@ -181,6 +184,7 @@ struct ula_ctx {
   Counters* ctrs = nullptr;
   std::vector<GroupHost> groups;
   int poisoned = 0;
+  int static_dev = -1;               // device whose static workspace the context holds, or -1
   int timing = 0;                    // ULA_TIMING_* flags
   // gather kernel durations: a ring of dispatch-recorded event pairs, summed
   // lazily (when the ring wraps, and by ula_read_gather_timing)
@@ -191,6 +195,46 @@ struct ula_ctx {
 };
 
 static constexpr int kGatherTimingRing = 256;
+
+// ---- the static device workspace (ula_init_static) --------------------------
+// For callers that cannot allocate device memory, one workspace per device lives
+// in this file-scope array; each device holds its own copy for the life of the
+// process. Host code never passes the array's name to a kernel or a copy (on the
+// host it is only a stand-in for the symbol): it resolves the device address once
+// per device with hipGetSymbolAddress, with that device current, and uses that.
+constexpr size_t kStaticWorkspaceBytes = 32ull << 20;
+constexpr int kMaxStaticDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+static std::mutex g_static_mu;
+static void* g_static_ptr[kMaxStaticDevices];     // resolved device address, per device
+static bool g_static_live[kMaxStaticDevices];     // a live context holds that device's copy
+
+// The current device's static workspace, resolved on first use, with its
+// device index; claims it for one context (released by destroy_ctx).
+static int claim_static_workspace(void** ptr, int* dev) {
+  int d = -1;
+  HIP_TRY(hipGetDevice(&d));
+  if (d < 0 || d >= kMaxStaticDevices) return ULA_EINVAL;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static_live[d]) return ULA_EBUSY;
+  if (!g_static_ptr[d]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p || (uintptr_t)p % kAlign) return ULA_EINVAL;
+    g_static_ptr[d] = p;
+  }
+  g_static_live[d] = true;
+  *ptr = g_static_ptr[d];
+  *dev = d;
+  return ULA_OK;
+}
+
+static void release_static_workspace(int dev) {
+  if (dev < 0) return;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  g_static_live[dev] = false;
+}
 
 // Add the oldest pending gather's kernel time to the total.
 static int retire_gather_timing(ula_ctx* ctx) {
@@ -220,7 +264,7 @@ size_t ula_host_bytes(const ula_config* cfg) {
 
 const char* ula_strerror(int code) {
   if (code == ULA_EHIP && !g_hip_error.empty()) return g_hip_error.c_str();
-  if (code > 0 || code < ULA_EHIP) return "unknown error code";
+  if (code > 0 || code < ULA_ETOOBIG) return "unknown error code";
   return kMessages[-code];
 }
 
@@ -237,6 +281,7 @@ int ula_host_free(void* p) {
 }
 
 static void destroy_ctx(ula_ctx* ctx) {
+  release_static_workspace(ctx->static_dev);
   for (hipEvent_t e : ctx->gt_ev)
     if (e) (void)hipEventDestroy(e);
   for (auto& g : ctx->groups) {
@@ -250,18 +295,22 @@ static void destroy_ctx(ula_ctx* ctx) {
   delete ctx;
 }
 
-int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t stream,
-             ula_ctx** out) {
-  if (!out) return ULA_EINVAL;
-  *out = nullptr;
+// ula_init's body. static_dev >= 0: dev_ws is that device's static workspace,
+// claimed by the caller; the context then allocates no pinned staging buffers
+// and no events (appends and releases copy addresses from the caller's memory,
+// and step timing creates its events when it is switched on).
+static int init_impl(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t stream,
+                     ula_ctx** out, int static_dev) {
   Dims d;
   if (!check_config(cfg, &d)) return ULA_EINVAL;
-  if (!dev_ws || ((uintptr_t)dev_ws % kAlign)) return ULA_EINVAL;
-  if (d.H > 0 && !host_pinned) return ULA_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   ula_ctx* ctx = new (std::nothrow) ula_ctx();
-  if (!ctx) return ULA_EINVAL;
+  if (!ctx) {
+    release_static_workspace(static_dev);
+    return ULA_EINVAL;
+  }
+  ctx->static_dev = static_dev;
   ctx->cfg = *cfg;
   ctx->dims = d;
   ctx->lay = layout_of(cfg, d);
@@ -272,7 +321,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     void* p = nullptr;
     hipError_t e = hipHostGetDevicePointer(&p, host_pinned, 0);
     if (e != hipSuccess) {
-      delete ctx;
+      destroy_ctx(ctx);
       return hip_fail(e, "hipHostGetDevicePointer(host pool)");
     }
     hdev = static_cast<uint8_t*>(p);
@@ -363,12 +412,12 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
     if (e == hipSuccess) e = launch_fill_u32(g.tcnt, d.NB * d.T, 0u, s);
     if (e == hipSuccess) e = launch_init_bitmap(g.bm + kFree * d.W, g.W, d.P, g.tcnt + kFree * d.T, g.T, s);
     if (e == hipSuccess) e = launch_init_bitmap(g.hbm, g.WH, d.H, g.htcnt, g.TH, s);
-    for (int i = 0; i < kStageSlots && e == hipSuccess; ++i) {
+    for (int i = 0; i < kStageSlots && e == hipSuccess && static_dev < 0; ++i) {
       e = hipHostMalloc(reinterpret_cast<void**>(&gh.stage[i]), sizeof(int32_t) * d.maxApp,
                         hipHostMallocDefault);
       if (e == hipSuccess) e = hipEventCreateWithFlags(&gh.stage_ev[i], hipEventDisableTiming);
     }
-    for (int i = 0; i < 4 && e == hipSuccess; ++i) e = hipEventCreate(&gh.ev[i]);
+    for (int i = 0; i < 4 && e == hipSuccess && static_dev < 0; ++i) e = hipEventCreate(&gh.ev[i]);
     if (e != hipSuccess) rc = hip_fail(e, "ula_init");
   }
   if (rc == ULA_OK) {
@@ -381,6 +430,32 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
   }
   *out = ctx;
   return ULA_OK;
+}
+
+int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t stream,
+             ula_ctx** out) {
+  if (!out) return ULA_EINVAL;
+  *out = nullptr;
+  Dims d;
+  if (!check_config(cfg, &d)) return ULA_EINVAL;
+  if (!dev_ws || ((uintptr_t)dev_ws % kAlign)) return ULA_EINVAL;
+  if (d.H > 0 && !host_pinned) return ULA_EINVAL;
+  return init_impl(cfg, dev_ws, host_pinned, stream, out, -1);
+}
+
+int ula_init_static(const ula_config* cfg, void* host_pinned, uint64_t stream, ula_ctx** out) {
+  if (!out) return ULA_EINVAL;
+  *out = nullptr;
+  Dims d;
+  if (!check_config(cfg, &d)) return ULA_EINVAL;
+  if (layout_of(cfg, d).total > kStaticWorkspaceBytes) return ULA_ETOOBIG;
+  if (d.H > 0 && !host_pinned) return ULA_EINVAL;
+  void* ws = nullptr;
+  int dev = -1;
+  int rc = claim_static_workspace(&ws, &dev);
+  if (rc) return rc;
+  rc = init_impl(cfg, ws, host_pinned, stream, out, dev);   // releases the claim on failure
+  return rc;
 }
 
 int ula_destroy(ula_ctx* ctx) {
@@ -443,6 +518,22 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
     a.n = n;
     std::memcpy(a.las, la_host, sizeof(int32_t) * n);
     HIP_TRY(launch_append_small(g, a, static_cast<const uint8_t*>(rows), s));
+  } else if (ctx->static_dev >= 0) {
+    // a context without pinned staging buffers: chunks whose addresses go by
+    // value; host rows are copied in and waited for before the next chunk
+    const int32_t chunk = (int32_t)std::min<int64_t>(kSmallAppend, d.maxApp);
+    for (int32_t off = 0; off < n; off += chunk) {
+      SmallAppend a{};
+      a.n = std::min(chunk, n - off);
+      std::memcpy(a.las, la_host + off, sizeof(int32_t) * a.n);
+      const uint8_t* src = static_cast<const uint8_t*>(rows) + (size_t)off * d.slot_bytes;
+      if (!rows_on_device) {
+        HIP_TRY(hipMemcpyAsync(g.app_rows, src, (size_t)a.n * d.slot_bytes, hipMemcpyHostToDevice, s));
+        HIP_TRY(hipStreamSynchronize(s));
+        src = g.app_rows;
+      }
+      HIP_TRY(launch_append_small(g, a, src, s));
+    }
   } else {
     for (int32_t off = 0; off < n; off += (int32_t)d.maxApp) {
       const int32_t cnt = (int32_t)std::min<int64_t>(n - off, d.maxApp);
@@ -505,13 +596,19 @@ int ula_release(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, 
   }
   for (int32_t off = 0; off < n; off += (int32_t)d.maxApp) {
     const int32_t cnt = (int32_t)std::min<int64_t>(n - off, d.maxApp);
-    const int k = gh.stage_next;
-    gh.stage_next = (k + 1) % kStageSlots;
-    if (gh.stage_used[k]) HIP_TRY(hipEventSynchronize(gh.stage_ev[k]));
-    gh.stage_used[k] = true;
-    std::memcpy(gh.stage[k], la_host + off, sizeof(int32_t) * cnt);
-    HIP_TRY(hipMemcpyAsync(g.app_la, gh.stage[k], sizeof(int32_t) * cnt, hipMemcpyHostToDevice, s));
-    HIP_TRY(hipEventRecord(gh.stage_ev[k], s));
+    if (ctx->static_dev >= 0) {
+      // no pinned staging buffers: copy from the caller's memory and wait for it
+      HIP_TRY(hipMemcpyAsync(g.app_la, la_host + off, sizeof(int32_t) * cnt, hipMemcpyHostToDevice, s));
+      HIP_TRY(hipStreamSynchronize(s));
+    } else {
+      const int k = gh.stage_next;
+      gh.stage_next = (k + 1) % kStageSlots;
+      if (gh.stage_used[k]) HIP_TRY(hipEventSynchronize(gh.stage_ev[k]));
+      gh.stage_used[k] = true;
+      std::memcpy(gh.stage[k], la_host + off, sizeof(int32_t) * cnt);
+      HIP_TRY(hipMemcpyAsync(g.app_la, gh.stage[k], sizeof(int32_t) * cnt, hipMemcpyHostToDevice, s));
+      HIP_TRY(hipEventRecord(gh.stage_ev[k], s));
+    }
     HIP_TRY(launch_release(g, cnt, s));
   }
   for (int32_t i = 0; i < n; ++i) {
@@ -783,6 +880,10 @@ int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr) {
 
 int ula_set_timing(ula_ctx* ctx, int32_t flags) {
   if (!ctx || (flags & ~(ULA_TIMING_STEP | ULA_TIMING_GATHER))) return ULA_EINVAL;
+  if (flags & ULA_TIMING_STEP)   // a static-workspace context creates its step events here
+    for (auto& gh : ctx->groups)
+      for (auto& e : gh.ev)
+        if (!e) HIP_TRY(hipEventCreate(&e));
   ctx->timing = flags;
   return ULA_OK;
 }
@@ -804,6 +905,7 @@ int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out3) {
   if (!ctx || !ms_out3) return ULA_EINVAL;
   if (group < 0 || group >= ctx->cfg.num_groups) return ULA_EINVAL;
   GroupHost& gh = ctx->groups[group];
+  if (!gh.ev[3]) return ULA_EINVAL;   // step timing never switched on
   HIP_TRY(hipEventSynchronize(gh.ev[3]));
   for (int i = 0; i < 3; ++i) HIP_TRY(hipEventElapsedTime(&ms_out3[i], gh.ev[i], gh.ev[i + 1]));
   return ULA_OK;

@@ -19,7 +19,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libula.so")
 
 ERROR_NAMES = {0: "OK", -1: "EINVAL", -2: "ERANGE", -3: "EDUP", -4: "EHOSTFULL",
-               -5: "ECAPACITY", -6: "ENOTRESIDENT", -7: "ESTATE", -8: "EHIP"}
+               -5: "ECAPACITY", -6: "ENOTRESIDENT", -7: "ESTATE", -8: "EHIP", -9: "EBUSY",
+               -10: "ETOOBIG"}
 
 
 POLICY_PBLRU, POLICY_LRU = 0, 1
@@ -62,6 +63,8 @@ SIGNATURES = [
     ("ula_host_bytes", ctypes.c_size_t, [ctypes.POINTER(UlaConfig)]),
     ("ula_init", ctypes.c_int, [ctypes.POINTER(UlaConfig), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.c_uint64, ctypes.POINTER(ctypes.c_void_p)]),
+    ("ula_init_static", ctypes.c_int, [ctypes.POINTER(UlaConfig), ctypes.c_void_p, ctypes.c_uint64,
+                                       ctypes.POINTER(ctypes.c_void_p)]),
     ("ula_append", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64]),
     ("ula_release", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
@@ -145,8 +148,10 @@ class Engine:
 
     def __init__(self, num_groups: int, layers: int, row_bytes: int, ring: int, logical_capacity: int,
                  gpu_slots: int, host_slots: int, max_sets: int, max_k: int, max_append: int = 4096,
-                 device: str = "cuda", stream=None, policy: int = 0):
-        """policy: POLICY_PBLRU (0) or POLICY_LRU (1)."""
+                 device: str = "cuda", stream=None, policy: int = 0, static_workspace: bool = False):
+        """policy: POLICY_PBLRU (0) or POLICY_LRU (1). static_workspace: take the device
+        workspace from the library's static array (ula_init_static) instead of a torch
+        allocation."""
         import torch
         self.cfg = UlaConfig(num_groups, layers, row_bytes, ring, logical_capacity, gpu_slots,
                              host_slots, max_sets, max_k, max_append, policy)
@@ -157,15 +162,22 @@ class Engine:
             raise UlaError(-1, "ula_device_bytes", "invalid configuration")
         self.device_bytes = nbytes
         self.host_bytes = L.ula_host_bytes(ctypes.byref(self.cfg))
-        self.ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.ws = None if static_workspace else torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.host = None
         if self.host_bytes:
             self.host = L.ula_host_alloc(self.host_bytes)
             if not self.host:
                 raise UlaError(-8, "ula_host_alloc", f"could not pin {self.host_bytes} bytes")
         self.ctx = ctypes.c_void_p()
-        _check(L.ula_init(ctypes.byref(self.cfg), self.ws.data_ptr(), self.host, _stream(stream),
-                          ctypes.byref(self.ctx)), "ula_init")
+        if static_workspace:
+            rc = L.ula_init_static(ctypes.byref(self.cfg), self.host, _stream(stream), ctypes.byref(self.ctx))
+            if rc:
+                L.ula_host_free(self.host)
+                self.host = None
+            _check(rc, "ula_init_static")
+        else:
+            _check(L.ula_init(ctypes.byref(self.cfg), self.ws.data_ptr(), self.host, _stream(stream),
+                              ctypes.byref(self.ctx)), "ula_init")
         self.num_groups, self.layers, self.row_bytes, self.ring = num_groups, layers, row_bytes, ring
         self.N, self.P, self.H = logical_capacity, gpu_slots, host_slots
 

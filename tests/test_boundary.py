@@ -114,3 +114,16 @@ def test_binding_rejects_unusable_device_buffers():
     for t in bad:
         with pytest.raises(ValueError):
             ula._dev(t, "int32", 8, "sel")
+
+
+def test_static_workspace_refuses_a_large_config_on_host():
+    """ula_init_static checks the configuration against its static workspace (32 MiB)
+    before it touches a device."""
+    L = ula.lib()
+    c = _cfg()   # about 1.1 GB of workspace
+    ctx = ctypes.c_void_p()
+    assert L.ula_init_static(ctypes.byref(c), None, 0, ctypes.byref(ctx)) == -10
+    assert not ctx.value
+    assert L.ula_strerror(-10).decode().startswith("the configuration needs more device workspace")
+    bad = _cfg(row_bytes=650)
+    assert L.ula_init_static(ctypes.byref(bad), None, 0, ctypes.byref(ctx)) == -1
