@@ -20,6 +20,12 @@ decision is the textbook one:
 * a hit or a load at step t sets the slot's stamp to t;
 * victims are the free slots in ascending order, then the occupied slots in
   (stamp ascending, slot ascending) order, excluding slots stamped t.
+
+With placement "ring" an append is an access of the last step's round instead:
+each appended entry in turn takes the first slot of the victim order of that
+round t (free slots ascending, then occupied slots by (stamp, slot), never one
+stamped t), is stamped t, and the entry it displaces moves to the lowest free
+host slot; with no such slot left it takes the lowest free host slot itself.
 """
 
 from __future__ import annotations
@@ -29,7 +35,9 @@ from typing import List
 
 
 class ExactLRUGroup:
-    def __init__(self, N: int, P: int, H: int):
+    def __init__(self, N: int, P: int, H: int, placement: str = "lowest"):
+        assert placement in ("lowest", "ring")
+        self.placement = placement
         self.N, self.P, self.H = N, P, H
         self.where = {}                 # la -> ("gpu", slot) | ("host", slot)
         self.gown: List[int] = [-1] * P
@@ -43,6 +51,9 @@ class ExactLRUGroup:
         self.free_host = list(range(H))
 
     def append(self, las) -> None:
+        if self.placement == "ring":
+            self._append_ring(las)
+            return
         for la in [int(x) for x in las]:
             assert la not in self.where
             if self.free_gpu:
@@ -54,6 +65,32 @@ class ExactLRUGroup:
                 h = heapq.heappop(self.free_host)
                 self.hown[h] = la
                 self.where[la] = ("host", h)
+
+    def _append_ring(self, las) -> None:
+        t = self.t
+        for la in [int(x) for x in las]:
+            assert la not in self.where
+            free = sorted(self.free_gpu)
+            occupied = [s for s in range(self.P) if self.gown[s] != -1 and self.stamp[s] != t]
+            occupied.sort(key=lambda s: (self.stamp[s], s))
+            order = free + occupied
+            if not order:
+                h = heapq.heappop(self.free_host)
+                self.hown[h] = la
+                self.where[la] = ("host", h)
+                continue
+            v = order[0]
+            old = self.gown[v]
+            if old == -1:
+                self.free_gpu.remove(v)
+                heapq.heapify(self.free_gpu)
+            else:
+                h = heapq.heappop(self.free_host)
+                self.hown[h] = old
+                self.where[old] = ("host", h)
+            self.gown[v] = la
+            self.stamp[v] = t
+            self.where[la] = ("gpu", v)
 
     def release(self, las) -> None:
         """The released entries' slots become free (GPU: back on the free list,

@@ -29,7 +29,12 @@ Readings where the pages are silent (each restated where it is used):
   free when the victim slot was free;
 * slots loaded by the step, like hits, join the current bucket;
 * an append takes the lowest free GPU slot (joining the cold bucket), else the
-  lowest free host slot; appends never evict;
+  lowest free host slot; appends never evict (placement "lowest", the default);
+  the alternative placement "ring" puts each appended entry on the GPU in the
+  current bucket, in the slot the next victim of the step's order would be
+  (free, cold, ring oldest -> newest, never the current bucket), and sends that
+  slot's entry to the lowest free host slot; once no victim is left, entries
+  take the lowest free host slots;
 * more unique entries than GPU slots is a capacity error and changes nothing;
 * the completion signal is a per-group step counter ``flag``.
 
@@ -85,9 +90,12 @@ class PBLRUGroup:
     """The state of one layer group: map, owners, buckets and (optionally) pools."""
 
     def __init__(self, N: int, P: int, H: int, B: int, layers: int, row_bytes: int,
-                 full_data: bool = True):
+                 full_data: bool = True, placement: str = "lowest"):
         if B < 1 or P < 1 or H < 0 or N < 1 or layers < 1:
             raise OracleError("EINVAL", "bad sizes")
+        if placement not in ("lowest", "ring"):
+            raise OracleError("EINVAL", "placement is 'lowest' or 'ring'")
+        self.placement = placement
         self.N, self.P, self.H, self.B = N, P, H, B
         self.layers, self.row_bytes = layers, row_bytes
         self.full_data = full_data
@@ -133,6 +141,9 @@ class PBLRUGroup:
             raise OracleError("EHOSTFULL", "no room for the append")
         if self.full_data:
             rows = np.asarray(rows, dtype=np.uint8).reshape(n, self.layers, self.row_bytes)
+        if self.placement == "ring":
+            self._append_ring(las, rows, free_host)
+            return
         n_gpu = min(n, free_gpu.size)
         s = free_gpu[:n_gpu]
         la_g = las[:n_gpu]
@@ -147,6 +158,47 @@ class PBLRUGroup:
         if self.full_data:
             self.gpu[s] = rows[:n_gpu]
             self.host[h] = rows[n_gpu:]
+
+    def _append_ring(self, las: np.ndarray, rows: Optional[np.ndarray], free_host: np.ndarray) -> None:
+        """Placement "ring" (an alternative reading of who places new KV, section 2;
+        section 3: entries of the current round stay on the GPU): in list order,
+        each entry takes the next slot of the step's victim order (free ascending,
+        then cold, then the ring from the oldest bucket to the newest, never the
+        current bucket) and joins the current bucket, the round the last step
+        used; an entry that held that slot moves to the lowest free host slot
+        (its rows with it). Entries placed later in the same call cannot take
+        earlier ones' slots (the current bucket is never a victim). Once no
+        victim is left, entries take the lowest free host slots. Taking the next
+        victim one entry at a time is taking the first q of the order at once,
+        q = min(n, victims available); every eviction comes before every
+        host-placed entry, so evicted entries take the lowest free host slots
+        in victim order and the host-placed entries the next ones."""
+        n = las.size
+        cand = np.concatenate([np.flatnonzero(b) for b in self._victim_order()])
+        q = min(n, cand.size)
+        V = cand[:q]
+        owners = self.gown[V].astype(np.int64)
+        ev = owners != -1
+        n_ev = int(ev.sum())
+        h_ev = free_host[:n_ev]
+        h_new = free_host[n_ev:n_ev + (n - q)]
+        # the data first: the evicted rows to the host, the appended rows in
+        if self.full_data:
+            self.host[h_ev] = self.gpu[V[ev]]
+            self.gpu[V] = rows[:q]
+            self.host[h_new] = rows[q:]
+        # then the mapping table and owners
+        self.map[owners[ev]] = HOST_BIT | h_ev.astype(np.uint32)
+        self.hown[h_ev] = owners[ev]
+        self.map[las[:q]] = V.astype(np.uint32)
+        self.gown[V] = las[:q]
+        self.map[las[q:]] = HOST_BIT | h_new.astype(np.uint32)
+        self.hown[h_new] = las[q:]
+        # the taken slots join the current bucket
+        self.free[V] = False
+        self.cold[V] = False
+        self.ring[:, V] = False
+        self.ring[self.cur, V] = True
 
     # ------------------------------------------------------------------
     def release(self, las: np.ndarray) -> None:

@@ -50,6 +50,35 @@ def test_invariants_random(seed):
             assert (out[valid] == ref).all()
 
 
+@pytest.mark.parametrize("seed", range(16))
+def test_invariants_ring_placement(seed):
+    """I1-I9 with appends placed in the current bucket: after every append (I1, I2:
+    the evicted entries moved to the host, nothing held twice) and every step,
+    stored and gathered rows against their closed form."""
+    wl = tiny_workload(seed, steps=10)
+    tr = Trace(wl)
+    g = PBLRUGroup(tr.N, tr.P, tr.H, wl.ring, wl.layers, wl.row_bytes, full_data=True, placement="ring")
+    load = tr.initial_load_order()
+    g.append(load, rows_for(wl.seed, 0, load, wl.layers, wl.row_bytes))
+    check_state(g.export_state(), tr.P, tr.H)
+    for t, sel in enumerate(padded_selections(tr, 0, seed), 1):
+        app = tr.appends(t)
+        g.append(app, rows_for(wl.seed, 0, app, wl.layers, wl.row_bytes))
+        check_state(g.export_state(), tr.P, tr.H)
+        prev = g.export_state()
+        g.step(sel)
+        st = g.export_state()
+        U, hit_slots, _, _, victims = g.last_lists
+        check_step(prev, st, tr.P, tr.H, U=U, victims=victims, hit_slots=hit_slots)
+        appended = np.flatnonzero(g.map != 0xFFFFFFFF)
+        want = rows_for(wl.seed, 0, appended, wl.layers, wl.row_bytes)
+        assert (np.stack([g.read_row(int(la)) for la in appended]) == want).all()
+        for layer in range(wl.layers):
+            out = g.gather(sel, layer, step=t)
+            valid = sel != -1
+            assert (out[valid] == rows_for(wl.seed, 0, sel[valid], wl.layers, wl.row_bytes)[:, layer]).all()
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_invariants_hold_with_releases(seed):
     """I1-I9 after every step of traces whose finished entries are released between

@@ -21,10 +21,11 @@ import dataclasses
 from tracegen import padded_selections, tiny_workload
 
 
-def _run_both(trace, sels):
+def _run_both(trace, sels, placement="lowest"):
     wl = trace.wl
-    pb = PBLRUGroup(trace.N, trace.P, trace.H, wl.ring, wl.layers, wl.row_bytes, full_data=False)
-    lru = ExactLRUGroup(trace.N, trace.P, trace.H)
+    pb = PBLRUGroup(trace.N, trace.P, trace.H, wl.ring, wl.layers, wl.row_bytes, full_data=False,
+                    placement=placement)
+    lru = ExactLRUGroup(trace.N, trace.P, trace.H, placement=placement)
     load = trace.initial_load_order()
     pb.append(load, None)
     lru.append(load)
@@ -46,6 +47,24 @@ def test_long_ring_equals_exact_lru(seed):
         assert list(pb.last_lists[4]) == lru.last_victims, f"step {t}"
         assert pb.last.as_tuple() == lru.last
         assert [int(x) for x in pb.map] == lru.map_array()
+        assert list(pb.gown) == lru.gown and list(pb.hown) == lru.hown
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_long_ring_equals_exact_lru_ring_placement(seed):
+    """The same equivalence with appends placed in the current bucket (evicting):
+    an appended entry counts as accessed in the last step's round, so with no fold
+    PB-LRU's victims (free, cold, ring oldest to newest, never current) are exact
+    LRU's (free, then by (stamp, slot), never a slot of the current round), for
+    the steps' misses and for the appends alike. Pools small enough that appends
+    evict and overflow to the host."""
+    wl = tiny_workload(seed)
+    wl = dataclasses.replace(wl, ring=wl.steps + 1, appends=int(np.random.default_rng(seed).integers(1, 4)))
+    tr = Trace(wl)
+    for t, pb, lru in _run_both(tr, padded_selections(tr, 0, seed), placement="ring"):
+        assert list(pb.last_lists[4]) == lru.last_victims, f"step {t}"
+        assert pb.last.as_tuple() == lru.last
+        assert [int(x) for x in pb.map] == lru.map_array(), f"step {t}"
         assert list(pb.gown) == lru.gown and list(pb.hown) == lru.hown
 
 

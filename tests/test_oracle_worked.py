@@ -71,3 +71,62 @@ def test_worked_example_exact_lru():
         g.step(s["sel"])
         assert g.last_victims == want
         assert g.map_array() == [_enc(x) for x in s["map"]]
+
+
+# ---- the "ring" placement of appended entries ------------------------------
+def _enc2(s):
+    return 0xFFFFFFFF if s == "-" else _enc(s)
+
+
+def _load_ring():
+    with open(os.path.join(HERE, "golden", "worked_example_ring_append.json")) as f:
+        return json.load(f)
+
+
+def test_worked_example_ring_append_pblru():
+    """Appends into the current bucket: evictions to the lowest free host slots,
+    an entry with no victim left on the host, then steps over the result; every
+    field after every call, stored rows and gathered rows against their closed
+    form."""
+    ex = _load_ring()
+    z = ex["sizes"]
+    g = PBLRUGroup(z["N"], z["P"], z["H"], z["B"], z["layers"], 656, full_data=True, placement="ring")
+    appended = []
+    for op in ex["ops"]:
+        prev = g.export_state()
+        if "append" in op:
+            las = np.array(op["append"])
+            g.append(las, rows_for(0, 0, las, 1, 656))
+            appended += op["append"]
+        else:
+            g.step(np.array(op["sel"]))
+            assert list(g.last_lists[4]) == op["victims"]
+            assert list(g.export_state()["stats"]) == op["stats"]
+        st = g.export_state()
+        assert [int(x) for x in st["map"]] == [_enc2(x) for x in op["map"]]
+        assert list(st["gown"]) == op["gown"] and list(st["hown"]) == op["hown"]
+        assert int(st["bitsets"][0][0]) == op["free"] and int(st["bitsets"][1][0]) == op["cold"]
+        assert [int(st["bitsets"][2 + b][0]) for b in range(2)] == op["ring"]
+        assert st["cur"] == op["cur"]
+        check_state(st, z["P"], z["H"])
+        if "sel" in op:
+            U, hit_slots, _, _, victims = g.last_lists
+            check_step(prev, st, z["P"], z["H"], U=U, victims=victims, hit_slots=hit_slots)
+            out = g.gather(np.array(op["sel"]), 0, step=st["flag"])
+            assert (out[0] == rows_for(0, 0, op["gather"], 1, 656)[:, 0]).all()
+        for la in appended:   # every entry holds its own rows wherever it lives
+            assert (g.read_row(la) == rows_for(0, 0, [la], 1, 656)[0]).all()
+
+
+def test_worked_example_ring_append_exact_lru():
+    ex = _load_ring()
+    z = ex["sizes"]
+    g = ExactLRUGroup(z["N"], z["P"], z["H"], placement="ring")
+    for op in ex["ops"]:
+        if "append" in op:
+            g.append(op["append"])
+        else:
+            g.step(op["sel"])
+            assert g.last_victims == op["victims"]
+        assert g.map_array() == [_enc2(x) for x in op["map"]]
+        assert g.gown == op["gown"] and g.hown == op["hown"]
