@@ -63,16 +63,19 @@ from synth import Trace, preset  # noqa: E402
 METRIC = "selected KV rows resolved+gathered/s; gather GB/s and miss GB/s vs peak"
 HBM_PEAK_GBS = 8000.0                    # MI355X HBM3E
 LINK_PEAK_GBS = 32 * 16 * 128 / 130 / 8  # PCIe 5.0 x16 per direction = 63.0 GB/s
-DEFAULT_WORKLOAD = "r16_64k_g1x3"
+DEFAULT_WORKLOAD = "evict_r256_128k_g2"
 
 
 def parse():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=56)
-    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--steps", type=int, default=14)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--replays", type=int, default=3, help="timed replays from a fresh start (median reported)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    p.add_argument("--cpu-seconds", type=float, default=10.0, help="timed CPU work of the oracle sample")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="timed CPU work of the oracle sample (three single-core replays)")
+    p.add_argument("--no-cpu-parallel", action="store_true", help="skip the groups-in-parallel CPU figure")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-phases", action="store_true", help="skip the per-phase replay")
     p.add_argument("--groups", type=int, default=0,
@@ -165,56 +168,204 @@ def gather_traffic(workload: str, mode: str = "layer"):
     return rec["traffic_bytes_per_launch"]
 
 
+LINK_SOURCES = ("k_select.hip", "miss_path.h", "device_util.h")
+
+
+def link_code_digest() -> str:
+    """Digest of the code the host-link launch (k_mark) is built from."""
+    import hashlib
+    parts = [code_digest(os.path.join(ROOT, "serving_pb_lru_amd", "csrc", f)) for f in LINK_SOURCES]
+    return hashlib.sha256(" ".join(parts).encode()).hexdigest()
+
+
+def link_traffic(workload: str):
+    """Host-link bytes per k_mark launch from the committed rocprofv3 counter record
+    (IO read and write requests of the L2, in 32-byte units), as {"read", "write"},
+    or None when there is no record for this workload or the kernel's code changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_k_mark_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("k_mark_code_sha256") != link_code_digest():
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def rows_per_step(tr) -> int:
     wl = tr.wl
     return wl.groups * tr.n_sets * tr.k * wl.layers
 
 
 # ---------------------------------------------------------------------------
-def cpu_baseline(tr, W: int, K: int, seconds: float) -> dict:
-    """Replay the trace through the oracle on one core and time steps W+1 .. W+K.
+_T0 = time.perf_counter()
 
-    The replay (untimed load and warm-up, timed steps) is repeated from a fresh
-    start until about `seconds` of timed CPU work have accumulated.
-    """
-    from oracle.replay import initial_load as oracle_load, new_group
-    from synth import rows_for
 
-    wl = tr.wl
-    old_aff = os.sched_getaffinity(0)
-    os.sched_setaffinity(0, {min(old_aff)})
+def note(msg: str) -> None:
+    """A progress line on stderr (the JSON result is the only line on stdout)."""
+    print(f"[bench {time.perf_counter() - _T0:7.1f}s] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
     try:
-        import copy
-        loaded = new_group(tr, full_data=True)
-        oracle_load(loaded, tr, 0)
-        spent, timed, rows, replays = 0.0, 0, 0, 0
-        while spent < seconds and replays < 20:
-            replays += 1
-            grp = copy.deepcopy(loaded)     # a fresh replay from the loaded state
-            sels = tr.selections(0)
-            for t in range(1, W + K + 1):
-                sel = next(sels)
-                app = tr.appends(t)
-                app_rows = rows_for(wl.seed, 0, app, wl.layers, wl.row_bytes)
-                t0 = time.perf_counter()
-                grp.append(app, app_rows)
-                grp.step(sel)
-                for l in range(wl.layers):
-                    grp.gather(sel, l, step=t)
-                dt = time.perf_counter() - t0
-                if t > W:
-                    spent += dt
-                    rows += tr.n_sets * tr.k * wl.layers
-                    timed += 1
-            del grp
-        return {"value": round(rows / spent, 1) if spent else None, "unit": "rows/s", "cores": 1,
-                "kind": "oracle",
-                "sample": (f"{wl.name} group 0 of {wl.groups}: steps {W + 1}..{W + K} of the trace, "
-                           f"replayed {replays}x from the untimed loaded state and {W} untimed steps "
-                           f"({timed} timed steps, {spent:.1f} s of CPU work); full-data mode "
-                           f"(rows moved and gathered); one core")}
-    finally:
-        os.sched_setaffinity(0, old_aff)
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _rows_chunk(args):
+    from synth import rows_for
+    seed, g, las, layers, row_bytes = args
+    return rows_for(seed, g, las, layers, row_bytes)
+
+
+def _loaded_group(tr, g: int, workers: int):
+    """The oracle's group g after the initial load, in full-data mode. The rows
+    (inputs from synth) are generated by `workers` processes; the oracle appends
+    them chunk by chunk in load order, as oracle.replay.initial_load does."""
+    import multiprocessing as mp
+
+    from oracle.replay import LOAD_CHUNK, new_group
+    wl = tr.wl
+    grp = new_group(tr, full_data=True)
+    order = tr.initial_load_order()
+    spans = [(s, min(s + LOAD_CHUNK, order.size)) for s in range(0, order.size, LOAD_CHUNK)]
+    jobs = [(wl.seed, g, order[s:e], wl.layers, wl.row_bytes) for s, e in spans]
+    with mp.get_context("fork").Pool(max(1, workers)) as pool:
+        for (s, e), rows in zip(spans, pool.imap(_rows_chunk, jobs, chunksize=1)):
+            grp.append(order[s:e], rows)
+    return grp
+
+
+def _oracle_step(grp, tr, g: int, t: int, sel, app_rows):
+    """One decode step of group g on the oracle: appends, step, every layer's gather."""
+    grp.append(tr.appends(t), app_rows)
+    grp.step(sel)
+    for l in range(tr.wl.layers):
+        grp.gather(sel, l, step=t)
+
+
+def _timed_steps(grp, tr, g: int, sels, first: int, count: int, core: int, conn) -> None:
+    """Child process: pinned to `core`, time steps first .. first+count-1 of group g
+    (the appended rows are generated before each step's clock starts); send
+    (row-layers, seconds) back."""
+    from synth import rows_for
+    os.sched_setaffinity(0, {core})
+    wl = tr.wl
+    rows, spent = 0, 0.0
+    for t in range(first, first + count):
+        sel = next(sels)
+        app_rows = rows_for(wl.seed, g, tr.appends(t), wl.layers, wl.row_bytes)
+        t0 = time.perf_counter()
+        _oracle_step(grp, tr, g, t, sel, app_rows)
+        spent += time.perf_counter() - t0
+        rows += tr.n_sets * tr.k * wl.layers
+    conn.send((rows, spent))
+    conn.close()
+
+
+def _fork_timed(jobs):
+    """Run _timed_steps jobs [(grp, tr, g, sels, first, count, core)] in forked
+    children at once; returns [(row-layers, seconds, wall)] per job."""
+    import multiprocessing as mp
+    ctx = mp.get_context("fork")
+    procs = []
+    t0 = time.perf_counter()
+    for job in jobs:
+        rd, wr = ctx.Pipe(duplex=False)
+        p = ctx.Process(target=_timed_steps, args=(*job, wr))
+        p.start()
+        wr.close()
+        procs.append((p, rd))
+    out = []
+    for p, rd in procs:
+        rows, spent = rd.recv()
+        p.join()
+        if p.exitcode != 0:
+            raise RuntimeError(f"oracle replay process failed ({p.exitcode})")
+        out.append((rows, spent))
+    wall = time.perf_counter() - t0
+    return [(r, s, wall) for r, s in out]
+
+
+def cpu_baseline(tr, W: int, K: int, seconds: float, parallel: bool = True) -> dict:
+    """The oracle (full-data mode: rows moved and gathered) timed on this host's cores.
+
+    Protocol: the initial load and W warm-up steps are untimed (the load's row
+    generation runs on every core; the oracle itself is single-threaded). From the
+    warmed state, three replays of the same steps W+1 .. W+Kc each run in a
+    forked child pinned to one core (a fork copies the state, so every replay
+    starts from the same point, as a fresh start would); the median replay is the
+    single-core figure. Kc is chosen so the three replays take about `seconds` of
+    CPU work (at most K). Groups are independent, so a second figure runs
+    min(G, cores) groups at once, one per core (each from its own warmed state),
+    when their pools fit in half the free host memory: rows/s summed over
+    processes, over the wall time of the slowest."""
+    import statistics
+
+    from synth import rows_for
+    wl = tr.wl
+    cores = sorted(os.sched_getaffinity(0))
+    per_group_bytes = (tr.P + tr.H) * wl.layers * wl.row_bytes
+    avail = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable"):
+                    avail = int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    n_par = min(wl.groups, len(cores)) if parallel else 1
+    if avail is not None:
+        n_par = max(1, min(n_par, int(0.5 * avail // max(per_group_bytes * 1.3, 1))))
+    t_load = time.perf_counter()
+    warmed = []
+    est = None
+    for g in range(n_par):
+        grp = _loaded_group(tr, g, len(cores))
+        sels = tr.selections(g)
+        t_w = time.perf_counter()
+        for t in range(1, W + 1):
+            sel = next(sels)
+            _oracle_step(grp, tr, g, t, sel, rows_for(wl.seed, g, tr.appends(t), wl.layers, wl.row_bytes))
+        if g == 0 and W:
+            est = (time.perf_counter() - t_w) / W
+        warmed.append((grp, sels))
+        note(f"cpu baseline: group {g} loaded and warmed ({time.perf_counter() - t_load:.1f}s so far)")
+    load_s = time.perf_counter() - t_load
+    kc = K if not est else max(1, min(K, int(round(seconds / 3 / est))))
+    grp0, sels0 = warmed[0]
+    single = []
+    for _ in range(3):
+        rows, spent, _ = _fork_timed([(grp0, tr, 0, sels0, W + 1, kc, cores[0])])[0]
+        single.append(rows / spent)
+        note(f"cpu baseline: replay {len(single)}: {kc} steps in {spent:.1f}s")
+    res = {"value": round(statistics.median(single), 1), "unit": "rows/s", "cores": 1, "kind": "oracle",
+           "cpu_model": cpu_model(), "host_cores": len(cores),
+           "replays": [round(v, 1) for v in single],
+           "sample": (f"{wl.name} group 0 of {wl.groups}: steps {W + 1}..{W + kc} of the trace timed "
+                      f"(load and {W} warm-up steps untimed), median of 3 replays from the same warmed "
+                      f"state, each in a process pinned to one core; full-data mode (rows moved and "
+                      f"gathered)")}
+    if n_par > 1:
+        jobs = [(grp, tr, g, sels, W + 1, kc, cores[g % len(cores)]) for g, (grp, sels) in enumerate(warmed)]
+        out = _fork_timed(jobs)
+        total_rows = sum(r for r, _, _ in out)
+        wall = max(w for _, _, w in out)
+        res["parallel"] = {"value": round(total_rows / wall, 1), "unit": "rows/s", "cores": n_par,
+                           "sample": f"groups 0..{n_par - 1} at once, one process per core, steps "
+                                     f"{W + 1}..{W + kc} each"}
+    elif wl.groups > 1:
+        res["parallel"] = {"value": None, "note": "the groups' full-data pools do not fit in half the free "
+                                                  "host memory together"}
+    res["untimed_setup_s"] = round(load_s, 1)
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -233,7 +384,10 @@ def gather_all_layers(eng, g, sel, outs, layers, mode, stream=None):
             eng.gather_layers(g, 1, layers - 1, sel, out=outs[1:], stream=stream)
 
 
-def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str = "layer") -> dict:
+def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str = "layer",
+            replays: int = 3) -> dict:
+    import statistics
+
     import torch
 
     from serving_pb_lru_amd.replay import engine_for, initial_load
@@ -276,45 +430,57 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
     warm.sync()
     warm.close()
 
-    # ---- timed replay ----------------------------------------------------
-    eng = engine_for(tr, max_append=1 << 16, policy=policy)
-    initial_load(eng, tr, groups, rows)
-    torch.cuda.synchronize()
-    # the first step (cold start: the most misses) is timed on its own
-    s1, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    first_ms = None
-    for t in range(1, W + 1):
-        if t == 1:
-            s1.record()
-        run_step(eng, t)
-        if t == 1:
-            e1.record()
-            torch.cuda.synchronize()
-            first_ms = s1.elapsed_time(e1)
-    torch.cuda.synchronize()
-    # every gather of the timed region records its kernel's start and end in its
-    # own dispatch (HIP events on the engine's stream, no launch overhead inside)
-    eng.set_timing(eng.TIMING_GATHER)
-    eng.read_gather_timing()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record()
-    t0 = time.perf_counter()
-    for t in range(W + 1, W + K + 1):
-        run_step(eng, t)
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    eng.sync()   # raises if the device latched an error
-    ev_ms = start.elapsed_time(end)
-    g_total_ms, g_launches = eng.read_gather_timing()
-    eng.set_timing(0)
-    eng.close()
-    del eng
-    res = dict(wall_s=wall, event_ms=ev_ms, gather_ms=g_total_ms / max(g_launches, 1),
-               gather_launches=g_launches, first_step_ms=first_ms)
+    def timed_replay():
+        eng = engine_for(tr, max_append=1 << 16, policy=policy)
+        initial_load(eng, tr, groups, rows)
+        torch.cuda.synchronize()
+        # the first step (cold start: the most misses) is timed on its own
+        s1, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        first_ms = None
+        for t in range(1, W + 1):
+            if t == 1:
+                s1.record()
+            run_step(eng, t)
+            if t == 1:
+                e1.record()
+                torch.cuda.synchronize()
+                first_ms = s1.elapsed_time(e1)
+        torch.cuda.synchronize()
+        # every gather and every step's host-link launch (k_mark) of the timed region
+        # records its kernel's start and end in its own dispatch (HIP events on the
+        # engine's stream, no launch overhead inside)
+        eng.set_timing(eng.TIMING_GATHER | eng.TIMING_LINK)
+        eng.read_gather_timing()
+        eng.read_link_timing()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        t0 = time.perf_counter()
+        for t in range(W + 1, W + K + 1):
+            run_step(eng, t)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        eng.sync()   # raises if the device latched an error
+        g_ms, g_n = eng.read_gather_timing()
+        l_ms, l_n = eng.read_link_timing()
+        eng.set_timing(0)
+        eng.close()
+        return dict(wall_s=wall, event_ms=start.elapsed_time(end), gather_ms=g_ms / max(g_n, 1),
+                    gather_launches=g_n, link_ms=l_ms / max(l_n, 1), link_launches=l_n, first_step_ms=first_ms)
+
+    runs = []
+    for i in range(max(1, replays)):
+        runs.append(timed_replay())
+        note(f"gpu replay {i + 1}: {runs[-1]['event_ms'] / K:.4f} ms per step")
+    order = sorted(range(len(runs)), key=lambda i: runs[i]["wall_s"])
+    res = dict(runs[order[len(order) // 2]])   # the median replay
+    res["replay_walls_s"] = [r["wall_s"] for r in runs]
 
     # ---- per-phase replay (diagnostic, synchronises every step) --------------
+    # also the step statistics: the host-link bytes of the timed steps (the engine
+    # is deterministic, so they are those of the timed replays)
     if phases:
         eng = engine_for(tr, max_append=1 << 16, policy=policy)
         initial_load(eng, tr, groups, rows)
@@ -338,6 +504,7 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
                     n += 1
                 prev_evict[g] = st[3]
         eng.close()
+        note("gpu per-phase replay done")
         res.update(phase_ms=(ph / max(n, 1)).tolist(), link_ms_total=float(ph[1]),
                    h2d_rows=int(h2d), d2h_rows=int(d2h), group_steps=n)
     return res
@@ -539,13 +706,16 @@ def main():
     policy = 1 if args.policy == "lru" else 0
     cpu = None
     if not args.no_cpu_baseline and policy == 0:
-        cpu = cpu_baseline(tr, W, K, args.cpu_seconds)
+        cpu = cpu_baseline(tr, W, K, args.cpu_seconds, parallel=not args.no_cpu_parallel)
 
     gather_mode = args.gather if wl.layers > 1 else "layer"   # one layer: the same launch
-    r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode)
+    r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode, replays=args.replays)
     value = per_step * K / r["wall_s"]
     ms_per_step = r["event_ms"] / K
+    replay_values = [round(per_step * K / w, 1) for w in r["replay_walls_s"]]
+    rnd = lambda x, d: None if x is None else round(x, d)
 
+    # ---- the gather against HBM peak ------------------------------------------
     g_ms = float(r["gather_ms"])
     # algorithmic bytes per launch: every gathered row-layer of the timed region
     # over the gather launches that moved them
@@ -553,42 +723,53 @@ def main():
     g_bytes = 2 * wl.row_bytes * tr.n_sets * tr.k * wl.layers / launches_per_group_step
     assert r["gather_launches"] == K * wl.groups * launches_per_group_step, r["gather_launches"]
     g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": "k_gather", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
-                "traffic": gather_traffic(wl.name, gather_mode),
-                "bytes_per_launch": round(g_bytes), "launch_ms": round(g_ms, 5),
-                "layers_per_launch": round(wl.layers / launches_per_group_step, 3)}
+    gather_line = {"bound": "hbm", "kernel": "k_gather", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
+                   "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                   "traffic": gather_traffic(wl.name, gather_mode),
+                   "bytes_per_launch": round(g_bytes), "launch_ms": round(g_ms, 5),
+                   "layers_per_launch": round(wl.layers / launches_per_group_step, 3)}
+
+    # ---- the host-link launch (k_mark) against the link's per-direction peak ---
+    link_line = None
     miss = None
     if "phase_ms" in r:
         slot = wl.layers * wl.row_bytes
-        up = r["h2d_rows"] * slot
-        down = r["d2h_rows"] * slot
-        t_in = t_out = r["link_ms_total"] * 1e-3
+        up = r["h2d_rows"] * slot          # missed rows in, over the timed steps
+        down = r["d2h_rows"] * slot        # the previous steps' evicted rows out
+        launches = r["link_launches"]
+        assert launches == K * wl.groups, launches
+        l_ms = float(r["link_ms"])
+        per_launch = max(up, down) / launches
+        l_gbs = per_launch / (l_ms * 1e-3) / 1e9 if l_ms > 0 else None
+        link_line = {"bound": "host-link", "kernel": "k_lru_pass (first pass)" if policy else "k_mark",
+                     "achieved": rnd(l_gbs, 2), "peak": round(LINK_PEAK_GBS, 1), "unit": "GB/s per direction",
+                     "frac": rnd(None if l_gbs is None else l_gbs / LINK_PEAK_GBS, 4),
+                     "traffic": link_traffic(wl.name) if not policy else None,
+                     "bytes_per_launch": round(per_launch),
+                     "h2d_bytes_per_launch": round(up / launches), "d2h_bytes_per_launch": round(down / launches),
+                     "launch_ms": round(l_ms, 5),
+                     "note": "max-direction algorithmic bytes (656 x layers per missed row in, per "
+                             "evicted row of the previous step out; both directions move "
+                             "concurrently) over the launch's average duration, which also marks "
+                             "hits and plans and extracts the victims"}
+        t_in = r["link_ms_total"] * 1e-3
         gin = up / t_in / 1e9 if t_in > 0 else None
-        gout = down / t_out / 1e9 if t_out > 0 else None
-        rnd = lambda x, d: None if x is None else round(x, d)
-        miss = {"bound": "host-link", "peak": round(LINK_PEAK_GBS, 1), "unit": "GB/s per direction",
-                "note": "both directions run concurrently in the k_mark launch (prefetch and "
-                        "write-back workgroups beside the hit marking and victim selection); rates "
-                        "are bytes over that launch's duration, a lower bound on the link rate",
-                "h2d": {"kernel": "k_mark (prefetch workgroups)", "achieved": rnd(gin, 2),
-                        "frac": rnd(None if gin is None else gin / LINK_PEAK_GBS, 4),
-                        "bytes_per_step": up / r["group_steps"]},
-                "d2h": {"kernel": "k_mark (write-back workgroups)", "achieved": rnd(gout, 2),
-                        "frac": rnd(None if gout is None else gout / LINK_PEAK_GBS, 4),
-                        "bytes_per_step": down / r["group_steps"]},
-                "phase_ms_per_group_step": {k: round(v, 5) for k, v in zip(
-                    ["lookup_dedup", "mark_select_link", "swap_commit"],
-                    r["phase_ms"])}}
+        gout = down / t_in / 1e9 if t_in > 0 else None
+        miss = {"phase_ms_per_group_step": {k: round(v, 5) for k, v in zip(
+                    ["lookup_dedup", "mark_select_link", "swap_commit"], r["phase_ms"])},
+                "h2d_GBps_over_phase": rnd(gin, 2), "d2h_GBps_over_phase": rnd(gout, 2)}
         try:
             peaks = copy_peaks()
             miss["measured_copy_peak_GBps"] = peaks
-            if gin is not None and peaks["bidirectional_each"]:
-                miss["frac_of_measured_bidirectional"] = {
-                    "h2d": round(gin / peaks["bidirectional_each"], 4),
-                    "d2h": round(gout / peaks["bidirectional_each"], 4) if gout else None}
+            if l_gbs is not None and peaks["bidirectional_each"]:
+                miss["link_frac_of_measured_bidirectional_copy"] = round(l_gbs / peaks["bidirectional_each"], 4)
         except RuntimeError as e:   # pinned memory refused: report without the measured peaks
             miss["measured_copy_peak_GBps"] = f"not measured: {e}"
+    # the dominant kernel of the step: the host-link launch when the step moves
+    # rows over the link for longer than it gathers, else the gather
+    link_dominant = link_line is not None and link_line["launch_ms"] > gather_line["launch_ms"] * \
+        launches_per_group_step
+    roofline, other = (link_line, gather_line) if link_dominant else (gather_line, link_line)
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K,
         "selections_per_s": round(value / wl.layers, 1),
@@ -604,6 +785,8 @@ def main():
                    "policy": "exact LRU" if policy else "PB-LRU", "gather": gather_mode,
                    "row_layers_per_step": per_step},
         "roofline": roofline,
+        "roofline_other": other,
+        "replays": replay_values,
         "miss_path": miss,
         "cpu_baseline": cpu,
     }

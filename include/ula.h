@@ -299,11 +299,18 @@ int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr);
  *  - ULA_TIMING_GATHER: every gather launch records events in its own dispatch,
  *    so their interval is the kernel's execution alone (no launch overhead).
  *    ula_read_gather_timing synchronises on them and returns the summed kernel
- *    time and the number of launches since the last read (then resets both). */
-enum { ULA_TIMING_STEP = 1, ULA_TIMING_GATHER = 2 };
+ *    time and the number of launches since the last read (then resets both).
+ *  - ULA_TIMING_LINK: the same for every step's host-link launch (the launch
+ *    that reads the missed rows in and writes the previous step's evicted rows
+ *    out while it marks hits and selects victims; under exact LRU, the first
+ *    select pass, which carries that work); read by ula_read_link_timing.
+ * Errors: ULA_EINVAL (unknown flag, null pointer, step timing never switched
+ * on), ULA_EHIP. */
+enum { ULA_TIMING_STEP = 1, ULA_TIMING_GATHER = 2, ULA_TIMING_LINK = 4 };
 int ula_set_timing(ula_ctx* ctx, int32_t flags);
 int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out3);
 int ula_read_gather_timing(ula_ctx* ctx, double* kernel_ms, int64_t* launches);
+int ula_read_link_timing(ula_ctx* ctx, double* kernel_ms, int64_t* launches);
 
 /* Release the context (not the caller's buffers). Waits for no stream. */
 int ula_destroy(ula_ctx* ctx);

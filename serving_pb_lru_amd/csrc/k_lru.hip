@@ -36,6 +36,7 @@
 //           the victim list (after the first C).
 //   sort    a stable radix sort of that list by key (8-bit digits, as many passes
 //           as the keys need) gives the first C victims in (K, slot) order.
+#include <hip/hip_ext.h>
 #include <algorithm>
 
 #include "miss_path.h"
@@ -443,8 +444,10 @@ __global__ __launch_bounds__(1024) void k_rs_scatter(GroupDev g, int32_t pass) {
   }
 }
 
+static inline uint32_t wb_pass_step(int wbb, uint32_t t) { return wbb > 0 ? t - 1u : 0u; }
+
 hipError_t launch_lru_select(const GroupDev& g, uint32_t t, int32_t max_pairs, int32_t wb_pairs,
-                             hipStream_t s) {
+                             hipStream_t s, hipEvent_t start, hipEvent_t stop) {
   // host-link workgroups of kLruThreads lanes, four 16-byte pieces per lane per
   // round: as many bytes in flight as the mark launch's prefetch and write-back
   const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
@@ -462,8 +465,13 @@ hipError_t launch_lru_select(const GroupDev& g, uint32_t t, int32_t max_pairs, i
   // keys are at most t: the digits of bits 21-31 (and 10-20) are zero for every
   // key while t < 2^21 (2^10), and those passes would pick digit 0
   const int first = t >= (1u << 21) ? 0 : (t >= (1u << 10) ? 1 : 2);
-  k_lru_pass<<<nsel + pf + wbb, kLruThreads, 0, s>>>(g, t, first, first, nsel, per_slot, pf, wbb,
-                                                       wbb > 0 ? t - 1u : 0u);
+  // the first pass also carries the host-link work (the launch ULA_TIMING_LINK times)
+  if (start)
+    hipExtLaunchKernelGGL(k_lru_pass, dim3(nsel + pf + wbb), dim3(kLruThreads), 0, s, start, stop, 0, g, t,
+                          first, first, nsel, per_slot, pf, wbb, wb_pass_step(wbb, t));
+  else
+    k_lru_pass<<<nsel + pf + wbb, kLruThreads, 0, s>>>(g, t, first, first, nsel, per_slot, pf, wbb,
+                                                         wb_pass_step(wbb, t));
   hipError_t e = hipGetLastError();
   for (int pass = first + 1; pass < 3 && e == hipSuccess; ++pass) {
     k_lru_pass<<<nsel, kLruThreads, 0, s>>>(g, t, pass, first, nsel, per_slot, 0, 0, 0u);

@@ -34,6 +34,7 @@
 //            each lane writes the slots of its lowest set bits that fall below
 //            the span's quota, in ascending slot order. The taken bits leave
 //            their bucket and join the destination bucket.
+#include <hip/hip_ext.h>
 #include <algorithm>
 
 #include "miss_path.h"
@@ -441,7 +442,8 @@ __global__ __launch_bounds__(1024) void k_tag_append(GroupDev g, SmallAppend a, 
 }
 
 hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArgs& a,
-                       int32_t max_pairs, int32_t wb_pairs, hipStream_t s) {
+                       int32_t max_pairs, int32_t wb_pairs, hipStream_t s, hipEvent_t start,
+                       hipEvent_t stop) {
   // Prefetch workgroups: enough for the largest possible miss list, at most
   // kPrefetchBlocks (about 2 MB of host reads in flight). Write-back
   // workgroups: enough for the previous step's pairs, at most kWritebackBlocks
@@ -455,8 +457,12 @@ hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArg
   const int pf = g.H > 0 ? blocks_for(max_pairs, kPrefetchBlocks) : 0;
   const int wbb = g.H > 0 ? blocks_for(wb_pairs, kWritebackBlocks) : 0;
   const int nh = kExtractHelpers;
-  k_mark<<<kMarkBlocks + pf + wbb + nh, 1024, 0, s>>>(g, t, cur, a, FastDiv(chunks), pf, wbb, nh,
-                                                      wbb > 0 ? t - 1u : 0u);
+  if (start)
+    hipExtLaunchKernelGGL(k_mark, dim3(kMarkBlocks + pf + wbb + nh), dim3(1024), 0, s, start, stop, 0, g, t,
+                          cur, a, FastDiv(chunks), pf, wbb, nh, wbb > 0 ? t - 1u : 0u);
+  else
+    k_mark<<<kMarkBlocks + pf + wbb + nh, 1024, 0, s>>>(g, t, cur, a, FastDiv(chunks), pf, wbb, nh,
+                                                        wbb > 0 ? t - 1u : 0u);
   return hipGetLastError();
 }
 

@@ -175,6 +175,15 @@ struct GroupHost {
   int64_t written_back = 0;         // last step whose staged rows a flush wrote to the host
 };
 
+static constexpr int kTimingRing = 256;
+
+struct TimingRing {
+  std::vector<hipEvent_t> ev;        // 2 * kTimingRing events
+  int head = 0, pending = 0;
+  double ms = 0.0;
+  int64_t launches = 0;
+};
+
 struct ula_ctx {
   ula_config cfg;
   Dims dims;
@@ -186,15 +195,12 @@ struct ula_ctx {
   int poisoned = 0;
   int static_dev = -1;               // device whose static workspace the context holds, or -1
   int timing = 0;                    // ULA_TIMING_* flags
-  // gather kernel durations: a ring of dispatch-recorded event pairs, summed
-  // lazily (when the ring wraps, and by ula_read_gather_timing)
-  std::vector<hipEvent_t> gt_ev;     // 2 * kGatherTimingRing events
-  int gt_head = 0, gt_pending = 0;
-  double gt_ms = 0.0;
-  int64_t gt_launches = 0;
+  // kernel durations of the gathers and of the steps' host-link launches: rings
+  // of dispatch-recorded event pairs, summed lazily (when a ring wraps, and by
+  // ula_read_gather_timing / ula_read_link_timing)
+  TimingRing gather_t, link_t;
 };
 
-static constexpr int kGatherTimingRing = 256;
 
 // ---- the static device workspace (ula_init_static) --------------------------
 // For callers that cannot allocate device memory, one workspace per device lives
@@ -236,15 +242,46 @@ static void release_static_workspace(int dev) {
   g_static_live[dev] = false;
 }
 
-// Add the oldest pending gather's kernel time to the total.
-static int retire_gather_timing(ula_ctx* ctx) {
-  const int i = (ctx->gt_head - ctx->gt_pending + kGatherTimingRing) % kGatherTimingRing;
-  HIP_TRY(hipEventSynchronize(ctx->gt_ev[2 * i + 1]));
+// Add the oldest pending launch's kernel time to the ring's total.
+static int retire_timing(TimingRing& r) {
+  const int i = (r.head - r.pending + kTimingRing) % kTimingRing;
+  HIP_TRY(hipEventSynchronize(r.ev[2 * i + 1]));
   float ms = 0.f;
-  HIP_TRY(hipEventElapsedTime(&ms, ctx->gt_ev[2 * i], ctx->gt_ev[2 * i + 1]));
-  ctx->gt_ms += ms;
-  ctx->gt_launches += 1;
-  ctx->gt_pending -= 1;
+  HIP_TRY(hipEventElapsedTime(&ms, r.ev[2 * i], r.ev[2 * i + 1]));
+  r.ms += ms;
+  r.launches += 1;
+  r.pending -= 1;
+  return ULA_OK;
+}
+
+// The next (start, stop) event pair of a ring, for a launch that records them in
+// its own dispatch (events are created on first use).
+static int next_timing_pair(TimingRing& r, hipEvent_t* start, hipEvent_t* stop) {
+  if (r.ev.empty()) {
+    r.ev.assign(2 * kTimingRing, nullptr);
+    for (auto& e : r.ev) HIP_TRY(hipEventCreate(&e));
+  }
+  if (r.pending == kTimingRing) {
+    int rc = retire_timing(r);
+    if (rc) return rc;
+  }
+  *start = r.ev[2 * r.head];
+  *stop = r.ev[2 * r.head + 1];
+  r.head = (r.head + 1) % kTimingRing;
+  r.pending += 1;
+  return ULA_OK;
+}
+
+// Every pending launch's time into the total; then hand the total out and reset.
+static int drain_timing(TimingRing& r, double* ms, int64_t* launches) {
+  while (r.pending > 0) {
+    int rc = retire_timing(r);
+    if (rc) return rc;
+  }
+  *ms = r.ms;
+  *launches = r.launches;
+  r.ms = 0.0;
+  r.launches = 0;
   return ULA_OK;
 }
 
@@ -282,8 +319,9 @@ int ula_host_free(void* p) {
 
 static void destroy_ctx(ula_ctx* ctx) {
   release_static_workspace(ctx->static_dev);
-  for (hipEvent_t e : ctx->gt_ev)
-    if (e) (void)hipEventDestroy(e);
+  for (TimingRing* r : {&ctx->gather_t, &ctx->link_t})
+    for (hipEvent_t e : r->ev)
+      if (e) (void)hipEventDestroy(e);
   for (auto& g : ctx->groups) {
     for (int i = 0; i < kStageSlots; ++i) {
       if (g.stage_ev[i]) (void)hipEventDestroy(g.stage_ev[i]);
@@ -675,15 +713,20 @@ static int step_impl(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, con
   a.order[1] = kCold;
   a.norder = 2;
   for (int j = 1; j < ctx->dims.B; ++j) a.order[a.norder++] = (int8_t)ring_id((cur + j) % ctx->dims.B);
+  hipEvent_t lk0 = nullptr, lk1 = nullptr;   // the host-link launch's own events (ULA_TIMING_LINK)
+  if (ctx->timing & ULA_TIMING_LINK) {
+    int rc = next_timing_pair(ctx->link_t, &lk0, &lk1);
+    if (rc) return rc;
+  }
   if (g.policy == ULA_POLICY_LRU) {
     // exact LRU: select passes over the whole pool (the first launch also carries
     // the host-link work), then the victim list in order
-    HIP_TRY(launch_lru_select(g, (uint32_t)t, max_pairs, wb_pairs, s));
+    HIP_TRY(launch_lru_select(g, (uint32_t)t, max_pairs, wb_pairs, s, lk0, lk1));
     HIP_TRY(launch_lru_order(g, (uint32_t)t, max_pairs, s));
   } else {
     // marking, victim plan and extraction, with the missed rows read in and the
     // previous step's evicted rows written out, in one launch
-    HIP_TRY(launch_mark(g, (uint32_t)t, cur, a, max_pairs, wb_pairs, s));
+    HIP_TRY(launch_mark(g, (uint32_t)t, cur, a, max_pairs, wb_pairs, s, lk0, lk1));
   }
   if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
   HIP_TRY(launch_swap_commit(g, (uint32_t)t, max_pairs, s));
@@ -747,18 +790,8 @@ static int gather_impl(ula_ctx* ctx, int32_t group, int32_t layer0, int32_t nl, 
   if (gh.steps == 0) return ULA_ENOTRESIDENT;
   hipEvent_t start = nullptr, stop = nullptr;
   if ((ctx->timing & ULA_TIMING_GATHER) && n > 0) {
-    if (ctx->gt_ev.empty()) {
-      ctx->gt_ev.assign(2 * kGatherTimingRing, nullptr);
-      for (auto& e : ctx->gt_ev) HIP_TRY(hipEventCreate(&e));
-    }
-    if (ctx->gt_pending == kGatherTimingRing) {
-      int rc = retire_gather_timing(ctx);
-      if (rc) return rc;
-    }
-    start = ctx->gt_ev[2 * ctx->gt_head];
-    stop = ctx->gt_ev[2 * ctx->gt_head + 1];
-    ctx->gt_head = (ctx->gt_head + 1) % kGatherTimingRing;
-    ctx->gt_pending += 1;
+    int rc = next_timing_pair(ctx->gather_t, &start, &stop);
+    if (rc) return rc;
   }
   HIP_TRY(launch_gather(gh.d, sel_dev, n, layer0, nl, static_cast<uint8_t*>(out_dev), (long long)gh.steps,
                         gh.last_n, reinterpret_cast<hipStream_t>(stream), start, stop));
@@ -879,7 +912,7 @@ int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr) {
 }
 
 int ula_set_timing(ula_ctx* ctx, int32_t flags) {
-  if (!ctx || (flags & ~(ULA_TIMING_STEP | ULA_TIMING_GATHER))) return ULA_EINVAL;
+  if (!ctx || (flags & ~(ULA_TIMING_STEP | ULA_TIMING_GATHER | ULA_TIMING_LINK))) return ULA_EINVAL;
   if (flags & ULA_TIMING_STEP)   // a static-workspace context creates its step events here
     for (auto& gh : ctx->groups)
       for (auto& e : gh.ev)
@@ -890,15 +923,12 @@ int ula_set_timing(ula_ctx* ctx, int32_t flags) {
 
 int ula_read_gather_timing(ula_ctx* ctx, double* kernel_ms, int64_t* launches) {
   if (!ctx || !kernel_ms || !launches) return ULA_EINVAL;
-  while (ctx->gt_pending > 0) {
-    int rc = retire_gather_timing(ctx);
-    if (rc) return rc;
-  }
-  *kernel_ms = ctx->gt_ms;
-  *launches = ctx->gt_launches;
-  ctx->gt_ms = 0.0;
-  ctx->gt_launches = 0;
-  return ULA_OK;
+  return drain_timing(ctx->gather_t, kernel_ms, launches);
+}
+
+int ula_read_link_timing(ula_ctx* ctx, double* kernel_ms, int64_t* launches) {
+  if (!ctx || !kernel_ms || !launches) return ULA_EINVAL;
+  return drain_timing(ctx->link_t, kernel_ms, launches);
 }
 
 int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out3) {

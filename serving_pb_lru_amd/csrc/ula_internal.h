@@ -194,8 +194,10 @@ hipError_t launch_init_bitmap(uint32_t* words, int32_t nwords, int64_t nbits, ui
 hipError_t launch_init_counters(Counters* c, int32_t P, int32_t H, hipStream_t s);
 
 hipError_t launch_tag(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
+// start / stop (both or neither): events the launch records in its own dispatch
 hipError_t launch_mark(const GroupDev& g, uint32_t t, int32_t cur, const PlanArgs& a,
-                       int32_t max_pairs, int32_t wb_pairs, hipStream_t s);
+                       int32_t max_pairs, int32_t wb_pairs, hipStream_t s, hipEvent_t start,
+                       hipEvent_t stop);
 hipError_t launch_compact(const GroupDev& g, const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
 hipError_t launch_plan(const GroupDev& g, const PlanArgs& a, hipStream_t s);
 hipError_t launch_extract(const GroupDev& g, int32_t mode, int32_t dest, int32_t max_items,
@@ -211,7 +213,7 @@ hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, 
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s);
 // exact-LRU victim selection (k_lru.hip)
 hipError_t launch_lru_select(const GroupDev& g, uint32_t t, int32_t max_pairs, int32_t wb_pairs,
-                             hipStream_t s);
+                             hipStream_t s, hipEvent_t start, hipEvent_t stop);
 hipError_t launch_lru_order(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s);
 
 // start / stop (both or neither): events recorded by the dispatch itself, so

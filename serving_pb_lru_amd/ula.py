@@ -89,6 +89,8 @@ SIGNATURES = [
     ("ula_read_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
     ("ula_read_gather_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
                                               ctypes.POINTER(ctypes.c_int64)]),
+    ("ula_read_link_timing", ctypes.c_int, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(ctypes.c_int64)]),
     ("ula_destroy", ctypes.c_int, [ctypes.c_void_p]),
     ("ula_strerror", ctypes.c_char_p, [ctypes.c_int]),
     ("ula_host_alloc", ctypes.c_void_p, [ctypes.c_size_t]),
@@ -288,6 +290,7 @@ class Engine:
 
     TIMING_STEP = 1      # phase events of every step (read_timing)
     TIMING_GATHER = 2    # kernel time of every gather (read_gather_timing)
+    TIMING_LINK = 4      # kernel time of every step's host-link launch (read_link_timing)
 
     def set_timing(self, flags) -> None:
         """flags: an OR of TIMING_STEP and TIMING_GATHER (True means TIMING_STEP)."""
@@ -304,6 +307,13 @@ class Engine:
         ms, n = ctypes.c_double(), ctypes.c_int64()
         _check(lib().ula_read_gather_timing(self.ctx, ctypes.byref(ms), ctypes.byref(n)),
                "ula_read_gather_timing")
+        return ms.value, n.value
+
+    def read_link_timing(self) -> tuple:
+        """(summed host-link launch milliseconds, launches) since the last read."""
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        _check(lib().ula_read_link_timing(self.ctx, ctypes.byref(ms), ctypes.byref(n)),
+               "ula_read_link_timing")
         return ms.value, n.value
 
     def close(self) -> None:

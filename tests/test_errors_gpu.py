@@ -453,18 +453,27 @@ def test_engine_on_dirty_workspace_matches_oracle():
     run_parity(wl, max_append=4096)
 
 
-def test_timing_modes_count_and_change_nothing():
-    """Gather timing records one kernel duration per launch; neither timing mode
-    changes any state or gathered byte."""
+@pytest.mark.parametrize("policy", [0, 1], ids=["pblru", "lru"])
+def test_timing_modes_count_and_change_nothing(policy):
+    """Gather timing and link timing record one kernel duration per launch (one
+    host-link launch per step); no timing mode changes any state or gathered byte."""
     from serving_pb_lru_amd import UlaError
-    tr, eng, rows = _engine()
-    tr2, ref, _ = _engine()
+    from serving_pb_lru_amd.replay import engine_for, initial_load
+    from synth.device import rows_device
+    tr = Trace(preset("tiny_4x4k"))
+    wl = tr.wl
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    eng = engine_for(tr, max_append=4096, policy=policy)
+    ref = engine_for(tr, max_append=4096, policy=policy)
+    for e in (eng, ref):
+        initial_load(e, tr, [0], rows)
     try:
         with pytest.raises(UlaError) as e:
-            eng.set_timing(4)
+            eng.set_timing(8)
         assert e.value.name == "EINVAL"
-        eng.set_timing(eng.TIMING_STEP | eng.TIMING_GATHER)
+        eng.set_timing(eng.TIMING_STEP | eng.TIMING_GATHER | eng.TIMING_LINK)
         assert eng.read_gather_timing() == (0.0, 0)
+        assert eng.read_link_timing() == (0.0, 0)
         sels = tr.selections(0)
         launches = 0
         for t in range(1, 4):
@@ -482,6 +491,9 @@ def test_timing_modes_count_and_change_nothing():
         ms, n = eng.read_gather_timing()
         assert n == launches and ms > 0
         assert eng.read_gather_timing() == (0.0, 0)   # reset by the read
+        ms, n = eng.read_link_timing()
+        assert n == 3 and ms > 0
+        assert eng.read_link_timing() == (0.0, 0)
         eng.sync(), ref.sync()
         assert _state(eng) == _state(ref)
     finally:
