@@ -84,6 +84,9 @@ def parse():
     p.add_argument("--policy", choices=("pblru", "lru"), default="pblru",
                    help="replacement policy: PB-LRU (the pages' policy) or exact LRU (the one it is "
                         "compared against); the CPU baseline is reported for PB-LRU only")
+    p.add_argument("--placement", choices=("lowest", "ring"), default="lowest",
+                   help="where appended entries go: the lowest free slot, GPU first, never evicting "
+                        "(default), or the current bucket, evicting (PB-LRU only)")
     p.add_argument("--gather", choices=("layer", "split", "all"), default="split",
                    help="gathers per group step: one per layer (ula_gather); layer 0 alone, then the "
                         "later layers in one ula_gather_layers launch (default); or every layer in "
@@ -225,7 +228,7 @@ def _rows_chunk(args):
     return rows_for(seed, g, las, layers, row_bytes)
 
 
-def _loaded_group(tr, g: int, workers: int):
+def _loaded_group(tr, g: int, workers: int, placement: str = "lowest"):
     """The oracle's group g after the initial load, in full-data mode. The rows
     (inputs from synth) are generated by `workers` processes; the oracle appends
     them chunk by chunk in load order, as oracle.replay.initial_load does."""
@@ -233,7 +236,7 @@ def _loaded_group(tr, g: int, workers: int):
 
     from oracle.replay import LOAD_CHUNK, new_group
     wl = tr.wl
-    grp = new_group(tr, full_data=True)
+    grp = new_group(tr, full_data=True, placement=placement)
     order = tr.initial_load_order()
     spans = [(s, min(s + LOAD_CHUNK, order.size)) for s in range(0, order.size, LOAD_CHUNK)]
     jobs = [(wl.seed, g, order[s:e], wl.layers, wl.row_bytes) for s, e in spans]
@@ -294,7 +297,8 @@ def _fork_timed(jobs):
     return [(r, s, wall) for r, s in out]
 
 
-def cpu_baseline(tr, W: int, K: int, seconds: float, parallel: bool = True) -> dict:
+def cpu_baseline(tr, W: int, K: int, seconds: float, parallel: bool = True,
+                 placement: str = "lowest") -> dict:
     """The oracle (full-data mode: rows moved and gathered) timed on this host's cores.
 
     Protocol: the initial load and W warm-up steps are untimed (the load's row
@@ -328,7 +332,7 @@ def cpu_baseline(tr, W: int, K: int, seconds: float, parallel: bool = True) -> d
     warmed = []
     est = None
     for g in range(n_par):
-        grp = _loaded_group(tr, g, len(cores))
+        grp = _loaded_group(tr, g, len(cores), placement)
         sels = tr.selections(g)
         t_w = time.perf_counter()
         for t in range(1, W + 1):
@@ -385,7 +389,7 @@ def gather_all_layers(eng, g, sel, outs, layers, mode, stream=None):
 
 
 def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str = "layer",
-            replays: int = 3) -> dict:
+            replays: int = 3, placement: int = 0) -> dict:
     import statistics
 
     import torch
@@ -431,7 +435,7 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
     warm.close()
 
     def timed_replay():
-        eng = engine_for(tr, max_append=1 << 16, policy=policy)
+        eng = engine_for(tr, max_append=1 << 16, policy=policy, placement=placement)
         initial_load(eng, tr, groups, rows)
         torch.cuda.synchronize()
         # the first step (cold start: the most misses) is timed on its own
@@ -482,12 +486,12 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
     # also the step statistics: the host-link bytes of the timed steps (the engine
     # is deterministic, so they are those of the timed replays)
     if phases:
-        eng = engine_for(tr, max_append=1 << 16, policy=policy)
+        eng = engine_for(tr, max_append=1 << 16, policy=policy, placement=placement)
         initial_load(eng, tr, groups, rows)
         eng.set_timing(True)
         torch.cuda.synchronize()
         ph = np.zeros(3)
-        h2d = d2h = 0
+        h2d = d2h = hits = uniq = 0
         n = 0
         prev_evict = {g: 0 for g in groups}
         for t in range(1, W + K + 1):
@@ -501,12 +505,15 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
                     ph += ms
                     h2d += st[2]
                     d2h += prev_evict[g]
+                    hits += st[1]
+                    uniq += st[0]
                     n += 1
                 prev_evict[g] = st[3]
         eng.close()
         note("gpu per-phase replay done")
         res.update(phase_ms=(ph / max(n, 1)).tolist(), link_ms_total=float(ph[1]),
-                   h2d_rows=int(h2d), d2h_rows=int(d2h), group_steps=n)
+                   h2d_rows=int(h2d), d2h_rows=int(d2h), group_steps=n,
+                   hit_rate=hits / uniq if uniq else None)
     return res
 
 
@@ -706,10 +713,13 @@ def main():
     policy = 1 if args.policy == "lru" else 0
     cpu = None
     if not args.no_cpu_baseline and policy == 0:
-        cpu = cpu_baseline(tr, W, K, args.cpu_seconds, parallel=not args.no_cpu_parallel)
+        cpu = cpu_baseline(tr, W, K, args.cpu_seconds, parallel=not args.no_cpu_parallel,
+                           placement=args.placement)
 
     gather_mode = args.gather if wl.layers > 1 else "layer"   # one layer: the same launch
-    r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode, replays=args.replays)
+    placement = 1 if args.placement == "ring" else 0
+    r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode, replays=args.replays,
+                placement=placement)
     value = per_step * K / r["wall_s"]
     ms_per_step = r["event_ms"] / K
     replay_values = [round(per_step * K / w, 1) for w in r["replay_walls_s"]]
@@ -755,7 +765,8 @@ def main():
         t_in = r["link_ms_total"] * 1e-3
         gin = up / t_in / 1e9 if t_in > 0 else None
         gout = down / t_in / 1e9 if t_in > 0 else None
-        miss = {"phase_ms_per_group_step": {k: round(v, 5) for k, v in zip(
+        miss = {"hit_rate": rnd(r["hit_rate"], 6),
+                "phase_ms_per_group_step": {k: round(v, 5) for k, v in zip(
                     ["lookup_dedup", "mark_select_link", "swap_commit"], r["phase_ms"])},
                 "h2d_GBps_over_phase": rnd(gin, 2), "d2h_GBps_over_phase": rnd(gout, 2)}
         try:
@@ -783,6 +794,7 @@ def main():
                    "layers_per_group": wl.layers, "k": wl.k, "gpu_slots": tr.P, "host_slots": tr.H,
                    "ring": wl.ring, "row_bytes": wl.row_bytes, "overlap": wl.overlap,
                    "policy": "exact LRU" if policy else "PB-LRU", "gather": gather_mode,
+                   "placement": args.placement,
                    "row_layers_per_step": per_step},
         "roofline": roofline,
         "roofline_other": other,

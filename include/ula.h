@@ -11,12 +11,12 @@
  *    mapping table. In DP mode an entry lives in exactly one of the two
  *    pools. Layers that share one sparse selection look up and de-duplicate
  *    it once per layer group.
- *  - Section 3: the shared GPU pool is managed by PB-LRU: a bucket per
- *    scheduling round, a ring of recent buckets plus a cold bucket per layer
- *    group, bucket bitmaps with summaries, victims taken from free slots, then
- *    cold, then ring buckets oldest to newest, never the current bucket. Data
- *    moves first, then the mapping is updated and completion is signalled;
- *    readers wait for the signal.
+ *  - Section 3: the GPU pool is managed by PB-LRU: slots are labelled with the
+ *    scheduling round that last touched them (a ring of recent buckets plus one
+ *    cold bucket per layer group, each a bitmap with summaries); victims come
+ *    from free slots, then cold, then older ring buckets, never the running
+ *    round's bucket. Rows move before the mapping changes, the completion
+ *    signal comes last, and readers wait for it.
  *
  * Conventions
  *  - Every layer group g in [0, num_groups) has its own GPU pool of
@@ -95,7 +95,24 @@ typedef struct {
   int32_t max_k;             /* most entries per selection set; max_sets * max_k < 2^31 */
   int32_t max_append;        /* most addresses staged per append chunk, >= 1 */
   int32_t policy;            /* ULA_POLICY_PBLRU (0, default) or ULA_POLICY_LRU (1) */
+  int32_t placement;         /* where ula_append puts new entries: ULA_PLACE_LOWEST (0, default)
+                                or ULA_PLACE_RING (1, PB-LRU only) */
 } ula_config;
+
+/* Placement of appended entries (section 2: the library decides which pool holds
+ * new KV; the pages do not say how).
+ *  - ULA_PLACE_LOWEST: in list order each entry takes the lowest free GPU slot,
+ *    joining the cold bucket, else the lowest free host slot; appends never
+ *    evict (with a full GPU pool, new entries start in the host pool and come
+ *    in through a step's miss path when selected).
+ *  - ULA_PLACE_RING: new entries count as used in the current round (section 3:
+ *    recent entries stay on the GPU): in list order each entry takes the next
+ *    slot of the step's victim order (free ascending, then cold, then ring
+ *    buckets oldest to newest, never the current bucket) and joins the current
+ *    bucket; an entry displaced from that slot moves, rows and all, to the
+ *    lowest free host slot; when no such slot is left, entries take the lowest
+ *    free host slots. The current bucket is that of the group's last step. */
+enum { ULA_PLACE_LOWEST = 0, ULA_PLACE_RING = 1 };
 
 /* Replacement policies. PB-LRU is the pages' policy (UlaCache summary, section 3).
  * Exact LRU is the standard policy the pages compare it against (sections 3 and 4):
@@ -163,9 +180,11 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
 int ula_init_static(const ula_config* cfg, void* host_pinned, uint64_t stream, ula_ctx** out);
 
 /* Append n new logical entries to group g (section 2: the library decides the
- * pool). In list order each entry takes the lowest free GPU slot (joining the
- * cold bucket) or, when none is free, the lowest free host slot; appends never
- * evict. la_host: n addresses in host memory. rows: n x layers_per_group x
+ * pool), placed as the configuration's placement says: by default, in list
+ * order each entry takes the lowest free GPU slot (joining the cold bucket) or,
+ * when none is free, the lowest free host slot, and appends never evict; under
+ * ULA_PLACE_RING each entry joins the current bucket, displacing entries to the
+ * host pool (see above). la_host: n addresses in host memory. rows: n x layers_per_group x
  * row_bytes bytes, packed, in device memory (rows_on_device = 1) or host memory
  * (rows_on_device = 0); rows must stay valid until the stream reaches the call.
  * Validated on the host first: ULA_EINVAL (bad g or n < 0), ULA_ERANGE (address

@@ -18,9 +18,10 @@ from .pblru import PBLRUGroup
 LOAD_CHUNK = 1 << 18
 
 
-def new_group(trace, full_data: bool = True) -> PBLRUGroup:
+def new_group(trace, full_data: bool = True, placement: str = "lowest") -> PBLRUGroup:
     wl = trace.wl
-    return PBLRUGroup(trace.N, trace.P, trace.H, wl.ring, wl.layers, wl.row_bytes, full_data)
+    return PBLRUGroup(trace.N, trace.P, trace.H, wl.ring, wl.layers, wl.row_bytes, full_data,
+                      placement=placement)
 
 
 def initial_load(grp: PBLRUGroup, trace, g: int) -> None:

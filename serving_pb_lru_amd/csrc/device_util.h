@@ -116,4 +116,43 @@ __device__ __forceinline__ void place_piece(const GroupDev& g, uint32_t d, uint3
   }
 }
 
+// Piece c (16 bytes, value v) of appended entry i (address la) under
+// ULA_PLACE_RING. dst holds the q GPU slots the append took (taken from the
+// free set: host bit set; the first qfree of them) and then its host slots. An
+// entry i < q goes to GPU slot dst[i]; the entry it displaces from an occupied
+// slot first moves, rows and all, to host slot dst[q + i - qfree]. An entry
+// i >= q goes to host slot dst[q + i - qfree] itself. The lane of piece 0 also
+// publishes the mapping and owner entries. A piece's old row is read before
+// the new one is written, by the same lane.
+__device__ __forceinline__ void place_piece_ring(const GroupDev& g, const uint32_t* dst, int q, int qfree,
+                                                 uint32_t i, uint32_t c, int32_t la, const vec4u v) {
+  if ((int)i < q) {
+    const uint32_t d = dst[i];
+    const uint32_t s = d & ~kHostBit;
+    vec4u* gp = reinterpret_cast<vec4u*>(g.pool + (size_t)s * g.slot_bytes) + c;
+    if (!(d & kHostBit)) {   // an occupied slot: its entry moves to the host pool
+      const uint32_t h = dst[q + (int)i - qfree] & ~kHostBit;
+      const vec4u old = *gp;
+      __builtin_nontemporal_store(old, reinterpret_cast<vec4u*>(g.host + (size_t)h * g.slot_bytes) + c);
+      if (c == 0) {
+        const int32_t o = g.gown[s];
+        g.map[o] = kHostBit | h;
+        g.hown[h] = o;
+      }
+    }
+    *gp = v;
+    if (c == 0) {
+      g.map[la] = s;
+      g.gown[s] = la;
+    }
+  } else {
+    const uint32_t h = dst[q + (int)i - qfree] & ~kHostBit;
+    __builtin_nontemporal_store(v, reinterpret_cast<vec4u*>(g.host + (size_t)h * g.slot_bytes) + c);
+    if (c == 0) {
+      g.map[la] = kHostBit | h;
+      g.hown[h] = la;
+    }
+  }
+}
+
 }  // namespace ula

@@ -1,9 +1,8 @@
 // Group lookup and de-duplication, then hit marking.
 //
-// UlaCache summary (paper-daily.com), section 2: layers sharing one sparse
-// selection do the address lookup and de-duplication once per group; section 3:
-// hit detection, recency update and de-duplication run in parallel on GPU
-// threads. The selection is n = n_sets * k logical addresses, row-major; -1 is
+// UlaCache summary (paper-daily.com), section 2: the layers of a group share a
+// selection, so its addresses are resolved and de-duplicated once for all of
+// them; section 3: that work and the recency bookkeeping run across GPU threads. The selection is n = n_sets * k logical addresses, row-major; -1 is
 // padding. The distinct addresses are kept in first-occurrence order.
 //
 //   tag      every in-range entry e stores key(t, e) = (t << 32) | ~e into

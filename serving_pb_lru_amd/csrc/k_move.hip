@@ -1,10 +1,10 @@
 // Data movement and commit: append placement, the HBM part of the miss-path
 // swap, and the commit that updates the mapping table and signals completion.
 //
-// UlaCache summary (paper-daily.com), section 3: move the data first, then
-// update the mapping and signal completion; readers wait for the signal, so
-// they never see half-moved data. Section 2: an entry lives in the GPU pool or
-// the host pool, never both. Here the i-th miss takes the i-th victim slot, the
+// Ordering (UlaCache summary, paper-daily.com, section 3): rows land before the
+// mapping table names their new slots, and the completion counter is raised
+// last, so a reader that waits for the counter only sees finished moves. Pools
+// (section 2): each entry is held by exactly one of the GPU and host pools. Here the i-th miss takes the i-th victim slot, the
 // missed rows come in from the miss's host slot and the victim's rows go out
 // to that same host slot (a swap), so host occupancy is unchanged and no entry
 // is ever held twice; a victim taken from the free bucket frees the host slot.
@@ -32,6 +32,27 @@ __global__ __launch_bounds__(256) void k_place(GroupDev g, int32_t n, const uint
     const uint32_t c = idx - i * chunks;
     const vec4u v = reinterpret_cast<const vec4u*>(rows + (size_t)i * g.slot_bytes)[c];
     place_piece(g, g.app_dst[i], c, c == 0 ? g.app_la[i] : 0, v);
+  }
+}
+
+// Append under ULA_PLACE_RING: destinations from the plan/extract pair (app_dst:
+// the GPU slots taken, then the host slots), the counts from the plan.
+__global__ __launch_bounds__(256) void k_place_ring(GroupDev g, int32_t n, const uint8_t* __restrict__ rows,
+                                                    FastDiv per_slot) {
+  __shared__ int s_status, s_q[2];
+  if (threadIdx.x == 0) s_status = status_of(g.ctr);
+  else if (threadIdx.x == kWave) s_q[0] = g.ctr->app_q;
+  else if (threadIdx.x == 2 * kWave) s_q[1] = g.ctr->app_qfree;
+  __syncthreads();
+  if (s_status) return;
+  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
+  const uint32_t total = (uint32_t)n * chunks;
+  for (uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+       idx += gridDim.x * blockDim.x) {
+    const uint32_t i = per_slot.div(idx);
+    const uint32_t c = idx - i * chunks;
+    const vec4u v = reinterpret_cast<const vec4u*>(rows + (size_t)i * g.slot_bytes)[c];
+    place_piece_ring(g, g.app_dst, s_q[0], s_q[1], i, c, c == 0 ? g.app_la[i] : 0, v);
   }
 }
 
@@ -235,6 +256,16 @@ hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipSt
   int blocks = (int)((total + 255) / 256);
   if (blocks > 4096) blocks = 4096;
   k_place<<<blocks, 256, 0, s>>>(g, n, rows, FastDiv(chunks));
+  return hipGetLastError();
+}
+
+hipError_t launch_place_ring(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const uint32_t chunks = (uint32_t)g.slot_bytes / 16u;
+  size_t total = (size_t)n * chunks;
+  int blocks = (int)((total + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  k_place_ring<<<blocks, 256, 0, s>>>(g, n, rows, FastDiv(chunks));
   return hipGetLastError();
 }
 

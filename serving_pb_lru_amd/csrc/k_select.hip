@@ -1,11 +1,11 @@
 // Ring advance with fold, and ordered selection of set bits (victims, free slots).
 //
-// UlaCache summary (paper-daily.com), section 3: each round the current bucket
-// advances one position and whatever is left in the bucket about to be reused
-// moves to the cold bucket, by relabelling only; victims are free slots first,
-// then the cold bucket, then ring buckets from oldest to newest, never the
-// current bucket; each bucket is a bitmap with one bit per GPU slot, and
-// summary levels above it let the selection skip empty segments.
+// Policy (UlaCache summary, paper-daily.com, section 3): a step moves the ring
+// index on by one; the bucket it lands on still holds slots from B steps ago,
+// which are relabelled cold (no data moves). Victims come from the free set,
+// then cold, then the other ring buckets in age order, and the bucket of the
+// running step is exempt. A bucket is a bit per GPU slot; counts per span above
+// the bits let the selection jump over spans with no set bit.
 //
 // Summary hierarchy used here:
 //   level 0  the bucket bitmaps, one bit per slot (canonical state)
@@ -45,13 +45,20 @@ namespace ula {
 // Selection plan (one 1024-thread workgroup). STEP mode: m = misses of the
 // step, sources in eviction order, destination ring[cur]. APPEND mode: m = n,
 // sources [free, free host slots]: the first min(n, free GPU slots) entries take
-// free GPU slots (joining cold), the rest free host slots. Work items go to
-// `items`; returns their number (in every thread). pre_avail / pre_hint
-// (nullable, LDS): the order's bucket counts and the free sets' span hints
-// (GPU, host), already loaded by the caller.
+// free GPU slots (joining cold), the rest free host slots. APPEND_RING mode:
+// the step's sources (free, cold, ring oldest to newest) give the first
+// q = min(n, available) slots, which join the current bucket; the free host
+// source then gives n - q_free slots, right after them in the output: one for
+// each entry displaced from an occupied slot, then one for each of the n - q
+// entries left over. The GPU slots taken and the free ones among them go to
+// the counter block (app_q, app_qfree) and, if s_q is given (LDS), to s_q[0..1].
+// Work items go to `items`; returns their number (in every thread). pre_avail /
+// pre_hint (nullable, LDS): the order's bucket counts and the free sets' span
+// hints (GPU, host), already loaded by the caller.
 __device__ int plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
                          unsigned long long* s_nonempty, SelItem* items,
-                         const int* pre_avail = nullptr, const int* pre_hint = nullptr) {
+                         const int* pre_avail = nullptr, const int* pre_hint = nullptr,
+                         int* s_q = nullptr) {
   Counters* c = g.ctr;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -66,13 +73,19 @@ __device__ int plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
     __syncthreads();
   }
   const int m = (a.mode == kPlanStep) ? c->n_miss : a.n;
+  const bool ring = a.mode == kPlanAppendRing;
   int off = 0;       // output entries planned so far
   int nitems = 0;    // work items written so far
   int q_free = 0;
-  for (int j = 0; j < a.norder && off < m; ++j) {
+  int q_gpu = 0;     // GPU slots taken (APPEND_RING)
+  for (int j = 0; j < a.norder && (off < m || ring); ++j) {
     const int id = a.order[j];
+    const bool ring_host = ring && id == kHostFreeId;
+    if (ring_host) q_gpu = off;
+    const int want = ring_host ? a.n - q_free : m - off;
+    if (want <= 0) continue;
     const int avail = pre_avail ? pre_avail[j] : *bucket_count(g, id);
-    const int q = min(m - off, avail);
+    const int q = min(want, avail);
     if (q <= 0) continue;
     const uint32_t* tc = bucket_tcnt(g, id);
     const int T = bucket_ntiles(g, id);
@@ -117,6 +130,14 @@ __device__ int plan_body(const GroupDev& g, const PlanArgs& a, int* scratch,
       c->bcnt[a.dest] += m;
       c->stats[3] = m - q_free;   // evictions
       c->stats[4] = q_free;       // from free slots
+    } else if (ring) {
+      c->bcnt[a.dest] += q_gpu;
+      c->app_q = q_gpu;
+      c->app_qfree = q_free;
+      if (s_q) {
+        s_q[0] = q_gpu;
+        s_q[1] = q_free;
+      }
     } else {
       c->bcnt[a.dest] += q_free;
     }
@@ -136,12 +157,14 @@ __global__ __launch_bounds__(1024) void k_plan(GroupDev g, PlanArgs a) {
 // and victims taken from the free bucket carry the top bit (their slot holds no
 // row to evict). APPEND: taken GPU slots join cold (dest), taken host slots
 // leave the free-host bitmap; the output list is the destinations (host slots
-// carry the host bit).
+// carry the host bit). APPEND_RING: as STEP for the GPU slots (dest: the current
+// bucket; free ones marked), then the host slots (host bit).
 __device__ __forceinline__ void extract_item(const GroupDev& g, const SelItem it, int32_t mode,
                                              int32_t dest, uint32_t* out) {
   const int lane = lane_id();
   const bool host = it.src == kHostFreeId;
-  const uint32_t flag = (host || (mode == kPlanStep && it.src == kFree)) ? kHostBit : 0u;
+  const bool mark_free = (mode == kPlanStep || mode == kPlanAppendRing) && it.src == kFree;
+  const uint32_t flag = (host || mark_free) ? kHostBit : 0u;
   uint32_t* words = bucket_words(g, it.src);
   const int w = it.tile * kTileWords + lane;
   const uint32_t x = w < bucket_nwords(g, it.src) ? words[w] : 0u;
@@ -371,9 +394,11 @@ __device__ void append_small_body(const GroupDev& g, const SmallAppend& a, const
                                   FastDiv per_slot) {
   __shared__ int scratch[1024 / kWave + 1];
   __shared__ unsigned long long s_nonempty[1024 / kWave];
-  __shared__ SelItem s_items[kSmallAppend];   // each item takes at least one entry
-  __shared__ uint32_t s_dst[kSmallAppend];
-  __shared__ int s_status, s_avail[2], s_hint[2];
+  // each item takes at least one output; under placement ring an entry can use
+  // two outputs (its GPU slot and the host slot of the entry it displaces)
+  __shared__ SelItem s_items[2 * kSmallAppend];
+  __shared__ uint32_t s_dst[2 * kSmallAppend];
+  __shared__ int s_status, s_avail[2], s_hint[2], s_q[2];
   const int tid = threadIdx.x;
   if (tid == 0) s_status = status_of(g.ctr);
   else if (tid == kWave) s_avail[0] = g.ctr->bcnt[kFree];
@@ -394,29 +419,38 @@ __device__ void append_small_body(const GroupDev& g, const SmallAppend& a, const
   }
   __syncthreads();
   if (s_status) return;
-  PlanArgs p{};
-  p.mode = kPlanAppend;
-  p.n = a.n;
-  p.norder = 2;
-  p.dest = kCold;
-  p.order[0] = kFree;
-  p.order[1] = kHostFreeId;
-  const int nitems = plan_body(g, p, scratch, s_nonempty, s_items, s_avail, s_hint);
-  for (int i = tid / kWave; i < nitems; i += blockDim.x / kWave)
-    extract_item(g, s_items[i], kPlanAppend, kCold, s_dst);
+  if (a.ring) {
+    const PlanArgs p = ring_append_plan(a.n, a.cur, g.B);
+    const int nitems = plan_body(g, p, scratch, s_nonempty, s_items, nullptr, s_hint, s_q);
+    for (int i = tid / kWave; i < nitems; i += blockDim.x / kWave)
+      extract_item(g, s_items[i], kPlanAppendRing, p.dest, s_dst);
+  } else {
+    PlanArgs p{};
+    p.mode = kPlanAppend;
+    p.n = a.n;
+    p.norder = 2;
+    p.dest = kCold;
+    p.order[0] = kFree;
+    p.order[1] = kHostFreeId;
+    const int nitems = plan_body(g, p, scratch, s_nonempty, s_items, s_avail, s_hint);
+    for (int i = tid / kWave; i < nitems; i += blockDim.x / kWave)
+      extract_item(g, s_items[i], kPlanAppend, kCold, s_dst);
+  }
   __syncthreads();
+  auto place = [&](uint32_t idx, const vec4u v) {
+    const uint32_t i = per_slot.div(idx);
+    const uint32_t c = idx - i * chunks;
+    if (a.ring) place_piece_ring(g, s_dst, s_q[0], s_q[1], i, c, a.las[i], v);
+    else place_piece(g, s_dst[i], c, a.las[i], v);
+  };
 #pragma unroll
   for (int r = 0; r < kEarly; ++r) {
     const uint32_t idx = (uint32_t)tid + (uint32_t)r * 1024u;
-    if (idx < total) {
-      const uint32_t i = per_slot.div(idx);
-      place_piece(g, s_dst[i], idx - i * chunks, a.las[i], early[r]);
-    }
+    if (idx < total) place(idx, early[r]);
   }
   for (uint32_t idx = (uint32_t)tid + kEarly * 1024u; idx < total; idx += blockDim.x) {
     const uint32_t i = per_slot.div(idx);
-    const uint32_t c = idx - i * chunks;
-    place_piece(g, s_dst[i], c, a.las[i], reinterpret_cast<const vec4u*>(rows + (size_t)i * g.slot_bytes)[c]);
+    place(idx, reinterpret_cast<const vec4u*>(rows + (size_t)i * g.slot_bytes)[idx - i * chunks]);
   }
 }
 

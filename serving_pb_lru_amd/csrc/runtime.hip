@@ -38,7 +38,7 @@ int hip_fail(hipError_t e, const char* what) {
 struct Dims {
   int64_t N, P, H, B, NB, W, T, WH, TH, Lg, row_bytes, slot_bytes;
   int64_t maxU, maxBlk, maxItems, maxApp, nsel, maxRs;
-  int policy;
+  int policy, placement;
 };
 
 bool check_config(const ula_config* c, Dims* d) {
@@ -52,6 +52,8 @@ bool check_config(const ula_config* c, Dims* d) {
   if ((int64_t)c->gpu_slots + c->host_slots >= (1ll << 31)) return false;
   if (c->max_sets < 1 || c->max_k < 1 || c->max_append < 1) return false;
   if (c->policy != ULA_POLICY_PBLRU && c->policy != ULA_POLICY_LRU) return false;
+  if (c->placement != ULA_PLACE_LOWEST && c->placement != ULA_PLACE_RING) return false;
+  if (c->placement == ULA_PLACE_RING && c->policy != ULA_POLICY_PBLRU) return false;
   const int64_t nsel = (int64_t)c->max_sets * c->max_k;
   if (nsel >= (1ll << 31)) return false;
   d->N = c->logical_capacity;
@@ -70,9 +72,12 @@ bool check_config(const ula_config* c, Dims* d) {
   d->nsel = nsel;
   d->maxBlk = (nsel + kScanBlock - 1) / kScanBlock;
   d->maxApp = c->max_append;
-  d->maxItems = std::max<int64_t>(d->maxU, d->maxApp) + 2;
+  // an append under placement ring takes up to two outputs per entry (its GPU
+  // slot and a host slot for the entry it displaces), each work item at least one
+  d->maxItems = std::max<int64_t>(d->maxU, 2 * d->maxApp) + 2;
   d->maxRs = (d->maxU + 1023) / 1024;
   d->policy = c->policy;
+  d->placement = c->placement;
   // selection entries (and so misses) fit the look-back descriptors' 30-bit counts
   if (nsel >= (1ll << 30)) return false;
   // 16-byte piece counts handled with 32-bit indices and FastDiv (< 2^31)
@@ -116,7 +121,7 @@ Layout layout_of(const ula_config* c, const Dims& d) {
   L.partial = take(4 * kMarkBlocks * kMaxBuckets);
   L.items = take(sizeof(SelItem) * d.maxItems);
   L.app_la = take(4 * d.maxApp);
-  L.app_dst = take(4 * d.maxApp);
+  L.app_dst = take(4 * 2 * d.maxApp);
   L.app_rows = take((size_t)d.maxApp * d.slot_bytes);
   L.evict_rows = take((size_t)d.maxU * d.slot_bytes);
   L.wb_h = take(4 * d.maxU);
@@ -550,10 +555,15 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
   // writes every staged row out before it frees a slot; and the host slot a miss
   // vacates when its victim was a free GPU slot receives no evicted row (nor had
   // one pending: its entry was in it during the previous step).
+  // placement ring: the current bucket is that of the group's last enqueued step
+  const int32_t cur = (int32_t)(gh.steps % d.B);
+  const int32_t ring = d.placement == ULA_PLACE_RING ? 1 : 0;
   if (n <= kSmallAppend && n <= d.maxApp && rows_on_device) {
     // decode-time appends: one workgroup, addresses passed by value
     SmallAppend a{};
     a.n = n;
+    a.ring = ring;
+    a.cur = cur;
     std::memcpy(a.las, la_host, sizeof(int32_t) * n);
     HIP_TRY(launch_append_small(g, a, static_cast<const uint8_t*>(rows), s));
   } else if (ctx->static_dev >= 0) {
@@ -563,6 +573,8 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
     for (int32_t off = 0; off < n; off += chunk) {
       SmallAppend a{};
       a.n = std::min(chunk, n - off);
+      a.ring = ring;
+      a.cur = cur;
       std::memcpy(a.las, la_host + off, sizeof(int32_t) * a.n);
       const uint8_t* src = static_cast<const uint8_t*>(rows) + (size_t)off * d.slot_bytes;
       if (!rows_on_device) {
@@ -587,6 +599,13 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
       if (!rows_on_device) {
         HIP_TRY(hipMemcpyAsync(g.app_rows, src, (size_t)cnt * d.slot_bytes, hipMemcpyHostToDevice, s));
         src = g.app_rows;
+      }
+      if (ring) {
+        const PlanArgs a = ring_append_plan(cnt, cur, (int32_t)d.B);
+        HIP_TRY(launch_plan(g, a, s));
+        HIP_TRY(launch_extract(g, kPlanAppendRing, a.dest, 2 * cnt, s));
+        HIP_TRY(launch_place_ring(g, cnt, src, s));
+        continue;
       }
       PlanArgs a{};
       a.mode = kPlanAppend;
@@ -762,6 +781,8 @@ int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* l
   if (n_app > 0 && n_app <= kSmallAppend && n_app <= ctx->dims.maxApp && rows_on_device) {
     SmallAppend a{};
     a.n = n_app;
+    a.ring = ctx->dims.placement == ULA_PLACE_RING ? 1 : 0;
+    a.cur = (int32_t)(ctx->groups[group].steps % ctx->dims.B);   // before the step advances it
     std::memcpy(a.las, la_host, sizeof(int32_t) * n_app);
     const int rc = step_impl(ctx, group, n_sets, k, sel_dev, stream, &a, static_cast<const uint8_t*>(rows));
     if (rc) return rc;

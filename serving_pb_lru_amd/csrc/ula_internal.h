@@ -87,6 +87,8 @@ struct alignas(64) Counters {
   // are taken lowest first, so every span before the hint is empty (a freed host
   // slot lowers its hint)
   int32_t free_lo, hfree_lo;
+  // an append under ULA_PLACE_RING: GPU slots it took, of which free ones
+  int32_t app_q, app_qfree;
 };
 static_assert(sizeof(Counters) % 64 == 0, "counter block alignment");
 
@@ -169,7 +171,11 @@ struct FastDiv {
   }
 };
 
-enum PlanMode : int32_t { kPlanStep = 0, kPlanAppend = 1 };
+// kPlanAppend: appends into free GPU slots (joining cold), then free host slots.
+// kPlanAppendRing: appends into the step's victim order (free, cold, ring oldest
+// to newest, never the current bucket), joining the current bucket; then free
+// host slots for the entries they displace and for the entries left over.
+enum PlanMode : int32_t { kPlanStep = 0, kPlanAppend = 1, kPlanAppendRing = 2 };
 
 struct PlanArgs {
   int32_t mode;
@@ -183,8 +189,25 @@ constexpr int kSmallAppend = 256;   // appends up to this size run as one workgr
 
 struct SmallAppend {
   int32_t n;
+  int32_t ring;          // 1: placement into the current bucket (ULA_PLACE_RING)
+  int32_t cur;           // the current bucket (placement ring)
   int32_t las[kSmallAppend];
 };
+
+// The plan of an append of n entries under ULA_PLACE_RING with current bucket
+// cur: the step's victim sources in order, then the free host slots.
+__host__ __device__ inline PlanArgs ring_append_plan(int32_t n, int32_t cur, int32_t B) {
+  PlanArgs a{};
+  a.mode = kPlanAppendRing;
+  a.n = n;
+  a.dest = ring_id(cur);
+  a.order[0] = kFree;
+  a.order[1] = kCold;
+  a.norder = 2;
+  for (int j = 1; j < B; ++j) a.order[a.norder++] = (int8_t)ring_id((cur + j) % B);
+  a.order[a.norder++] = (int8_t)kHostFreeId;
+  return a;
+}
 
 // ---- launchers (one translation unit per kernel family) ----------------
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
@@ -208,6 +231,7 @@ hipError_t launch_append_small(const GroupDev& g, const SmallAppend& a, const ui
 hipError_t launch_tag_append(const GroupDev& g, const SmallAppend& a, const uint8_t* rows,
                              const int32_t* sel, int32_t n, uint32_t t, hipStream_t s);
 hipError_t launch_place(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s);
+hipError_t launch_place_ring(const GroupDev& g, int32_t n, const uint8_t* rows, hipStream_t s);
 hipError_t launch_release(const GroupDev& g, int32_t n, hipStream_t s);
 hipError_t launch_swap_commit(const GroupDev& g, uint32_t t, int32_t max_pairs, hipStream_t s);
 hipError_t launch_writeback(const GroupDev& g, int32_t max_pairs, hipStream_t s);

@@ -16,11 +16,12 @@ from .ula import Engine
 LOAD_CHUNK = 1 << 18
 
 
-def engine_for(trace, max_append: int = 1 << 16, policy: int = 0) -> Engine:
+def engine_for(trace, max_append: int = 1 << 16, policy: int = 0, placement: int = 0) -> Engine:
     wl = trace.wl
     return Engine(num_groups=wl.groups, layers=wl.layers, row_bytes=wl.row_bytes, ring=wl.ring,
                   logical_capacity=trace.N, gpu_slots=trace.P, host_slots=trace.H,
-                  max_sets=trace.n_sets, max_k=trace.k, max_append=max_append, policy=policy)
+                  max_sets=trace.n_sets, max_k=trace.k, max_append=max_append, policy=policy,
+                  placement=placement)
 
 
 def initial_load(eng: Engine, trace, groups, rows) -> None:

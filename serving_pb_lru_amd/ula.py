@@ -24,6 +24,7 @@ ERROR_NAMES = {0: "OK", -1: "EINVAL", -2: "ERANGE", -3: "EDUP", -4: "EHOSTFULL",
 
 
 POLICY_PBLRU, POLICY_LRU = 0, 1
+PLACE_LOWEST, PLACE_RING = 0, 1
 
 
 class UlaConfig(ctypes.Structure):
@@ -31,7 +32,8 @@ class UlaConfig(ctypes.Structure):
                 ("row_bytes", ctypes.c_int32), ("ring_buckets", ctypes.c_int32),
                 ("logical_capacity", ctypes.c_int32), ("gpu_slots", ctypes.c_int32),
                 ("host_slots", ctypes.c_int32), ("max_sets", ctypes.c_int32),
-                ("max_k", ctypes.c_int32), ("max_append", ctypes.c_int32), ("policy", ctypes.c_int32)]
+                ("max_k", ctypes.c_int32), ("max_append", ctypes.c_int32), ("policy", ctypes.c_int32),
+                ("placement", ctypes.c_int32)]
 
 
 class UlaStepStats(ctypes.Structure):
@@ -150,13 +152,14 @@ class Engine:
 
     def __init__(self, num_groups: int, layers: int, row_bytes: int, ring: int, logical_capacity: int,
                  gpu_slots: int, host_slots: int, max_sets: int, max_k: int, max_append: int = 4096,
-                 device: str = "cuda", stream=None, policy: int = 0, static_workspace: bool = False):
+                 device: str = "cuda", stream=None, policy: int = 0, static_workspace: bool = False,
+                 placement: int = 0):
         """policy: POLICY_PBLRU (0) or POLICY_LRU (1). static_workspace: take the device
         workspace from the library's static array (ula_init_static) instead of a torch
-        allocation."""
+        allocation. placement: PLACE_LOWEST (0) or PLACE_RING (1) for appended entries."""
         import torch
         self.cfg = UlaConfig(num_groups, layers, row_bytes, ring, logical_capacity, gpu_slots,
-                             host_slots, max_sets, max_k, max_append, policy)
+                             host_slots, max_sets, max_k, max_append, policy, placement)
         self.policy = policy
         L = lib()
         nbytes = L.ula_device_bytes(ctypes.byref(self.cfg))

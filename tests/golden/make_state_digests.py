@@ -6,9 +6,11 @@ synthetic trace and the digest of its exported state is stored: after the
 initial load (step 0) and after each step. The GPU parity tests replay the same
 inputs through the engine and compare digests. With --lru the exact-LRU oracle
 (array form) replays the same traces into digests_lru_<workload>.json, with the
-timestamps in the digest. Usage:
+timestamps in the digest. With --ring the PB-LRU oracle places appended
+entries in the current bucket (placement "ring") and writes
+digests_ring_<workload>.json. Usage:
 
-    python tests/golden/make_state_digests.py [--lru] [workload ...]
+    python tests/golden/make_state_digests.py [--lru | --ring] [workload ...]
 """
 
 import json
@@ -40,9 +42,9 @@ def lru_group_digests(name: str, g: int) -> list:
     return out
 
 
-def group_digests(name: str, g: int) -> list:
+def group_digests(name: str, g: int, placement: str = "lowest") -> list:
     tr = Trace(preset(name))
-    grp = new_group(tr, full_data=False)
+    grp = new_group(tr, full_data=False, placement=placement)
     initial_load(grp, tr, g)
     out = [digest(grp.export_state())]
     sels = tr.selections(g)
@@ -53,9 +55,13 @@ def group_digests(name: str, g: int) -> list:
     return out
 
 
-def main(names, lru=False):
+def ring_group_digests(name: str, g: int) -> list:
+    return group_digests(name, g, placement="ring")
+
+
+def main(names, lru=False, ring=False):
     jobs = [(n, g) for n in names for g in range(preset(n).groups)]
-    fn = lru_group_digests if lru else group_digests
+    fn = lru_group_digests if lru else (ring_group_digests if ring else group_digests)
     with ProcessPoolExecutor(max_workers=min(6, len(jobs))) as ex:
         res = list(ex.map(fn, [j[0] for j in jobs], [j[1] for j in jobs]))
     by = {}
@@ -64,12 +70,13 @@ def main(names, lru=False):
     for n in names:
         wl = preset(n)
         doc = {"workload": n, "policy": "exact LRU" if lru else "PB-LRU",
+               "placement": "ring" if ring else "lowest",
                "source": ("oracle/exact_lru_np.py" if lru else "oracle/ (metadata mode)")
                + " via tests/golden/make_state_digests.py",
                "digest": "xxh3_64 of the little-endian bytes of map, gown, hown, bitsets"
                + (", stamps" if lru else ""),
                "steps": wl.steps, "groups": [by[n][g] for g in range(wl.groups)]}
-        fname = f"digests_lru_{n}.json" if lru else f"digests_{n}.json"
+        fname = f"digests_lru_{n}.json" if lru else (f"digests_ring_{n}.json" if ring else f"digests_{n}.json")
         with open(os.path.join(HERE, fname), "w") as f:
             json.dump(doc, f, separators=(",", ":"))
         print("wrote", n, flush=True)
@@ -78,5 +85,6 @@ def main(names, lru=False):
 if __name__ == "__main__":
     args = sys.argv[1:]
     lru = "--lru" in args
-    names = [a for a in args if a != "--lru"]
-    main(names or list(PRESETS), lru=lru)
+    ring = "--ring" in args
+    names = [a for a in args if a not in ("--lru", "--ring")]
+    main(names or list(PRESETS), lru=lru, ring=ring)

@@ -53,7 +53,7 @@ def gather_layers_by(eng, g, layers, dsel, mode):
 
 
 def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, check_every=1,
-               releases=None, combined=False, gather_mode="layer"):
+               releases=None, combined=False, gather_mode="layer", placement=0):
     """selections: optional {g: list of int32 [n_sets][k]} overriding the trace's.
 
     The state is exported (which writes any staged evicted rows out to the host
@@ -65,18 +65,19 @@ def run_parity(wl, steps=None, selections=None, max_append=4096, groups=None, ch
     gather_mode: "layer" (one ula_gather per layer), "all" (one ula_gather_layers
     for every layer) or "split" (layer 0 alone, the later layers in one
     ula_gather_layers call).
+    placement: 0 (appends into the lowest free slots) or 1 (into the current bucket).
     """
     import torch
     tr = Trace(wl, steps)
     groups = list(range(wl.groups)) if groups is None else groups
     say(f"parity {wl.name}: N={tr.N} P={tr.P} H={tr.H} groups={groups} steps={tr.steps}")
-    eng = engine_for(tr, max_append=max_append)
+    eng = engine_for(tr, max_append=max_append, placement=placement)
     rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
     try:
         initial_load(eng, tr, groups, rows)
         ora = {}
         for g in groups:
-            ora[g] = new_group(tr, full_data=True)
+            ora[g] = new_group(tr, full_data=True, placement="ring" if placement else "lowest")
             oracle_load(ora[g], tr, g)
             assert_same_state(eng.export_state(g), ora[g].export_state(), f"group {g} after load")
         sels = {g: (iter(selections[g]) if selections else tr.selections(g)) for g in groups}

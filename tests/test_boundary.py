@@ -65,7 +65,8 @@ def test_sizes_cover_pools():
     dict(gpu_slots=0), dict(host_slots=-1), dict(num_groups=0), dict(max_k=0),
     dict(logical_capacity=0), dict(gpu_slots=2 ** 31 - 10, host_slots=100),
     dict(max_sets=1 << 16, max_k=1 << 16), dict(policy=2), dict(policy=-1), dict(max_append=0),
-    dict(layers_per_group=0), dict(layers_per_group=257), dict(row_bytes=4112)])
+    dict(layers_per_group=0), dict(layers_per_group=257), dict(row_bytes=4112),
+    dict(placement=2), dict(placement=-1), dict(placement=1, policy=1)])
 def test_bad_configs_rejected_on_host(bad):
     L = ula.lib()
     c = _cfg(**bad)

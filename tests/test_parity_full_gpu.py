@@ -21,6 +21,10 @@ step; the stored rows of sampled addresses (wherever they live, GPU or host
 pool) are read back every eighth step and after the last, which writes the
 staged rows out first.
 
+The second placement of appended entries (into the current bucket, evicting)
+is checked the same way against the oracle's placement "ring"
+(tests/golden/digests_ring_<workload>.json).
+
 The exact-LRU policy is checked the same way against the array form of the
 oracle's exact LRU (tests/golden/digests_lru_<workload>.json, timestamps
 included), on every workload and on three of the 24 groups of the largest.
@@ -44,8 +48,9 @@ pytestmark = pytest.mark.gpu
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def _golden(name, policy=0):
-    fname = f"digests_lru_{name}.json" if policy else f"digests_{name}.json"
+def _golden(name, policy=0, placement=0):
+    fname = f"digests_lru_{name}.json" if policy else (
+        f"digests_ring_{name}.json" if placement else f"digests_{name}.json")
     with open(os.path.join(HERE, "golden", fname)) as f:
         return json.load(f)
 
@@ -56,17 +61,19 @@ def _cmp(got, want, where):
             assert got[k] == want[k], f"{where}: {k} differs (engine {got[k]}, oracle {want[k]})"
 
 
-def run_group(name: str, g: int, samples: int = 128, policy: int = 0, bench_calls: bool = True):
+def run_group(name: str, g: int, samples: int = 128, policy: int = 0, bench_calls: bool = True,
+              placement: int = 0):
     import torch
     from serving_pb_lru_amd import Engine
     from synth.device import rows_device
 
     wl = preset(name)
     tr = Trace(wl)
-    gold = _golden(name, policy)["groups"][g]
-    say(f"full parity {name} group {g} policy {policy}: N={tr.N} P={tr.P} H={tr.H} steps={tr.steps}")
+    gold = _golden(name, policy, placement)["groups"][g]
+    say(f"full parity {name} group {g} policy {policy} placement {placement}: N={tr.N} P={tr.P} "
+        f"H={tr.H} steps={tr.steps}")
     eng = Engine(1, wl.layers, wl.row_bytes, wl.ring, tr.N, tr.P, tr.H, tr.n_sets, tr.k,
-                 max_append=1 << 16, policy=policy)
+                 max_append=1 << 16, policy=policy, placement=placement)
     rows = lambda las: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
     rng = np.random.default_rng([g, 2024])
     try:
@@ -137,3 +144,17 @@ LRU_CASES = ([("tiny_4x4k", 0), ("r16_64k_g1x3", 0)]
 @pytest.mark.parametrize("name,g", LRU_CASES, ids=[f"lru-{n}-g{g}" for n, g in LRU_CASES])
 def test_full_size_lru_parity(name, g):
     run_group(name, g, policy=1, bench_calls=False)
+
+
+# appends placed in the current bucket (ULA_PLACE_RING) against the oracle's
+# placement "ring" (tests/golden/digests_ring_<workload>.json)
+RING_CASES = ([("tiny_4x4k", 0), ("r16_64k_g1x3", 0)]
+              + [("r64_64k128k_g24x3", g) for g in (0, 23)]
+              + [("spec3_r128_64k128k_g4", g) for g in range(4)]
+              + [("evict_r256_128k_g2", g) for g in range(2)]
+              + [("evict_r256_128k_g2_ctl98", g) for g in range(2)])
+
+
+@pytest.mark.parametrize("name,g", RING_CASES, ids=[f"ring-{n}-g{g}" for n, g in RING_CASES])
+def test_full_size_ring_placement_parity(name, g):
+    run_group(name, g, placement=1)
