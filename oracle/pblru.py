@@ -3,18 +3,17 @@
 Source: UlaCache summary (paper-daily.com, "UlaCache: Unified Logical
 Addressing for Sparse LLM Serving").
 
-* Section 2 (unified logical addresses): every KV entry has a fixed logical
-  address; a mapping table records the GPU slot or CPU slot holding it; a move
-  changes only the mapping. In DP mode a GPU has one GPU pool and one CPU pool,
-  and an entry lives in exactly one of them, never both. Layers that share a
-  selection do the lookup and de-duplication once per group.
-* Section 3 (PB-LRU): every slot accessed in the same scheduling round goes
-  into the same bucket; each layer group keeps a ring of recent buckets and a
-  cold bucket; each round the current bucket advances by one and whatever is
-  left in the bucket about to be reused moves to cold (labels only, no data
-  moves); victims are free slots first, then the cold bucket, then the ring
-  buckets from oldest to newest, never the current bucket. Data moves first,
-  then the mapping is updated and completion is signalled.
+* Section 2 (unified logical addresses): an entry's logical address never
+  changes; a table maps it to the GPU or host slot that holds it, so moving an
+  entry means copying its rows and rewriting one table entry. In the DP form
+  there is one GPU pool and one host pool per GPU and each entry is in one of
+  them only. A layer group resolves and de-duplicates its shared selection once.
+* Section 3 (PB-LRU): the slots touched in one scheduling round share a bucket;
+  a group has a ring of such buckets and one cold bucket. Each round moves the
+  ring index on; the slots still labelled with the bucket being reused become
+  cold, a relabelling only. Victims are taken from free slots, then cold, then
+  the other ring buckets by age, never from the running round's bucket. Rows
+  move before the table changes, and a completion signal comes last.
 
 Readings where the pages are silent (each restated where it is used):
 
@@ -262,8 +261,8 @@ class PBLRUGroup:
         if U.size > self.P:
             raise OracleError("ECAPACITY", "more unique entries than GPU slots")
 
-        # S5 the current bucket advances one position; the survivors of the
-        # bucket about to be reused move to cold (labels only) (section 3)
+        # S5 the ring index moves on; slots still labelled with the reused
+        # bucket become cold, a relabelling only (section 3)
         self.cur = (self.cur + 1) % self.B
         self.cold |= self.ring[self.cur]
         self.ring[self.cur] = False
@@ -281,7 +280,7 @@ class PBLRUGroup:
         victims = candidates[:m]
         assert victims.size == m   # guaranteed by S4: |free|+|cold|+|other rings| >= P - |hits| >= m
 
-        # S8 move the data first (section 3): the missed rows come from the host,
+        # S8 rows before the table (section 3): the missed rows come from the host,
         # the victims' rows go to the host slot the miss vacated. Pairs are
         # disjoint (distinct victims, distinct host slots), so the moves commute.
         owners = self.gown[victims].astype(np.int64)
