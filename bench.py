@@ -754,7 +754,7 @@ def main():
         link_line = {"bound": "host-link", "kernel": "k_lru_pass (first pass)" if policy else "k_mark",
                      "achieved": rnd(l_gbs, 2), "peak": round(LINK_PEAK_GBS, 1), "unit": "GB/s per direction",
                      "frac": rnd(None if l_gbs is None else l_gbs / LINK_PEAK_GBS, 4),
-                     "traffic": link_traffic(wl.name) if not policy else None,
+                     "traffic": None,
                      "bytes_per_launch": round(per_launch),
                      "h2d_bytes_per_launch": round(up / launches), "d2h_bytes_per_launch": round(down / launches),
                      "launch_ms": round(l_ms, 5),
@@ -762,6 +762,10 @@ def main():
                              "evicted row of the previous step out; both directions move "
                              "concurrently) over the launch's average duration, which also marks "
                              "hits and plans and extracts the victims"}
+        counted = link_traffic(wl.name) if not policy else None
+        if counted:   # counted host-link bytes per launch, the roofline's direction and both
+            link_line["traffic"] = counted["read"] if up >= down else counted["write"]
+            link_line["traffic_read_write"] = [counted["read"], counted["write"]]
         t_in = r["link_ms_total"] * 1e-3
         gin = up / t_in / 1e9 if t_in > 0 else None
         gout = down / t_in / 1e9 if t_in > 0 else None

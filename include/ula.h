@@ -147,12 +147,17 @@ typedef struct {             /* caller-allocated host buffers filled by ula_expo
 } ula_state_host;
 
 /* Bytes of device workspace / pinned host pool a configuration needs; 0 for an
- * invalid configuration. Pure host functions (no device is touched). */
+ * invalid configuration (section 2: in DP mode each GPU has one GPU pool and one
+ * host pool; here every layer group has its own of each, plus its mapping table
+ * and replacement state in the workspace). Pure host functions (no device is
+ * touched). */
 size_t ula_device_bytes(const ula_config* cfg);
 size_t ula_host_bytes(const ula_config* cfg);
 
 /* Lay out the workspace, initialise every group (nothing appended, all GPU slots
- * free, all host slots free, cur = 0, flag = 0) on `stream`, and return a context.
+ * free, all host slots free, cur = 0, flag = 0) on `stream`, and return a context
+ * (section 2: the pools and the mapping table; section 3: one ring plus a cold
+ * bucket per layer group).
  * dev_ws: device memory of ula_device_bytes(cfg) bytes, 256-byte aligned.
  * host_pinned: pinned, device-mapped host memory of ula_host_bytes(cfg) bytes
  * (may be NULL when host_slots == 0). Errors: ULA_EINVAL, ULA_EHIP. */
@@ -282,8 +287,10 @@ int ula_gather_layers(ula_ctx* ctx, int32_t group, int32_t layer0, int32_t n_lay
                       int32_t k, const int32_t* sel_dev, void* out_dev, uint64_t stream);
 
 /* Wait for `stream`, then report the first latched device error of any group
- * (poisoning the context) or ULA_OK. per_group_out (nullable, num_groups
- * entries) receives each group's last step statistics. */
+ * (poisoning the context) or ULA_OK (section 3: a host waiter for the steps'
+ * completion). per_group_out (nullable, num_groups entries) receives each
+ * group's last step statistics (section 4: the GPU hit rate is hits over
+ * distinct selected entries). Errors: ULA_EINVAL, ULA_EHIP, or the latched code. */
 int ula_sync(ula_ctx* ctx, uint64_t stream, ula_step_stats* per_group_out);
 
 /* Copy group g's canonical state (mapping table, owners, bucket bitsets, the
@@ -297,7 +304,7 @@ int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out);
 
 /* Read back the stored rows (all layers, layers_per_group x row_bytes bytes
  * each) of n appended entries of group g into host memory, from whichever pool
- * holds them (writes any staged evicted rows to the host pool and synchronises
+ * holds them (for checks of stored data; no passage of the pages behind it) (writes any staged evicted rows to the host pool and synchronises
  * the device first). ULA_ERANGE if an address was never
  * appended. */
 int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host,
@@ -331,14 +338,17 @@ int ula_read_timing(ula_ctx* ctx, int32_t group, float* ms_out3);
 int ula_read_gather_timing(ula_ctx* ctx, double* kernel_ms, int64_t* launches);
 int ula_read_link_timing(ula_ctx* ctx, double* kernel_ms, int64_t* launches);
 
-/* Release the context (not the caller's buffers). Waits for no stream. */
+/* Release the context (not the caller's buffers). Waits for no stream.
+ * Resource management only; no passage of the pages behind it. */
 int ula_destroy(ula_ctx* ctx);
 
-/* Text of an error code (also the last HIP error text for ULA_EHIP). */
+/* Text of an error code (also the last HIP error text for ULA_EHIP). Plumbing;
+ * no passage of the pages behind it. */
 const char* ula_strerror(int code);
 
 /* Pinned, device-mapped host memory for the host pool (hipHostMalloc);
- * NULL on failure. ula_host_free returns ULA_OK or ULA_EHIP. */
+ * NULL on failure. ula_host_free returns ULA_OK or ULA_EHIP. Plumbing (section
+ * 2's host pool lives in it). */
 void* ula_host_alloc(size_t bytes);
 int ula_host_free(void* p);
 
