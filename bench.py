@@ -549,10 +549,9 @@ def copy_peaks(gib: float = 1.0) -> dict:
 
 
 def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
-    """Later-layer prefetch on a second stream (UlaCache summary, section 2: the
-    lookup and de-duplication run once per layer group, and while the current
-    layer computes a separate stream fetches the data of the group's later
-    layers). Here a step moves every layer of a missed entry at once, so the
+    """Later-layer prefetch on a second stream (UlaCache summary, section 2: one
+    lookup and de-duplication serves a whole layer group, and a second stream
+    brings in the group's later layers during the compute of an earlier one). Here a step moves every layer of a missed entry at once, so the
     later layers' gathers are what a second stream can take off the critical path.
 
     Two schedules of the same steps, each group's layers followed by a synthetic
@@ -562,7 +561,11 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
                 on a second stream ordered after the step by an event; layer l's
                 compute waits for its gather's event;
       prefetch_one_launch  as prefetch, with layers 1.. gathered by one
-                ula_gather_layers launch (one event for all of them).
+                ula_gather_layers launch (one event for all of them);
+      prefetch_flag  as prefetch_one_launch, but the second stream is gated on the
+                device by the group's completion counter (hipStreamWaitValue64 on
+                ula_flag_address reaching the step) instead of an event recorded
+                after the step on the main stream.
     Two stand-ins for the compute: a single-lane spin (occupies no resources: the
     upper bound of what overlap can hide) and a bf16 matrix product sized to the
     same duration (occupies the matrix cores of the whole chip, like attention
@@ -611,13 +614,21 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
     stand_ins = {"spin": (lambda: torch.cuda._sleep(spin_cycles), timed(lambda: torch.cuda._sleep(spin_cycles))),
                  "bf16_matmul": (lambda: torch.mm(xa, xb), mm_us)}
 
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")   # the HIP runtime torch has loaded
+    hip.hipStreamWaitValue64.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_uint,
+                                         ctypes.c_uint64]
+    hip.hipStreamWaitValue64.restype = ctypes.c_int
+    WAIT_GTE = 0x0
+
     results = []
     for kind, (compute, c_us) in stand_ins.items():
         per = {}
-        for sched in ("serial", "prefetch", "prefetch_one_launch"):
+        for sched in ("serial", "prefetch", "prefetch_one_launch", "prefetch_flag"):
             eng = engine_for(tr, max_append=1 << 16)
             initial_load(eng, tr, groups, rows)
             torch.cuda.synchronize()
+            flags = [eng.flag_address(g) for g in groups]
 
             def step(t):
                 for g in groups:
@@ -629,11 +640,19 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
                             compute()
                         continue
                     eng.gather(g, 0, sel, out=outs[g][0])
-                    after_step = torch.cuda.Event()
-                    after_step.record(main_s)
-                    side_s.wait_event(after_step)
+                    if sched == "prefetch_flag":
+                        # the step of group g is its t-th: wait on the device for its
+                        # counter (a failed step sets a bit that also releases this)
+                        rc = hip.hipStreamWaitValue64(ctypes.c_void_p(side_s.cuda_stream),
+                                                      ctypes.c_void_p(flags[g]), t, WAIT_GTE,
+                                                      0xFFFFFFFFFFFFFFFF)
+                        assert rc == 0, rc
+                    else:
+                        after_step = torch.cuda.Event()
+                        after_step.record(main_s)
+                        side_s.wait_event(after_step)
                     ready = []
-                    if sched == "prefetch_one_launch" and wl.layers > 1:
+                    if sched in ("prefetch_one_launch", "prefetch_flag") and wl.layers > 1:
                         eng.gather_layers(g, 1, wl.layers - 1, sel, out=outs[g][1:], stream=side_s)
                         ev = torch.cuda.Event()
                         ev.record(side_s)
@@ -672,10 +691,13 @@ def layer_prefetch(tr, W: int, K: int, compute_us: float) -> list:
             "layers_per_group": wl.layers, "groups": wl.groups, "steps": K, "warmup": W,
             "serial_ms_per_step": round(per["serial"], 5), "prefetch_ms_per_step": round(per["prefetch"], 5),
             "prefetch_one_launch_ms_per_step": round(per["prefetch_one_launch"], 5),
+            "prefetch_flag_ms_per_step": round(per["prefetch_flag"], 5),
+            "hidden_us_per_step_flag": round((per["serial"] - per["prefetch_flag"]) * 1e3, 2),
             "hidden_us_per_step": round((per["serial"] - per["prefetch"]) * 1e3, 2),
             "hidden_us_per_step_one_launch": round((per["serial"] - per["prefetch_one_launch"]) * 1e3, 2),
             "host_enqueue_ms_per_step": {k: round(per[k + "_host"], 5)
-                                         for k in ("serial", "prefetch", "prefetch_one_launch")},
+                                         for k in ("serial", "prefetch", "prefetch_one_launch",
+                                                   "prefetch_flag")},
             "compute_only_ms_per_step": round(c_us * wl.layers * wl.groups * 1e-3, 5)})
     return results
 

@@ -12,8 +12,8 @@
  *    pools. Layers that share one sparse selection look up and de-duplicate
  *    it once per layer group.
  *  - Section 3: the GPU pool is managed by PB-LRU: slots are labelled with the
- *    scheduling round that last touched them (a ring of recent buckets plus one
- *    cold bucket per layer group, each a bitmap with summaries); victims come
+ *    scheduling round that last touched them (per layer group, a ring of round
+ *    buckets and one cold bucket, each a bitmap with summaries); victims come
  *    from free slots, then cold, then older ring buckets, never the running
  *    round's bucket. Rows move before the mapping changes, the completion
  *    signal comes last, and readers wait for it.
@@ -311,7 +311,13 @@ int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host
                   void* out_host);
 
 /* Device address of group g's completion counter (int64, equals the last
- * completed step), for hipStreamWaitValue64 on another stream. */
+ * completed step), for hipStreamWaitValue64 on another stream (section 3:
+ * readers wait for the completion signal). A step that fails on the device
+ * leaves the last completed step in the counter and sets bit 62, so a stream
+ * waiting for the counter to be greater than or equal to that step's number is
+ * released rather than left waiting; a gather it then issues is refused, and
+ * ula_sync reports the failure. ula_export_state reports the counter without
+ * that bit. */
 int ula_flag_address(ula_ctx* ctx, int32_t group, void** dev_ptr);
 
 /* Timing, off by default; ula_set_timing takes an OR of these flags (ULA_EINVAL

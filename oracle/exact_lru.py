@@ -1,8 +1,8 @@
 """Exact LRU over one GPU pool plus one host pool, by brute force (oracle; tests only).
 
 Source: UlaCache summary (paper-daily.com, "UlaCache: Unified Logical
-Addressing for Sparse LLM Serving"), section 3: standard LRU keeps one
-timestamp per slot and scans the whole pool to choose victims; section 4
+Addressing for Sparse LLM Serving"), section 3: the textbook LRU it compares against stamps every slot with
+its last use and looks at every slot of the pool when it picks victims; section 4
 reports that PB-LRU's GPU hit rate on replayed traces stays within 0.1
 percentage point of exact LRU.
 

@@ -1,8 +1,8 @@
 // Exact-LRU victim selection: one timestamp per GPU slot and a scan of the
 // whole pool every step (the standard policy the pages compare PB-LRU against).
 //
-// UlaCache summary (paper-daily.com), section 3: standard LRU keeps one
-// timestamp per slot and scans the whole pool to choose its victims, the cost
+// UlaCache summary (paper-daily.com), section 3: textbook LRU stamps each slot
+// with its last use and passes over the whole pool to pick victims, the cost
 // PB-LRU's buckets avoid; section 4 compares the two (hit rate within 0.1 point,
 // PB-LRU 1.5-2.3x faster to schedule at large batch, LRU faster when little is
 // replaced). Lookup, pairing, data movement, commit and signal are shared with

@@ -178,9 +178,17 @@ __global__ __launch_bounds__(512) void k_swap_commit(GroupDev g, uint32_t t, Fas
 // store needs no release of its own: the swap's writes were made visible at
 // the end of its kernel, before this one started, and this kernel's end makes
 // the counter visible to other streams and the host.
+// A step that failed on the device leaves the counter at the last completed
+// step but sets kFlagFailed in it, so that a stream waiting for the counter to
+// reach this step (hipStreamWaitValue64, "greater or equal") is released
+// instead of waiting forever; a gather it then runs finds the latched status
+// and refuses.
 __global__ __launch_bounds__(64) void k_publish(GroupDev g, uint32_t t) {
-  if (threadIdx.x == 0 && !status_of(g.ctr))
+  if (threadIdx.x != 0) return;
+  if (!status_of(g.ctr))
     __hip_atomic_store(&g.ctr->flag, (long long)t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    __hip_atomic_fetch_or(&g.ctr->flag, kFlagFailed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Stand-alone write-back of whatever rows the last swap staged, for when the

@@ -885,10 +885,10 @@ int ula_export_state(ula_ctx* ctx, int32_t group, ula_state_host* out) {
   }
   Counters c;
   HIP_TRY(hipMemcpy(&c, g.ctr, sizeof(Counters), hipMemcpyDeviceToHost));
-  out->flag = c.flag;
+  out->flag = c.flag & ~kFlagFailed;   // the last completed step
   // derived, not read back: the ring advances once per step, so after step t the
   // current bucket is t mod B (the bucket bitsets show where the step's entries went)
-  out->cur = (int32_t)(c.flag % d.B);
+  out->cur = (int32_t)(out->flag % d.B);
   fill_stats(c, &out->last);
   return ULA_OK;
 }

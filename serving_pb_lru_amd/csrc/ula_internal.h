@@ -38,6 +38,7 @@
 namespace ula {
 
 constexpr uint32_t kAbsent = 0xFFFFFFFFu;
+constexpr long long kFlagFailed = 1ll << 62;    // completion counter: a step failed on the device
 constexpr uint32_t kHostBit = 0x80000000u;
 constexpr int kWave = 64;
 constexpr int kTileWords = 64;                  // bitmap words per summary span

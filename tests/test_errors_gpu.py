@@ -453,6 +453,49 @@ def test_engine_on_dirty_workspace_matches_oracle():
     run_parity(wl, max_append=4096)
 
 
+def test_failed_step_marks_the_counter_and_releases_a_waiter():
+    """A step that fails on the device (an address never appended) leaves the last
+    completed step in the completion counter and sets bit 62, so a stream waiting
+    for the counter to reach that step is released. The counter is read with the
+    device idle before any wait is enqueued, so the wait is known to end; the
+    gather behind it is refused and ula_sync reports the step's error."""
+    import ctypes
+    import torch
+    hip = ctypes.CDLL("libamdhip64.so.7")   # the runtime torch has already loaded
+    hip.hipStreamWaitValue64.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                         ctypes.c_uint, ctypes.c_uint64]
+    hip.hipStreamWaitValue64.restype = ctypes.c_int
+    hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    hip.hipMemcpy.restype = ctypes.c_int
+    wait_gte = 0x0
+    tr, eng, rows = _engine()
+    try:
+        sels = tr.selections(0)
+        sel = next(sels)
+        app = tr.appends(1)
+        eng.append(0, app, rows(app, 0))
+        eng.step(0, _cuda(sel))
+        eng.sync()
+        bad = next(sels).copy()
+        bad.reshape(-1)[3] = tr.N - 1            # never appended (the last step's position)
+        eng.step(0, _cuda(bad))
+        torch.cuda.synchronize()
+        raw = ctypes.c_int64()
+        assert hip.hipMemcpy(ctypes.byref(raw), ctypes.c_void_p(eng.flag_address(0)), 8, 2) == 0
+        assert raw.value == (1 << 62) | 1, hex(raw.value)
+        side = torch.cuda.Stream()
+        rc = hip.hipStreamWaitValue64(ctypes.c_void_p(side.cuda_stream), ctypes.c_void_p(eng.flag_address(0)),
+                                      2, wait_gte, 0xFFFFFFFFFFFFFFFF)
+        assert rc == 0, rc
+        eng.gather(0, 0, _cuda(bad), stream=side)
+        torch.cuda.synchronize()
+        assert eng.sync_code() == -2              # ERANGE, the step's error
+        st = eng.export_state(0)
+        assert st["flag"] == 1                    # exported without the failure bit
+    finally:
+        eng.close()
+
+
 @pytest.mark.parametrize("policy", [0, 1], ids=["pblru", "lru"])
 def test_timing_modes_count_and_change_nothing(policy):
     """Gather timing and link timing record one kernel duration per launch (one

@@ -1,7 +1,7 @@
 """Exact-LRU policy of the HIP engine against the oracle's brute-force exact LRU (GPU).
 
-UlaCache summary (paper-daily.com), sections 3-4: standard LRU keeps one
-timestamp per slot and scans the whole pool for its victims; it is the policy
+UlaCache summary (paper-daily.com), sections 3-4: textbook LRU, a last-use stamp
+on every slot and a pass over the whole pool to pick victims, is the policy
 PB-LRU is compared against. The engine's exact-LRU mode (select passes over the
 whole pool, slot-ordered emission, stable radix sort) must pick the same
 victims in the same order as the oracle's plain scan-and-sort, so after every
