@@ -87,6 +87,9 @@ def parse():
     p.add_argument("--placement", choices=("lowest", "ring"), default="lowest",
                    help="where appended entries go: the lowest free slot, GPU first, never evicting "
                         "(default), or the current bucket, evicting (PB-LRU only)")
+    p.add_argument("--streams", choices=("one", "group"), default="one",
+                   help="one stream for every group's calls (default), or a stream per group, so "
+                        "that one group's HBM phases can run beside another's host-link launch")
     p.add_argument("--gather", choices=("layer", "split", "all"), default="split",
                    help="gathers per group step: one per layer (ula_gather); layer 0 alone, then the "
                         "later layers in one ula_gather_layers launch (default); or every layer in "
@@ -389,7 +392,7 @@ def gather_all_layers(eng, g, sel, outs, layers, mode, stream=None):
 
 
 def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str = "layer",
-            replays: int = 3, placement: int = 0) -> dict:
+            replays: int = 3, placement: int = 0, per_group_streams: bool = False) -> dict:
     import statistics
 
     import torch
@@ -412,13 +415,25 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
     outs = {g: torch.empty((wl.layers, tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
             for g in groups}
 
+    gstreams = [torch.cuda.Stream() for _ in groups] if per_group_streams else [stream for _ in groups]
+
+    def fork():   # the group streams start after what the main stream has recorded
+        for gs in gstreams:
+            if gs is not stream:
+                gs.wait_stream(stream)
+
+    def join():   # and the main stream continues after all of them
+        for gs in gstreams:
+            if gs is not stream:
+                stream.wait_stream(gs)
+
     def run_step(eng, t):
         for g in groups:
             sel = sels[g][t - 1]
             # the step's appends and the step in one call (the appends run in the
             # step's first launch when they are small)
-            eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel)
-            gather_all_layers(eng, g, sel, outs[g], wl.layers, gather_mode)
+            eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel, stream=gstreams[g])
+            gather_all_layers(eng, g, sel, outs[g], wl.layers, gather_mode, stream=gstreams[g])
 
     # every step kernel runs once on a tiny engine first, so that the first
     # timed step does not also pay for loading kernel code
@@ -444,8 +459,10 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
         for t in range(1, W + 1):
             if t == 1:
                 s1.record()
+                fork()
             run_step(eng, t)
             if t == 1:
+                join()
                 e1.record()
                 torch.cuda.synchronize()
                 first_ms = s1.elapsed_time(e1)
@@ -460,9 +477,11 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
         end = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record()
+        fork()
         t0 = time.perf_counter()
         for t in range(W + 1, W + K + 1):
             run_step(eng, t)
+        join()
         end.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -741,7 +760,7 @@ def main():
     gather_mode = args.gather if wl.layers > 1 else "layer"   # one layer: the same launch
     placement = 1 if args.placement == "ring" else 0
     r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode, replays=args.replays,
-                placement=placement)
+                placement=placement, per_group_streams=args.streams == "group")
     value = per_step * K / r["wall_s"]
     ms_per_step = r["event_ms"] / K
     replay_values = [round(per_step * K / w, 1) for w in r["replay_walls_s"]]
@@ -820,7 +839,7 @@ def main():
                    "layers_per_group": wl.layers, "k": wl.k, "gpu_slots": tr.P, "host_slots": tr.H,
                    "ring": wl.ring, "row_bytes": wl.row_bytes, "overlap": wl.overlap,
                    "policy": "exact LRU" if policy else "PB-LRU", "gather": gather_mode,
-                   "placement": args.placement,
+                   "placement": args.placement, "streams": args.streams,
                    "row_layers_per_step": per_step},
         "roofline": roofline,
         "roofline_other": other,
