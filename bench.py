@@ -87,9 +87,10 @@ def parse():
     p.add_argument("--placement", choices=("lowest", "ring"), default="lowest",
                    help="where appended entries go: the lowest free slot, GPU first, never evicting "
                         "(default), or the current bucket, evicting (PB-LRU only)")
-    p.add_argument("--streams", choices=("one", "group"), default="one",
-                   help="one stream for every group's calls (default), or a stream per group, so "
-                        "that one group's HBM phases can run beside another's host-link launch")
+    p.add_argument("--streams", choices=("one", "group"), default="group",
+                   help="a stream per group (default), so that one group's HBM phases run beside "
+                        "another's host-link launch (the library keeps the host-link launches one "
+                        "at a time), or one stream for every group's calls")
     p.add_argument("--gather", choices=("layer", "split", "all"), default="split",
                    help="gathers per group step: one per layer (ula_gather); layer 0 alone, then the "
                         "later layers in one ula_gather_layers launch (default); or every layer in "
@@ -507,15 +508,20 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
     if phases:
         eng = engine_for(tr, max_append=1 << 16, policy=policy, placement=placement)
         initial_load(eng, tr, groups, rows)
-        eng.set_timing(True)
+        eng.set_timing(eng.TIMING_STEP | eng.TIMING_GATHER)
         torch.cuda.synchronize()
         ph = np.zeros(3)
         h2d = d2h = hits = uniq = 0
         n = 0
         prev_evict = {g: 0 for g in groups}
         for t in range(1, W + K + 1):
+            if t == W + 1:
+                eng.read_gather_timing()   # from here on: the timed steps' gathers
             for g in groups:
                 eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sels[g][t - 1])
+                # the gathers alone: one group at a time, right behind its step on
+                # the same stream (as in the timed steps, so no idle queue before them)
+                gather_all_layers(eng, g, sels[g][t - 1], outs[g], wl.layers, gather_mode)
                 # [0] includes a small append (it runs in the lookup's first launch);
                 # [1] also moves this step's misses in, last step's evictions out
                 ms = eng.read_timing(g)
@@ -528,8 +534,10 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
                     uniq += st[0]
                     n += 1
                 prev_evict[g] = st[3]
+        g_alone_ms, g_alone_n = eng.read_gather_timing()
         eng.close()
         note("gpu per-phase replay done")
+        res.update(gather_alone_ms=g_alone_ms / max(g_alone_n, 1), gather_alone_launches=g_alone_n)
         res.update(phase_ms=(ph / max(n, 1)).tolist(), link_ms_total=float(ph[1]),
                    h2d_rows=int(h2d), d2h_rows=int(d2h), group_steps=n,
                    hit_rate=hits / uniq if uniq else None)
@@ -767,17 +775,24 @@ def main():
     rnd = lambda x, d: None if x is None else round(x, d)
 
     # ---- the gather against HBM peak ------------------------------------------
-    g_ms = float(r["gather_ms"])
+    # its own duration: from the per-phase replay, where every gather runs alone
+    # (in the timed steps a group's gathers run beside another group's host-link
+    # launch, hidden under it and slowed by it)
+    g_ms = float(r.get("gather_alone_ms") or r["gather_ms"])
     # algorithmic bytes per launch: every gathered row-layer of the timed region
     # over the gather launches that moved them
     launches_per_group_step = {"layer": wl.layers, "all": 1, "split": 2}[gather_mode]
     g_bytes = 2 * wl.row_bytes * tr.n_sets * tr.k * wl.layers / launches_per_group_step
     assert r["gather_launches"] == K * wl.groups * launches_per_group_step, r["gather_launches"]
+    if "gather_alone_launches" in r:
+        assert r["gather_alone_launches"] == K * wl.groups * launches_per_group_step, r["gather_alone_launches"]
     g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
     gather_line = {"bound": "hbm", "kernel": "k_gather", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
                    "traffic": gather_traffic(wl.name, gather_mode),
                    "bytes_per_launch": round(g_bytes), "launch_ms": round(g_ms, 5),
+                   "launch_ms_in_timed_steps": round(float(r["gather_ms"]), 5),
+                   "measured": "alone (per-phase replay)" if r.get("gather_alone_ms") else "timed steps",
                    "layers_per_launch": round(wl.layers / launches_per_group_step, 3)}
 
     # ---- the host-link launch (k_mark) against the link's per-direction peak ---

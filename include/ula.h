@@ -55,7 +55,11 @@
  *    after it is the state before the failed step.
  *
  * Threading: a context belongs to one host thread. Groups are independent and
- * may be driven on different streams; calls on one group must be ordered.
+ * may be driven on different streams; calls on one group must be ordered. The
+ * groups share one host link, so once steps arrive on more than one stream the
+ * library orders each step's host-link launch after the previous step's (of any
+ * group) with an event; the rest of one group's step (lookup, swap, gathers)
+ * still runs beside another group's host-link launch.
  */
 #ifndef ULA_H
 #define ULA_H
@@ -179,8 +183,10 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
  * itself is ordinary host memory; host_pinned is still the caller's pool). Such
  * a context has no pinned staging buffers, so ula_append of more than 256
  * entries or of host-resident rows, and ula_release, copy addresses and rows
- * from the caller's memory and wait for the copy before they return. Everything
- * else behaves as for a context from ula_init.
+ * from the caller's memory and wait for the copy before they return; the events
+ * of step timing and of the ordering of host-link launches across streams are
+ * created by the call that first needs them. Everything else behaves as for a
+ * context from ula_init.
  * Errors: ULA_EINVAL, ULA_ETOOBIG, ULA_EBUSY, ULA_EHIP. */
 int ula_init_static(const ula_config* cfg, void* host_pinned, uint64_t stream, ula_ctx** out);
 

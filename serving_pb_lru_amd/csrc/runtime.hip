@@ -199,6 +199,14 @@ struct ula_ctx {
   std::vector<GroupHost> groups;
   int poisoned = 0;
   int static_dev = -1;               // device whose static workspace the context holds, or -1
+  // Host-link launches of different groups share one link: once steps arrive on
+  // more than one stream, each step's host-link launch records link_ev and the
+  // next one on another stream waits for it, so they never run at once (the
+  // rest of a group's step still overlaps another group's).
+  hipStream_t first_step_stream = nullptr;
+  bool multi_stream = false;
+  hipEvent_t link_ev = nullptr;
+  hipStream_t link_ev_stream = nullptr;   // stream of the launch link_ev last recorded
   int timing = 0;                    // ULA_TIMING_* flags
   // kernel durations of the gathers and of the steps' host-link launches: rings
   // of dispatch-recorded event pairs, summed lazily (when a ring wraps, and by
@@ -324,6 +332,7 @@ int ula_host_free(void* p) {
 
 static void destroy_ctx(ula_ctx* ctx) {
   release_static_workspace(ctx->static_dev);
+  if (ctx->link_ev) (void)hipEventDestroy(ctx->link_ev);
   for (TimingRing* r : {&ctx->gather_t, &ctx->link_t})
     for (hipEvent_t e : r->ev)
       if (e) (void)hipEventDestroy(e);
@@ -737,6 +746,14 @@ static int step_impl(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, con
     int rc = next_timing_pair(ctx->link_t, &lk0, &lk1);
     if (rc) return rc;
   }
+  // one host-link launch at a time across streams (see ula_ctx)
+  if (!ctx->first_step_stream) ctx->first_step_stream = s;
+  if (s != ctx->first_step_stream && !ctx->multi_stream) {
+    ctx->multi_stream = true;
+    HIP_TRY(hipEventCreateWithFlags(&ctx->link_ev, hipEventDisableTiming));
+  }
+  if (ctx->multi_stream && ctx->link_ev_stream && ctx->link_ev_stream != s)
+    HIP_TRY(hipStreamWaitEvent(s, ctx->link_ev, 0));
   if (g.policy == ULA_POLICY_LRU) {
     // exact LRU: select passes over the whole pool (the first launch also carries
     // the host-link work), then the victim list in order
@@ -746,6 +763,10 @@ static int step_impl(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, con
     // marking, victim plan and extraction, with the missed rows read in and the
     // previous step's evicted rows written out, in one launch
     HIP_TRY(launch_mark(g, (uint32_t)t, cur, a, max_pairs, wb_pairs, s, lk0, lk1));
+  }
+  if (ctx->multi_stream) {
+    HIP_TRY(hipEventRecord(ctx->link_ev, s));
+    ctx->link_ev_stream = s;
   }
   if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
   HIP_TRY(launch_swap_commit(g, (uint32_t)t, max_pairs, s));
