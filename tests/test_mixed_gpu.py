@@ -1,7 +1,10 @@
 """Randomised parity across the engine's paths at once (GPU).
 
 Each seed draws a small workload with one to three layer groups, one of the two
-policies, a random ring, and per step and group a random way to append: rows in
+policies (under PB-LRU one of the two placements of appended entries), a random
+ring, one stream for every group or a stream per group (the library then runs
+the groups' host-link launches one at a time), and per step and group a random
+way to append: rows in
 device memory or in host memory, with a per-call append limit small enough that
 most appends run in several chunks (the plan / extract / place kernels) and the
 rest in the one-workgroup path, through ula_append before ula_step or through
@@ -25,11 +28,11 @@ from tracegen import padded_selections, release_plan, tiny_workload
 pytestmark = pytest.mark.gpu
 
 
-def _oracle(tr, g, policy):
+def _oracle(tr, g, policy, placement=0):
     from oracle.exact_lru_np import ExactLRUArrays
     from oracle.replay import initial_load, new_group
     if policy == 0:
-        o = new_group(tr, full_data=True)
+        o = new_group(tr, full_data=True, placement="ring" if placement else "lowest")
         initial_load(o, tr, g)
     else:
         o = ExactLRUArrays(tr.N, tr.P, tr.H, tr.wl.ring)
@@ -61,13 +64,16 @@ def test_mixed_paths_random(seed):
     wl = dataclasses.replace(wl, groups=groups, appends=int(rng.integers(1, 4)), name=f"mixed{seed}")
     tr = Trace(wl)
     max_append = int(rng.integers(2, 6))
-    say(f"mixed {seed}: policy {policy} groups {groups} ring {wl.ring} steps {tr.steps} "
-        f"N={tr.N} P={tr.P} H={tr.H} max_append={max_append}")
-    eng = engine_for(tr, max_append=max_append, policy=policy)
+    placement = int(rng.integers(0, 2)) if policy == 0 else 0
+    streams = [torch.cuda.Stream() for _ in range(groups)] if groups > 1 and rng.random() < 0.5 else None
+    say(f"mixed {seed}: policy {policy} placement {placement} groups {groups} ring {wl.ring} "
+        f"steps {tr.steps} N={tr.N} P={tr.P} H={tr.H} max_append={max_append} "
+        f"streams {'per group' if streams else 'one'}")
+    eng = engine_for(tr, max_append=max_append, policy=policy, placement=placement)
     rows_dev = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
     try:
         initial_load(eng, tr, range(groups), rows_dev)
-        ora = {g: _oracle(tr, g, policy) for g in range(groups)}
+        ora = {g: _oracle(tr, g, policy, placement) for g in range(groups)}
         for g in range(groups):
             _same(eng.export_state(g), ora[g].export_state(), policy, f"group {g} after load")
         sels = {g: padded_selections(tr, g, seed + 7 * g) for g in range(groups)}
@@ -87,15 +93,24 @@ def test_mixed_paths_random(seed):
                         ora[g].append(app, rows_for(wl.seed, g, app, wl.layers, wl.row_bytes))
                     else:
                         ora[g].append(app)
+                gs = None
+                if streams:   # the group's own stream, after the inputs made on the current one
+                    gs = streams[g]
+                    gs.wait_stream(torch.cuda.current_stream())
                 if combined:
-                    eng.append_step(g, app, rows, dsel)
+                    eng.append_step(g, app, rows, dsel, stream=gs)
                 else:
                     if app.size:
-                        eng.append(g, app, rows)
-                    eng.step(g, dsel)
-                outs = gather_layers_by(eng, g, wl.layers, dsel, str(rng.choice(["layer", "all", "split"])))
+                        eng.append(g, app, rows, stream=gs)
+                    eng.step(g, dsel, stream=gs)
+                mode = str(rng.choice(["layer", "all", "split"]))
+                if gs is None:
+                    outs = gather_layers_by(eng, g, wl.layers, dsel, mode)
+                else:
+                    with torch.cuda.stream(gs):
+                        outs = gather_layers_by(eng, g, wl.layers, dsel, mode)
                 ora[g].step(sel)
-                eng.sync()
+                eng.sync(stream=gs)
                 _same(eng.export_state(g), ora[g].export_state(), policy, f"group {g} step {t}")
                 flat = np.asarray(sel, dtype=np.int64).reshape(-1)
                 want = np.zeros((flat.size, wl.layers, wl.row_bytes), np.uint8)
