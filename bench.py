@@ -19,26 +19,37 @@ value = selected row-layers resolved and gathered per second
       = K * sum over groups of (n_sets * k * layers) / timed wall seconds.
 
 Printed as one JSON line, with:
-  roofline      the gather kernel against HBM peak (1312 algorithmic bytes per
-                gathered row-layer: 656 read + 656 written; bytes per launch =
-                the timed region's row-layers over its gather launches, which
-                on the default split are 1 and layers - 1 layers each), its
-                average kernel duration over the timed region from HIP events
-                that every gather records in its own dispatch on the engine's
-                stream (the kernel's execution, as rocprofv3 reports it);
-  miss_path     the miss path against the host link, per direction: missed rows
-                in (656 * layers bytes per miss) and the previous step's
-                evicted rows out (656 * layers bytes per eviction), both moved
-                concurrently by workgroups of the k_mark launch, timed over
-                that whole launch (which also marks hits and plans victims),
-                from a second replay with per-phase events;
+  roofline      the step's dominant kernel against its peak. On a workload
+                whose step moves rows over the host link for longer than it
+                gathers (the default one) that is the host-link launch k_mark:
+                the larger direction's algorithmic bytes per launch (656 x
+                layers per missed row in, per evicted row of the previous step
+                out; both directions move at once) over its average duration,
+                from HIP events the launch records in its own dispatch, against
+                63 GB/s per direction; `traffic` is the counted host-link bytes
+                of rocprofv3's IO request counters where they were taken for the
+                same k_mark code. Otherwise the gather (below).
+  roofline_other the other one: the gather against HBM peak (1312 algorithmic
+                bytes per gathered row-layer: 656 read + 656 written), its
+                average duration alone (the per-phase replay runs each group's
+                gathers right behind its step with nothing beside them), with
+                its duration inside the timed steps next to it;
+  replays       the value of each of the three timed replays (value = median);
+  miss_path     the per-phase replay: phase times per group step, GPU hit
+                rate, and hipMemcpyAsync pinned-host peaks (each direction and
+                both at once) next to the host-link rates;
   cpu_baseline  the CPU oracle timed on this host's cores over the same steps
                 (a bounded sample; a baseline, not the target).
-Also: selections_per_s (selection entries resolved per second, all groups),
+Also: selections_per_s (selection entries resolved per second, all groups) and
 first_step_ms (step 1, the cold start with the most misses, timed alone, after
-every step kernel has run once on a tiny engine), and
-hipMemcpyAsync pinned-host peaks (each direction and both at once) next to the
-miss-path rates.
+every step kernel has run once on a tiny engine).
+
+Other modes print their own line and exit: --layer-prefetch (the later-layer
+prefetch experiment), --copy-ceiling and --calibrate-copy (plain device copies:
+the HBM rate at the gather's sizes, the counter scale), --link-probe and
+--gather-probe (plain moves of random rows, one direction per launch, and
+copy-engine transfers of the same bytes, measure/libprobes.so: the simple and
+the alternative forms of the miss path's and the gather's traffic).
 """
 
 from __future__ import annotations
@@ -103,6 +114,17 @@ def parse():
     p.add_argument("--copy-ceiling", type=int, default=0, metavar="BYTES",
                    help="only run plain device-to-device copies moving BYTES each (half read, half "
                         "written), from buffers larger than the memory-side cache, and exit")
+    p.add_argument("--link-probe", type=int, default=0, metavar="ROWS",
+                   help="only time plain moves of ROWS random host-pool rows into HBM and as many out "
+                        "to other random host slots (each alone, both at once, and next to copy-engine "
+                        "transfers) with measure/libprobes.so, print one JSON line and exit")
+    p.add_argument("--gather-probe", type=int, default=0, metavar="ROWS",
+                   help="only time a plain gather of ROWS random HBM-pool slots into a contiguous "
+                        "buffer with measure/libprobes.so, cold and warm, print one JSON line and exit")
+    p.add_argument("--slot-bytes", type=int, default=656, help="row size of the probes")
+    p.add_argument("--pool-rows", type=int, default=0,
+                   help="rows of the probe's pool (host pool for --link-probe, HBM pool for "
+                        "--gather-probe)")
     return p.parse_args()
 
 
@@ -743,6 +765,14 @@ def main():
         return
     if args.copy_ceiling:
         copy_ceiling(args.copy_ceiling)
+        return
+    if args.link_probe or args.gather_probe:
+        from measure import probes
+        if args.link_probe:
+            r = probes.link(args.link_probe, args.slot_bytes, args.pool_rows or 8 * args.link_probe)
+        else:
+            r = probes.gather(args.gather_probe, args.slot_bytes, args.pool_rows or 4 * args.gather_probe)
+        print(json.dumps({"probe": "link" if args.link_probe else "gather", **r}), flush=True)
         return
     if args.layer_prefetch:
         wl = preset(args.workload)

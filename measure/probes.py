@@ -1,0 +1,160 @@
+"""Measurement probes with the plain row moves of libprobes.so.
+
+link(): the miss path's traffic with nothing else in the launch: `rows` random
+host-pool rows read into contiguous HBM (zero-copy loads of pinned host memory) and
+as many contiguous HBM rows written to other random host slots, alone and both at
+once on two streams, over several launch shapes; beside them a contiguous copy-engine
+transfer of the same bytes (hipMemcpyAsync: alone each way, both ways at once, and
+device to host beside the zero-copy reads).
+
+gather(): `rows` random slots of an HBM pool read into a contiguous buffer, each
+launch after a 1 GiB write that pushes the pool out of the memory-side cache.
+
+Times are per launch (events on the launch's stream, median of `reps`).
+"""
+
+import ctypes
+import os
+import statistics
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libprobes.so")
+_lib = None
+
+LINK_PEAK_GBPS = 63.0     # PCIe 5.0 x16 per direction: 32 GT/s x 16 x 128/130 / 8
+HBM_PEAK_GBPS = 8000.0
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with measure.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        L.probe_move_rows.restype = ctypes.c_int
+        L.probe_move_rows.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_uint64]
+        _lib = L
+    return _lib
+
+
+def move_rows(mode: int, src, idx, dst, n: int, row_bytes: int, blocks: int, stream) -> None:
+    """mode 0: dst row r = src row idx[r]; mode 1: dst row idx[r] = src row r (r < n).
+    Every index must be a row of the buffer it indexes: checked here, before the launch."""
+    import torch
+    assert idx.dtype == torch.int32 and idx.is_cuda and idx.numel() >= n
+    indexed = src if mode == 0 else dst
+    other = dst if mode == 0 else src
+    if n:
+        hi = int(idx[:n].max().item())
+        lo = int(idx[:n].min().item())
+        assert 0 <= lo and (hi + 1) * row_bytes <= indexed.numel(), "row index outside its buffer"
+    assert n * row_bytes <= other.numel()
+    rc = lib().probe_move_rows(mode, src.data_ptr(), idx.data_ptr(), dst.data_ptr(), n, row_bytes, blocks,
+                              stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"probe_move_rows failed ({rc})")
+
+
+def _timed(first, second, s1, s2, reps, before=None):
+    """Median over reps of the time from a start event on s1 to the later of the two
+    streams' end events (second may be None)."""
+    import torch
+    out = []
+    for _ in range(reps + 1):          # the first round warms up and is dropped
+        if before:
+            before()
+        torch.cuda.synchronize()
+        st = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e2 = torch.cuda.Event(enable_timing=True)
+        st.record(s1)
+        s2.wait_event(st)
+        first(s1)
+        e1.record(s1)
+        if second:
+            second(s2)
+        e2.record(s2)
+        torch.cuda.synchronize()
+        out.append(max(st.elapsed_time(e1), st.elapsed_time(e2)))
+    return statistics.median(out[1:])
+
+
+def link(rows: int, slot_bytes: int, host_rows: int, shapes=(96, 256, 1024), reps: int = 5,
+         seed: int = 1) -> dict:
+    import numpy as np
+    import torch
+    assert 2 * rows <= host_rows
+    torch.cuda.set_device(0)
+    host = torch.empty(host_rows * slot_bytes, dtype=torch.uint8, pin_memory=True)
+    contig = torch.empty(rows * slot_bytes, dtype=torch.uint8, pin_memory=True)
+    contig2 = torch.empty(rows * slot_bytes, dtype=torch.uint8, pin_memory=True)
+    perm = np.random.default_rng(seed).permutation(host_rows)[:2 * rows].astype(np.int32)
+    rd_idx = torch.from_numpy(perm[:rows].copy()).cuda()
+    wr_idx = torch.from_numpy(perm[rows:].copy()).cuda()
+    dev_in = torch.empty(rows * slot_bytes, dtype=torch.uint8, device="cuda")
+    dev_out = torch.randint(0, 256, (rows * slot_bytes,), dtype=torch.uint8, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def rd(b):
+        return lambda s: move_rows(0, host, rd_idx, dev_in, rows, slot_bytes, b, s)
+
+    def wr(b):
+        return lambda s: move_rows(1, dev_out, wr_idx, host, rows, slot_bytes, b, s)
+
+    def d2h(s):
+        with torch.cuda.stream(s):
+            contig.copy_(dev_out, non_blocking=True)
+
+    def h2d(s):
+        with torch.cuda.stream(s):
+            dev_in.copy_(contig2, non_blocking=True)
+
+    ms = {}
+    for b in shapes:
+        ms[f"read_{b}"] = _timed(rd(b), None, s1, s2, reps)
+        ms[f"write_{b}"] = _timed(wr(b), None, s1, s2, reps)
+        ms[f"both_{b}"] = _timed(rd(b), wr(b), s1, s2, reps)
+        ms[f"read_{b}+copy_d2h"] = _timed(rd(b), d2h, s1, s2, reps)
+    ms["copy_d2h"] = _timed(d2h, None, s1, s2, reps)
+    ms["copy_h2d"] = _timed(h2d, None, s1, s2, reps)
+    ms["copy_both"] = _timed(h2d, d2h, s1, s2, reps)
+    mb = rows * slot_bytes / 1e6
+    best = min((v, k) for k, v in ms.items() if k.startswith("both_"))
+    return {"rows": rows, "slot_bytes": slot_bytes, "host_rows": host_rows, "MB_each_way": round(mb, 3),
+            "ms": {k: round(v, 4) for k, v in ms.items()},
+            "both_best": {"shape": best[1], "ms": round(best[0], 4),
+                          "GBps_each_way": round(mb / best[0], 2),
+                          "frac_of_peak": round(mb / best[0] / LINK_PEAK_GBPS, 4)}}
+
+
+def gather(rows: int, slot_bytes: int, pool_rows: int, shapes=(1024, 4096, 16384), reps: int = 7,
+           seed: int = 2) -> dict:
+    import numpy as np
+    import torch
+    assert rows <= pool_rows
+    torch.cuda.set_device(0)
+    pool = torch.randint(0, 256, (pool_rows * slot_bytes,), dtype=torch.uint8, device="cuda")
+    idx = torch.from_numpy(np.random.default_rng(seed).permutation(pool_rows)[:rows].astype(np.int32)).cuda()
+    out = torch.empty(rows * slot_bytes, dtype=torch.uint8, device="cuda")
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    state = {"i": 0}
+
+    def evict_caches():
+        state["i"] += 1
+        flush.fill_(state["i"] & 0xFF)
+
+    ms = {}
+    for b in shapes:
+        ms[f"gather_{b}"] = _timed(lambda s: move_rows(0, pool, idx, out, rows, slot_bytes, b, s), None,
+                                   s1, s2, reps, before=evict_caches)
+        ms[f"gather_{b}_warm"] = _timed(lambda s: move_rows(0, pool, idx, out, rows, slot_bytes, b, s), None,
+                                        s1, s2, reps)
+    algo = 2 * rows * slot_bytes
+    best = min((v, k) for k, v in ms.items() if not k.endswith("_warm"))
+    return {"rows": rows, "slot_bytes": slot_bytes, "pool_rows": pool_rows, "algorithmic_MB": round(algo / 1e6, 3),
+            "ms": {k: round(v, 4) for k, v in ms.items()},
+            "cold_best": {"shape": best[1], "us": round(best[0] * 1e3, 2),
+                          "GBps": round(algo / best[0] / 1e6, 1),
+                          "frac_of_peak": round(algo / best[0] / 1e6 / HBM_PEAK_GBPS, 4)}}

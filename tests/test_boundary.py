@@ -36,6 +36,19 @@ def test_synth_device_library_exports_filler():
     assert hasattr(device.lib(), "ulasynth_fill_rows")
 
 
+def test_probe_library_exports_and_rejects_bad_arguments():
+    """bench.py's measurement probes: the row-move entry point refuses bad
+    arguments on the host, before any device call."""
+    from measure import probes
+    L = probes.lib()
+    p = ctypes.c_void_p(16)
+    assert L.probe_move_rows(2, p, p, p, 1, 656, 1, 0) == -1            # no such mode
+    assert L.probe_move_rows(0, None, p, p, 1, 656, 1, 0) == -1         # null pointer
+    assert L.probe_move_rows(0, p, p, p, 1, 650, 1, 0) == -1            # not 16-byte pieces
+    assert L.probe_move_rows(1, p, p, p, 1, 656, 0, 0) == -1            # no workgroups
+    assert L.probe_move_rows(0, p, p, p, 1 << 27, 656, 1, 0) == -1      # piece index past 32 bits
+
+
 def _cfg(**kw):
     base = dict(num_groups=1, layers_per_group=3, row_bytes=656, ring_buckets=8,
                 logical_capacity=1049600, gpu_slots=524288, host_slots=525312, max_sets=16,
