@@ -98,10 +98,17 @@ def parse():
     p.add_argument("--placement", choices=("lowest", "ring"), default="lowest",
                    help="where appended entries go: the lowest free slot, GPU first, never evicting "
                         "(default), or the current bucket, evicting (PB-LRU only)")
-    p.add_argument("--streams", choices=("one", "group"), default="group",
-                   help="a stream per group (default), so that one group's HBM phases run beside "
+    p.add_argument("--streams", choices=("auto", "one", "group", "two", "two+gather"), default="auto",
+                   help="group: a stream per group, so that one group's HBM phases run beside "
                         "another's host-link launch (the library keeps the host-link launches one "
-                        "at a time), or one stream for every group's calls")
+                        "at a time); two: two streams with the groups alternating over them; "
+                        "two+gather: the same with every group's gathers on a third stream (each "
+                        "gather waits for its step by an event, each step for the group's previous "
+                        "gathers); one: one stream for every call. auto (default): group for up to "
+                        "two groups, two+gather for more (HIP spreads a process's streams over four "
+                        "hardware queues, two of them left for created streams, and a queue runs "
+                        "its launches in order, so more than two step streams queue one group's "
+                        "lookup behind another's gathers)")
     p.add_argument("--gather", choices=("layer", "split", "all"), default="split",
                    help="gathers per group step: one per layer (ula_gather); layer 0 alone, then the "
                         "later layers in one ula_gather_layers launch (default); or every layer in "
@@ -422,7 +429,7 @@ def gather_all_layers(eng, g, sel, outs, layers, mode, stream=None):
 
 
 def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str = "layer",
-            replays: int = 3, placement: int = 0, per_group_streams: bool = False) -> dict:
+            replays: int = 3, placement: int = 0, streams: str = "one") -> dict:
     import statistics
 
     import torch
@@ -445,25 +452,44 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
     outs = {g: torch.empty((wl.layers, tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
             for g in groups}
 
-    gstreams = [torch.cuda.Stream() for _ in groups] if per_group_streams else [stream for _ in groups]
+    if streams == "group":
+        gstreams = [torch.cuda.Stream() for _ in groups]
+    elif streams in ("two", "two+gather"):
+        pair = [torch.cuda.Stream(), torch.cuda.Stream()]
+        gstreams = [pair[g % 2] for g in groups]
+    else:
+        gstreams = [stream for _ in groups]
+    side = [gs for i, gs in enumerate(gstreams) if gs is not stream and gs not in gstreams[:i]]
+    # two+gather: the gathers go to the main stream, after an event their step
+    # recorded; a group's next step waits for an event after its gathers (the
+    # step's swap rewrites slots those gathers read)
+    gather_stream = stream if streams == "two+gather" else None
+    step_done = {g: torch.cuda.Event() for g in groups}
+    gathers_done = {g: torch.cuda.Event() for g in groups}
 
     def fork():   # the group streams start after what the main stream has recorded
-        for gs in gstreams:
-            if gs is not stream:
-                gs.wait_stream(stream)
+        for gs in side:
+            gs.wait_stream(stream)
 
     def join():   # and the main stream continues after all of them
-        for gs in gstreams:
-            if gs is not stream:
-                stream.wait_stream(gs)
+        for gs in side:
+            stream.wait_stream(gs)
 
     def run_step(eng, t):
         for g in groups:
             sel = sels[g][t - 1]
             # the step's appends and the step in one call (the appends run in the
             # step's first launch when they are small)
-            eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel, stream=gstreams[g])
-            gather_all_layers(eng, g, sel, outs[g], wl.layers, gather_mode, stream=gstreams[g])
+            if gather_stream is None:
+                eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel, stream=gstreams[g])
+                gather_all_layers(eng, g, sel, outs[g], wl.layers, gather_mode, stream=gstreams[g])
+            else:
+                gstreams[g].wait_event(gathers_done[g])
+                eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel, stream=gstreams[g])
+                step_done[g].record(gstreams[g])
+                gather_stream.wait_event(step_done[g])
+                gather_all_layers(eng, g, sel, outs[g], wl.layers, gather_mode, stream=gather_stream)
+                gathers_done[g].record(gather_stream)
 
     # every step kernel runs once on a tiny engine first, so that the first
     # timed step does not also pay for loading kernel code
@@ -803,9 +829,12 @@ def main():
                            placement=args.placement)
 
     gather_mode = args.gather if wl.layers > 1 else "layer"   # one layer: the same launch
+    streams = args.streams
+    if streams == "auto":
+        streams = "group" if wl.groups <= 2 else "two+gather"
     placement = 1 if args.placement == "ring" else 0
     r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode, replays=args.replays,
-                placement=placement, per_group_streams=args.streams == "group")
+                placement=placement, streams=streams)
     value = per_step * K / r["wall_s"]
     ms_per_step = r["event_ms"] / K
     replay_values = [round(per_step * K / w, 1) for w in r["replay_walls_s"]]
@@ -891,7 +920,7 @@ def main():
                    "layers_per_group": wl.layers, "k": wl.k, "gpu_slots": tr.P, "host_slots": tr.H,
                    "ring": wl.ring, "row_bytes": wl.row_bytes, "overlap": wl.overlap,
                    "policy": "exact LRU" if policy else "PB-LRU", "gather": gather_mode,
-                   "placement": args.placement, "streams": args.streams,
+                   "placement": args.placement, "streams": streams,
                    "row_layers_per_step": per_step},
         "roofline": roofline,
         "roofline_other": other,

@@ -59,7 +59,14 @@
  * groups share one host link, so once steps arrive on more than one stream the
  * library orders each step's host-link launch after the previous step's (of any
  * group) with an event; the rest of one group's step (lookup, swap, gathers)
- * still runs beside another group's host-link launch.
+ * still runs beside another group's host-link launch. A gather issued on a
+ * stream other than its step's must be ordered after the step (an event, or a
+ * stream wait on ula_flag_address), and the group's next append, step or
+ * release after that gather (they move rows out of slots it reads). HIP
+ * places a process's streams on a few hardware queues, each running its
+ * launches in order: with more step streams than queues, one group's lookup
+ * can wait behind another group's gathers, so many groups run best on two step
+ * streams (groups alternating) with the gathers on a third.
  */
 #ifndef ULA_H
 #define ULA_H
@@ -272,7 +279,9 @@ int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* l
  * gather is a relaxed read that only catches a gather that runs before the
  * counter is raised (ULA_ENOTRESIDENT); the rows of an unordered gather that
  * finds the counter raised are undefined, since nothing orders its reads after
- * the step's writes on another cache.
+ * the step's writes on another cache. Likewise the group's next append, step
+ * or release must be ordered after such a gather: they move rows out of the
+ * slots it reads.
  * Host errors: ULA_EINVAL, ULA_ESTATE, ULA_ENOTRESIDENT (no step yet).
  * Device errors (reported by ula_sync): ULA_ENOTRESIDENT (counter not reached,
  * or an entry not on the GPU), ULA_ERANGE. */

@@ -222,11 +222,16 @@ def test_large_gather_ragged_parity():
     assert ora[0].last.misses > 0
 
 
+@pytest.mark.parametrize("schedule", ["group", "two+gather"])
 @pytest.mark.parametrize("policy", [0, 1], ids=["pblru", "lru"])
-def test_groups_on_separate_streams(policy):
+def test_groups_on_separate_streams(policy, schedule):
     """Layer groups are independent and may be driven on different streams: each
-    group's appends, steps and gathers go to a stream of its own, interleaved with
-    no synchronisation between the groups; every group matches its own oracle
+    group's appends, steps and gathers go to a stream of its own (schedule
+    "group"), or the groups' appends and steps alternate over two streams and
+    every gather runs on a third, after an event its step recorded, with each
+    group's next append waiting for an event after its gathers (schedule
+    "two+gather", bench.py's for more than two groups); no other
+    synchronisation between the groups. Every group matches its own oracle
     (every gathered byte of every step, and the state after the last step)."""
     import torch
     from oracle.exact_lru_np import ExactLRUArrays
@@ -236,7 +241,7 @@ def test_groups_on_separate_streams(policy):
     wl = scaled(preset("spec3_r128_64k128k_g4"), 32)
     tr = Trace(wl, 6)
     G = wl.groups
-    say(f"separate streams {wl.name} policy {policy}: groups={G} steps={tr.steps}")
+    say(f"separate streams {wl.name} policy {policy} schedule {schedule}: groups={G} steps={tr.steps}")
     eng = engine_for(tr, max_append=1 << 15, policy=policy)
     rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
     try:
@@ -247,15 +252,31 @@ def test_groups_on_separate_streams(policy):
         app_rows = {(g, t): rows(tr.appends(t), g) for g in range(G) for t in range(1, tr.steps + 1)
                     if tr.appends(t).size}
         torch.cuda.synchronize()
-        streams = [torch.cuda.Stream() for _ in range(G)]
+        if schedule == "group":
+            streams = [torch.cuda.Stream() for _ in range(G)]
+            gstreams = streams
+        else:
+            pair = [torch.cuda.Stream(), torch.cuda.Stream()]
+            streams = [pair[g % 2] for g in range(G)]
+            gather_stream = torch.cuda.Stream()
+            gstreams = [gather_stream] * G
+        step_done = [torch.cuda.Event() for _ in range(G)]
+        gathers_done = [torch.cuda.Event() for _ in range(G)]
         outs = {}
         for t in range(1, tr.steps + 1):
             app = tr.appends(t)
             for g in range(G):
+                if schedule != "group":
+                    streams[g].wait_event(gathers_done[g])
                 if app.size:
                     eng.append(g, app, app_rows[(g, t)], stream=streams[g])
                 eng.step(g, dsel[g][t - 1], stream=streams[g])
-                outs[(g, t)] = [eng.gather(g, l, dsel[g][t - 1], stream=streams[g]) for l in range(wl.layers)]
+                if schedule != "group":
+                    step_done[g].record(streams[g])
+                    gstreams[g].wait_event(step_done[g])
+                outs[(g, t)] = [eng.gather(g, l, dsel[g][t - 1], stream=gstreams[g]) for l in range(wl.layers)]
+                if schedule != "group":
+                    gathers_done[g].record(gstreams[g])
         torch.cuda.synchronize()
         eng.sync()
         for g in range(G):
