@@ -98,17 +98,18 @@ def parse():
     p.add_argument("--placement", choices=("lowest", "ring"), default="lowest",
                    help="where appended entries go: the lowest free slot, GPU first, never evicting "
                         "(default), or the current bucket, evicting (PB-LRU only)")
-    p.add_argument("--streams", choices=("auto", "one", "group", "two", "two+gather"), default="auto",
-                   help="group: a stream per group, so that one group's HBM phases run beside "
-                        "another's host-link launch (the library keeps the host-link launches one "
-                        "at a time); two: two streams with the groups alternating over them; "
-                        "two+gather: the same with every group's gathers on a third stream (each "
-                        "gather waits for its step by an event, each step for the group's previous "
-                        "gathers); one: one stream for every call. auto (default): group for up to "
-                        "two groups, two+gather for more (HIP spreads a process's streams over four "
-                        "hardware queues, two of them left for created streams, and a queue runs "
-                        "its launches in order, so more than two step streams queue one group's "
-                        "lookup behind another's gathers)")
+    p.add_argument("--streams", choices=("auto", "one", "group", "two", "one+gather", "group+gather",
+                                         "two+gather"), default="auto",
+                   help="where each group's calls go. one: one stream for every call; group: a "
+                        "stream per group (one group's HBM phases run beside another's host-link "
+                        "launch; the library keeps the host-link launches one at a time); two: two "
+                        "streams with the groups alternating over them; X+gather: the steps as in X "
+                        "and every gather on a stream of its own, after an event its step recorded "
+                        "(the library makes the group's next row moves wait for it, so the next "
+                        "step's lookup and marking run beside it). auto (default): one+gather for one "
+                        "group, group+gather for two, two+gather for more (HIP spreads a process's "
+                        "streams over four hardware queues, two of them left for created streams, "
+                        "and a queue runs its launches in order)")
     p.add_argument("--gather", choices=("layer", "split", "all"), default="split",
                    help="gathers per group step: one per layer (ula_gather); layer 0 alone, then the "
                         "later layers in one ula_gather_layers launch (default); or every layer in "
@@ -454,18 +455,21 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
 
     if streams == "group":
         gstreams = [torch.cuda.Stream() for _ in groups]
-    elif streams in ("two", "two+gather"):
+    if streams.startswith("group"):
+        gstreams = [torch.cuda.Stream() for _ in groups]
+    elif streams.startswith("two"):
         pair = [torch.cuda.Stream(), torch.cuda.Stream()]
         gstreams = [pair[g % 2] for g in groups]
+    elif streams == "one+gather":
+        one = torch.cuda.Stream()
+        gstreams = [one for _ in groups]
     else:
         gstreams = [stream for _ in groups]
     side = [gs for i, gs in enumerate(gstreams) if gs is not stream and gs not in gstreams[:i]]
-    # two+gather: the gathers go to the main stream, after an event their step
-    # recorded; a group's next step waits for an event after its gathers (the
-    # step's swap rewrites slots those gathers read)
-    gather_stream = stream if streams == "two+gather" else None
+    # X+gather: the gathers go to the main stream, after an event their step
+    # recorded (the library orders the group's next swap after them)
+    gather_stream = stream if streams.endswith("+gather") else None
     step_done = {g: torch.cuda.Event() for g in groups}
-    gathers_done = {g: torch.cuda.Event() for g in groups}
 
     def fork():   # the group streams start after what the main stream has recorded
         for gs in side:
@@ -484,12 +488,10 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
                 eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel, stream=gstreams[g])
                 gather_all_layers(eng, g, sel, outs[g], wl.layers, gather_mode, stream=gstreams[g])
             else:
-                gstreams[g].wait_event(gathers_done[g])
                 eng.append_step(g, apps[t - 1], app_rows[g][t - 1], sel, stream=gstreams[g])
                 step_done[g].record(gstreams[g])
                 gather_stream.wait_event(step_done[g])
                 gather_all_layers(eng, g, sel, outs[g], wl.layers, gather_mode, stream=gather_stream)
-                gathers_done[g].record(gather_stream)
 
     # every step kernel runs once on a tiny engine first, so that the first
     # timed step does not also pay for loading kernel code
@@ -830,8 +832,8 @@ def main():
 
     gather_mode = args.gather if wl.layers > 1 else "layer"   # one layer: the same launch
     streams = args.streams
-    if streams == "auto":
-        streams = "group" if wl.groups <= 2 else "two+gather"
+    if streams == "auto":   # measured fastest (or as fast) on each workload
+        streams = {1: "one+gather", 2: "group+gather"}.get(wl.groups, "two+gather")
     placement = 1 if args.placement == "ring" else 0
     r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode, replays=args.replays,
                 placement=placement, streams=streams)

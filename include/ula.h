@@ -61,12 +61,17 @@
  * group) with an event; the rest of one group's step (lookup, swap, gathers)
  * still runs beside another group's host-link launch. A gather issued on a
  * stream other than its step's must be ordered after the step (an event, or a
- * stream wait on ula_flag_address), and the group's next append, step or
- * release after that gather (they move rows out of slots it reads). HIP
- * places a process's streams on a few hardware queues, each running its
- * launches in order: with more step streams than queues, one group's lookup
- * can wait behind another group's gathers, so many groups run best on two step
- * streams (groups alternating) with the gathers on a third.
+ * stream wait on ula_flag_address). The library orders what comes after it:
+ * the group's next launch that moves rows out of GPU slots (the next step's
+ * swap, an append under ULA_PLACE_RING, a release) waits, by events, for the
+ * group's gathers enqueued since its last such launch, on any stream; the next
+ * step's lookup, marking and host-link transfers do not wait and may run beside
+ * those gathers (each step resolves its selection into one of two buffers, by
+ * step parity, and a gather reads its step's). HIP places a process's streams
+ * on a few hardware queues, each running its launches in order: with more step
+ * streams than queues, one group's lookup can wait behind another group's
+ * gathers, so many groups run best on two step streams (groups alternating)
+ * with the gathers on a third.
  */
 #ifndef ULA_H
 #define ULA_H
@@ -279,9 +284,12 @@ int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* l
  * gather is a relaxed read that only catches a gather that runs before the
  * counter is raised (ULA_ENOTRESIDENT); the rows of an unordered gather that
  * finds the counter raised are undefined, since nothing orders its reads after
- * the step's writes on another cache. Likewise the group's next append, step
- * or release must be ordered after such a gather: they move rows out of the
- * slots it reads.
+ * the step's writes on another cache. The group's later calls need no
+ * ordering after the gather: the library makes the next launch that moves rows
+ * out of GPU slots wait for it (see Threading). A gather that runs while the
+ * group's next step fails on the device may find that step's error and write
+ * nothing (ula_sync reports the error); a gather of an address appended only
+ * after its step is an error, or undefined if that append runs beside it.
  * Host errors: ULA_EINVAL, ULA_ESTATE, ULA_ENOTRESIDENT (no step yet).
  * Device errors (reported by ula_sync): ULA_ENOTRESIDENT (counter not reached,
  * or an entry not on the GPU), ULA_ERANGE. */

@@ -129,7 +129,7 @@ Layout layout_of(const ula_config* c, const Dims& d) {
   L.miss_stage = take(4 * d.maxU);
   L.miss_rows = take((size_t)d.maxU * d.slot_bytes);
   L.hs_stage = take(8 * d.H);
-  L.res = take(8 * d.nsel);
+  L.res = take(8 * 2 * d.nsel);   // two buffers, by step parity
   if (d.policy == ULA_POLICY_LRU) {   // exact-LRU timestamps and selection scratch
     L.lru_ts = take(4 * 32 * d.W);
     L.lru_hist = take(4 * 2048);
@@ -165,6 +165,14 @@ const char* kMessages[] = {
 
 }  // namespace
 
+constexpr int kGatherStreams = 8;   // streams with gathers tracked per group
+
+struct PendingGather {
+  hipStream_t s = nullptr;
+  hipEvent_t ev = nullptr;
+  bool live = false;
+};
+
 struct GroupHost {
   GroupDev d;
   std::vector<uint64_t> appended;   // host mirror: which addresses were appended
@@ -178,6 +186,14 @@ struct GroupHost {
   hipEvent_t ev[4] = {};
   int32_t last_pairs = 0;           // most miss pairs the last step could have staged
   int64_t written_back = 0;         // last step whose staged rows a flush wrote to the host
+  // The resolved selection (res) has two buffers, by step parity: a step writes
+  // its own, the gathers of the step before read the other, so the next step's
+  // lookup may run while those gathers still do.
+  uint2* res_base = nullptr;
+  // Gathers enqueued since the group's last row move, one event per stream: the
+  // next launch that moves rows in or out of GPU slots (the swap, an append that
+  // evicts, a release) waits for those on other streams.
+  PendingGather pending[kGatherStreams];
 };
 
 static constexpr int kTimingRing = 256;
@@ -298,6 +314,42 @@ static int drain_timing(TimingRing& r, double* ms, int64_t* launches) {
   return ULA_OK;
 }
 
+// The group's resolved-selection buffer for step t (or for the gathers of step t).
+static uint2* res_for(const ula_ctx* ctx, const GroupHost& gh, int64_t t) {
+  return gh.res_base + (size_t)(t & 1) * (size_t)ctx->dims.nsel;
+}
+
+// A gather of the group was enqueued on stream s: record that stream's event.
+// With more streams than slots, the host waits for the oldest slot's gathers.
+static int note_gather(GroupHost& gh, hipStream_t s) {
+  PendingGather* slot = nullptr;
+  for (auto& p : gh.pending)
+    if (p.live && p.s == s) slot = &p;
+  for (int i = 0; !slot && i < kGatherStreams; ++i)
+    if (!gh.pending[i].live) slot = &gh.pending[i];
+  if (!slot) {
+    slot = &gh.pending[0];
+    HIP_TRY(hipEventSynchronize(slot->ev));
+  }
+  if (!slot->ev) HIP_TRY(hipEventCreateWithFlags(&slot->ev, hipEventDisableTiming));
+  HIP_TRY(hipEventRecord(slot->ev, s));
+  slot->s = s;
+  slot->live = true;
+  return ULA_OK;
+}
+
+// Before the first launch on stream s that moves rows in or out of the group's
+// GPU slots: wait for the gathers enqueued on other streams since the last such
+// launch (those on s are ordered by the stream itself).
+static int wait_gathers(GroupHost& gh, hipStream_t s) {
+  for (auto& p : gh.pending) {
+    if (!p.live) continue;
+    if (p.s != s) HIP_TRY(hipStreamWaitEvent(s, p.ev, 0));
+    p.live = false;
+  }
+  return ULA_OK;
+}
+
 extern "C" {
 
 size_t ula_device_bytes(const ula_config* cfg) {
@@ -343,6 +395,8 @@ static void destroy_ctx(ula_ctx* ctx) {
     }
     for (auto& e : g.ev)
       if (e) (void)hipEventDestroy(e);
+    for (auto& p : g.pending)
+      if (p.ev) (void)hipEventDestroy(p.ev);
   }
   delete ctx;
 }
@@ -414,6 +468,7 @@ static int init_impl(const ula_config* cfg, void* dev_ws, void* host_pinned, uin
     g.miss_rows = b + L.miss_rows;
     g.hs_stage = reinterpret_cast<unsigned long long*>(b + L.hs_stage);
     g.res = reinterpret_cast<uint2*>(b + L.res);
+    gh.res_base = g.res;
     if (d.policy == ULA_POLICY_LRU) {
       g.lru_ts = reinterpret_cast<int32_t*>(b + L.lru_ts);
       g.lru_hist = reinterpret_cast<uint32_t*>(b + L.lru_hist);
@@ -567,6 +622,12 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
   // placement ring: the current bucket is that of the group's last enqueued step
   const int32_t cur = (int32_t)(gh.steps % d.B);
   const int32_t ring = d.placement == ULA_PLACE_RING ? 1 : 0;
+  // Under ULA_PLACE_RING an append evicts GPU entries, so it waits for pending
+  // gathers; otherwise it takes only free slots, which no gather reads.
+  if (ring) {
+    const int rc = wait_gathers(gh, s);
+    if (rc) return rc;
+  }
   if (n <= kSmallAppend && n <= d.maxApp && rows_on_device) {
     // decode-time appends: one workgroup, addresses passed by value
     SmallAppend a{};
@@ -654,6 +715,10 @@ int ula_release(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, 
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const GroupDev& g = gh.d;
+  {   // a released GPU slot may be taken by the next append: pending gathers first
+    const int rc = wait_gathers(gh, s);
+    if (rc) return rc;
+  }
   // A released host slot may be waiting for the last step's evicted row, and an
   // append may take it next: write the staged rows out first.
   if (gh.steps > 0 && gh.written_back != gh.steps) {
@@ -720,15 +785,20 @@ static int step_impl(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, con
                      uint64_t stream, const SmallAppend* app, const uint8_t* app_rows) {
   const int32_t n = n_sets * k;
   GroupHost& gh = ctx->groups[group];
-  const GroupDev& g = gh.d;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t t = gh.steps + 1;
+  GroupDev g = gh.d;
+  g.res = res_for(ctx, gh, t);   // the other buffer may still be read by the last step's gathers
   const int32_t cur = (int32_t)(t % ctx->dims.B);
   const bool tm = (ctx->timing & ULA_TIMING_STEP) != 0;
   const int32_t max_pairs = (int32_t)std::min<int64_t>(n, ctx->dims.maxU);
   // the previous step's evicted rows, unless a flush already wrote them out
   const int32_t wb_pairs = (gh.steps > 0 && gh.written_back != gh.steps) ? gh.last_pairs : 0;
 
+  if (app && app->ring) {   // this append evicts GPU entries: pending gathers first
+    const int rc = wait_gathers(gh, s);
+    if (rc) return rc;
+  }
   if (tm) HIP_TRY(hipEventRecord(gh.ev[0], s));
   if (app) HIP_TRY(launch_tag_append(g, *app, app_rows, sel_dev, n, (uint32_t)t, s));
   else HIP_TRY(launch_tag(g, sel_dev, n, (uint32_t)t, s));
@@ -769,6 +839,10 @@ static int step_impl(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, con
     ctx->link_ev_stream = s;
   }
   if (tm) HIP_TRY(hipEventRecord(gh.ev[2], s));
+  {   // the swap moves rows out of GPU slots the last step's gathers may still read
+    const int rc = wait_gathers(gh, s);
+    if (rc) return rc;
+  }
   HIP_TRY(launch_swap_commit(g, (uint32_t)t, max_pairs, s));
   if (tm) HIP_TRY(hipEventRecord(gh.ev[3], s));
   gh.steps = t;
@@ -835,9 +909,13 @@ static int gather_impl(ula_ctx* ctx, int32_t group, int32_t layer0, int32_t nl, 
     int rc = next_timing_pair(ctx->gather_t, &start, &stop);
     if (rc) return rc;
   }
-  HIP_TRY(launch_gather(gh.d, sel_dev, n, layer0, nl, static_cast<uint8_t*>(out_dev), (long long)gh.steps,
-                        gh.last_n, reinterpret_cast<hipStream_t>(stream), start, stop));
-  return ULA_OK;
+  if (n == 0) return ULA_OK;
+  GroupDev g = gh.d;
+  g.res = res_for(ctx, gh, gh.steps);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(launch_gather(g, sel_dev, n, layer0, nl, static_cast<uint8_t*>(out_dev), (long long)gh.steps,
+                        gh.last_n, s, start, stop));
+  return note_gather(gh, s);
 }
 
 int ula_gather(ula_ctx* ctx, int32_t group, int32_t layer, int32_t n_sets, int32_t k,
