@@ -44,12 +44,16 @@ constexpr int kSmallGatherRows = 1 << 16;   // up to this many rows (one layer):
 // (q div nrows); layer l's output rows start layer_stride pieces after layer
 // l - 1's. s_off[r]: source offset of row r's first layer (-1: zero row).
 // MULTI = false is the one-layer case, without the layer arithmetic.
-// Rows are read with plain (cached) loads: repeated entries of one step (the
-// speculative sets) and the heavy overlap between consecutive steps both hit the
-// caches; non-temporal loads measured 18% slower on the speculative workload and
-// only 3% faster where nothing repeats. Output pieces are written with
-// non-temporal stores: plain stores measured 5-12% slower per launch.
-template <int ROWS, int UNROLL, int THREADS, bool MULTI>
+// NT: rows are read with non-temporal loads. A one-layer gather of a step whose
+// selection repeats no entry reads every row once, so it does (measured: 17%
+// faster on the eviction-heavy workload, whose rows come cold after the swap,
+// and the next step's lookups find more of their tables in the caches). Other
+// gathers use plain loads: repeated entries (the speculative sets) and the
+// neighbouring layers of one slot (a 128-byte line spans two of them) hit the
+// caches, and non-temporal loads there measured 18% and 14% slower. Output
+// pieces are written with non-temporal stores: plain stores measured 5-12%
+// slower per launch.
+template <int ROWS, int UNROLL, int THREADS, bool MULTI, bool NT>
 __device__ __forceinline__ void stream_rows(const GroupDev& g, const long long* s_off, int nrows, int nl,
                                             size_t layer_stride, vec4u* o, uint32_t C, FastDiv per_row) {
   const uint32_t per_layer = (uint32_t)nrows * C;
@@ -78,7 +82,8 @@ __device__ __forceinline__ void stream_rows(const GroupDev& g, const long long* 
         if (off >= 0) {
           const vec4u* p = reinterpret_cast<const vec4u*>(g.pool + off + (size_t)l * g.row_bytes +
                                                           (size_t)(i - q * C) * 16);
-          v[u] = *p;
+          if constexpr (NT) v[u] = __builtin_nontemporal_load(p);
+          else v[u] = *p;
         }
         dst[u] = MULTI ? o + (size_t)l * layer_stride + (i - l * per_layer) : o + i;
       }
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(THREADS) void k_gather(GroupDev g, const int32_t* _
   static_assert(ROWS < THREADS, "one lane per staged row plus the checking lane");
   static_assert((ROWS & (ROWS - 1)) == 0, "full blocks split piece indexes with shifts");
   __shared__ long long s_off[ROWS];   // source byte offset of each staged row, -1 = zero row
-  __shared__ int s_ok;
+  __shared__ int s_ok, s_nt;
   const uint32_t C = (uint32_t)g.row_bytes / 16u;
   const size_t layer_off = (size_t)layer * g.row_bytes;
   int err = 0;
@@ -120,6 +125,9 @@ __global__ __launch_bounds__(THREADS) void k_gather(GroupDev g, const int32_t* _
         ok = 0;
       }
       s_ok = ok;
+      // the load hint: a one-layer gather of the step's own selection, which
+      // repeats no entry (a hint only: either kind of load reads the same bytes)
+      s_nt = g.Lg == 1 && n == n_res && g.ctr->res_dup[want_flag & 1] == 0;
     }
     if (threadIdx.x < ROWS) {
       const int r = row0 + threadIdx.x;
@@ -161,10 +169,14 @@ __global__ __launch_bounds__(THREADS) void k_gather(GroupDev g, const int32_t* _
     // 2. stream the staged rows (one layer: no layer arithmetic per piece)
     const int nrows = min(ROWS, n - row0);
     vec4u* o = reinterpret_cast<vec4u*>(out) + (size_t)row0 * C;
-    if (nl == 1)   // kernel-uniform
-      stream_rows<ROWS, UNROLL, THREADS, false>(g, s_off, nrows, 1, 0, o, C, per_row);
-    else
-      stream_rows<ROWS, UNROLL, THREADS, true>(g, s_off, nrows, nl, layer_stride, o, C, per_row);
+    if (nl == 1) {   // kernel-uniform
+      if (s_nt)      // block-uniform
+        stream_rows<ROWS, UNROLL, THREADS, false, true>(g, s_off, nrows, 1, 0, o, C, per_row);
+      else
+        stream_rows<ROWS, UNROLL, THREADS, false, false>(g, s_off, nrows, 1, 0, o, C, per_row);
+    } else {
+      stream_rows<ROWS, UNROLL, THREADS, true, false>(g, s_off, nrows, nl, layer_stride, o, C, per_row);
+    }
     __syncthreads();
   }
   if (err) latch_gather(g.ctr, err);

@@ -185,6 +185,7 @@ __global__ __launch_bounds__(kScanBlock) void k_compact(GroupDev g, const int32_
           cs->stats[3] = 0;
           cs->stats[4] = 0;
           cs->stats[5] = tp;
+          cs->res_dup[t & 1u] = n - u - tp;
         }
       }
       if (s_fail && !status_of(g.ctr)) latch(g.ctr, ULA_ESTATE);   // a wait that never ended: give up cleanly

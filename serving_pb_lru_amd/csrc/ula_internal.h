@@ -90,6 +90,9 @@ struct alignas(64) Counters {
   int32_t free_lo, hfree_lo;
   // an append under ULA_PLACE_RING: GPU slots it took, of which free ones
   int32_t app_q, app_qfree;
+  // entries of a step's selection that repeat an earlier one (padding aside), by
+  // step parity: a gather of that selection with none reads its rows once
+  int32_t res_dup[2];
 };
 static_assert(sizeof(Counters) % 64 == 0, "counter block alignment");
 
