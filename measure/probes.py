@@ -30,6 +30,11 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with measure.build.build()")
+        # torch ships its own HIP runtime under the same soname as the one this
+        # library links; importing torch first makes the library bind to that
+        # runtime (loaded the other way round, the process ends up with two HIP
+        # runtimes and device calls fail)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         L.probe_move_rows.restype = ctypes.c_int
         L.probe_move_rows.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,

@@ -106,6 +106,11 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with serving_pb_lru_amd.build.build()")
+        # torch ships its own HIP runtime under the same soname as the one this
+        # library links; importing torch first makes the library bind to that
+        # runtime (loaded the other way round, the process ends up with two HIP
+        # runtimes and device calls fail)
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         for name, res, args in SIGNATURES:
             fn = getattr(L, name)
