@@ -109,7 +109,8 @@ def parse():
                         "step's lookup and marking run beside it). auto (default): one+gather for one "
                         "group, group+gather for two, two+gather for more (HIP spreads a process's "
                         "streams over four hardware queues, two of them left for created streams, "
-                        "and a queue runs its launches in order)")
+                        "and a queue runs its launches in order); without the gather stream under "
+                        "--placement ring")
     p.add_argument("--gather", choices=("layer", "split", "all"), default="split",
                    help="gathers per group step: one per layer (ula_gather); layer 0 alone, then the "
                         "later layers in one ula_gather_layers launch (default); or every layer in "
@@ -834,6 +835,10 @@ def main():
     streams = args.streams
     if streams == "auto":   # measured fastest (or as fast) on each workload
         streams = {1: "one+gather", 2: "group+gather"}.get(wl.groups, "two+gather")
+        if args.placement == "ring":
+            # appends that evict make each step's first launch wait for the last
+            # step's gathers, so a gather stream overlaps nothing there
+            streams = streams.split("+")[0]
     placement = 1 if args.placement == "ring" else 0
     r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode, replays=args.replays,
                 placement=placement, streams=streams)
