@@ -21,9 +21,11 @@ under tests/golden, the special case "ring longer than the trace" where PB-LRU
 must equal exact LRU bit for bit, the special case of a one-bucket ring, the
 special case "pool holds everything" where the gather is a plain fancy index,
 the closed-form row contents, the invariants, and the pages' claim that the
-hit rate stays within 0.1 percentage point of exact LRU. The readings of the
-pages that no such check can arbitrate (first-occurrence order, miss/victim
-pairing, the placement of appended entries, the initial residents, the
-capacity error) are "parity unpinned" by the pages: they are fixed only by the
-statements in this package, which the HIP engine implements independently.
+hit rate stays within 0.1 percentage point of exact LRU. Some points the pages
+leave open (first-occurrence order, miss/victim pairing, the placement of
+appended entries, the initial residents, the capacity error): no page passage
+decides them, so they are choices stated in this package, which the HIP engine
+implements independently; the checks above (the worked examples field by field,
+the exact-LRU equivalences, the error-path tests) still pin the functions that
+carry them.
 """
