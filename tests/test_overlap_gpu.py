@@ -146,3 +146,16 @@ def test_overlap_random_exact_lru_with_releases(seed):
     wl = tiny_workload(seed + 400, steps=10)
     wl = dataclasses.replace(wl, appends=1 + seed % 2, name=f"ovl_lru{seed}")
     run_overlapped(wl, None, policy=1, release_frac=0.3, seed=seed)
+
+
+@pytest.mark.parametrize("placement", [0, 1], ids=["lowest", "ring"])
+def test_overlap_bulk_appends(placement):
+    """300 appends per step, more than the step's first launch takes: they go
+    through the bulk append kernels (ula_append inside ula_append_step), which
+    under the second placement must also wait for the previous step's gathers."""
+    from synth.configs import Workload
+    wl = Workload(name=f"ovl_bulk{placement}", requests=300, ctx_fixed=2048, ctx_range=None,
+                  sets_per_request=1, draft_keep=0.0, groups=1, layers=2, k=64, pool_frac=0.0,
+                  pool_slots=40_000, ring=4, steps=5, appends=1, overlap=0.8, p_recent=0.7,
+                  window=256, row_bytes=64, seed=5)
+    run_overlapped(wl, None, placement=placement, release_frac=0.2, seed=placement)
