@@ -454,8 +454,6 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
     outs = {g: torch.empty((wl.layers, tr.n_sets, tr.k, wl.row_bytes), dtype=torch.uint8, device="cuda")
             for g in groups}
 
-    if streams == "group":
-        gstreams = [torch.cuda.Stream() for _ in groups]
     if streams.startswith("group"):
         gstreams = [torch.cuda.Stream() for _ in groups]
     elif streams.startswith("two"):
