@@ -177,6 +177,20 @@ def copy_ceiling(nbytes: int, copies: int = 64) -> None:
           flush=True)
 
 
+def schedule_for(groups: int, placement: str, streams: str = "auto") -> str:
+    """The stream schedule of --streams auto (measured fastest, or as fast, on each
+    workload): the steps on one stream for one group, a stream per group for two,
+    two alternating streams for more (HIP spreads a process's streams over four
+    hardware queues, and a queue runs its launches in order), with every gather on
+    a stream of its own; under the second placement of appends no gather stream,
+    since appends that evict make each step's first launch wait for the last
+    step's gathers. Any other value is returned as given."""
+    if streams != "auto":
+        return streams
+    s = {1: "one+gather", 2: "group+gather"}.get(groups, "two+gather")
+    return s.split("+")[0] if placement == "ring" else s
+
+
 def code_digest(path: str) -> str:
     """sha256 of a C/C++ source with its comments removed and whitespace runs
     collapsed: it changes when the code changes, not when a comment does."""
@@ -830,13 +844,7 @@ def main():
                            placement=args.placement)
 
     gather_mode = args.gather if wl.layers > 1 else "layer"   # one layer: the same launch
-    streams = args.streams
-    if streams == "auto":   # measured fastest (or as fast) on each workload
-        streams = {1: "one+gather", 2: "group+gather"}.get(wl.groups, "two+gather")
-        if args.placement == "ring":
-            # appends that evict make each step's first launch wait for the last
-            # step's gathers, so a gather stream overlaps nothing there
-            streams = streams.split("+")[0]
+    streams = schedule_for(wl.groups, args.placement, args.streams)
     placement = 1 if args.placement == "ring" else 0
     r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode, replays=args.replays,
                 placement=placement, streams=streams)

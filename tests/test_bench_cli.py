@@ -1,6 +1,7 @@
 """bench.py's host-side contract, without a GPU: a request for more than one GPU
-exits with a message before touching a device, and the kernel-code digest that
-keys the committed counter records ignores comments but not code."""
+exits with a message before touching a device, the kernel-code digest that keys
+the committed counter records ignores comments but not code, and the default
+stream schedule follows the number of groups and the placement of appends."""
 
 import os
 import subprocess
@@ -52,3 +53,18 @@ def test_traffic_record_needs_matching_code(tmp_path, monkeypatch):
     assert bench.gather_traffic("w", "split") == 12345           # a comment changes nothing
     (csrc / "k_gather.hip").write_text("int g() { return 2; }\n")
     assert bench.gather_traffic("w", "split") is None            # the code changed
+
+
+def test_auto_stream_schedule():
+    """--streams auto: a gather stream beside one step stream (one group), a stream
+    per group (two) or two alternating step streams (more); no gather stream under
+    the second placement of appends; an explicit schedule is kept."""
+    import bench
+    assert bench.schedule_for(1, "lowest") == "one+gather"
+    assert bench.schedule_for(2, "lowest") == "group+gather"
+    assert bench.schedule_for(4, "lowest") == "two+gather"
+    assert bench.schedule_for(24, "lowest") == "two+gather"
+    assert bench.schedule_for(1, "ring") == "one"
+    assert bench.schedule_for(2, "ring") == "group"
+    assert bench.schedule_for(4, "ring") == "two"
+    assert bench.schedule_for(4, "lowest", "group") == "group"
