@@ -49,7 +49,8 @@ prefetch experiment), --copy-ceiling and --calibrate-copy (plain device copies:
 the HBM rate at the gather's sizes, the counter scale), --link-probe and
 --gather-probe (plain moves of random rows, one direction per launch, and
 copy-engine transfers of the same bytes, measure/libprobes.so: the simple and
-the alternative forms of the miss path's and the gather's traffic).
+the alternative forms of the miss path's and the gather's traffic), --copy-probe
+(a contiguous device copy of a gather's bytes by launch size, the same library).
 """
 
 from __future__ import annotations
@@ -130,6 +131,11 @@ def parse():
     p.add_argument("--gather-probe", type=int, default=0, metavar="ROWS",
                    help="only time a plain gather of ROWS random HBM-pool slots into a contiguous "
                         "buffer with measure/libprobes.so, cold and warm, print one JSON line and exit")
+    p.add_argument("--copy-probe", type=str, default="", metavar="ROWS[,ROWS...]",
+                   help="only time a contiguous device copy of ROWS x --slot-bytes bytes (a gather's "
+                        "algorithmic bytes with no row indexing) with measure/libprobes.so, each launch "
+                        "behind another copy, over several launch shapes and beside torch's copy, print "
+                        "one JSON line and exit")
     p.add_argument("--slot-bytes", type=int, default=656, help="row size of the probes")
     p.add_argument("--pool-rows", type=int, default=0,
                    help="rows of the probe's pool (host pool for --link-probe, HBM pool for "
@@ -806,6 +812,11 @@ def main():
         return
     if args.copy_ceiling:
         copy_ceiling(args.copy_ceiling)
+        return
+    if args.copy_probe:
+        from measure import probes
+        rows = [int(x) for x in args.copy_probe.split(",")]
+        print(json.dumps({"probe": "copy", **probes.copy(rows, args.slot_bytes)}), flush=True)
         return
     if args.link_probe or args.gather_probe:
         from measure import probes

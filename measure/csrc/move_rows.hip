@@ -45,6 +45,27 @@ __global__ __launch_bounds__(kThreads) void k_move_rows(const uint8_t* __restric
   }
 }
 
+// A contiguous device copy of `pieces` 16-byte pieces, grid-stride, kUnroll pieces
+// in flight per lane, non-temporal stores: the plain form of the gather's HBM
+// traffic with no row indexing at all.
+__global__ __launch_bounds__(kThreads) void k_copy(const vec4u* __restrict__ src, vec4u* __restrict__ dst,
+                                                  uint32_t pieces) {
+  const uint32_t stride = gridDim.x * kThreads;
+  for (uint32_t base = blockIdx.x * kThreads + threadIdx.x; base < pieces; base += stride * kUnroll) {
+    vec4u v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = base + u * stride;
+      if (i < pieces) v[u] = src[i];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = base + u * stride;
+      if (i < pieces) __builtin_nontemporal_store(v[u], dst + i);
+    }
+  }
+}
+
 }  // namespace
 
 // mode 0: gather, dst[r] = src[idx[r]] for r < n; mode 1: scatter, dst[idx[r]] = src[r].
@@ -67,5 +88,21 @@ extern "C" int probe_move_rows(int mode, const void* src, const uint32_t* idx, v
     k_move_rows<false><<<blocks, kThreads, 0, s>>>(a, idx, b, n, C, row_bytes);
   else
     k_move_rows<true><<<blocks, kThreads, 0, s>>>(a, idx, b, n, C, row_bytes);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// dst[0, nbytes) = src[0, nbytes): device pointers, 16-byte aligned, nbytes a multiple
+// of 16. blocks: workgroups of 256 lanes (grid-stride). Returns 0, -1 for bad
+// arguments, -2 if the launch failed.
+extern "C" int probe_copy(const void* src, void* dst, uint64_t nbytes, int blocks, uint64_t stream) {
+  if (!src || !dst || nbytes % 16 || blocks < 1 || blocks > (1 << 20) ||
+      ((uintptr_t)src | (uintptr_t)dst) % 16)
+    return -1;
+  const uint64_t pieces = nbytes / 16;
+  if (pieces + (uint64_t)blocks * kThreads * kUnroll >= (1ull << 32)) return -1;
+  if (pieces == 0) return 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  k_copy<<<blocks, kThreads, 0, s>>>(static_cast<const vec4u*>(src), static_cast<vec4u*>(dst),
+                                     (uint32_t)pieces);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }

@@ -8,9 +8,18 @@ transfer of the same bytes (hipMemcpyAsync: alone each way, both ways at once, a
 device to host beside the zero-copy reads).
 
 gather(): `rows` random slots of an HBM pool read into a contiguous buffer, each
-launch after a 1 GiB write that pushes the pool out of the memory-side cache.
+launch right behind a 1 GiB write that pushes the pool out of the memory-side cache
+(cold), or right behind the same gather (warm).
 
-Times are per launch (events on the launch's stream, median of `reps`).
+copy(): a contiguous device copy of the same bytes as a gather of `rows` rows (no
+row indexing at all), each launch right behind another copy, over
+several launch shapes and beside torch's own copy: the HBM rate a launch of that
+size reaches.
+
+Times are per launch (events on the launch's stream, median of `reps`), each timed
+launch enqueued behind other work on its stream (link(): a 256 MiB device fill), so
+that the host's launch time stays out of the interval; the row indexes are checked
+once, before the timed launches.
 """
 
 import ctypes
@@ -39,14 +48,18 @@ def lib():
         L.probe_move_rows.restype = ctypes.c_int
         L.probe_move_rows.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_uint64]
+        L.probe_copy.restype = ctypes.c_int
+        L.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
+                                 ctypes.c_uint64]
         _lib = L
     return _lib
 
 
-def move_rows(mode: int, src, idx, dst, n: int, row_bytes: int, blocks: int, stream) -> None:
-    """mode 0: dst row r = src row idx[r]; mode 1: dst row idx[r] = src row r (r < n).
-    Every index must be a row of the buffer it indexes: checked here, before the launch."""
+def check_move(mode: int, src, idx, dst, n: int, row_bytes: int) -> None:
+    """Every index of a row move must be a row of the buffer it indexes, and the
+    contiguous side must hold n rows: checked on the host (with a device sync)."""
     import torch
+    assert mode in (0, 1)
     assert idx.dtype == torch.int32 and idx.is_cuda and idx.numel() >= n
     indexed = src if mode == 0 else dst
     other = dst if mode == 0 else src
@@ -55,21 +68,42 @@ def move_rows(mode: int, src, idx, dst, n: int, row_bytes: int, blocks: int, str
         lo = int(idx[:n].min().item())
         assert 0 <= lo and (hi + 1) * row_bytes <= indexed.numel(), "row index outside its buffer"
     assert n * row_bytes <= other.numel()
+
+
+def move_rows(mode: int, src, idx, dst, n: int, row_bytes: int, blocks: int, stream,
+              checked: bool = False) -> None:
+    """mode 0: dst row r = src row idx[r]; mode 1: dst row idx[r] = src row r (r < n).
+    Every index must be a row of the buffer it indexes: checked here before the launch,
+    unless the caller has run check_move on the same arguments (checked=True), as the
+    timed loops do so that the check's sync stays out of the timed interval."""
+    if not checked:
+        check_move(mode, src, idx, dst, n, row_bytes)
     rc = lib().probe_move_rows(mode, src.data_ptr(), idx.data_ptr(), dst.data_ptr(), n, row_bytes, blocks,
-                              stream.cuda_stream)
+                               stream.cuda_stream)
     if rc != 0:
         raise RuntimeError(f"probe_move_rows failed ({rc})")
 
 
-def _timed(first, second, s1, s2, reps, before=None):
+def copy_bytes(src, dst, nbytes: int, blocks: int, stream) -> None:
+    """dst[:nbytes] = src[:nbytes] (device tensors, checked here before the launch)."""
+    assert src.is_cuda and dst.is_cuda
+    assert nbytes <= src.numel() * src.element_size() and nbytes <= dst.numel() * dst.element_size()
+    rc = lib().probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, blocks, stream.cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"probe_copy failed ({rc})")
+
+
+def _timed(first, second, s1, s2, reps, lead):
     """Median over reps of the time from a start event on s1 to the later of the two
-    streams' end events (second may be None)."""
+    streams' end events (second may be None). lead(s1) is enqueued on s1 right before
+    the start event, so that the stream is still busy while the host enqueues the
+    timed launches (on an idle stream the start event fires at once and the host's
+    launch time falls into the interval)."""
     import torch
     out = []
     for _ in range(reps + 1):          # the first round warms up and is dropped
-        if before:
-            before()
         torch.cuda.synchronize()
+        lead(s1)
         st = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e2 = torch.cuda.Event(enable_timing=True)
@@ -99,13 +133,20 @@ def link(rows: int, slot_bytes: int, host_rows: int, shapes=(96, 256, 1024), rep
     wr_idx = torch.from_numpy(perm[rows:].copy()).cuda()
     dev_in = torch.empty(rows * slot_bytes, dtype=torch.uint8, device="cuda")
     dev_out = torch.randint(0, 256, (rows * slot_bytes,), dtype=torch.uint8, device="cuda")
+    busy = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    check_move(0, host, rd_idx, dev_in, rows, slot_bytes)
+    check_move(1, dev_out, wr_idx, host, rows, slot_bytes)
+
+    def lead(s):
+        with torch.cuda.stream(s):
+            busy.fill_(1)
 
     def rd(b):
-        return lambda s: move_rows(0, host, rd_idx, dev_in, rows, slot_bytes, b, s)
+        return lambda s: move_rows(0, host, rd_idx, dev_in, rows, slot_bytes, b, s, checked=True)
 
     def wr(b):
-        return lambda s: move_rows(1, dev_out, wr_idx, host, rows, slot_bytes, b, s)
+        return lambda s: move_rows(1, dev_out, wr_idx, host, rows, slot_bytes, b, s, checked=True)
 
     def d2h(s):
         with torch.cuda.stream(s):
@@ -117,13 +158,13 @@ def link(rows: int, slot_bytes: int, host_rows: int, shapes=(96, 256, 1024), rep
 
     ms = {}
     for b in shapes:
-        ms[f"read_{b}"] = _timed(rd(b), None, s1, s2, reps)
-        ms[f"write_{b}"] = _timed(wr(b), None, s1, s2, reps)
-        ms[f"both_{b}"] = _timed(rd(b), wr(b), s1, s2, reps)
-        ms[f"read_{b}+copy_d2h"] = _timed(rd(b), d2h, s1, s2, reps)
-    ms["copy_d2h"] = _timed(d2h, None, s1, s2, reps)
-    ms["copy_h2d"] = _timed(h2d, None, s1, s2, reps)
-    ms["copy_both"] = _timed(h2d, d2h, s1, s2, reps)
+        ms[f"read_{b}"] = _timed(rd(b), None, s1, s2, reps, lead=lead)
+        ms[f"write_{b}"] = _timed(wr(b), None, s1, s2, reps, lead=lead)
+        ms[f"both_{b}"] = _timed(rd(b), wr(b), s1, s2, reps, lead=lead)
+        ms[f"read_{b}+copy_d2h"] = _timed(rd(b), d2h, s1, s2, reps, lead=lead)
+    ms["copy_d2h"] = _timed(d2h, None, s1, s2, reps, lead=lead)
+    ms["copy_h2d"] = _timed(h2d, None, s1, s2, reps, lead=lead)
+    ms["copy_both"] = _timed(h2d, d2h, s1, s2, reps, lead=lead)
     mb = rows * slot_bytes / 1e6
     best = min((v, k) for k, v in ms.items() if k.startswith("both_"))
     return {"rows": rows, "slot_bytes": slot_bytes, "host_rows": host_rows, "MB_each_way": round(mb, 3),
@@ -144,18 +185,21 @@ def gather(rows: int, slot_bytes: int, pool_rows: int, shapes=(1024, 4096, 16384
     out = torch.empty(rows * slot_bytes, dtype=torch.uint8, device="cuda")
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    check_move(0, pool, idx, out, rows, slot_bytes)
     state = {"i": 0}
 
-    def evict_caches():
+    def evict_caches(s):
         state["i"] += 1
-        flush.fill_(state["i"] & 0xFF)
+        with torch.cuda.stream(s):
+            flush.fill_(state["i"] & 0xFF)
+
+    def run(b):
+        return lambda s: move_rows(0, pool, idx, out, rows, slot_bytes, b, s, checked=True)
 
     ms = {}
     for b in shapes:
-        ms[f"gather_{b}"] = _timed(lambda s: move_rows(0, pool, idx, out, rows, slot_bytes, b, s), None,
-                                   s1, s2, reps, before=evict_caches)
-        ms[f"gather_{b}_warm"] = _timed(lambda s: move_rows(0, pool, idx, out, rows, slot_bytes, b, s), None,
-                                        s1, s2, reps)
+        ms[f"gather_{b}"] = _timed(run(b), None, s1, s2, reps, lead=evict_caches)
+        ms[f"gather_{b}_warm"] = _timed(run(b), None, s1, s2, reps, lead=run(b))
     algo = 2 * rows * slot_bytes
     best = min((v, k) for k, v in ms.items() if not k.endswith("_warm"))
     return {"rows": rows, "slot_bytes": slot_bytes, "pool_rows": pool_rows, "algorithmic_MB": round(algo / 1e6, 3),
@@ -163,3 +207,53 @@ def gather(rows: int, slot_bytes: int, pool_rows: int, shapes=(1024, 4096, 16384
             "cold_best": {"shape": best[1], "us": round(best[0] * 1e3, 2),
                           "GBps": round(algo / best[0] / 1e6, 1),
                           "frac_of_peak": round(algo / best[0] / 1e6 / HBM_PEAK_GBPS, 4)}}
+
+
+def copy(rows_list, slot_bytes: int, shapes=(1024, 4096, 16384, 0), reps: int = 7) -> dict:
+    """Per size: a contiguous copy of rows x slot_bytes bytes (the algorithmic bytes of
+    a gather of that many rows: as many read as written), each launch right behind
+    another copy (of the same size, at least 256 MiB) on its stream, between other
+    buffers (as a gather runs in a step loop: its source is not in the caches, which
+    hold the previous launch's written lines). Shape 0 = one round per lane (as many
+    workgroups as the pieces need)."""
+    import torch
+    torch.cuda.set_device(0)
+    lead_min = 256 << 20      # long enough that the host has enqueued the timed launch
+    most = max(max(rows_list) * slot_bytes, lead_min)
+    src = torch.randint(0, 256, (2, most), dtype=torch.uint8, device="cuda")
+    dst = torch.empty((2, most), dtype=torch.uint8, device="cuda")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+
+    def lead(nb):
+        nb = max(nb, lead_min)
+        def run(s):
+            copy_bytes(src[0], dst[0], nb, -(-nb // (16 * 256 * 4)), s)
+        return run
+
+    def torch_copy(nb):
+        def run(s):
+            with torch.cuda.stream(s):
+                dst[1, :nb].copy_(src[1, :nb])
+        return run
+
+    sizes = []
+    for rows in rows_list:
+        nb = rows * slot_bytes
+        ms = {}
+        for b in shapes:
+            blocks = b or -(-nb // (16 * 256 * 4))
+            ms[f"copy_{b or 'one_round'}"] = _timed(lambda s: copy_bytes(src[1], dst[1], nb, blocks, s), None,
+                                                    s1, s2, reps, lead=lead(nb))
+        ms["torch_copy"] = _timed(torch_copy(nb), None, s1, s2, reps, lead=lead(nb))
+        dst[1, :nb].zero_()
+        copy_bytes(src[1], dst[1], nb, shapes[0] or 1024, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert torch.equal(dst[1, :nb], src[1, :nb]), "probe_copy moved the wrong bytes"
+        algo = 2 * nb
+        best = min((v, k) for k, v in ms.items() if k != "torch_copy")
+        sizes.append({"rows": rows, "algorithmic_MB": round(algo / 1e6, 3),
+                      "us": {k: round(v * 1e3, 2) for k, v in ms.items()},
+                      "best": {"shape": best[1], "us": round(best[0] * 1e3, 2),
+                               "GBps": round(algo / best[0] / 1e6, 1),
+                               "frac_of_peak": round(algo / best[0] / 1e6 / HBM_PEAK_GBPS, 4)}})
+    return {"slot_bytes": slot_bytes, "sizes": sizes}

@@ -37,8 +37,8 @@ def test_synth_device_library_exports_filler():
 
 
 def test_probe_library_exports_and_rejects_bad_arguments():
-    """bench.py's measurement probes: the row-move entry point refuses bad
-    arguments on the host, before any device call."""
+    """bench.py's measurement probes: the row-move and copy entry points refuse
+    bad arguments on the host, before any device call."""
     from measure import probes
     L = probes.lib()
     p = ctypes.c_void_p(16)
@@ -47,6 +47,12 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     assert L.probe_move_rows(0, p, p, p, 1, 650, 1, 0) == -1            # not 16-byte pieces
     assert L.probe_move_rows(1, p, p, p, 1, 656, 0, 0) == -1            # no workgroups
     assert L.probe_move_rows(0, p, p, p, 1 << 27, 656, 1, 0) == -1      # piece index past 32 bits
+    assert L.probe_copy(None, p, 16, 1, 0) == -1                          # null pointer
+    assert L.probe_copy(p, p, 24, 1, 0) == -1                             # not 16-byte pieces
+    assert L.probe_copy(ctypes.c_void_p(8), p, 16, 1, 0) == -1            # misaligned
+    assert L.probe_copy(p, p, 16, 0, 0) == -1                             # no workgroups
+    assert L.probe_copy(p, p, 1 << 36, 1, 0) == -1                        # piece index past 32 bits
+    assert L.probe_copy(p, p, 0, 1, 0) == 0                               # nothing to copy
 
 
 def _cfg(**kw):

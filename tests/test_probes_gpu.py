@@ -1,6 +1,7 @@
 """bench.py's measurement probes move the right bytes: a plain gather and scatter of
 random rows (measure/libprobes.so) against torch indexing, in HBM and between pinned
-host memory and HBM, with a ragged last round."""
+host memory and HBM, with a ragged last round, and a contiguous copy that stops at its
+end."""
 
 import numpy as np
 import pytest
@@ -35,3 +36,16 @@ def test_move_rows_gather_and_scatter(row_bytes, n, pool, blocks, host):
     want = torch.zeros((pool, row_bytes), dtype=torch.uint8)
     want[torch.from_numpy(idx_np).long()] = rows.cpu()
     assert torch.equal(dst.cpu(), want)
+
+
+@pytest.mark.parametrize("nbytes,blocks", [(16, 1), (656 * 777, 3), (16 * 1_000_003, 1024)])
+def test_copy_probe(nbytes, blocks):
+    import torch
+    from measure import probes
+    torch.cuda.set_device(0)
+    src = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device="cuda")
+    probes.copy_bytes(src, dst, nbytes, blocks, torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:nbytes], src[:nbytes])
+    assert not dst[nbytes:].any(), "copied past its end"
