@@ -25,24 +25,30 @@ Printed as one JSON line, with:
                 the larger direction's algorithmic bytes per launch (656 x
                 layers per missed row in, per evicted row of the previous step
                 out; both directions move at once) over its average duration,
-                from HIP events the launch records in its own dispatch, against
-                63 GB/s per direction; `traffic` is the counted host-link bytes
-                of rocprofv3's IO request counters where they were taken for the
-                same k_mark code. Otherwise the gather (below).
+                from HIP events the launch records in its own dispatch (in one
+                more replay of the same timed steps: the replays that give the
+                value carry no such events), against 63 GB/s per direction;
+                `traffic` is the counted host-link bytes of rocprofv3's IO
+                request counters where they were taken for the same k_mark
+                code. Otherwise the gather (below).
   roofline_other the other one: the gather against HBM peak (1312 algorithmic
                 bytes per gathered row-layer: 656 read + 656 written), its
                 average duration alone (the per-phase replay runs each group's
                 gathers right behind its step with nothing beside them), with
                 its duration inside the timed steps next to it;
   replays       the value of each of the three timed replays (value = median);
+                instrumented_ms_per_step is the step time of the replay that
+                carries the kernels' timing events;
   miss_path     the per-phase replay: phase times per group step, GPU hit
                 rate, and hipMemcpyAsync pinned-host peaks (each direction and
                 both at once) next to the host-link rates;
   cpu_baseline  the CPU oracle timed on this host's cores over the same steps
                 (a bounded sample; a baseline, not the target).
-Also: selections_per_s (selection entries resolved per second, all groups) and
+Also: selections_per_s (selection entries resolved per second, all groups),
 first_step_ms (step 1, the cold start with the most misses, timed alone, after
-every step kernel has run once on a tiny engine).
+every step kernel has run once on a tiny engine) and host_enqueue_ms_per_step (the
+host's time to enqueue a timed step's calls, median replay: near ms_per_step, the
+GPU waits for the host).
 
 Other modes print their own line and exit: --layer-prefetch (the later-layer
 prefetch experiment), --copy-ceiling and --calibrate-copy (plain device copies:
@@ -526,7 +532,7 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
     warm.sync()
     warm.close()
 
-    def timed_replay():
+    def timed_replay(timed_kernels: bool):
         eng = engine_for(tr, max_append=1 << 16, policy=policy, placement=placement)
         initial_load(eng, tr, groups, rows)
         torch.cuda.synchronize()
@@ -544,10 +550,11 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
                 torch.cuda.synchronize()
                 first_ms = s1.elapsed_time(e1)
         torch.cuda.synchronize()
-        # every gather and every step's host-link launch (k_mark) of the timed region
-        # records its kernel's start and end in its own dispatch (HIP events on the
-        # engine's stream, no launch overhead inside)
-        eng.set_timing(eng.TIMING_GATHER | eng.TIMING_LINK)
+        # timed_kernels: every gather and every step's host-link launch (k_mark) of
+        # the timed region records its kernel's start and end in its own dispatch
+        # (HIP events on the launch's stream, no launch overhead inside; they cost
+        # the host 6-13 us per launch to enqueue)
+        eng.set_timing(eng.TIMING_GATHER | eng.TIMING_LINK if timed_kernels else 0)
         eng.read_gather_timing()
         eng.read_link_timing()
         start = torch.cuda.Event(enable_timing=True)
@@ -560,6 +567,7 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
             run_step(eng, t)
         join()
         end.record()
+        enqueue = time.perf_counter() - t0   # the host's time to enqueue the K steps
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         eng.sync()   # raises if the device latched an error
@@ -567,16 +575,23 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
         l_ms, l_n = eng.read_link_timing()
         eng.set_timing(0)
         eng.close()
-        return dict(wall_s=wall, event_ms=start.elapsed_time(end), gather_ms=g_ms / max(g_n, 1),
+        return dict(wall_s=wall, enqueue_s=enqueue, event_ms=start.elapsed_time(end), gather_ms=g_ms / max(g_n, 1),
                     gather_launches=g_n, link_ms=l_ms / max(l_n, 1), link_launches=l_n, first_step_ms=first_ms)
 
+    # the replays that give the value carry no timing events; one more replay of
+    # the same steps, with them, gives the kernels' live durations
     runs = []
     for i in range(max(1, replays)):
-        runs.append(timed_replay())
+        runs.append(timed_replay(False))
         note(f"gpu replay {i + 1}: {runs[-1]['event_ms'] / K:.4f} ms per step")
     order = sorted(range(len(runs)), key=lambda i: runs[i]["wall_s"])
     res = dict(runs[order[len(order) // 2]])   # the median replay
     res["replay_walls_s"] = [r["wall_s"] for r in runs]
+    inst = timed_replay(True)
+    note(f"gpu replay with kernel timing: {inst['event_ms'] / K:.4f} ms per step")
+    for key in ("gather_ms", "gather_launches", "link_ms", "link_launches"):
+        res[key] = inst[key]
+    res["instrumented_ms_per_step"] = inst["event_ms"] / K
 
     # ---- per-phase replay (diagnostic, synchronises every step) --------------
     # also the step statistics: the host-link bytes of the timed steps (the engine
@@ -935,7 +950,10 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1, "steps": K,
         "selections_per_s": round(value / wl.layers, 1),
         "first_step_ms": None if r.get("first_step_ms") is None else round(r["first_step_ms"], 5),
-        "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": W, "ms_per_step": round(ms_per_step, 5),
+        "host_enqueue_ms_per_step": round(r["enqueue_s"] * 1e3 / K, 5),
+        "instrumented_ms_per_step": round(r["instrumented_ms_per_step"], 5),
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "u8", "data": "synthetic",
         "config": {"workload": wl.name, "requests": wl.requests,
                    "context": wl.ctx_fixed if wl.ctx_fixed else list(wl.ctx_range),
