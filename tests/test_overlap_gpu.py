@@ -35,7 +35,10 @@ def _expected(wl, g, sel, layer):
 
 
 def run_overlapped(wl, steps, policy=0, placement=0, release_frac=0.0, split=False, step_streams=1,
-                   seed=0):
+                   seed=0, release_side=False):
+    """release_side: each release goes to a stream of its own, ordered after its
+    group's step by an event, and the group's next step after the release by
+    another (the library alone orders the release after the step's gathers)."""
     import torch
     from oracle.exact_lru_np import ExactLRUArrays
     from oracle.replay import initial_load as oracle_load, new_group
@@ -46,7 +49,8 @@ def run_overlapped(wl, steps, policy=0, placement=0, release_frac=0.0, split=Fal
     G = wl.groups
     L = wl.layers
     say(f"overlapped {wl.name}: groups={G} layers={L} steps={tr.steps} policy={policy} "
-        f"placement={placement} releases={release_frac} split={split} step_streams={step_streams}")
+        f"placement={placement} releases={release_frac} split={split} step_streams={step_streams} "
+        f"release_side={release_side}")
     eng = engine_for(tr, max_append=1 << 15, policy=policy, placement=placement)
     rows = lambda las, g: rows_device(las, L, wl.row_bytes, wl.seed, g)
     try:
@@ -63,6 +67,7 @@ def run_overlapped(wl, steps, policy=0, placement=0, release_frac=0.0, split=Fal
         torch.cuda.synchronize()
         step_s = [torch.cuda.Stream() for _ in range(step_streams)]
         gather_s = torch.cuda.Stream()
+        rel_s = torch.cuda.Stream()
         done = [torch.cuda.Event() for _ in range(G)]
         for t in range(1, tr.steps + 1):
             app = tr.appends(t)
@@ -80,7 +85,14 @@ def run_overlapped(wl, steps, policy=0, placement=0, release_frac=0.0, split=Fal
                     for l in range(L):
                         eng.gather(g, l, dsel[g][t - 1], out=o[l], stream=gather_s)
                 if t in rel[g] and rel[g][t].size:
-                    eng.release(g, rel[g][t], stream=s)
+                    if release_side:
+                        rel_s.wait_event(done[g])
+                        eng.release(g, rel[g][t], stream=rel_s)
+                        back = torch.cuda.Event()
+                        back.record(rel_s)
+                        s.wait_event(back)
+                    else:
+                        eng.release(g, rel[g][t], stream=s)
         torch.cuda.synchronize()
         eng.sync()
         for g in range(G):
@@ -139,6 +151,16 @@ def test_overlap_random_with_releases(seed, placement):
     wl = dataclasses.replace(wl, appends=1 + seed % 3, groups=1 + seed % 2, name=f"ovl{seed}")
     run_overlapped(wl, None, placement=placement, release_frac=0.3, seed=seed,
                    step_streams=1 + seed % 2)
+
+
+@pytest.mark.parametrize("seed", range(3))
+@pytest.mark.parametrize("placement", [0, 1], ids=["lowest", "ring"])
+def test_overlap_releases_on_their_own_stream(seed, placement):
+    """Releases on a third stream: ordered after the step and before the next
+    step by the caller's events, after the step's gathers by the library."""
+    wl = tiny_workload(seed + 500, steps=10)
+    wl = dataclasses.replace(wl, appends=1 + seed % 3, groups=1 + seed % 2, name=f"ovl_rel{seed}")
+    run_overlapped(wl, None, placement=placement, release_frac=0.4, seed=seed, release_side=True)
 
 
 @pytest.mark.parametrize("seed", range(4))
