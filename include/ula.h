@@ -193,7 +193,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
  * fully initialised workspace whatever an earlier context left in it.
  * The call allocates no device memory and no pinned host memory (the context
  * itself is ordinary host memory; host_pinned is still the caller's pool). Such
- * a context has no pinned staging buffers, so ula_append of more than 256
+ * a context has no pinned staging buffers, so ula_append of more than 128
  * entries or of host-resident rows, and ula_release, copy addresses and rows
  * from the caller's memory and wait for the copy before they return; the events
  * of step timing and of the ordering of host-link launches across streams are
@@ -210,6 +210,10 @@ int ula_init_static(const ula_config* cfg, void* host_pinned, uint64_t stream, u
  * host pool (see above). la_host: n addresses in host memory. rows: n x layers_per_group x
  * row_bytes bytes, packed, in device memory (rows_on_device = 1) or host memory
  * (rows_on_device = 0); rows must stay valid until the stream reaches the call.
+ * An append of more than 128 entries, or of host-resident rows, copies its
+ * addresses through one of four pinned staging buffers of the group: with all
+ * four still in use by enqueued appends, the call first waits for the oldest to
+ * be consumed (the host runs at most four such appends ahead of the device).
  * Validated on the host first: ULA_EINVAL (bad g or n < 0), ULA_ERANGE (address
  * outside [0, N)), ULA_EDUP (already appended or repeated), ULA_EHOSTFULL (not
  * enough free slots in total); nothing changes on error. */
@@ -261,7 +265,7 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
  * step produces are appended, then the step selects among all entries):
  * exactly ula_append(ctx, group, n_app, la_host, rows, rows_on_device, stream)
  * followed by ula_step(ctx, group, n_sets, k, sel_dev, stream), with the same
- * arguments, placement and results, in fewer launches: an append of at most 256
+ * arguments, placement and results, in fewer launches: an append of at most 128
  * entries (and at most max_append) with rows in device memory runs in the
  * step's first launch, beside the de-duplication, which does not read the
  * mapping table; other appends run as ula_append does, before the step.

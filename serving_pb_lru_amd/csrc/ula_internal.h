@@ -189,7 +189,10 @@ struct PlanArgs {
   int8_t order[kMaxBuckets + 1];
 };
 
-constexpr int kSmallAppend = 256;   // appends up to this size run as one workgroup
+// Appends up to this size run as one workgroup (in the step's first launch under
+// ula_append_step); larger ones through the multi-workgroup plan / extract / place
+// kernels, which place 256 rows per group step faster than one workgroup does.
+constexpr int kSmallAppend = 128;
 
 struct SmallAppend {
   int32_t n;

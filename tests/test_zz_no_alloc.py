@@ -39,7 +39,7 @@ def _run_pair(tr, max_append):
     try:
         order = tr.initial_load_order()
         for eng in (ref, sta):
-            eng.append(0, order, rows(order))           # one large append (more than 256 entries)
+            eng.append(0, order, rows(order))           # one large append (more than 128 entries)
         oracle_load(ora, tr, 0)
         assert digest(sta.export_state(0)) == digest(ref.export_state(0)) == digest(ora.export_state())
         released = set()
