@@ -1005,13 +1005,23 @@ int ula_read_rows(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host
     if (rc) return rc;
   }
   const GroupDev& g = ctx->groups[group].d;
-  std::vector<uint32_t> map(d.N);
-  HIP_TRY(hipMemcpy(map.data(), g.map, 4 * d.N, hipMemcpyDeviceToHost));
+  // the requested entries' locations: the whole mapping table when they are a
+  // large share of it, else their words one by one (the table may hold up to
+  // 2^31 - 1 words, 8.6 GB)
+  std::vector<uint32_t> where(n);
+  if ((int64_t)n * 64 >= d.N) {
+    std::vector<uint32_t> map(d.N);
+    HIP_TRY(hipMemcpy(map.data(), g.map, 4 * d.N, hipMemcpyDeviceToHost));
+    for (int32_t i = 0; i < n; ++i) where[i] = map[la_host[i]];
+  } else {
+    for (int32_t i = 0; i < n; ++i)
+      HIP_TRY(hipMemcpy(&where[i], g.map + la_host[i], 4, hipMemcpyDeviceToHost));
+  }
   for (int32_t i = 0; i < n; ++i)
-    if (map[la_host[i]] == kAbsent) return ULA_ERANGE;
+    if (where[i] == kAbsent) return ULA_ERANGE;
   uint8_t* o = static_cast<uint8_t*>(out_host);
   for (int32_t i = 0; i < n; ++i) {
-    const uint32_t loc = map[la_host[i]];
+    const uint32_t loc = where[i];
     if (loc & kHostBit) {
       HIP_TRY(hipMemcpy(o + (size_t)i * d.slot_bytes,
                         g.host + (size_t)(loc & ~kHostBit) * d.slot_bytes, d.slot_bytes,
