@@ -100,6 +100,9 @@ def parse():
     p.add_argument("--groups", type=int, default=0,
                    help="run only the first N layer groups of the workload (groups are independent; "
                         "for workloads whose pinned host pools exceed one host's memory)")
+    p.add_argument("--first-group", type=int, default=0, metavar="G0",
+                   help="with --groups N: run groups G0..G0+N-1 of the workload instead of the first N "
+                        "(the same traces as in the full workload; no CPU baseline, no counters)")
     p.add_argument("--policy", choices=("pblru", "lru"), default="pblru",
                    help="replacement policy: PB-LRU (the pages' policy) or exact LRU (the one it is "
                         "compared against); the CPU baseline is reported for PB-LRU only")
@@ -458,7 +461,8 @@ def gather_all_layers(eng, g, sel, outs, layers, mode, stream=None):
 
 
 def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str = "layer",
-            replays: int = 3, placement: int = 0, streams: str = "one") -> dict:
+            replays: int = 3, placement: int = 0, streams: str = "one", group0: int = 0) -> dict:
+    """group0: engine group g runs the workload's group group0 + g (its rows and selections)."""
     import statistics
 
     import torch
@@ -471,10 +475,10 @@ def gpu_run(tr, W: int, K: int, phases: bool, policy: int = 0, gather_mode: str 
     torch.cuda.set_device(0)
     stream = torch.cuda.Stream()   # a created stream: launches on the legacy null stream cost more
     torch.cuda.set_stream(stream)
-    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, g)
+    rows = lambda las, g: rows_device(las, wl.layers, wl.row_bytes, wl.seed, group0 + g)
 
     # inputs for every step, resident in HBM before timing
-    sels = {g: [torch.from_numpy(s).cuda() for s in tr.selections(g)] for g in groups}
+    sels = {g: [torch.from_numpy(s).cuda() for s in tr.selections(group0 + g)] for g in groups}
     apps = [tr.appends(t) for t in range(1, tr.steps + 1)]
     app_rows = {g: [rows(a, g) for a in apps] for g in groups}
     # one buffer per group: its layers' gathered rows one after the other
@@ -861,12 +865,18 @@ def main():
         # the first N groups are the same traces as in the full workload (each
         # group's selections come from its own seeded stream)
         wl = dataclasses.replace(wl, groups=min(args.groups, wl.groups))
+    g0 = args.first_group
+    if g0:
+        if not args.groups or not 0 < g0 < groups_total:
+            print(f"--first-group {g0} needs --groups and 0 < G0 < {groups_total}", file=sys.stderr)
+            sys.exit(2)
+        wl = dataclasses.replace(wl, groups=min(args.groups, groups_total - g0))
     tr = Trace(wl, steps=max(W + K, 1))
     per_step = rows_per_step(tr)
 
     policy = 1 if args.policy == "lru" else 0
     cpu = None
-    if not args.no_cpu_baseline and policy == 0:
+    if not args.no_cpu_baseline and policy == 0 and not g0:
         cpu = cpu_baseline(tr, W, K, args.cpu_seconds, parallel=not args.no_cpu_parallel,
                            placement=args.placement)
 
@@ -874,7 +884,7 @@ def main():
     streams = schedule_for(wl.groups, args.placement, args.streams)
     placement = 1 if args.placement == "ring" else 0
     r = gpu_run(tr, W, K, not args.no_phases, policy, gather_mode, replays=args.replays,
-                placement=placement, streams=streams)
+                placement=placement, streams=streams, group0=g0)
     value = per_step * K / r["wall_s"]
     ms_per_step = r["event_ms"] / K
     replay_values = [round(per_step * K / w, 1) for w in r["replay_walls_s"]]
@@ -895,7 +905,7 @@ def main():
     g_gbs = g_bytes / (g_ms * 1e-3) / 1e9
     gather_line = {"bound": "hbm", "kernel": "k_gather", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
                    "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
-                   "traffic": gather_traffic(wl.name, gather_mode),
+                   "traffic": None if g0 else gather_traffic(wl.name, gather_mode),
                    "bytes_per_launch": round(g_bytes), "launch_ms": round(g_ms, 5),
                    "launch_ms_in_timed_steps": round(float(r["gather_ms"]), 5),
                    "measured": "alone (per-phase replay)" if r.get("gather_alone_ms") else "timed steps",
@@ -924,7 +934,7 @@ def main():
                              "evicted row of the previous step out; both directions move "
                              "concurrently) over the launch's average duration, which also marks "
                              "hits and plans and extracts the victims"}
-        counted = link_traffic(wl.name) if not policy else None
+        counted = link_traffic(wl.name) if not policy and not g0 else None
         if counted:   # counted host-link bytes per launch, the roofline's direction and both
             link_line["traffic"] = counted["read"] if up >= down else counted["write"]
             link_line["traffic_read_write"] = [counted["read"], counted["write"]]
@@ -959,7 +969,7 @@ def main():
         "config": {"workload": wl.name, "requests": wl.requests,
                    "context": wl.ctx_fixed if wl.ctx_fixed else list(wl.ctx_range),
                    "sets_per_request": wl.sets_per_request, "groups": wl.groups,
-                   "groups_of_workload": groups_total,
+                   "groups_of_workload": groups_total, **({"first_group": g0} if g0 else {}),
                    "layers_per_group": wl.layers, "k": wl.k, "gpu_slots": tr.P, "host_slots": tr.H,
                    "ring": wl.ring, "row_bytes": wl.row_bytes, "overlap": wl.overlap,
                    "policy": "exact LRU" if policy else "PB-LRU", "gather": gather_mode,
