@@ -19,6 +19,18 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
+def test_first_group_needs_a_group_count_in_range():
+    """--first-group picks groups G0.. of a workload: refused (before any device call)
+    without --groups or with G0 outside the workload's groups."""
+    for extra in (["--first-group", "6"], ["--groups", "6", "--first-group", "24"],
+                  ["--groups", "2", "--first-group", "2"]):
+        wl = "evict_r256_128k_g2" if extra[-1] == "2" else "r64_64k128k_g24x3"
+        r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", wl] + extra,
+                           capture_output=True, text=True, timeout=300)
+        assert r.returncode == 2, extra
+        assert "--first-group" in r.stderr and r.stdout == ""
+
+
 def test_code_digest_ignores_comments_only(tmp_path):
     import bench
     base = "int f(int a) {\n  return a + 1;  // one more\n}\n/* block\n   comment */\n"
