@@ -7,14 +7,14 @@ once on two streams, over several launch shapes; beside them a contiguous copy-e
 transfer of the same bytes (hipMemcpyAsync: alone each way, both ways at once, and
 device to host beside the zero-copy reads).
 
-gather(): `rows` random slots of an HBM pool read into a contiguous buffer, each
-launch right behind a 1 GiB write that pushes the pool out of the memory-side cache
-(cold), or right behind the same gather (warm).
+gather(): `rows` random slots of an HBM pool read into a contiguous buffer, with
+plain and with non-temporal loads, each launch right behind a 1 GiB write that pushes
+the pool out of the memory-side cache (cold), or right behind the same gather (warm).
 
 copy(): a contiguous device copy of the same bytes as a gather of `rows` rows (no
-row indexing at all), each launch right behind another copy, over
-several launch shapes and beside torch's own copy: the HBM rate a launch of that
-size reaches.
+row indexing at all), with plain and with non-temporal loads, each launch right behind
+another copy, over several launch shapes and beside torch's own copy: the HBM rate a
+launch of that size reaches.
 
 Times are per launch (events on the launch's stream, median of `reps`), each timed
 launch enqueued behind other work on its stream (link(): a 256 MiB device fill), so
@@ -50,7 +50,7 @@ def lib():
                                      ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int, ctypes.c_uint64]
         L.probe_copy.restype = ctypes.c_int
         L.probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int,
-                                 ctypes.c_uint64]
+                                 ctypes.c_int, ctypes.c_uint64]
         _lib = L
     return _lib
 
@@ -59,10 +59,10 @@ def check_move(mode: int, src, idx, dst, n: int, row_bytes: int) -> None:
     """Every index of a row move must be a row of the buffer it indexes, and the
     contiguous side must hold n rows: checked on the host (with a device sync)."""
     import torch
-    assert mode in (0, 1)
+    assert mode in (0, 1, 2)
     assert idx.dtype == torch.int32 and idx.is_cuda and idx.numel() >= n
-    indexed = src if mode == 0 else dst
-    other = dst if mode == 0 else src
+    indexed = src if mode != 1 else dst
+    other = dst if mode != 1 else src
     if n:
         hi = int(idx[:n].max().item())
         lo = int(idx[:n].min().item())
@@ -72,7 +72,8 @@ def check_move(mode: int, src, idx, dst, n: int, row_bytes: int) -> None:
 
 def move_rows(mode: int, src, idx, dst, n: int, row_bytes: int, blocks: int, stream,
               checked: bool = False) -> None:
-    """mode 0: dst row r = src row idx[r]; mode 1: dst row idx[r] = src row r (r < n).
+    """mode 0: dst row r = src row idx[r]; mode 1: dst row idx[r] = src row r (r < n);
+    mode 2: as mode 0 with non-temporal loads.
     Every index must be a row of the buffer it indexes: checked here before the launch,
     unless the caller has run check_move on the same arguments (checked=True), as the
     timed loops do so that the check's sync stays out of the timed interval."""
@@ -84,11 +85,12 @@ def move_rows(mode: int, src, idx, dst, n: int, row_bytes: int, blocks: int, str
         raise RuntimeError(f"probe_move_rows failed ({rc})")
 
 
-def copy_bytes(src, dst, nbytes: int, blocks: int, stream) -> None:
-    """dst[:nbytes] = src[:nbytes] (device tensors, checked here before the launch)."""
+def copy_bytes(src, dst, nbytes: int, blocks: int, stream, nt: bool = False) -> None:
+    """dst[:nbytes] = src[:nbytes] (device tensors, checked here before the launch);
+    nt: non-temporal loads."""
     assert src.is_cuda and dst.is_cuda
     assert nbytes <= src.numel() * src.element_size() and nbytes <= dst.numel() * dst.element_size()
-    rc = lib().probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, blocks, stream.cuda_stream)
+    rc = lib().probe_copy(src.data_ptr(), dst.data_ptr(), nbytes, blocks, int(nt), stream.cuda_stream)
     if rc != 0:
         raise RuntimeError(f"probe_copy failed ({rc})")
 
@@ -193,13 +195,14 @@ def gather(rows: int, slot_bytes: int, pool_rows: int, shapes=(1024, 4096, 16384
         with torch.cuda.stream(s):
             flush.fill_(state["i"] & 0xFF)
 
-    def run(b):
-        return lambda s: move_rows(0, pool, idx, out, rows, slot_bytes, b, s, checked=True)
+    def run(b, mode):
+        return lambda s: move_rows(mode, pool, idx, out, rows, slot_bytes, b, s, checked=True)
 
     ms = {}
-    for b in shapes:
-        ms[f"gather_{b}"] = _timed(run(b), None, s1, s2, reps, lead=evict_caches)
-        ms[f"gather_{b}_warm"] = _timed(run(b), None, s1, s2, reps, lead=run(b))
+    for mode, tag in ((0, ""), (2, "_nt")):
+        for b in shapes:
+            ms[f"gather{tag}_{b}"] = _timed(run(b, mode), None, s1, s2, reps, lead=evict_caches)
+            ms[f"gather{tag}_{b}_warm"] = _timed(run(b, mode), None, s1, s2, reps, lead=run(b, mode))
     algo = 2 * rows * slot_bytes
     best = min((v, k) for k, v in ms.items() if not k.endswith("_warm"))
     return {"rows": rows, "slot_bytes": slot_bytes, "pool_rows": pool_rows, "algorithmic_MB": round(algo / 1e6, 3),
@@ -240,15 +243,17 @@ def copy(rows_list, slot_bytes: int, shapes=(1024, 4096, 16384, 0), reps: int = 
     for rows in rows_list:
         nb = rows * slot_bytes
         ms = {}
-        for b in shapes:
-            blocks = b or -(-nb // (16 * 256 * 4))
-            ms[f"copy_{b or 'one_round'}"] = _timed(lambda s: copy_bytes(src[1], dst[1], nb, blocks, s), None,
-                                                    s1, s2, reps, lead=lead(nb))
+        for nt in (False, True):
+            for b in shapes:
+                blocks = b or -(-nb // (16 * 256 * 4))
+                ms[f"copy{'_nt' if nt else ''}_{b or 'one_round'}"] = _timed(
+                    lambda s: copy_bytes(src[1], dst[1], nb, blocks, s, nt=nt), None, s1, s2, reps, lead=lead(nb))
         ms["torch_copy"] = _timed(torch_copy(nb), None, s1, s2, reps, lead=lead(nb))
-        dst[1, :nb].zero_()
-        copy_bytes(src[1], dst[1], nb, shapes[0] or 1024, torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        assert torch.equal(dst[1, :nb], src[1, :nb]), "probe_copy moved the wrong bytes"
+        for nt in (False, True):
+            dst[1, :nb].zero_()
+            copy_bytes(src[1], dst[1], nb, shapes[0] or 1024, torch.cuda.current_stream(), nt=nt)
+            torch.cuda.synchronize()
+            assert torch.equal(dst[1, :nb], src[1, :nb]), "probe_copy moved the wrong bytes"
         algo = 2 * nb
         best = min((v, k) for k, v in ms.items() if k != "torch_copy")
         sizes.append({"rows": rows, "algorithmic_MB": round(algo / 1e6, 3),

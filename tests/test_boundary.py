@@ -42,17 +42,18 @@ def test_probe_library_exports_and_rejects_bad_arguments():
     from measure import probes
     L = probes.lib()
     p = ctypes.c_void_p(16)
-    assert L.probe_move_rows(2, p, p, p, 1, 656, 1, 0) == -1            # no such mode
+    assert L.probe_move_rows(3, p, p, p, 1, 656, 1, 0) == -1            # no such mode
+    assert L.probe_move_rows(-1, p, p, p, 1, 656, 1, 0) == -1           # no such mode
     assert L.probe_move_rows(0, None, p, p, 1, 656, 1, 0) == -1         # null pointer
     assert L.probe_move_rows(0, p, p, p, 1, 650, 1, 0) == -1            # not 16-byte pieces
     assert L.probe_move_rows(1, p, p, p, 1, 656, 0, 0) == -1            # no workgroups
     assert L.probe_move_rows(0, p, p, p, 1 << 27, 656, 1, 0) == -1      # piece index past 32 bits
-    assert L.probe_copy(None, p, 16, 1, 0) == -1                          # null pointer
-    assert L.probe_copy(p, p, 24, 1, 0) == -1                             # not 16-byte pieces
-    assert L.probe_copy(ctypes.c_void_p(8), p, 16, 1, 0) == -1            # misaligned
-    assert L.probe_copy(p, p, 16, 0, 0) == -1                             # no workgroups
-    assert L.probe_copy(p, p, 1 << 36, 1, 0) == -1                        # piece index past 32 bits
-    assert L.probe_copy(p, p, 0, 1, 0) == 0                               # nothing to copy
+    assert L.probe_copy(None, p, 16, 1, 0, 0) == -1                          # null pointer
+    assert L.probe_copy(p, p, 24, 1, 1, 0) == -1                             # not 16-byte pieces
+    assert L.probe_copy(ctypes.c_void_p(8), p, 16, 1, 0, 0) == -1            # misaligned
+    assert L.probe_copy(p, p, 16, 0, 1, 0) == -1                             # no workgroups
+    assert L.probe_copy(p, p, 1 << 36, 1, 0, 0) == -1                        # piece index past 32 bits
+    assert L.probe_copy(p, p, 0, 1, 1, 0) == 0                               # nothing to copy
 
 
 def _cfg(**kw):

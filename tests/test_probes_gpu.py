@@ -1,7 +1,7 @@
-"""bench.py's measurement probes move the right bytes: a plain gather and scatter of
-random rows (measure/libprobes.so) against torch indexing, in HBM and between pinned
-host memory and HBM, with a ragged last round, and a contiguous copy that stops at its
-end."""
+"""bench.py's measurement probes move the right bytes: a plain gather (plain and
+non-temporal loads) and scatter of random rows (measure/libprobes.so) against torch
+indexing, in HBM and between pinned host memory and HBM, with a ragged last round, and
+a contiguous copy (both loads) that stops at its end."""
 
 import numpy as np
 import pytest
@@ -25,9 +25,11 @@ def test_move_rows_gather_and_scatter(row_bytes, n, pool, blocks, host):
     src = src.pin_memory() if host else src.cuda()
     out = torch.zeros((n, row_bytes), dtype=torch.uint8, device="cuda")
     s = torch.cuda.current_stream()
-    probes.move_rows(0, src, idx, out, n, row_bytes, blocks, s)
-    torch.cuda.synchronize()
-    assert torch.equal(out.cpu(), src.cpu()[torch.from_numpy(idx_np).long()])
+    for mode in (0, 2):                       # plain and non-temporal loads
+        out.zero_()
+        probes.move_rows(mode, src, idx, out, n, row_bytes, blocks, s)
+        torch.cuda.synchronize()
+        assert torch.equal(out.cpu(), src.cpu()[torch.from_numpy(idx_np).long()]), mode
     rows = torch.randint(0, 256, (n, row_bytes), dtype=torch.uint8, device="cuda")
     dst = torch.zeros((pool, row_bytes), dtype=torch.uint8)
     dst = dst.pin_memory() if host else dst.cuda()
@@ -45,7 +47,9 @@ def test_copy_probe(nbytes, blocks):
     torch.cuda.set_device(0)
     src = torch.randint(0, 256, (nbytes + 64,), dtype=torch.uint8, device="cuda")
     dst = torch.zeros(nbytes + 64, dtype=torch.uint8, device="cuda")
-    probes.copy_bytes(src, dst, nbytes, blocks, torch.cuda.current_stream())
-    torch.cuda.synchronize()
-    assert torch.equal(dst[:nbytes], src[:nbytes])
-    assert not dst[nbytes:].any(), "copied past its end"
+    for nt in (False, True):                  # plain and non-temporal loads
+        dst.zero_()
+        probes.copy_bytes(src, dst, nbytes, blocks, torch.cuda.current_stream(), nt=nt)
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:nbytes], src[:nbytes]), nt
+        assert not dst[nbytes:].any(), "copied past its end"
