@@ -48,7 +48,8 @@ Also: selections_per_s (selection entries resolved per second, all groups),
 first_step_ms (step 1, the cold start with the most misses, timed alone, after
 every step kernel has run once on a tiny engine) and host_enqueue_ms_per_step (the
 host's time to enqueue a timed step's calls, median replay, including any wait of
-an append of more than 128 entries for a staging buffer: near ms_per_step with no
+an append of more than 128 entries (256 under exact LRU) for a staging buffer: near
+ms_per_step with no
 such appends, the GPU waits for the host).
 
 Other modes print their own line and exit: --layer-prefetch (the later-layer

@@ -194,7 +194,7 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
  * The call allocates no device memory and no pinned host memory (the context
  * itself is ordinary host memory; host_pinned is still the caller's pool). Such
  * a context has no pinned staging buffers, so ula_append of more than 128
- * entries or of host-resident rows, and ula_release, copy addresses and rows
+ * entries (256 under ULA_POLICY_LRU) or of host-resident rows, and ula_release, copy addresses and rows
  * from the caller's memory and wait for the copy before they return; the events
  * of step timing and of the ordering of host-link launches across streams are
  * created by the call that first needs them. Everything else behaves as for a
@@ -210,7 +210,8 @@ int ula_init_static(const ula_config* cfg, void* host_pinned, uint64_t stream, u
  * host pool (see above). la_host: n addresses in host memory. rows: n x layers_per_group x
  * row_bytes bytes, packed, in device memory (rows_on_device = 1) or host memory
  * (rows_on_device = 0); rows must stay valid until the stream reaches the call.
- * An append of more than 128 entries, or of host-resident rows, copies its
+ * An append of more than 128 entries (256 under ULA_POLICY_LRU), or of
+ * host-resident rows, copies its
  * addresses through one of four pinned staging buffers of the group: with all
  * four still in use by enqueued appends, the call first waits for the oldest to
  * be consumed (the host runs at most four such appends ahead of the device).
@@ -266,7 +267,8 @@ int ula_step(ula_ctx* ctx, int32_t group, int32_t n_sets, int32_t k, const int32
  * exactly ula_append(ctx, group, n_app, la_host, rows, rows_on_device, stream)
  * followed by ula_step(ctx, group, n_sets, k, sel_dev, stream), with the same
  * arguments, placement and results, in fewer launches: an append of at most 128
- * entries (and at most max_append) with rows in device memory runs in the
+ * entries (256 under ULA_POLICY_LRU; and at most max_append) with rows in device
+ * memory runs in the
  * step's first launch, beside the de-duplication, which does not read the
  * mapping table; other appends run as ula_append does, before the step.
  * n_app = 0 is a plain step. Both parts are validated on the host before

@@ -628,7 +628,7 @@ int ula_append(ula_ctx* ctx, int32_t group, int32_t n, const int32_t* la_host, c
     const int rc = wait_gathers(gh, s);
     if (rc) return rc;
   }
-  if (n <= kSmallAppend && n <= d.maxApp && rows_on_device) {
+  if (n <= small_append_limit(d.policy) && n <= d.maxApp && rows_on_device) {
     // decode-time appends: one workgroup, addresses passed by value
     SmallAppend a{};
     a.n = n;
@@ -873,7 +873,8 @@ int ula_append_step(ula_ctx* ctx, int32_t group, int32_t n_app, const int32_t* l
     const int rc = validate_append(ctx, ctx->groups[group], n_app, la_host);
     if (rc) return rc;
   }
-  if (n_app > 0 && n_app <= kSmallAppend && n_app <= ctx->dims.maxApp && rows_on_device) {
+  if (n_app > 0 && n_app <= small_append_limit(ctx->dims.policy) && n_app <= ctx->dims.maxApp &&
+      rows_on_device) {
     SmallAppend a{};
     a.n = n_app;
     a.ring = ctx->dims.placement == ULA_PLACE_RING ? 1 : 0;

@@ -189,10 +189,15 @@ struct PlanArgs {
   int8_t order[kMaxBuckets + 1];
 };
 
-// Appends up to this size run as one workgroup (in the step's first launch under
-// ula_append_step); larger ones through the multi-workgroup plan / extract / place
-// kernels, which place 256 rows per group step faster than one workgroup does.
-constexpr int kSmallAppend = 128;
+// Appends of up to small_append_limit(policy) entries run as one workgroup (in the
+// step's first launch under ula_append_step); larger ones through the
+// multi-workgroup plan / extract / place kernels. Under PB-LRU the limit is 128:
+// the multi-workgroup kernels place 256 rows per group step faster than the one
+// workgroup, which the step's first launch would wait for. Under exact LRU it is
+// 256: its step already has more launches in a row after the host link, and three
+// more launches before the step cost it more than the one workgroup does.
+constexpr int kSmallAppend = 256;   // the most entries one workgroup places
+inline int small_append_limit(int policy) { return policy == ULA_POLICY_LRU ? kSmallAppend : 128; }
 
 struct SmallAppend {
   int32_t n;
