@@ -29,7 +29,11 @@ namespace ula {
 // and a lane keeps about one host request in flight. That depth is deliberate:
 // issuing every piece's records first and then all U host reads together (U
 // host reads in flight per lane) made the default workload's link phase 7%
-// slower and the eviction-heavy one 9% slower, with the same link bytes.
+// slower and the eviction-heavy one 9% slower, with the same link bytes. The
+// interleaved loop further below keeps one piece per direction in flight too,
+// but loads the next piece's records while the current piece's data is on its
+// way (the eviction-heavy workload's link launch 4.09 -> 3.98 ms); the same in
+// these two loops changed the one-group workload's steps by less than 1%.
 
 // Missed rows of step t (all layers, one contiguous slot_bytes run each) into
 // miss_rows[i], from the host pool or from the staging copy of step t - 1. m is
