@@ -193,9 +193,11 @@ int ula_init(const ula_config* cfg, void* dev_ws, void* host_pinned, uint64_t st
  * fully initialised workspace whatever an earlier context left in it.
  * The call allocates no device memory and no pinned host memory (the context
  * itself is ordinary host memory; host_pinned is still the caller's pool). Such
- * a context has no pinned staging buffers, so ula_append of more than 128
- * entries (256 under ULA_POLICY_LRU) or of host-resident rows, and ula_release, copy addresses and rows
- * from the caller's memory and wait for the copy before they return; the events
+ * a context has no pinned staging buffers: ula_append of more than 128 entries
+ * (256 under ULA_POLICY_LRU) runs in chunks whose addresses travel by value in
+ * the launches, host-resident rows are copied in and waited for chunk by chunk,
+ * and ula_release copies its addresses from the caller's memory and waits for
+ * that copy before it returns; the events
  * of step timing and of the ordering of host-link launches across streams are
  * created by the call that first needs them. Everything else behaves as for a
  * context from ula_init.
